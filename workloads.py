@@ -1,0 +1,132 @@
+"""Seeded synthetic inputs for the scaled_mm workloads.
+
+This module only draws random numbers and casts them to the storage types;
+it holds none of the quantization or GEMM arithmetic.  Both the CPU oracle
+(tests) and the HIP path (tests, bench) take their inputs from here, so both
+sides see the same bytes.
+
+Every array comes from ``numpy.random.default_rng([0, *key])`` (seed 0 for
+every workload), is drawn and scaled in float32 and is then cast once, with
+round-to-nearest-even, to bfloat16 by torch's CPU cast where a bf16 tensor is
+wanted.  Shapes follow the layouts of the library: activations A are [M][K]
+row-major, weights B are [N][K] row-major (the K x N operand stored
+column-major, as a linear layer keeps it).
+
+Workloads (the shapes of the pages' serving GEMMs: lm_head scale N=12288,
+MLP down-projection N=2048 K=6144, attention projection N=4096, a large
+vocabulary N=151936 and a square N=K=2048 weight):
+  W8A8 INT8    M=16, N=K=2048; int8 uniform in [-127, 127]; fp32 scales
+               uniform in [1e-3, 1e-2] per row of A and per row of B.
+  FP8 dynamic  (N, K) in {(4096, 2048), (2048, 6144)}, M in FP8_M; A bf16
+               N(0, 1) with round(0.01 K) outlier channels (the same columns in
+               every row) multiplied by 20; W bf16 N(0, 0.02).
+  Block-FP8    (N, K) in {(12288, 2048), (2048, 6144)}, M in BLOCK_M; A bf16
+               N(0, 1); W bf16 N(0, 0.02).
+  bf16 BI      (N, K) in {(2048, 2048), (4096, 2048)}, M in BI_M; A and B bf16
+               N(0, 1) / sqrt(K); each M uses the first M rows of a 2048-row A.
+  Vocab        N=151936, K=2048, M in VOCAB_M; A bf16 N(0, 1), W bf16
+               N(0, 0.02); both the bf16 and the FP8 path on the same data.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+INT8_SHAPE = (16, 2048, 2048)  # M, N, K
+FP8_SHAPES = [(4096, 2048), (2048, 6144)]  # (N, K)
+FP8_M = [1, 4, 8, 16, 32, 64, 256, 512, 1024, 2048]
+BLOCK_SHAPES = [(12288, 2048), (2048, 6144)]
+BLOCK_M = [1, 16, 64, 256, 2048]
+BI_SHAPES = [(2048, 2048), (4096, 2048)]
+BI_M = [1, 4, 8, 16, 32, 64, 256, 512, 1024, 2048]
+VOCAB_SHAPE = (151936, 2048)
+VOCAB_M = [1, 8, 64, 512, 2048]
+MAX_M = 2048
+
+# workload ids used in the seeds
+W_INT8, W_FP8, W_BLOCK, W_BI, W_VOCAB, W_TEST = 1, 2, 3, 4, 5, 9
+
+
+def rng(*key) -> np.random.Generator:
+    return np.random.default_rng([0, *[int(k) for k in key]])
+
+
+def to_bf16_bits(x32: np.ndarray) -> np.ndarray:
+    """float32 array -> bfloat16 bit patterns (uint16), one RNE cast by torch."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x32, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def int8_uniform(shape, key) -> np.ndarray:
+    """Integers uniform in [-127, 127] inclusive."""
+    return rng(*key).integers(-127, 128, size=shape, dtype=np.int8)
+
+
+def scales_uniform(n, key, lo=1e-3, hi=1e-2) -> np.ndarray:
+    return rng(*key).uniform(lo, hi, size=n).astype(np.float32)
+
+
+def normal_f32(shape, key, std=1.0) -> np.ndarray:
+    g = rng(*key)
+    x = g.standard_normal(size=shape, dtype=np.float32)
+    if std != 1.0:
+        x = x * np.float32(std)
+    return x
+
+
+def bf16_normal(shape, key, std=1.0, inv_sqrt_k=False, outlier_frac=0.0,
+                outlier_mult=20.0) -> np.ndarray:
+    """bf16 bits of N(0, std) (optionally / sqrt(K)), with an optional set of
+    outlier columns (round(outlier_frac * K) distinct columns, drawn without
+    replacement, the same for every row) multiplied by outlier_mult."""
+    x = normal_f32(shape, key, std)
+    K = shape[-1]
+    if inv_sqrt_k:
+        x = x / np.float32(np.sqrt(np.float32(K)))
+    if outlier_frac > 0.0:
+        n_out = int(round(outlier_frac * K))
+        cols = rng(*key, 1).choice(K, size=n_out, replace=False)
+        x[..., cols] *= np.float32(outlier_mult)
+    return to_bf16_bits(x)
+
+
+# --------------------------------------------------------------------------
+# Per-workload inputs
+# --------------------------------------------------------------------------
+
+def int8_inputs(M=16, N=2048, K=2048, key=(W_INT8,)):
+    """A int8 [M][K], B int8 [N][K], sa fp32 [M], sb fp32 [N]."""
+    return dict(A=int8_uniform((M, K), (*key, 0)),
+                B=int8_uniform((N, K), (*key, 1)),
+                sa=scales_uniform(M, (*key, 2)),
+                sb=scales_uniform(N, (*key, 3)))
+
+
+def fp8_activations(M, K, key=(W_FP8,)):
+    """bf16 activations with 1% outlier channels x20 (first M rows of a
+    MAX_M-row draw when M <= MAX_M, so every M shares its leading rows)."""
+    rows = max(M, MAX_M)
+    return bf16_normal((rows, K), (*key, K, 0), outlier_frac=0.01)[:M].copy()
+
+
+def weights_bf16(N, K, key=(W_FP8,), std=0.02):
+    return bf16_normal((N, K), (*key, N, K, 1), std=std)
+
+
+def block_activations(M, K, key=(W_BLOCK,)):
+    rows = max(M, MAX_M)
+    return bf16_normal((rows, K), (*key, K, 0))[:M].copy()
+
+
+def bi_inputs(N, K, key=(W_BI,)):
+    """A_full bf16 [2048][K] and B bf16 [N][K], both N(0,1)/sqrt(K)."""
+    return dict(A_full=bf16_normal((MAX_M, K), (*key, N, K, 0), inv_sqrt_k=True),
+                B=bf16_normal((N, K), (*key, N, K, 1), inv_sqrt_k=True))
+
+
+def vocab_activations(K=2048, key=(W_VOCAB,)):
+    return bf16_normal((MAX_M, K), (*key, K, 0))
+
+
+def vocab_weights(N=151936, K=2048, key=(W_VOCAB,)):
+    return bf16_normal((N, K), (*key, N, K, 1), std=0.02)
