@@ -1,0 +1,229 @@
+/*
+ * qll.h -- C ABI of libqll.so, the scaled_mm quantized linear-layer GEMM
+ * library for AMD Instinct MI355X (gfx950).
+ *
+ * Operations (all described by the page "Helion in vLLM: A Unified Route to
+ * Tunable Linear Kernels", section "What the integration changes", and by
+ * vLLM PR #53446 "Hopper (SM90) tuned config for batch-invariant persistent
+ * matmul", sections "Summary" and "Test Plan"):
+ *   quantize_per_token_fp8      FP8 dynamic (per-token / per-1x128) quantization
+ *   quantize_weight_block_fp8   128x128 Block-FP8 weight quantization (offline)
+ *   gemm_w8a8_int8              W8A8 INT8 GEMM, per-token x per-channel scales
+ *   gemm_fp8_scaled             FP8 GEMM, per-token x per-channel scales
+ *   gemm_block_fp8              Block-FP8 GEMM (1x128 and 128x128 scales)
+ *   gemm_bf16_batch_invariant   bf16 GEMM whose rows do not depend on M
+ * Each GEMM runs as an ordinary tiled GEMM, as Split-K or as Swap-AB (the
+ * three strategies of "What the integration changes"), chosen per (M, N, K)
+ * by a dispatch table that an on-device sweep fills, or forced with the _ex
+ * entry points.
+ *
+ * Conventions shared by every entry point
+ *   - Tensor arguments are DEVICE pointers, owned by the caller, dense and
+ *     row-major: activations A [M][K], weights B [N][K] (the K x N operand
+ *     stored column-major, as a linear layer keeps it), output [M][N].
+ *     A, B, q, x and out must be 16-byte aligned; scales 4-byte aligned.
+ *     Inputs and outputs must not overlap.
+ *   - e4m3 is the OCP FP8 E4M3 format (e4m3fn: bias 7, max 448, no inf).
+ *     Scales are fp32.  bf16 outputs are rounded to nearest even.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *     enqueues work on that stream: the library never allocates, frees or
+ *     synchronizes on these paths, so calls can be captured into HIP graphs.
+ *   - Arguments are validated before any HIP call; a launch failure reported
+ *     by hipGetLastError maps to QLL_ERR_HIP.  Faults inside a kernel surface
+ *     at the caller's next synchronization, as usual in HIP.  M == 0 is a
+ *     valid no-op.  No C++ exception crosses this interface.
+ *   - Split-K needs a caller-owned workspace of qll_workspace_bytes() bytes
+ *     (16-byte aligned); a smaller one returns QLL_ERR_WORKSPACE.  Split-K
+ *     partial sums are added in a fixed, ascending order by a second kernel
+ *     (no atomics), so results are deterministic run to run.
+ *   - After qll_init, calls are thread-safe; qll_init itself must not race
+ *     with other calls.
+ */
+#ifndef QLL_H
+#define QLL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    QLL_OK = 0,
+    QLL_ERR_INVALID_ARG = 1, /* null pointer, bad size, bad dtype, bad cfg */
+    QLL_ERR_UNSUPPORTED = 2, /* valid request this build does not implement */
+    QLL_ERR_MISALIGNED = 3,  /* pointer alignment below the stated minimum */
+    QLL_ERR_WORKSPACE = 4,   /* Split-K workspace missing or too small */
+    QLL_ERR_NO_DEVICE = 5,   /* no usable gfx950 device */
+    QLL_ERR_TABLE = 6,       /* dispatch table unreadable / for another device */
+    QLL_ERR_HIP = 7          /* a HIP runtime call or kernel launch failed */
+} qll_status;
+
+typedef enum {
+    QLL_OUT_BF16 = 0,
+    QLL_OUT_FP32 = 1,
+    QLL_OUT_INT32 = 2 /* gemm_w8a8_int8 only: the raw int32 accumulators */
+} qll_out;
+
+typedef enum {
+    QLL_OP_INT8 = 0,
+    QLL_OP_FP8 = 1,
+    QLL_OP_BLOCK_FP8 = 2,
+    QLL_OP_BF16_BI = 3
+} qll_op;
+
+/* A GEMM configuration: which registered kernel variant (tile shape, wave
+ * layout, ordinary or Swap-AB orientation) and how many K splits.  splits is
+ * the requested Split-K factor; the K range is cut into contiguous chunks of
+ * ceil(K_bytes / splits) rounded up to 512 bytes, so fewer splits may result
+ * (qll_effective_splits). */
+typedef struct {
+    int32_t variant; /* index into the op's variant registry */
+    int32_t splits;  /* >= 1 */
+} qll_cfg;
+
+/* ------------------------------------------------------------------ */
+/* Quantizers                                                          */
+/* ------------------------------------------------------------------ */
+
+/* FP8 dynamic activation quantization ("FP8 dynamic quantization", page
+ * "Helion in vLLM ...", section "What the integration changes").
+ * For each row m and each group g of `group` consecutive columns:
+ *   amax = max |x|;  s = amax / 448 (fp32);  q = e4m3_rne(clamp(x / s, +-448))
+ * (x / s is a correctly rounded fp32 division; an all-zero group gives s = 0
+ * and zero codes; the sign of a value that rounds to zero is kept).
+ *   x      bf16 [M][K] (in)
+ *   q      e4m3 [M][K] (out)
+ *   scales fp32 [M][K/group] (out)
+ *   group  0 or K: one scale per row (per token); 128: one per 1x128 group.
+ *   K      multiple of 16 (of 128 for group 128).
+ * Non-finite inputs give unspecified codes. */
+int quantize_per_token_fp8(const void* x, void* q, float* scales, int64_t M,
+                           int64_t K, int64_t group, void* stream);
+
+/* Block-FP8 weight quantization, one scale per 128 x 128 block of the [N][K]
+ * weight ("Block-FP8", same section), with the same rule as above applied to
+ * each block.  w bf16 [N][K] (in); q e4m3 [N][K] (out);
+ * scales fp32 [ceil(N/128)][K/128] (out).  K must be a multiple of 128; a
+ * last partial block of rows is allowed.  Weight preparation, not the hot
+ * path, but kept on the device like everything else. */
+int quantize_weight_block_fp8(const void* w, void* q, float* scales, int64_t N,
+                              int64_t K, void* stream);
+
+/* ------------------------------------------------------------------ */
+/* GEMMs                                                               */
+/* ------------------------------------------------------------------ */
+
+/* W8A8 INT8 ("W8A8 INT8", same section):
+ *   acc[m][n] = sum_k A[m][k] * B[n][k]            (exact int32)
+ *   out = bf16_rne((float(acc) * sa[m]) * sb[n])   (two fp32 multiplies)
+ *   or the fp32 value (QLL_OUT_FP32) or acc itself (QLL_OUT_INT32).
+ *   A int8 [M][K]; B int8 [N][K]; sa fp32 [M]; sb fp32 [N].
+ *   K multiple of 16 and at most 131071 (int32 accumulators cannot overflow). */
+int gemm_w8a8_int8(const void* A, const void* B, const float* sa,
+                   const float* sb, void* out, int out_dtype, int64_t M,
+                   int64_t N, int64_t K, void* ws, size_t ws_bytes,
+                   void* stream);
+
+/* FP8 with per-token x per-channel scales ("FP8 dynamic quantization"):
+ *   out = bf16_rne((acc * sa[m]) * sb[n]), acc = sum_k A[m][k] * B[n][k]
+ *   accumulated in fp32 on the matrix cores.
+ *   A e4m3 [M][K] (e.g. from quantize_per_token_fp8); B e4m3 [N][K];
+ *   sa fp32 [M]; sb fp32 [N]; out bf16 or fp32; K multiple of 16. */
+int gemm_fp8_scaled(const void* A, const void* B, const float* sa,
+                    const float* sb, void* out, int out_dtype, int64_t M,
+                    int64_t N, int64_t K, void* ws, size_t ws_bytes,
+                    void* stream);
+
+/* Block-FP8 ("Block-FP8"): for each 128-wide K group g
+ *   P_g = sum_{k in g} A[m][k] * B[n][k]  (fp32, matrix cores)
+ *   acc += (sa[m][g] * sb[n/128][g]) * P_g
+ *   out = bf16_rne(acc) (or fp32).
+ *   A e4m3 [M][K]; B e4m3 [N][K]; sa fp32 [M][K/128]; sb fp32
+ *   [ceil(N/128)][K/128]; K multiple of 128. */
+int gemm_block_fp8(const void* A, const void* B, const float* sa,
+                   const float* sb, void* out, int out_dtype, int64_t M,
+                   int64_t N, int64_t K, void* ws, size_t ws_bytes,
+                   void* stream);
+
+/* Batch-invariant bf16 GEMM (vLLM PR #53446, "Summary" and "Test Plan"):
+ *   out = bf16_rne(sum_k A[m][k] * B[n][k]) (or fp32), fp32 accumulation.
+ * Row m of the output depends only on row m of A, on B and on (N, K): the
+ * matrix-core instruction, the K order and the Split-K boundaries used are a
+ * function of (N, K) alone, so row m is bitwise identical for every M.
+ *   A bf16 [M][K]; B bf16 [N][K]; K multiple of 8. */
+int gemm_bf16_batch_invariant(const void* A, const void* B, void* out,
+                              int out_dtype, int64_t M, int64_t N, int64_t K,
+                              void* ws, size_t ws_bytes, void* stream);
+
+/* The same five GEMMs with a forced configuration (the sweep and the tests
+ * use these).  cfg == NULL behaves like the plain entry point.  For the
+ * batch-invariant entry a forced cfg is the caller's responsibility: only
+ * the table / heuristic choice is guaranteed M-independent. */
+int gemm_w8a8_int8_ex(const void* A, const void* B, const float* sa,
+                      const float* sb, void* out, int out_dtype, int64_t M,
+                      int64_t N, int64_t K, void* ws, size_t ws_bytes,
+                      void* stream, const qll_cfg* cfg);
+int gemm_fp8_scaled_ex(const void* A, const void* B, const float* sa,
+                       const float* sb, void* out, int out_dtype, int64_t M,
+                       int64_t N, int64_t K, void* ws, size_t ws_bytes,
+                       void* stream, const qll_cfg* cfg);
+int gemm_block_fp8_ex(const void* A, const void* B, const float* sa,
+                      const float* sb, void* out, int out_dtype, int64_t M,
+                      int64_t N, int64_t K, void* ws, size_t ws_bytes,
+                      void* stream, const qll_cfg* cfg);
+int gemm_bf16_batch_invariant_ex(const void* A, const void* B, void* out,
+                                 int out_dtype, int64_t M, int64_t N,
+                                 int64_t K, void* ws, size_t ws_bytes,
+                                 void* stream, const qll_cfg* cfg);
+
+/* ------------------------------------------------------------------ */
+/* Dispatch, registry and support                                      */
+/* ------------------------------------------------------------------ */
+
+/* Load the dispatch table (per-shape tuning, "What the integration changes").
+ * table_path NULL: $QLL_TABLE if set, else no table (built-in heuristic).
+ * A table whose device line does not match the current device (gfx arch and
+ * CU count) is not used: QLL_ERR_TABLE is returned and the heuristic stays in
+ * force.  A batch-invariant section whose Split-K factor or orientation varies
+ * with M for one (N, K) is rejected the same way.  Without a device the call
+ * returns QLL_ERR_NO_DEVICE. */
+int qll_init(const char* table_path);
+
+/* Parse and check a dispatch table against a device signature (gfx arch name
+ * and CU count) without installing it; no device needed.  Returns QLL_OK or
+ * QLL_ERR_TABLE with a reason in err (NUL-terminated, truncated to cap). */
+int qll_table_validate(const char* path, const char* arch, int cus, char* err,
+                       size_t cap);
+
+/* The configuration the entry point would use for this shape (table entry if
+ * one exists, else the heuristic). */
+int qll_select(int op, int64_t M, int64_t N, int64_t K, qll_cfg* cfg_out);
+
+/* Workspace bytes the op needs for this shape: with cfg == NULL for the
+ * configuration qll_select picks, else for cfg.  Returns 0 when no Split-K is
+ * involved, a negative value (-status) for invalid arguments. */
+int64_t qll_workspace_bytes(int op, int64_t M, int64_t N, int64_t K,
+                            const qll_cfg* cfg);
+
+/* Number of K splits actually used for (op, K, cfg->splits). */
+int qll_effective_splits(int op, int64_t K, int32_t splits);
+
+/* Registered kernel variants of an op.  qll_variant_info writes a one-line
+ * JSON description (name, orientation, tile, waves, K stage, LDS bytes) into
+ * buf (NUL-terminated, truncated to cap) and returns QLL_OK. */
+int qll_num_variants(int op);
+int qll_variant_info(int op, int idx, char* buf, size_t cap);
+int qll_variant_index(int op, const char* name);
+
+/* Number of table entries in force (0 = heuristic only). */
+int qll_table_entries(void);
+
+const char* qll_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLL_H */

@@ -1,0 +1,643 @@
+// C ABI of libqll.so: argument validation, the per-shape dispatch table with
+// its heuristic fallback, and the launches.  Declarations and the contract of
+// every entry point are in include/qll.h.
+//
+// Dispatch follows "Helion in vLLM: A Unified Route to Tunable Linear
+// Kernels", section "What the integration changes": the algorithm (ordinary,
+// Split-K, Swap-AB) is chosen per shape together with its tile configuration,
+// from a table an offline on-device search fills, with a fixed rule for the
+// shapes the table does not cover.  As in vLLM PR #53446 (the per-device
+// configuration keys of its review), a table is used only on the device it
+// was measured on.  The lookup happens on the host in O(1), with no
+// allocation, no synchronization and no HIP call before the launch.
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "../../include/qll.h"
+#include "qll_internal.h"
+
+namespace qll {
+
+extern const Variant kVariantsInt8[];
+extern const int kNumVariantsInt8;
+extern const Variant kVariantsFp8[];
+extern const int kNumVariantsFp8;
+extern const Variant kVariantsBlock[];
+extern const int kNumVariantsBlock;
+extern const Variant kVariantsBf16[];
+extern const int kNumVariantsBf16;
+hipError_t launch_reduce_int8(const GemmArgs&, hipStream_t);
+hipError_t launch_reduce_fp8(const GemmArgs&, hipStream_t);
+hipError_t launch_reduce_block(const GemmArgs&, hipStream_t);
+hipError_t launch_reduce_bf16(const GemmArgs&, hipStream_t);
+
+const Variant* variants(int op, int* count)
+{
+    switch (op) {
+    case OP_INT8: *count = kNumVariantsInt8; return kVariantsInt8;
+    case OP_FP8: *count = kNumVariantsFp8; return kVariantsFp8;
+    case OP_BLOCK: *count = kNumVariantsBlock; return kVariantsBlock;
+    case OP_BF16: *count = kNumVariantsBf16; return kVariantsBf16;
+    default: *count = 0; return nullptr;
+    }
+}
+
+hipError_t launch_splitk_reduce(int op, const GemmArgs& a, hipStream_t stream)
+{
+    switch (op) {
+    case OP_INT8: return launch_reduce_int8(a, stream);
+    case OP_FP8: return launch_reduce_fp8(a, stream);
+    case OP_BLOCK: return launch_reduce_block(a, stream);
+    default: return launch_reduce_bf16(a, stream);
+    }
+}
+
+namespace {
+
+const char* const kOpNames[OP_COUNT] = {"int8", "fp8", "block_fp8", "bf16_bi"};
+
+int op_esz(int op) { return op == OP_BF16 ? 2 : 1; }
+
+// ------------------------------------------------------------------ device
+struct DeviceInfo {
+    bool ok = false;
+    int cus = 256;
+    char arch[64] = {0};
+};
+
+DeviceInfo& device_info()
+{
+    static DeviceInfo info;
+    static std::once_flag once;
+    std::call_once(once, [] {
+        int n = 0;
+        if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) {
+            (void)hipGetLastError();
+            return;
+        }
+        int dev = 0;
+        hipDeviceProp_t p;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipGetDeviceProperties(&p, dev) != hipSuccess) {
+            (void)hipGetLastError();
+            return;
+        }
+        info.cus = p.multiProcessorCount;
+        std::snprintf(info.arch, sizeof info.arch, "%s", p.gcnArchName);
+        char* colon = std::strchr(info.arch, ':');
+        if (colon)
+            *colon = 0;
+        info.ok = std::strcmp(info.arch, "gfx950") == 0;
+    });
+    return info;
+}
+
+// ------------------------------------------------------------------ table
+int bucket_of(int64_t M)
+{
+    int b = 1;
+    while (b < M && b < 4096)
+        b <<= 1;
+    return b;
+}
+
+uint64_t table_key(int op, int64_t N, int64_t K, int bucket)
+{
+    return ((uint64_t)op << 60) ^ ((uint64_t)(N & 0xFFFFFF) << 36) ^
+           ((uint64_t)(K & 0xFFFFFF) << 12) ^ (uint64_t)bucket;
+}
+
+uint64_t shape_key(int op, int64_t N, int64_t K) { return table_key(op, N, K, 0); }
+
+struct Table {
+    std::unordered_map<uint64_t, qll_cfg> entries;
+    // batch-invariant: the Split-K factor and orientation fixed per (N, K)
+    std::unordered_map<uint64_t, std::pair<int, int>> bi_fixed;
+};
+
+Table* g_table = nullptr;  // replaced only by qll_init
+
+int find_variant(int op, const char* name)
+{
+    int n = 0;
+    const Variant* v = variants(op, &n);
+    for (int i = 0; i < n; ++i)
+        if (std::strcmp(v[i].name, name) == 0)
+            return i;
+    return -1;
+}
+
+int effective_splits(int op, int64_t K, int splits)
+{
+    const int64_t kbytes = K * op_esz(op);
+    if (splits <= 1)
+        return 1;
+    int64_t chunk = (kbytes + splits - 1) / splits;
+    chunk = (chunk + kSplitGranule - 1) / kSplitGranule * kSplitGranule;
+    return (int)((kbytes + chunk - 1) / chunk);
+}
+
+int64_t split_chunk(int op, int64_t K, int splits)
+{
+    const int64_t kbytes = K * op_esz(op);
+    if (splits <= 1)
+        return kbytes;
+    int64_t chunk = (kbytes + splits - 1) / splits;
+    return (chunk + kSplitGranule - 1) / kSplitGranule * kSplitGranule;
+}
+
+int load_table(const char* path, const char* arch, int cus_want, Table** out,
+               std::string* err)
+{
+    FILE* f = std::fopen(path, "r");
+    if (!f) {
+        *err = "cannot open table";
+        return QLL_ERR_TABLE;
+    }
+    Table* t = new Table;
+    char line[512];
+    bool device_ok = false, device_seen = false;
+    int rc = QLL_OK;
+    std::unordered_map<uint64_t, std::pair<int, int>> bi_seen;
+    while (std::fgets(line, sizeof line, f)) {
+        char* p = line;
+        while (*p == ' ' || *p == '\t')
+            ++p;
+        if (*p == '#' || *p == '\n' || *p == 0)
+            continue;
+        char a0[64], a1[128], a2[64];
+        if (std::strncmp(p, "device", 6) == 0) {
+            int cus = 0;
+            if (std::sscanf(p, "%63s %127s %d", a0, a1, &cus) != 3) {
+                rc = QLL_ERR_TABLE;
+                *err = "bad device line";
+                break;
+            }
+            device_seen = true;
+            device_ok = std::strcmp(a1, arch) == 0 && cus == cus_want;
+            continue;
+        }
+        long long N = 0, K = 0;
+        int bucket = 0, splits = 0;
+        if (std::sscanf(p, "%63s %lld %lld %d %63s %d", a0, &N, &K, &bucket, a2,
+                        &splits) != 6) {
+            rc = QLL_ERR_TABLE;
+            *err = std::string("bad entry: ") + p;
+            break;
+        }
+        int op = -1;
+        for (int i = 0; i < OP_COUNT; ++i)
+            if (std::strcmp(a0, kOpNames[i]) == 0)
+                op = i;
+        const int vi = op >= 0 ? find_variant(op, a2) : -1;
+        if (op < 0 || vi < 0 || splits < 1 || splits > kMaxSplits || N <= 0 ||
+            K <= 0 || bucket < 1 || bucket > 4096 || (bucket & (bucket - 1))) {
+            rc = QLL_ERR_TABLE;
+            *err = std::string("bad entry: ") + p;
+            break;
+        }
+        const int seff = effective_splits(op, K, splits);
+        if (op == OP_BF16) {
+            int n = 0;
+            const Variant* v = variants(op, &n);
+            const std::pair<int, int> fx(seff, v[vi].swap);
+            auto it = bi_seen.find(shape_key(op, N, K));
+            if (it == bi_seen.end()) {
+                bi_seen.emplace(shape_key(op, N, K), fx);
+            } else if (it->second != fx) {
+                rc = QLL_ERR_TABLE;
+                *err = "batch-invariant entries vary the K split or orientation with M";
+                break;
+            }
+        }
+        t->entries[table_key(op, N, K, bucket)] = qll_cfg{vi, splits};
+    }
+    std::fclose(f);
+    if (rc == QLL_OK && (!device_seen || !device_ok)) {
+        rc = QLL_ERR_TABLE;
+        *err = "table was measured on another device";
+    }
+    if (rc != QLL_OK || !out) {
+        delete t;
+        return rc;
+    }
+    t->bi_fixed = std::move(bi_seen);
+    *out = t;
+    return QLL_OK;
+}
+
+// ------------------------------------------------------------------ heuristic
+// Used when the table has no entry.  Small M: Swap-AB (weights on the MFMA row
+// side) and, for the ordinary ops, Split-K until the grid has about two
+// workgroups per CU; large M: big ordinary tiles.  The batch-invariant op
+// never splits K here and always uses the ordinary orientation.
+qll_cfg heuristic(int op, int64_t M, int64_t N, int64_t K)
+{
+    const int cus = device_info().cus;
+    const char* name;
+    if (op == OP_BF16 && M <= 128)
+        name = M <= 16 ? "n16x64_w1x4_k" : (M <= 32 ? "n32x128_w1x4_k" : "n64x128_w2x2_k");
+    else if (M <= 16)
+        name = N >= 8192 ? "s256x16_w4x1_k" : (N >= 2048 ? "s128x16_w4x1_k" : "s64x16_w4x1_k");
+    else if (M <= 32)
+        name = "s128x32_w4x1_k";
+    else if (M <= 64)
+        name = "s128x64_w2x2_k";
+    else if (M <= 128)
+        name = "n64x128_w2x2_k";
+    else if (M * N >= (int64_t)cus * 4 * 128 * 256)
+        name = "n128x256_w2x2_k";
+    else
+        name = "n128x128_w2x2_k";
+    // complete the name with the K stage the registry has for it
+    int n = 0;
+    const Variant* v = variants(op, &n);
+    int vi = 0;
+    for (int i = 0; i < n; ++i)
+        if (std::strncmp(v[i].name, name, std::strlen(name)) == 0) {
+            vi = i;
+            break;
+        }
+    if (op == OP_BF16)
+        return qll_cfg{vi, 1};
+    const int64_t tiles = ((v[vi].swap ? N : M) + v[vi].bp - 1) / v[vi].bp *
+                          (((v[vi].swap ? M : N) + v[vi].bq - 1) / v[vi].bq);
+    const int64_t kbytes = K * op_esz(op);
+    int s = 1;
+    while (tiles * s < 2 * cus && (int64_t)s * 2 * 1024 <= kbytes && s < 16)
+        s *= 2;
+    return qll_cfg{vi, s};
+}
+
+qll_cfg select_cfg(int op, int64_t M, int64_t N, int64_t K)
+{
+    Table* t = g_table;
+    if (t) {
+        auto it = t->entries.find(table_key(op, N, K, bucket_of(M)));
+        if (it != t->entries.end())
+            return it->second;
+        if (op == OP_BF16) {
+            // a covered (N, K) keeps its table's split and orientation at
+            // every M
+            auto fx = t->bi_fixed.find(shape_key(op, N, K));
+            if (fx != t->bi_fixed.end()) {
+                qll_cfg c = heuristic(op, M, N, K);
+                int n = 0;
+                const Variant* v = variants(op, &n);
+                if (v[c.variant].swap != fx->second.second) {
+                    const char* alt = fx->second.second ? "s128x16_w4x1_k" : "n128x128_w2x2_k";
+                    for (int i = 0; i < n; ++i)
+                        if (std::strncmp(v[i].name, alt, std::strlen(alt)) == 0)
+                            c.variant = i;
+                }
+                // the table stores the requested split; recover one that
+                // yields the same effective split
+                c.splits = fx->second.first;
+                return c;
+            }
+        }
+    }
+    return heuristic(op, M, N, K);
+}
+
+// ------------------------------------------------------------------ validation
+bool misaligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) != 0; }
+
+int validate_gemm(int op, const void* A, const void* B, const float* sa,
+                  const float* sb, const void* out, int out_dtype, int64_t M,
+                  int64_t N, int64_t K)
+{
+    if (M < 0 || N <= 0 || K <= 0)
+        return QLL_ERR_INVALID_ARG;
+    if (M > 0x7FFFFFFF || N > 0x7FFFFFFF || K > 0x3FFFFFFF)
+        return QLL_ERR_INVALID_ARG;
+    if (M * K > ((int64_t)1 << 40) || N * K > ((int64_t)1 << 40) ||
+        M * N > ((int64_t)1 << 40))
+        return QLL_ERR_INVALID_ARG;
+    if (out_dtype != QLL_OUT_BF16 && out_dtype != QLL_OUT_FP32 &&
+        !(out_dtype == QLL_OUT_INT32 && op == OP_INT8))
+        return QLL_ERR_INVALID_ARG;
+    if (op == OP_BF16) {
+        if (K % 8)
+            return QLL_ERR_INVALID_ARG;
+    } else if (op == OP_BLOCK) {
+        if (K % 128)
+            return QLL_ERR_INVALID_ARG;
+    } else if (K % 16) {
+        return QLL_ERR_INVALID_ARG;
+    }
+    if (op == OP_INT8 && K > 131071)
+        return QLL_ERR_INVALID_ARG;
+    if (M == 0)
+        return QLL_OK;
+    if (!A || !B || !out || (op != OP_BF16 && (!sa || !sb)))
+        return QLL_ERR_INVALID_ARG;
+    if (misaligned(A, 16) || misaligned(B, 16) || misaligned(out, 16))
+        return QLL_ERR_MISALIGNED;
+    if (op != OP_BF16 && (misaligned(sa, 4) || misaligned(sb, 4)))
+        return QLL_ERR_MISALIGNED;
+    return QLL_OK;
+}
+
+int validate_cfg(int op, const qll_cfg* c)
+{
+    int n = 0;
+    variants(op, &n);
+    if (c->variant < 0 || c->variant >= n || c->splits < 1 || c->splits > kMaxSplits)
+        return QLL_ERR_INVALID_ARG;
+    return QLL_OK;
+}
+
+int run_gemm(int op, const void* A, const void* B, const float* sa,
+             const float* sb, void* out, int out_dtype, int64_t M, int64_t N,
+             int64_t K, void* ws, size_t ws_bytes, void* stream,
+             const qll_cfg* forced)
+{
+    int rc = validate_gemm(op, A, B, sa, sb, out, out_dtype, M, N, K);
+    if (rc != QLL_OK)
+        return rc;
+    if (forced && (rc = validate_cfg(op, forced)) != QLL_OK)
+        return rc;
+    if (M == 0)
+        return QLL_OK;
+    const qll_cfg cfg = forced ? *forced : select_cfg(op, M, N, K);
+    int nv = 0;
+    const Variant* vs = variants(op, &nv);
+    const Variant& v = vs[cfg.variant];
+    GemmArgs a;
+    a.A = A;
+    a.B = B;
+    a.sa = sa;
+    a.sb = sb;
+    a.out = out;
+    a.ws = ws;
+    a.out_dtype = out_dtype;
+    a.M = (int)M;
+    a.N = (int)N;
+    a.K = (int)K;
+    a.kbytes = (int)(K * op_esz(op));
+    a.splits = effective_splits(op, K, cfg.splits);
+    a.kchunk = (int)split_chunk(op, K, cfg.splits);
+    if (a.splits > 1) {
+        const uint64_t need = (uint64_t)a.splits * M * N * 4;
+        if (!ws || ws_bytes < need)
+            return QLL_ERR_WORKSPACE;
+        if (misaligned(ws, 16))
+            return QLL_ERR_MISALIGNED;
+    }
+    hipStream_t s = (hipStream_t)stream;
+    if (v.launch(a, s) != hipSuccess)
+        return QLL_ERR_HIP;
+    if (a.splits > 1 && launch_splitk_reduce(op, a, s) != hipSuccess)
+        return QLL_ERR_HIP;
+    return QLL_OK;
+}
+
+}  // namespace
+}  // namespace qll
+
+using namespace qll;
+
+extern "C" {
+
+int quantize_per_token_fp8(const void* x, void* q, float* scales, int64_t M,
+                           int64_t K, int64_t group, void* stream)
+{
+    if (M < 0 || K <= 0 || K % 16 || M > 0x7FFFFFFF || K > 0x3FFFFFFF ||
+        M * K > ((int64_t)1 << 40))
+        return QLL_ERR_INVALID_ARG;
+    const bool per_token = group == 0 || group == K;
+    if (!per_token && group != 128)
+        return QLL_ERR_UNSUPPORTED;
+    if (!per_token && K % 128)
+        return QLL_ERR_INVALID_ARG;
+    if (M == 0)
+        return QLL_OK;
+    if (!x || !q || !scales)
+        return QLL_ERR_INVALID_ARG;
+    if (misaligned(x, 16) || misaligned(q, 16) || misaligned(scales, 4))
+        return QLL_ERR_MISALIGNED;
+    hipError_t e = per_token
+                       ? launch_quant_rows(x, q, scales, (int)M, (int)K, (hipStream_t)stream)
+                       : launch_quant_groups128(x, q, scales, (int)M, (int)K,
+                                                (hipStream_t)stream);
+    return e == hipSuccess ? QLL_OK : QLL_ERR_HIP;
+}
+
+int quantize_weight_block_fp8(const void* w, void* q, float* scales, int64_t N,
+                              int64_t K, void* stream)
+{
+    if (N < 0 || K <= 0 || K % 128 || N > 0x7FFFFFFF || K > 0x3FFFFFFF ||
+        N * K > ((int64_t)1 << 40))
+        return QLL_ERR_INVALID_ARG;
+    if (N == 0)
+        return QLL_OK;
+    if (!w || !q || !scales)
+        return QLL_ERR_INVALID_ARG;
+    if (misaligned(w, 16) || misaligned(q, 16) || misaligned(scales, 4))
+        return QLL_ERR_MISALIGNED;
+    if ((N + 127) / 128 > 0x7FFFFFFF || K / 128 > 65535)
+        return QLL_ERR_INVALID_ARG;
+    hipError_t e = launch_quant_weight_blocks(w, q, scales, (int)N, (int)K,
+                                              (hipStream_t)stream);
+    return e == hipSuccess ? QLL_OK : QLL_ERR_HIP;
+}
+
+int gemm_w8a8_int8_ex(const void* A, const void* B, const float* sa,
+                      const float* sb, void* out, int out_dtype, int64_t M,
+                      int64_t N, int64_t K, void* ws, size_t ws_bytes,
+                      void* stream, const qll_cfg* cfg)
+{
+    return run_gemm(OP_INT8, A, B, sa, sb, out, out_dtype, M, N, K, ws,
+                    ws_bytes, stream, cfg);
+}
+
+int gemm_fp8_scaled_ex(const void* A, const void* B, const float* sa,
+                       const float* sb, void* out, int out_dtype, int64_t M,
+                       int64_t N, int64_t K, void* ws, size_t ws_bytes,
+                       void* stream, const qll_cfg* cfg)
+{
+    return run_gemm(OP_FP8, A, B, sa, sb, out, out_dtype, M, N, K, ws, ws_bytes,
+                    stream, cfg);
+}
+
+int gemm_block_fp8_ex(const void* A, const void* B, const float* sa,
+                      const float* sb, void* out, int out_dtype, int64_t M,
+                      int64_t N, int64_t K, void* ws, size_t ws_bytes,
+                      void* stream, const qll_cfg* cfg)
+{
+    return run_gemm(OP_BLOCK, A, B, sa, sb, out, out_dtype, M, N, K, ws,
+                    ws_bytes, stream, cfg);
+}
+
+int gemm_bf16_batch_invariant_ex(const void* A, const void* B, void* out,
+                                 int out_dtype, int64_t M, int64_t N, int64_t K,
+                                 void* ws, size_t ws_bytes, void* stream,
+                                 const qll_cfg* cfg)
+{
+    return run_gemm(OP_BF16, A, B, nullptr, nullptr, out, out_dtype, M, N, K,
+                    ws, ws_bytes, stream, cfg);
+}
+
+int gemm_w8a8_int8(const void* A, const void* B, const float* sa,
+                   const float* sb, void* out, int out_dtype, int64_t M,
+                   int64_t N, int64_t K, void* ws, size_t ws_bytes, void* stream)
+{
+    return run_gemm(OP_INT8, A, B, sa, sb, out, out_dtype, M, N, K, ws,
+                    ws_bytes, stream, nullptr);
+}
+
+int gemm_fp8_scaled(const void* A, const void* B, const float* sa,
+                    const float* sb, void* out, int out_dtype, int64_t M,
+                    int64_t N, int64_t K, void* ws, size_t ws_bytes, void* stream)
+{
+    return run_gemm(OP_FP8, A, B, sa, sb, out, out_dtype, M, N, K, ws, ws_bytes,
+                    stream, nullptr);
+}
+
+int gemm_block_fp8(const void* A, const void* B, const float* sa,
+                   const float* sb, void* out, int out_dtype, int64_t M,
+                   int64_t N, int64_t K, void* ws, size_t ws_bytes, void* stream)
+{
+    return run_gemm(OP_BLOCK, A, B, sa, sb, out, out_dtype, M, N, K, ws,
+                    ws_bytes, stream, nullptr);
+}
+
+int gemm_bf16_batch_invariant(const void* A, const void* B, void* out,
+                              int out_dtype, int64_t M, int64_t N, int64_t K,
+                              void* ws, size_t ws_bytes, void* stream)
+{
+    return run_gemm(OP_BF16, A, B, nullptr, nullptr, out, out_dtype, M, N, K,
+                    ws, ws_bytes, stream, nullptr);
+}
+
+int qll_init(const char* table_path)
+{
+    const char* path = table_path;
+    if (!path || !*path)
+        path = std::getenv("QLL_TABLE");
+    if (!device_info().ok) {
+        int n = 0;
+        if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) {
+            (void)hipGetLastError();
+            return QLL_ERR_NO_DEVICE;
+        }
+        return QLL_ERR_NO_DEVICE;
+    }
+    if (!path || !*path) {
+        g_table = nullptr;  // an old table stays allocated: calls may race
+        return QLL_OK;
+    }
+    Table* t = nullptr;
+    std::string err;
+    const DeviceInfo& dev = device_info();
+    int rc = load_table(path, dev.arch, dev.cus, &t, &err);
+    if (rc != QLL_OK) {
+        if (std::getenv("QLL_LOG"))
+            std::fprintf(stderr, "qll: table %s not used: %s\n", path, err.c_str());
+        g_table = nullptr;
+        return rc;
+    }
+    g_table = t;
+    if (std::getenv("QLL_LOG"))
+        std::fprintf(stderr, "qll: table %s: %zu entries\n", path, t->entries.size());
+    return QLL_OK;
+}
+
+int qll_table_validate(const char* path, const char* arch, int cus, char* err,
+                       size_t cap)
+{
+    if (!path || !arch)
+        return QLL_ERR_INVALID_ARG;
+    std::string e;
+    const int rc = load_table(path, arch, cus, nullptr, &e);
+    if (err && cap)
+        std::snprintf(err, cap, "%s", e.c_str());
+    return rc;
+}
+
+int qll_select(int op, int64_t M, int64_t N, int64_t K, qll_cfg* cfg_out)
+{
+    if (op < 0 || op >= OP_COUNT || M < 0 || N <= 0 || K <= 0 || !cfg_out)
+        return QLL_ERR_INVALID_ARG;
+    *cfg_out = select_cfg(op, M, N, K);
+    return QLL_OK;
+}
+
+int64_t qll_workspace_bytes(int op, int64_t M, int64_t N, int64_t K,
+                            const qll_cfg* cfg)
+{
+    if (op < 0 || op >= OP_COUNT || M < 0 || N <= 0 || K <= 0)
+        return -QLL_ERR_INVALID_ARG;
+    qll_cfg c = cfg ? *cfg : select_cfg(op, M, N, K);
+    if (validate_cfg(op, &c) != QLL_OK)
+        return -QLL_ERR_INVALID_ARG;
+    const int s = effective_splits(op, K, c.splits);
+    return s > 1 ? (int64_t)s * M * N * 4 : 0;
+}
+
+int qll_effective_splits(int op, int64_t K, int32_t splits)
+{
+    if (op < 0 || op >= OP_COUNT || K <= 0 || splits < 1)
+        return -QLL_ERR_INVALID_ARG;
+    return effective_splits(op, K, splits);
+}
+
+int qll_num_variants(int op)
+{
+    int n = 0;
+    variants(op, &n);
+    return n;
+}
+
+int qll_variant_info(int op, int idx, char* buf, size_t cap)
+{
+    int n = 0;
+    const Variant* v = variants(op, &n);
+    if (idx < 0 || idx >= n || !buf || cap == 0)
+        return QLL_ERR_INVALID_ARG;
+    std::snprintf(buf, cap,
+                  "{\"name\": \"%s\", \"op\": \"%s\", \"swap\": %d, \"bp\": %d, "
+                  "\"bq\": %d, \"wp\": %d, \"wq\": %d, \"kstage\": %d, \"lds\": %d}",
+                  v[idx].name, kOpNames[op], v[idx].swap, v[idx].bp, v[idx].bq,
+                  v[idx].wp, v[idx].wq, v[idx].kstage, v[idx].lds);
+    return QLL_OK;
+}
+
+int qll_variant_index(int op, const char* name)
+{
+    if (op < 0 || op >= OP_COUNT || !name)
+        return -QLL_ERR_INVALID_ARG;
+    return find_variant(op, name);
+}
+
+int qll_table_entries(void)
+{
+    Table* t = g_table;
+    return t ? (int)t->entries.size() : 0;
+}
+
+const char* qll_status_str(int status)
+{
+    switch (status) {
+    case QLL_OK: return "ok";
+    case QLL_ERR_INVALID_ARG: return "invalid argument";
+    case QLL_ERR_UNSUPPORTED: return "unsupported";
+    case QLL_ERR_MISALIGNED: return "misaligned pointer";
+    case QLL_ERR_WORKSPACE: return "workspace missing or too small";
+    case QLL_ERR_NO_DEVICE: return "no gfx950 device";
+    case QLL_ERR_TABLE: return "dispatch table not usable";
+    case QLL_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+    }
+}
+
+}  // extern "C"

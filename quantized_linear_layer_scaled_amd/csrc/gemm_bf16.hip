@@ -1,0 +1,21 @@
+// Kernel instantiations and variant registry of the bf16 GEMM.
+#include "gemm_tile.h"
+#include "variant_list.h"
+
+QLL_FOR_EACH_VARIANT(QLL_INSTANTIATE, qll::OP_BF16, 256, 128)
+template __global__ void qll::splitk_reduce_kernel<qll::OP_BF16>(qll::GemmArgs);
+
+namespace qll {
+
+// host-side registry (the device pass only needs the kernels above)
+#if !defined(__HIP_DEVICE_COMPILE__)
+extern const Variant kVariantsBf16[] = {QLL_FOR_EACH_VARIANT(QLL_ENTRY, OP_BF16, 256, 128)};
+extern const int kNumVariantsBf16 = sizeof(kVariantsBf16) / sizeof(Variant);
+#endif
+
+hipError_t launch_reduce_bf16(const GemmArgs& a, hipStream_t stream)
+{
+    return launch_reduce<OP_BF16>(a, stream);
+}
+
+}  // namespace qll

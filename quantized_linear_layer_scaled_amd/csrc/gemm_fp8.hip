@@ -1,0 +1,21 @@
+// Kernel instantiations and variant registry of the fp8 GEMM.
+#include "gemm_tile.h"
+#include "variant_list.h"
+
+QLL_FOR_EACH_VARIANT(QLL_INSTANTIATE, qll::OP_FP8, 256, 128)
+template __global__ void qll::splitk_reduce_kernel<qll::OP_FP8>(qll::GemmArgs);
+
+namespace qll {
+
+// host-side registry (the device pass only needs the kernels above)
+#if !defined(__HIP_DEVICE_COMPILE__)
+extern const Variant kVariantsFp8[] = {QLL_FOR_EACH_VARIANT(QLL_ENTRY, OP_FP8, 256, 128)};
+extern const int kNumVariantsFp8 = sizeof(kVariantsFp8) / sizeof(Variant);
+#endif
+
+hipError_t launch_reduce_fp8(const GemmArgs& a, hipStream_t stream)
+{
+    return launch_reduce<OP_FP8>(a, stream);
+}
+
+}  // namespace qll

@@ -1,0 +1,406 @@
+// Tiled scaled GEMM for gfx950: one kernel template behind every GEMM of the
+// library (W8A8 INT8, FP8 per-token x per-channel, Block-FP8, bf16), in the
+// ordinary orientation or as Swap-AB, with or without Split-K.  These are the
+// strategies of "Helion in vLLM: A Unified Route to Tunable Linear Kernels",
+// section "What the integration changes".
+//
+// Design (CDNA4):
+//   * Both operands are K-contiguous ([M][K] activations, [N][K] weights), so
+//     every lane of a 16x16 MFMA reads a contiguous 16- or 32-byte run of one
+//     row: int8 v_mfma_i32_16x16x64_i8 and bf16 v_mfma_f32_16x16x32_bf16 take
+//     16 bytes per lane, fp8 v_mfma_f32_16x16x128_f8f6f4 takes 32 bytes.
+//   * A workgroup owns a BP x BQ output tile; its waves form a WP x WQ grid and
+//     each wave owns (BP/WP) x (BQ/WQ) = RP x RQ blocks of 16x16.
+//   * K advances KSTAGE bytes per iteration.  Tiles are staged through LDS in
+//     two buffers: 128-bit coalesced global loads for stage k+1 are in flight
+//     while the MFMAs consume stage k.  Each 16-byte chunk of an LDS row is
+//     XOR-swizzled with the row index so that the 16 lanes reading one column
+//     of chunks from 16 rows spread over the banks.
+//   * Split-K: blockIdx.y selects a contiguous K piece; the partial tile goes
+//     to the caller's workspace and a second kernel adds the pieces in
+//     ascending order (no atomics, deterministic).
+//   * Every output element accumulates its K range in ascending k, one MFMA
+//     K-slab after another, whatever the tile shape; so only the MFMA kind and
+//     the split boundaries decide the rounding, which is what the
+//     batch-invariant entry point relies on.
+#pragma once
+
+#include "qll_internal.h"
+
+namespace qll {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+template <int OP> struct OpTraits;
+template <> struct OpTraits<OP_INT8> {
+    static constexpr int esz = 1, kb = 16;  // bytes per lane per MFMA
+    using acc_t = v4i;
+    using elem_t = int;
+};
+template <> struct OpTraits<OP_FP8> {
+    static constexpr int esz = 1, kb = 32;
+    using acc_t = v4f;
+    using elem_t = float;
+};
+template <> struct OpTraits<OP_BLOCK> {
+    static constexpr int esz = 1, kb = 32;
+    using acc_t = v4f;
+    using elem_t = float;
+};
+template <> struct OpTraits<OP_BF16> {
+    static constexpr int esz = 2, kb = 16;
+    using acc_t = v4f;
+    using elem_t = float;
+};
+
+template <int OP>
+__device__ __forceinline__ typename OpTraits<OP>::acc_t
+mfma_step(const uint4* a, const uint4* b, typename OpTraits<OP>::acc_t c)
+{
+    if constexpr (OP == OP_INT8) {
+        return __builtin_amdgcn_mfma_i32_16x16x64_i8(
+            __builtin_bit_cast(v4i, a[0]), __builtin_bit_cast(v4i, b[0]), c, 0,
+            0, 0);
+    } else if constexpr (OP == OP_BF16) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(v8bf, a[0]), __builtin_bit_cast(v8bf, b[0]), c,
+            0, 0, 0);
+    } else {
+        // e4m3 x e4m3 (format code 0 for both operands), no block scaling:
+        // the scale operands are zero, which selects the unscaled
+        // v_mfma_f32_16x16x128_f8f6f4.
+        v8i av, bv;
+        av.lo = __builtin_bit_cast(v4i, a[0]);
+        av.hi = __builtin_bit_cast(v4i, a[1]);
+        bv.lo = __builtin_bit_cast(v4i, b[0]);
+        bv.hi = __builtin_bit_cast(v4i, b[1]);
+        return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 0, 0,
+                                                                0, 0, 0, 0);
+    }
+}
+
+__device__ __forceinline__ uint16_t bf16_rne(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// Epilogue value of one accumulator element (before the output cast).
+template <int OP>
+__device__ __forceinline__ float epilogue_value(typename OpTraits<OP>::elem_t v,
+                                                const GemmArgs& a, int m, int n)
+{
+    if constexpr (OP == OP_INT8) {
+        float t = (float)v * a.sa[m];
+        return t * a.sb[n];
+    } else if constexpr (OP == OP_FP8) {
+        float t = v * a.sa[m];
+        return t * a.sb[n];
+    } else {
+        return v;
+    }
+}
+
+template <int OP>
+__device__ __forceinline__ void store_one(const GemmArgs& a, size_t idx,
+                                          typename OpTraits<OP>::elem_t v,
+                                          int m, int n)
+{
+    if constexpr (OP == OP_INT8) {
+        if (a.out_dtype == OUT_INT32) {
+            ((int*)a.out)[idx] = v;
+            return;
+        }
+    }
+    float y = epilogue_value<OP>(v, a, m, n);
+    if (a.out_dtype == OUT_BF16)
+        ((uint16_t*)a.out)[idx] = bf16_rne(y);
+    else
+        ((float*)a.out)[idx] = y;
+}
+
+template <int OP, int SWAP, int BP, int BQ, int WP, int WQ, int KSTAGE>
+__global__ __launch_bounds__(WP* WQ * 64) void gemm_tile_kernel(GemmArgs a)
+{
+    using Tr = OpTraits<OP>;
+    using acc_t = typename Tr::acc_t;
+    using elem_t = typename Tr::elem_t;
+    constexpr int THREADS = WP * WQ * 64;
+    constexpr int NC = KSTAGE / 16;  // 16-byte chunks per staged row
+    constexpr int KB = Tr::kb;
+    constexpr int KSTEP = 4 * KB;    // bytes of K per MFMA
+    constexpr int NSTEP = KSTAGE / KSTEP;
+    constexpr int SP = BP / WP, SQ = BQ / WQ;  // per-wave extent
+    constexpr int RP = SP / 16, RQ = SQ / 16;
+    constexpr int LP = (BP * NC + THREADS - 1) / THREADS;
+    constexpr int LQ = (BQ * NC + THREADS - 1) / THREADS;
+    constexpr int STAGE_BYTES = (BP + BQ) * KSTAGE;
+    static_assert(KSTAGE % KSTEP == 0 && RP >= 1 && RQ >= 1, "bad tile");
+    static_assert((NC & (NC - 1)) == 0, "KSTAGE must be a power of two");
+
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * STAGE_BYTES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wpi = wave % WP, wqi = wave / WP;
+
+    const int Pdim = SWAP ? a.N : a.M;
+    const int Qdim = SWAP ? a.M : a.N;
+    const uint8_t* __restrict__ Pptr = (const uint8_t*)(SWAP ? a.B : a.A);
+    const uint8_t* __restrict__ Qptr = (const uint8_t*)(SWAP ? a.A : a.B);
+    const int tp = (Pdim + BP - 1) / BP;
+    const int tile_p = blockIdx.x % tp, tile_q = blockIdx.x / tp;
+    const int p0 = tile_p * BP, q0 = tile_q * BQ;
+    const int z = blockIdx.y;
+    const int kbeg = z * a.kchunk;
+    const int kend = min(a.kbytes, kbeg + a.kchunk);
+    const int nk = (kend - kbeg + KSTAGE - 1) / KSTAGE;
+    const size_t ldk = (size_t)a.kbytes;
+
+    uint4 rp[LP], rq[LQ];
+
+    auto gload = [&](int kt) {
+        const int kb0 = kbeg + kt * KSTAGE;
+#pragma unroll
+        for (int i = 0; i < LP; ++i) {
+            const int c = tid + i * THREADS;
+            const int row = c / NC, ch = c % NC;
+            const int gr = p0 + row, kb = kb0 + ch * 16;
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if ((BP * NC % THREADS == 0 || c < BP * NC) && gr < Pdim && kb < kend)
+                v = *(const uint4*)(Pptr + (size_t)gr * ldk + kb);
+            rp[i] = v;
+        }
+#pragma unroll
+        for (int i = 0; i < LQ; ++i) {
+            const int c = tid + i * THREADS;
+            const int row = c / NC, ch = c % NC;
+            const int gr = q0 + row, kb = kb0 + ch * 16;
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if ((BQ * NC % THREADS == 0 || c < BQ * NC) && gr < Qdim && kb < kend)
+                v = *(const uint4*)(Qptr + (size_t)gr * ldk + kb);
+            rq[i] = v;
+        }
+    };
+
+    auto sstore = [&](int buf) {
+        uint8_t* sp = lds + buf * STAGE_BYTES;
+        uint8_t* sq = sp + BP * KSTAGE;
+#pragma unroll
+        for (int i = 0; i < LP; ++i) {
+            const int c = tid + i * THREADS;
+            if (BP * NC % THREADS == 0 || c < BP * NC) {
+                const int row = c / NC, ch = c % NC;
+                *(uint4*)(sp + row * KSTAGE + ((ch ^ (row & (NC - 1))) << 4)) = rp[i];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < LQ; ++i) {
+            const int c = tid + i * THREADS;
+            if (BQ * NC % THREADS == 0 || c < BQ * NC) {
+                const int row = c / NC, ch = c % NC;
+                *(uint4*)(sq + row * KSTAGE + ((ch ^ (row & (NC - 1))) << 4)) = rq[i];
+            }
+        }
+    };
+
+    acc_t acc[RP][RQ];
+#pragma unroll
+    for (int i = 0; i < RP; ++i)
+#pragma unroll
+        for (int j = 0; j < RQ; ++j)
+            acc[i][j] = acc_t{0, 0, 0, 0};
+
+    // Block-FP8 scale bookkeeping: the rows/columns of this lane.
+    const int KG = a.K / 128;
+    int prow[RP][4];
+    int qcol[RQ];
+    if constexpr (OP == OP_BLOCK) {
+#pragma unroll
+        for (int i = 0; i < RP; ++i)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                prow[i][v] = min(p0 + wpi * SP + i * 16 + (lane >> 4) * 4 + v, Pdim - 1);
+#pragma unroll
+        for (int j = 0; j < RQ; ++j)
+            qcol[j] = min(q0 + wqi * SQ + j * 16 + (lane & 15), Qdim - 1);
+    }
+
+    auto compute = [&](int buf, int kt) {
+        const uint8_t* sp = lds + buf * STAGE_BYTES;
+        const uint8_t* sq = sp + BP * KSTAGE;
+#pragma unroll
+        for (int ks = 0; ks < NSTEP; ++ks) {
+            if constexpr (OP == OP_BLOCK) {
+                if (kbeg + kt * KSTAGE + ks * KSTEP >= kend)
+                    break;
+            }
+            uint4 fa[RP][KB / 16], fb[RQ][KB / 16];
+            const int off = ks * KSTEP + (lane >> 4) * KB;
+#pragma unroll
+            for (int i = 0; i < RP; ++i) {
+                const int row = wpi * SP + i * 16 + (lane & 15);
+#pragma unroll
+                for (int j = 0; j < KB / 16; ++j) {
+                    const int ch = (off >> 4) + j;
+                    fa[i][j] = *(const uint4*)(sp + row * KSTAGE + ((ch ^ (row & (NC - 1))) << 4));
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < RQ; ++i) {
+                const int row = wqi * SQ + i * 16 + (lane & 15);
+#pragma unroll
+                for (int j = 0; j < KB / 16; ++j) {
+                    const int ch = (off >> 4) + j;
+                    fb[i][j] = *(const uint4*)(sq + row * KSTAGE + ((ch ^ (row & (NC - 1))) << 4));
+                }
+            }
+            if constexpr (OP == OP_BLOCK) {
+                const int g = (kbeg + kt * KSTAGE + ks * KSTEP) >> 7;
+                float ps[RP][4], qs[RQ];
+#pragma unroll
+                for (int i = 0; i < RP; ++i)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        ps[i][v] = SWAP ? a.sb[(prow[i][v] >> 7) * KG + g]
+                                        : a.sa[prow[i][v] * KG + g];
+#pragma unroll
+                for (int j = 0; j < RQ; ++j)
+                    qs[j] = SWAP ? a.sa[qcol[j] * KG + g]
+                                 : a.sb[(qcol[j] >> 7) * KG + g];
+#pragma unroll
+                for (int i = 0; i < RP; ++i)
+#pragma unroll
+                    for (int j = 0; j < RQ; ++j) {
+                        v4f pg = mfma_step<OP>(fa[i], fb[j], v4f{0, 0, 0, 0});
+#pragma unroll
+                        for (int v = 0; v < 4; ++v)
+                            acc[i][j][v] = __builtin_fmaf(ps[i][v] * qs[j], pg[v], acc[i][j][v]);
+                    }
+            } else {
+#pragma unroll
+                for (int i = 0; i < RP; ++i)
+#pragma unroll
+                    for (int j = 0; j < RQ; ++j)
+                        acc[i][j] = mfma_step<OP>(fa[i], fb[j], acc[i][j]);
+            }
+        }
+    };
+
+    gload(0);
+    sstore(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const int cur = kt & 1;
+        if (kt + 1 < nk)
+            gload(kt + 1);
+        compute(cur, kt);
+        if (kt + 1 < nk)
+            sstore(cur ^ 1);
+        __syncthreads();
+    }
+
+    // Epilogue.
+    const int M = a.M, N = a.N;
+#pragma unroll
+    for (int i = 0; i < RP; ++i) {
+#pragma unroll
+        for (int j = 0; j < RQ; ++j) {
+            const int pb = p0 + wpi * SP + i * 16 + (lane >> 4) * 4;
+            const int q = q0 + wqi * SQ + j * 16 + (lane & 15);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int p = pb + v;
+                const int m = SWAP ? q : p;
+                const int n = SWAP ? p : q;
+                if (m < M && n < N) {
+                    const elem_t e = acc[i][j][v];
+                    if (a.splits > 1) {
+                        ((elem_t*)a.ws)[((size_t)z * M + m) * N + n] = e;
+                    } else {
+                        store_one<OP>(a, (size_t)m * N + n, e, m, n);
+                    }
+                }
+            }
+        }
+    }
+}
+
+template <int OP, int SWAP, int BP, int BQ, int WP, int WQ, int KSTAGE>
+hipError_t launch_tile(const GemmArgs& a, hipStream_t stream)
+{
+    const int Pdim = SWAP ? a.N : a.M;
+    const int Qdim = SWAP ? a.M : a.N;
+    const long tiles = (long)((Pdim + BP - 1) / BP) * ((Qdim + BQ - 1) / BQ);
+    if (tiles > 0x7FFFFFFFL)
+        return hipErrorInvalidValue;
+    dim3 grid((unsigned)tiles, (unsigned)a.splits);
+    hipLaunchKernelGGL((gemm_tile_kernel<OP, SWAP, BP, BQ, WP, WQ, KSTAGE>), grid,
+                       dim3(WP * WQ * 64), 0, stream, a);
+    return hipGetLastError();
+}
+
+// Second Split-K stage: each thread owns up to 4 consecutive columns of one
+// row and adds the partials of the pieces s = 0, 1, ..., S-1 in that order.
+template <int OP>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs a)
+{
+    using elem_t = typename OpTraits<OP>::elem_t;
+    const int NQ = (a.N + 3) / 4;
+    const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (long)a.M * NQ)
+        return;
+    const int m = (int)(idx / NQ);
+    const int n0 = (int)(idx % NQ) * 4;
+    const elem_t* ws = (const elem_t*)a.ws;
+    const size_t plane = (size_t)a.M * a.N;
+    const size_t base = (size_t)m * a.N + n0;
+    elem_t s[4] = {0, 0, 0, 0};
+    if ((a.N & 3) == 0) {
+        for (int z = 0; z < a.splits; ++z) {
+            typedef elem_t v4e __attribute__((ext_vector_type(4)));
+            const v4e t = *(const v4e*)(ws + z * plane + base);
+            s[0] += t[0];
+            s[1] += t[1];
+            s[2] += t[2];
+            s[3] += t[3];
+        }
+    } else {
+        for (int z = 0; z < a.splits; ++z)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (n0 + j < a.N)
+                    s[j] += ws[z * plane + base + j];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        if (n0 + j < a.N)
+            store_one<OP>(a, base + j, s[j], m, n0 + j);
+}
+
+template <int OP>
+hipError_t launch_reduce(const GemmArgs& a, hipStream_t stream)
+{
+    const long total = (long)a.M * ((a.N + 3) / 4);
+    const long blocks = (total + 255) / 256;
+    if (blocks > 0x7FFFFFFFL)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(splitk_reduce_kernel<OP>, dim3((unsigned)blocks),
+                       dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace qll
+
+// One registry entry: orientation (n = ordinary, s = Swap-AB), tile BPxBQ,
+// wave grid WPxWQ, K stage bytes.
+#define QLL_VARIANT(OP, SW, BP, BQ, WP, WQ, KS)                                \
+    {(SW) ? "s" #BP "x" #BQ "_w" #WP "x" #WQ "_k" #KS                            \
+          : "n" #BP "x" #BQ "_w" #WP "x" #WQ "_k" #KS,                           \
+     OP, SW, BP, BQ, WP, WQ, KS, 2 * ((BP) + (BQ)) * (KS),                      \
+     &qll::launch_tile<OP, SW, BP, BQ, WP, WQ, KS>}

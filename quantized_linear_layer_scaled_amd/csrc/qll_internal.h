@@ -1,0 +1,64 @@
+// Internal declarations shared by the host API and the kernel translation
+// units of libqll.so.  Not part of the public interface (see include/qll.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qll {
+
+enum Op : int { OP_INT8 = 0, OP_FP8 = 1, OP_BLOCK = 2, OP_BF16 = 3, OP_COUNT = 4 };
+enum Out : int { OUT_BF16 = 0, OUT_FP32 = 1, OUT_INT32 = 2 };
+
+// The K range of one Split-K piece is a multiple of this many bytes, for every
+// variant, so that the split boundaries depend only on (K, splits).
+constexpr int kSplitGranule = 512;
+constexpr int kMaxSplits = 64;
+
+// Everything a GEMM launch needs.  P/Q naming: the matrix-core "A" operand
+// supplies the rows (P) of each 16x16 output block and the "B" operand its
+// columns (Q).  In the ordinary orientation P = tokens (A, M rows) and
+// Q = weights (B, N rows); Swap-AB exchanges the two.
+struct GemmArgs {
+    const void* A;   // [M][K]
+    const void* B;   // [N][K]
+    const float* sa; // per-token [M] or per-group [M][K/128]
+    const float* sb; // per-channel [N] or per-block [ceil(N/128)][K/128]
+    void* out;       // [M][N]
+    void* ws;        // [splits][M][N] int32 / fp32 partials (splits > 1)
+    int out_dtype;
+    int M, N, K;     // K in elements
+    int kbytes;      // K * element size
+    int splits;      // effective number of K pieces
+    int kchunk;      // bytes of K per piece (multiple of kSplitGranule)
+};
+
+using LaunchFn = hipError_t (*)(const GemmArgs&, hipStream_t);
+
+struct Variant {
+    const char* name;
+    int op;
+    int swap;    // 0 ordinary, 1 Swap-AB
+    int bp, bq;  // tile rows along P and Q
+    int wp, wq;  // wave grid
+    int kstage;  // bytes of K staged per iteration
+    int lds;     // LDS bytes
+    LaunchFn launch;       // the tile kernel (writes out, or ws when splits > 1)
+};
+
+// Registries, one per op (defined in the kernel translation units).
+const Variant* variants(int op, int* count);
+
+// Second Split-K stage: out = epilogue(sum_{s ascending} ws[s]).
+hipError_t launch_splitk_reduce(int op, const GemmArgs& a, hipStream_t stream);
+
+// Quantizers.
+hipError_t launch_quant_rows(const void* x, void* q, float* s, int M, int K,
+                             hipStream_t stream);
+hipError_t launch_quant_groups128(const void* x, void* q, float* s, int M,
+                                  int K, hipStream_t stream);
+hipError_t launch_quant_weight_blocks(const void* w, void* q, float* s, int N,
+                                      int K, hipStream_t stream);
+
+}  // namespace qll

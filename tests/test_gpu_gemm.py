@@ -1,0 +1,267 @@
+"""GPU parity of the four GEMMs against the oracle, for every registered
+kernel variant (ordinary and Swap-AB tiles) with and without Split-K, on
+shapes that span several tiles and end in ragged M, N and K tails.
+
+Operations: W8A8 INT8, FP8 (per-token x per-channel), Block-FP8 of "Helion in
+vLLM: A Unified Route to Tunable Linear Kernels" ("What the integration
+changes": ordinary GEMM, Split-K and Swap-AB compute the same product), and
+the bf16 product of the batch-invariant matmul (vLLM PR #53446, "Summary").
+
+Bars: INT8 int32 accumulators bit-exact (and the fp32/bf16 epilogue bit-exact,
+since it is fully determined by acc and the scales); floating point within
+the rule of tests/gpu_util.py; integer-valued FP8 / bf16 inputs bit-exact.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+from gpu_util import (check_fp, dev, dev_bf16, dev_e4m3, host_f64)  # noqa: E402
+
+
+@pytest.fixture(scope="module")
+def qll():
+    import quantized_linear_layer_scaled_amd as q
+    q.load_library()
+    q.init(None)  # heuristic only: the variants are forced below anyway
+    return q
+
+
+def names(qll, op):
+    return [v["name"] for v in qll.variants(op)]
+
+
+INT8_SHAPES = [(1, 520, 1040), (37, 300, 2064), (130, 264, 512)]
+FP8_SHAPES = [(1, 520, 1040), (37, 300, 2064), (130, 264, 512)]
+BLOCK_SHAPES = [(1, 520, 1024), (37, 300, 2048), (130, 264, 512)]
+BF16_SHAPES = [(1, 520, 1032), (37, 300, 2056), (130, 264, 512)]
+SPLITS = [1, 3]
+
+
+# ------------------------------------------------------------------ INT8
+@pytest.fixture(scope="module")
+def int8_cases():
+    out = {}
+    for (M, N, K) in INT8_SHAPES:
+        d = workloads.int8_inputs(M, N, K, key=(workloads.W_TEST, 30, M, N, K))
+        acc, y = oracle.gemm_w8a8_int8(d["A"], d["B"], d["sa"], d["sb"])
+        out[(M, N, K)] = (d, acc, y)
+    return out
+
+
+@pytest.mark.parametrize("shape", INT8_SHAPES)
+@pytest.mark.parametrize("splits", SPLITS)
+def test_int8_all_variants_bit_exact(qll, int8_cases, shape, splits):
+    d, acc, y = int8_cases[shape]
+    A, B, sa, sb = dev(d["A"]), dev(d["B"]), dev(d["sa"]), dev(d["sb"])
+    ybf = oracle.bf16_encode(y)
+    for name in names(qll, "int8"):
+        cfg = (name, splits)
+        o32 = qll.gemm_w8a8_int8(A, B, sa, sb, out_dtype="int32", cfg=cfg)
+        of = qll.gemm_w8a8_int8(A, B, sa, sb, out_dtype="fp32", cfg=cfg)
+        ob = qll.gemm_w8a8_int8(A, B, sa, sb, out_dtype="bf16", cfg=cfg)
+        torch.cuda.synchronize()
+        assert np.array_equal(o32.cpu().numpy(), acc), f"{name} S={splits} acc"
+        assert np.array_equal(of.cpu().numpy().view(np.uint32), y.view(np.uint32)), \
+            f"{name} S={splits} fp32 epilogue"
+        assert np.array_equal(ob.view(torch.int16).cpu().numpy().view(np.uint16), ybf), \
+            f"{name} S={splits} bf16 epilogue"
+
+
+def test_int8_closed_forms(qll):
+    K = 2048
+    for a, b, expect in [(127, -127, -16129 * K), (-128, -128, 16384 * K), (1, 1, K)]:
+        A = torch.full((5, K), a, dtype=torch.int8, device="cuda")
+        B = torch.full((70, K), b, dtype=torch.int8, device="cuda")
+        one = torch.ones(5, device="cuda"), torch.ones(70, device="cuda")
+        for name in names(qll, "int8"):
+            o = qll.gemm_w8a8_int8(A, B, *one, out_dtype="int32", cfg=(name, 2))
+            assert bool((o == expect).all()), (name, a, b)
+
+
+# ------------------------------------------------------------------ FP8
+def fp8_case(M, N, K, key):
+    x = workloads.bf16_normal((M, K), (*key, 0), outlier_frac=0.01)
+    w = workloads.bf16_normal((N, K), (*key, 1), std=0.02)
+    A, sa = oracle.quantize_fp8(x)
+    B, sb = oracle.quantize_fp8(w)
+    ref, absref = oracle.gemm_fp8(A, B, sa, sb, with_abs=True)
+    return A, B, sa[:, 0].copy(), sb[:, 0].copy(), ref, absref
+
+
+@pytest.fixture(scope="module")
+def fp8_cases():
+    return {s: fp8_case(*s, key=(workloads.W_TEST, 31, *s)) for s in FP8_SHAPES}
+
+
+@pytest.mark.parametrize("shape", FP8_SHAPES)
+@pytest.mark.parametrize("splits", SPLITS)
+def test_fp8_all_variants(qll, fp8_cases, shape, splits):
+    A, B, sa, sb, ref, absref = fp8_cases[shape]
+    M, N, K = shape
+    dA, dB, dsa, dsb = dev_e4m3(A), dev_e4m3(B), dev(sa), dev(sb)
+    for name in names(qll, "fp8"):
+        for od in ("bf16", "fp32"):
+            y = qll.gemm_fp8_scaled(dA, dB, dsa, dsb, out_dtype=od, cfg=(name, splits))
+            torch.cuda.synchronize()
+            check_fp(host_f64(y), ref, absref, K, od, f"fp8 {name} S={splits} {od}")
+
+
+def test_fp8_integer_valued_exact(qll):
+    # integers in [-16, 16] are exact in e4m3 and every partial sum stays
+    # below 2^24, so with unit scales every summation order is exact
+    g = np.random.default_rng(32)
+    M, N, K = 33, 200, 2048
+    ia = g.integers(-16, 17, (M, K)).astype(np.int8)
+    ib = g.integers(-16, 17, (N, K)).astype(np.int8)
+    A = oracle.e4m3_encode(ia.astype(np.float32))
+    B = oracle.e4m3_encode(ib.astype(np.float32))
+    exact = oracle.gemm_int8_acc(ia, ib).astype(np.float64)
+    ones_m, ones_n = torch.ones(M, device="cuda"), torch.ones(N, device="cuda")
+    for name in names(qll, "fp8"):
+        for s in (1, 4):
+            y = qll.gemm_fp8_scaled(dev_e4m3(A), dev_e4m3(B), ones_m, ones_n,
+                                    out_dtype="fp32", cfg=(name, s))
+            torch.cuda.synchronize()
+            assert np.array_equal(host_f64(y), exact), (name, s)
+
+
+# ------------------------------------------------------------------ Block-FP8
+def block_case(M, N, K, key):
+    x = workloads.bf16_normal((M, K), (*key, 0))
+    w = workloads.bf16_normal((N, K), (*key, 1), std=0.02)
+    A, sa = oracle.quantize_fp8(x, group=128)
+    B, sb = oracle.quantize_fp8_block(w)
+    ref, absref = oracle.gemm_block_fp8(A, B, sa, sb, with_abs=True)
+    return A, B, sa, sb, ref, absref
+
+
+@pytest.fixture(scope="module")
+def block_cases():
+    return {s: block_case(*s, key=(workloads.W_TEST, 33, *s)) for s in BLOCK_SHAPES}
+
+
+@pytest.mark.parametrize("shape", BLOCK_SHAPES)
+@pytest.mark.parametrize("splits", SPLITS)
+def test_block_all_variants(qll, block_cases, shape, splits):
+    A, B, sa, sb, ref, absref = block_cases[shape]
+    M, N, K = shape
+    dA, dB, dsa, dsb = dev_e4m3(A), dev_e4m3(B), dev(sa), dev(sb)
+    for name in names(qll, "block_fp8"):
+        for od in ("bf16", "fp32"):
+            y = qll.gemm_block_fp8(dA, dB, dsa, dsb, out_dtype=od, cfg=(name, splits))
+            torch.cuda.synchronize()
+            check_fp(host_f64(y), ref, absref, K, od, f"block {name} S={splits} {od}")
+
+
+def test_block_equal_scales_match_fp8_exactly(qll):
+    # integer-valued codes and power-of-two scales that are equal along K:
+    # Block-FP8 reduces to the per-channel FP8 product, exactly
+    g = np.random.default_rng(34)
+    M, N, K = 20, 256, 1024
+    A = oracle.e4m3_encode(g.integers(-16, 17, (M, K)).astype(np.float32))
+    B = oracle.e4m3_encode(g.integers(-16, 17, (N, K)).astype(np.float32))
+    ra = (2.0 ** g.integers(-3, 4, M)).astype(np.float32)
+    rb = (2.0 ** g.integers(-3, 4, N // 128)).astype(np.float32)
+    sa = np.repeat(ra[:, None], K // 128, 1)
+    sb = np.repeat(rb[:, None], K // 128, 1)
+    ref = oracle.gemm_fp8(A, B, ra, np.repeat(rb, 128))
+    for name in names(qll, "block_fp8"):
+        y = qll.gemm_block_fp8(dev_e4m3(A), dev_e4m3(B), dev(sa), dev(sb),
+                               out_dtype="fp32", cfg=(name, 2))
+        torch.cuda.synchronize()
+        assert np.array_equal(host_f64(y), ref), name
+
+
+# ------------------------------------------------------------------ bf16
+def bf16_case(M, N, K, key):
+    A = workloads.bf16_normal((M, K), (*key, 0), inv_sqrt_k=True)
+    B = workloads.bf16_normal((N, K), (*key, 1), inv_sqrt_k=True)
+    ref, absref = oracle.gemm_bf16(A, B, with_abs=True)
+    return A, B, ref, absref
+
+
+@pytest.fixture(scope="module")
+def bf16_cases():
+    return {s: bf16_case(*s, key=(workloads.W_TEST, 35, *s)) for s in BF16_SHAPES}
+
+
+@pytest.mark.parametrize("shape", BF16_SHAPES)
+@pytest.mark.parametrize("splits", SPLITS)
+def test_bf16_all_variants(qll, bf16_cases, shape, splits):
+    A, B, ref, absref = bf16_cases[shape]
+    M, N, K = shape
+    dA, dB = dev_bf16(A), dev_bf16(B)
+    for name in names(qll, "bf16_bi"):
+        for od in ("bf16", "fp32"):
+            y = qll.gemm_bf16_batch_invariant(dA, dB, out_dtype=od, cfg=(name, splits))
+            torch.cuda.synchronize()
+            check_fp(host_f64(y), ref, absref, K, od, f"bf16 {name} S={splits} {od}")
+
+
+def test_bf16_integer_valued_exact(qll):
+    g = np.random.default_rng(36)
+    M, N, K = 17, 150, 1024
+    ia = g.integers(-16, 17, (M, K)).astype(np.float32)
+    ib = g.integers(-16, 17, (N, K)).astype(np.float32)
+    A, B = workloads.to_bf16_bits(ia), workloads.to_bf16_bits(ib)
+    exact = oracle.gemm_bf16(A, B)
+    for name in names(qll, "bf16_bi"):
+        for s in (1, 2):
+            y = qll.gemm_bf16_batch_invariant(dev_bf16(A), dev_bf16(B), out_dtype="fp32",
+                                              cfg=(name, s))
+            torch.cuda.synchronize()
+            assert np.array_equal(host_f64(y), exact), (name, s)
+
+
+# ------------------------------------------------------------------ strategies
+def test_splitk_and_swap_are_deterministic(qll, fp8_cases):
+    A, B, sa, sb, ref, absref = fp8_cases[(37, 300, 2064)]
+    dA, dB, dsa, dsb = dev_e4m3(A), dev_e4m3(B), dev(sa), dev(sb)
+    for name in names(qll, "fp8"):
+        first = qll.gemm_fp8_scaled(dA, dB, dsa, dsb, out_dtype="fp32", cfg=(name, 4))
+        for _ in range(9):
+            again = qll.gemm_fp8_scaled(dA, dB, dsa, dsb, out_dtype="fp32", cfg=(name, 4))
+            assert torch.equal(first.view(torch.int32), again.view(torch.int32)), name
+
+
+def test_zero_m_is_noop(qll):
+    A = torch.empty((0, 256), dtype=torch.int8, device="cuda")
+    B = torch.zeros((64, 256), dtype=torch.int8, device="cuda")
+    out = qll.gemm_w8a8_int8(A, B, torch.empty(0, device="cuda"),
+                             torch.ones(64, device="cuda"))
+    assert out.shape == (0, 64)
+
+
+def test_workspace_too_small_is_rejected(qll):
+    A = torch.zeros((4, 2048), dtype=torch.int8, device="cuda")
+    B = torch.zeros((64, 2048), dtype=torch.int8, device="cuda")
+    ws = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(qll.QllError) as e:
+        qll.gemm_w8a8_int8(A, B, torch.ones(4, device="cuda"), torch.ones(64, device="cuda"),
+                           cfg=("s64x16_w4x1_k256", 4), workspace=ws)
+    assert e.value.status == 4
+
+
+@pytest.mark.parametrize("op", ["bf16_bi", "fp8"])
+def test_swap_equals_ordinary_bitwise(qll, op, fp8_cases, bf16_cases):
+    # whether the Swap-AB orientation reproduces the ordinary one bit for bit
+    # (same MFMA, operands exchanged); the batch-invariant dispatch only mixes
+    # orientations if this holds
+    if op == "fp8":
+        A, B, sa, sb, _, _ = fp8_cases[(37, 300, 2064)]
+        args = (dev_e4m3(A), dev_e4m3(B), dev(sa), dev(sb))
+        fn = qll.gemm_fp8_scaled
+    else:
+        A, B, _, _ = bf16_cases[(37, 300, 2056)]
+        args = (dev_bf16(A), dev_bf16(B))
+        fn = qll.gemm_bf16_batch_invariant
+    outs = {n: fn(*args, out_dtype="fp32", cfg=(n, 1)) for n in names(qll, op)}
+    torch.cuda.synchronize()
+    ref = outs["n128x128_w2x2_k128"].view(torch.int32)
+    diff = [n for n, y in outs.items() if not torch.equal(y.view(torch.int32), ref)]
+    assert not diff, f"{op}: variants differing bitwise from n128x128: {diff}"

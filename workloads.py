@@ -29,6 +29,8 @@ vocabulary N=151936 and a square N=K=2048 weight):
 """
 from __future__ import annotations
 
+import os
+
 import numpy as np
 
 INT8_SHAPE = (16, 2048, 2048)  # M, N, K
@@ -66,12 +68,34 @@ def scales_uniform(n, key, lo=1e-3, hi=1e-2) -> np.ndarray:
     return rng(*key).uniform(lo, hi, size=n).astype(np.float32)
 
 
+_CHUNK = 1 << 20  # elements per independently seeded block of rows
+
+
 def normal_f32(shape, key, std=1.0) -> np.ndarray:
-    g = rng(*key)
-    x = g.standard_normal(size=shape, dtype=np.float32)
-    if std != 1.0:
-        x = x * np.float32(std)
-    return x
+    """N(0, std) in float32.  Rows are drawn in blocks of about 2^20 elements,
+    block j from rng(*key, j), on a few threads; the values depend only on
+    the shape and the key."""
+    shape = tuple(int(s) for s in shape)
+    rows = shape[0] if len(shape) > 1 else 1
+    cols = int(np.prod(shape[1:])) if len(shape) > 1 else int(np.prod(shape))
+    x = np.empty((rows, cols), dtype=np.float32)
+    per = max(1, _CHUNK // max(cols, 1))
+    blocks = [(j, r, min(rows, r + per)) for j, r in enumerate(range(0, rows, per))]
+
+    def fill(b):
+        j, r0, r1 = b
+        rng(*key, j).standard_normal(out=x[r0:r1], dtype=np.float32)
+        if std != 1.0:
+            np.multiply(x[r0:r1], np.float32(std), out=x[r0:r1])
+
+    if len(blocks) > 4:
+        import concurrent.futures as cf
+        with cf.ThreadPoolExecutor(min(16, os.cpu_count() or 4)) as ex:
+            list(ex.map(fill, blocks))
+    else:
+        for b in blocks:
+            fill(b)
+    return x.reshape(shape)
 
 
 def bf16_normal(shape, key, std=1.0, inv_sqrt_k=False, outlier_frac=0.0,
@@ -85,7 +109,7 @@ def bf16_normal(shape, key, std=1.0, inv_sqrt_k=False, outlier_frac=0.0,
         x = x / np.float32(np.sqrt(np.float32(K)))
     if outlier_frac > 0.0:
         n_out = int(round(outlier_frac * K))
-        cols = rng(*key, 1).choice(K, size=n_out, replace=False)
+        cols = rng(*key, 1 << 30).choice(K, size=n_out, replace=False)
         x[..., cols] *= np.float32(outlier_mult)
     return to_bf16_bits(x)
 
