@@ -1,0 +1,410 @@
+#!/usr/bin/env python3
+"""Benchmark of the scaled_mm hot path on one MI355X.
+
+Default workload (one "step"): the FP8 dynamic per-token sweep -- for
+(N, K) in {(4096, 2048), (2048, 6144)} and M in {1, 4, 8, 16, 32, 64, 256,
+512, 1024, 2048}: quantize the bf16 activations per token on the device
+(quantize_per_token_fp8), then run the scaled FP8 GEMM (gemm_fp8_scaled) with
+the configuration the dispatch picks, bf16 out.  Weights are quantized per
+output channel on the device once, before timing.  Every (N, K, M) problem
+has its own buffers (about 350 MB touched per step, more than the 256 MB
+Infinity Cache), so a problem's weights come from HBM, not from a cache.
+
+Timing: W untimed warm-up steps, then K timed steps bracketed by
+torch.cuda.synchronize(); each kernel launch is bracketed by HIP events on the
+stream the library launches on, which gives per-kernel durations.  value =
+GEMM flops of a step / step time (TFLOPS).  The line also carries the
+roofline of the dominant kernel (the GEMM kernel with the most time per step)
+and the CPU oracle timed on a bounded sample of the same workload.
+
+Other workloads (--workload int8|block|bi|vocab) print the same JSON shape.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload fp8]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK = {"fp8": 5000.0, "int8": 5000.0, "bf16": 2500.0}  # dense TFLOP/s (TOP/s)
+HBM_GBS = 8000.0
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="fp8",
+                   choices=["fp8", "int8", "block", "bi", "vocab"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-rows", type=int, default=128,
+                   help="rows per problem the CPU oracle computes")
+    p.add_argument("--table", default="default",
+                   help="dispatch table ('default', a path, or 'none')")
+    p.add_argument("--traffic", default=None,
+                   help="JSON file with the measured HBM bytes of the dominant kernel")
+    return p.parse_args()
+
+
+# --------------------------------------------------------------------------
+# problems
+# --------------------------------------------------------------------------
+
+class Problem:
+    """One (op, M, N, K) GEMM with its own device buffers and a prebuilt
+    launch plan (raw pointers, so that the timed loop only makes the C calls)."""
+
+    def __init__(self, op, M, N, K):
+        self.op, self.M, self.N, self.K = op, M, N, K
+        self.calls = []       # [(name, cfunc, args)]
+        self.keep = []        # tensors that must stay alive
+
+    @property
+    def flops(self):
+        return 2.0 * self.M * self.N * self.K
+
+    def algo_bytes(self):
+        """Algorithmic HBM bytes of the GEMM: A + B + scales + bf16 out."""
+        M, N, K = self.M, self.N, self.K
+        if self.op == "bf16_bi":
+            return 2 * M * K + 2 * N * K + 2 * M * N
+        if self.op == "block_fp8":
+            return M * K + N * K + 4 * M * (K // 128) + 4 * ((N + 127) // 128) * (K // 128) + 2 * M * N
+        return M * K + N * K + 4 * M + 4 * N + 2 * M * N
+
+    def quant_bytes(self):
+        return 3 * self.M * self.K + 4 * self.M * max(1, self.K // (128 if self.op == "block_fp8" else self.K))
+
+
+def dev_bf16(torch, bits):
+    import numpy as np
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def build_problems(torch, qll, workload):
+    import numpy as np
+
+    import workloads as W
+    L = qll.load_library()
+    stream = torch.cuda.current_stream().cuda_stream
+    probs = []
+
+    def ws_for(op, M, N, K):
+        n = qll.workspace_bytes(op, M, N, K)
+        if n == 0:
+            return None, 0
+        t = torch.empty(n, dtype=torch.uint8, device="cuda")
+        return t, n
+
+    def add_gemm(p, fn, A, B, sa, sb):
+        out = torch.empty((p.M, p.N), dtype=torch.bfloat16, device="cuda")
+        ws, wsb = ws_for(p.op, p.M, p.N, p.K)
+        p.keep += [A, B, out] + [t for t in (sa, sb, ws) if t is not None]
+        wsp = ws.data_ptr() if ws is not None else None
+        if p.op == "bf16_bi":
+            args = (A.data_ptr(), B.data_ptr(), out.data_ptr(), 0, p.M, p.N, p.K,
+                    wsp, wsb, stream)
+        else:
+            args = (A.data_ptr(), B.data_ptr(), sa.data_ptr(), sb.data_ptr(),
+                    out.data_ptr(), 0, p.M, p.N, p.K, wsp, wsb, stream)
+        p.calls.append(("gemm", getattr(L, fn), args))
+        p.variant, p.splits = qll.select(p.op, p.M, p.N, p.K)
+        p.eff_splits = qll.effective_splits(p.op, p.K, p.splits)
+
+    def add_quant(p, x, group):
+        q = torch.empty((p.M, p.K), dtype=torch.float8_e4m3fn, device="cuda")
+        G = p.K if group == 0 else group
+        s = torch.empty((p.M, p.K // G), dtype=torch.float32, device="cuda")
+        p.keep += [x, q, s]
+        p.calls.append(("quant", L.quantize_per_token_fp8,
+                        (x.data_ptr(), q.data_ptr(), s.data_ptr(), p.M, p.K, group, stream)))
+        return q, s
+
+    if workload in ("fp8", "vocab"):
+        shapes = W.FP8_SHAPES if workload == "fp8" else [W.VOCAB_SHAPE]
+        mlist = W.FP8_M if workload == "fp8" else W.VOCAB_M
+        for N, K in shapes:
+            if workload == "fp8":
+                w = dev_bf16(torch, W.weights_bf16(N, K))
+                x_all = dev_bf16(torch, W.fp8_activations(W.MAX_M, K))
+            else:
+                w = dev_bf16(torch, W.vocab_weights(N, K))
+                x_all = dev_bf16(torch, W.vocab_activations(K))
+            qw, sw = qll.quantize_per_token_fp8(w)
+            del w
+            for M in mlist:
+                p = Problem("fp8", M, N, K)
+                q, s = add_quant(p, x_all[:M].clone(), 0)
+                # own copy of the weights per problem (cold for every problem)
+                add_gemm(p, "gemm_fp8_scaled", q, qw.clone(), s, sw.clone())
+                probs.append(p)
+    elif workload == "int8":
+        M, N, K = W.INT8_SHAPE
+        d = W.int8_inputs(M, N, K)
+        for rep in range(8):
+            p = Problem("int8", M, N, K)
+            t = lambda a: torch.from_numpy(a).cuda()
+            add_gemm(p, "gemm_w8a8_int8", t(d["A"]), t(d["B"]), t(d["sa"]), t(d["sb"]))
+            probs.append(p)
+    elif workload == "block":
+        for N, K in W.BLOCK_SHAPES:
+            w = dev_bf16(torch, W.weights_bf16(N, K, key=(W.W_BLOCK,)))
+            qw, sw = qll.quantize_weight_block_fp8(w)
+            x_all = dev_bf16(torch, W.block_activations(W.MAX_M, K))
+            for M in W.BLOCK_M:
+                p = Problem("block_fp8", M, N, K)
+                q, s = add_quant(p, x_all[:M].clone(), 128)
+                add_gemm(p, "gemm_block_fp8", q, qw.clone(), s, sw.clone())
+                probs.append(p)
+    elif workload == "bi":
+        for N, K in W.BI_SHAPES:
+            d = W.bi_inputs(N, K)
+            a_full, b = dev_bf16(torch, d["A_full"]), dev_bf16(torch, d["B"])
+            for M in W.BI_M:
+                p = Problem("bf16_bi", M, N, K)
+                add_gemm(p, "gemm_bf16_batch_invariant", a_full[:M].clone(), b.clone(),
+                         None, None)
+                probs.append(p)
+    torch.cuda.synchronize()
+    return probs
+
+
+# --------------------------------------------------------------------------
+# timing
+# --------------------------------------------------------------------------
+
+def run_step(probs, events=None):
+    for i, p in enumerate(probs):
+        for j, (_, fn, args) in enumerate(p.calls):
+            if events is not None:
+                events[i][j][0].record()
+            rc = fn(*args)
+            if events is not None:
+                events[i][j][1].record()
+            if rc != 0:
+                raise RuntimeError(f"{fn.__name__} returned {rc} for M={p.M} N={p.N} K={p.K}")
+
+
+def kernel_symbol(qll, op, variant):
+    """The kernel's name as rocprofv3 prints it."""
+    opn = {"int8": 0, "fp8": 1, "block_fp8": 2, "bf16_bi": 3}[op]
+    v = next(x for x in qll.variants(op) if x["name"] == variant)
+    return (f"void qll::gemm_tile_kernel<{opn}, {v['swap']}, {v['bp']}, {v['bq']}, "
+            f"{v['wp']}, {v['wq']}, {v['kstage']}>(qll::GemmArgs)")
+
+
+def cpu_baseline(workload, rows_cap):
+    """Time the oracle (as it stands) on a bounded sample of the workload:
+    the first min(M, rows_cap) rows of every problem, quantization included."""
+    import numpy as np
+
+    import oracle
+    import workloads as W
+    oracle.num_threads()
+    flops = 0.0
+    t_total = 0.0
+    sample = []
+    if workload in ("fp8", "vocab"):
+        shapes = W.FP8_SHAPES if workload == "fp8" else [W.VOCAB_SHAPE]
+        mlist = W.FP8_M if workload == "fp8" else W.VOCAB_M
+        for N, K in shapes:
+            w = W.weights_bf16(N, K) if workload == "fp8" else W.vocab_weights(N, K)
+            x_all = W.fp8_activations(W.MAX_M, K) if workload == "fp8" else W.vocab_activations(K)
+            B, sb = oracle.quantize_fp8(w)
+            sb = sb[:, 0].copy()
+            for M in mlist:
+                r = min(M, rows_cap)
+                t0 = time.perf_counter()
+                A, sa = oracle.quantize_fp8(np.ascontiguousarray(x_all[:r]))
+                oracle.gemm_fp8(A, B, sa[:, 0].copy(), sb)
+                t_total += time.perf_counter() - t0
+                flops += 2.0 * r * N * K
+            sample.append(f"N={N},K={K}")
+        desc = (f"first min(M,{rows_cap}) rows of every (N,K,M) problem "
+                f"({', '.join(sample)}), per-token quantization + FP8 GEMM")
+    elif workload == "int8":
+        M, N, K = W.INT8_SHAPE
+        d = W.int8_inputs(M, N, K)
+        t0 = time.perf_counter()
+        for _ in range(4):
+            oracle.gemm_w8a8_int8(d["A"], d["B"], d["sa"], d["sb"])
+        t_total = time.perf_counter() - t0
+        flops = 4 * 2.0 * M * N * K
+        desc = "4 full W8A8 INT8 GEMMs M=16 N=K=2048"
+    elif workload == "block":
+        for N, K in W.BLOCK_SHAPES:
+            w = W.weights_bf16(N, K, key=(W.W_BLOCK,))
+            B, sb = oracle.quantize_fp8_block(w)
+            x_all = W.block_activations(W.MAX_M, K)
+            for M in W.BLOCK_M:
+                r = min(M, rows_cap)
+                t0 = time.perf_counter()
+                A, sa = oracle.quantize_fp8(np.ascontiguousarray(x_all[:r]), group=128)
+                oracle.gemm_block_fp8(A, B, sa, sb)
+                t_total += time.perf_counter() - t0
+                flops += 2.0 * r * N * K
+        desc = f"first min(M,{rows_cap}) rows of every Block-FP8 problem"
+    else:
+        for N, K in W.BI_SHAPES:
+            d = W.bi_inputs(N, K)
+            for M in W.BI_M:
+                r = min(M, rows_cap)
+                t0 = time.perf_counter()
+                oracle.gemm_bf16(d["A_full"][:r], d["B"])
+                t_total += time.perf_counter() - t0
+                flops += 2.0 * r * N * K
+        desc = f"first min(M,{rows_cap}) rows of every bf16 problem"
+    return {"value": round(flops / t_total / 1e12, 6), "unit": "TFLOPS",
+            "cores": oracle.num_threads(), "kind": "oracle", "sample": desc,
+            "seconds": round(t_total, 2)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the "
+              "scaled_mm path is measured on a single MI355X and has no multi-GPU "
+              "mode.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import quantized_linear_layer_scaled_amd as qll
+
+    qll.load_library()
+    rc = qll.init(None if args.table == "none" else args.table)
+    table_used = qll.table_entries()
+    props = torch.cuda.get_device_properties(0)
+    print(f"# device {props.name} {getattr(props, 'gcnArchName', '?')} "
+          f"{props.multi_processor_count} CUs; table entries {table_used} (init rc {rc})",
+          file=sys.stderr, flush=True)
+
+    probs = build_problems(torch, qll, args.workload)
+    print(f"# {len(probs)} problems built", file=sys.stderr, flush=True)
+    def new_events():
+        return [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in p.calls] for p in probs]
+
+    for _ in range(args.warmup):
+        run_step(probs)
+    torch.cuda.synchronize()
+
+    # one set of events per timed step, created before the timed region
+    step_events = [new_events() for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    start.record()
+    for step in range(args.steps):
+        run_step(probs, step_events[step])
+    end.record()
+    torch.cuda.synchronize()
+    durations = [[[ev[i][j] for ev in step_events] for j in range(len(p.calls))]
+                 for i, p in enumerate(probs)]
+    wall = time.perf_counter() - t_wall0
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+
+    # per-kernel average durations (ms)
+    per_shape = []
+    kernels = {}  # symbol -> [total_ms, launches, flops, bytes]
+    gemm_flops_step = 0.0
+    for i, p in enumerate(probs):
+        rec = {"op": p.op, "M": p.M, "N": p.N, "K": p.K, "variant": p.variant,
+               "splits": p.eff_splits}
+        for j, (kind, _, _) in enumerate(p.calls):
+            ts = [a.elapsed_time(b) for a, b in durations[i][j]]
+            avg = sum(ts) / len(ts)
+            rec[f"{kind}_us"] = round(avg * 1e3, 3)
+        t_gemm = rec["gemm_us"] * 1e-6
+        dt = {"fp8": "fp8", "block_fp8": "fp8", "int8": "int8", "bf16_bi": "bf16"}[p.op]
+        t_mem = p.algo_bytes() / (HBM_GBS * 1e9)
+        t_mfma = p.flops / (PEAK[dt] * 1e12)
+        rec["tflops"] = round(p.flops / t_gemm / 1e12, 2)
+        rec["gbs"] = round(p.algo_bytes() / t_gemm / 1e9, 1)
+        rec["bound"] = "hbm" if t_mem >= t_mfma else "mfma"
+        rec["roof_frac"] = round(max(t_mem, t_mfma) / t_gemm, 3)
+        if "quant_us" in rec:
+            rec["quant_gbs"] = round(p.quant_bytes() / (rec["quant_us"] * 1e-6) / 1e9, 1)
+        per_shape.append(rec)
+        gemm_flops_step += p.flops
+        sym = kernel_symbol(qll, p.op, p.variant)
+        k = kernels.setdefault(sym, [0.0, 0, 0.0, 0.0, dt, []])
+        k[0] += t_gemm
+        k[1] += 1
+        k[2] += p.flops
+        k[3] += p.algo_bytes()
+        k[5].append(rec["bound"])
+
+    dom_sym, dom = max(kernels.items(), key=lambda kv: kv[1][0])
+    avg_dur = dom[0] / dom[1]
+    bound = "mfma" if dom[5].count("mfma") >= dom[5].count("hbm") else "hbm"
+    if bound == "mfma":
+        achieved = dom[2] / dom[1] / avg_dur / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK[dom[4]],
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK[dom[4]], 4)}
+    else:
+        achieved = dom[3] / dom[1] / avg_dur / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_GBS, 4)}
+    roof["traffic"] = None
+    if args.traffic and os.path.exists(args.traffic):
+        with open(args.traffic) as f:
+            tr = json.load(f)
+        if tr.get("kernel") == dom_sym:
+            roof["traffic"] = tr.get("bytes_per_launch")
+    roof["kernel"] = dom_sym
+    roof["launches_per_step"] = dom[1]
+    roof["avg_us"] = round(avg_dur * 1e6, 3)
+    roof["algorithmic_per_launch"] = (round(dom[2] / dom[1]) if bound == "mfma"
+                                      else round(dom[3] / dom[1]))
+
+    value = gemm_flops_step / (ms_per_step * 1e-3) / 1e12
+    names = {"fp8": "FP8 dynamic per-token sweep: (N,K) in {(4096,2048),(2048,6144)}, "
+                    "M in {1,4,8,16,32,64,256,512,1024,2048}; per-token quantization + "
+                    "scaled FP8 GEMM, bf16 out",
+             "int8": "W8A8 INT8 GEMM M=16 N=2048 K=2048, bf16 out (8 independent copies)",
+             "block": "Block-FP8 sweep: (N,K) in {(12288,2048),(2048,6144)}, "
+                      "M in {1,16,64,256,2048}; 1x128 quantization + GEMM, bf16 out",
+             "bi": "batch-invariant bf16 sweep: (N,K) in {(2048,2048),(4096,2048)}, "
+                   "M in {1,4,...,2048}, bf16 out",
+             "vocab": "large-vocab FP8 dynamic projection N=151936 K=2048, "
+                      "M in {1,8,64,512,2048}"}
+    dtype = {"fp8": "fp8e4m3", "vocab": "fp8e4m3", "block": "fp8e4m3", "int8": "int8",
+             "bi": "bf16"}[args.workload]
+    line = {
+        "metric": "TFLOPS/TOPS + % of HBM or MFMA roofline per (M,N,K), FP8/INT8 scaled_mm",
+        "value": round(value, 3),
+        "unit": "TOPS" if args.workload == "int8" else "TFLOPS",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": dtype, "data": "synthetic (seeded, shapes and distributions of the workload)",
+        "config": {"workload": names[args.workload],
+                   "problems_per_step": len(probs),
+                   "dispatch": "table" if table_used else "heuristic",
+                   "cold_weights": True},
+        "roofline": roof,
+        "cpu_baseline": None,
+        "wall_s_timed": round(wall, 3),
+        "device": {"name": props.name, "cus": props.multi_processor_count,
+                   "arch": getattr(props, "gcnArchName", "?")},
+        "per_shape": per_shape,
+    }
+    if not args.no_cpu_baseline:
+        print("# timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_rows)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -208,13 +208,19 @@ int load_table(const char* path, const char* arch, int cus_want, Table** out,
         if (op == OP_BF16) {
             int n = 0;
             const Variant* v = variants(op, &n);
-            const std::pair<int, int> fx(seff, v[vi].swap);
+            // waves that split K inside the workgroup change the reduction
+            if (std::strncmp(v[vi].name, "k16x", 4) == 0) {
+                rc = QLL_ERR_TABLE;
+                *err = "batch-invariant entry uses a variant that splits K across waves";
+                break;
+            }
+            const std::pair<int, int> fx(seff, 0);
             auto it = bi_seen.find(shape_key(op, N, K));
             if (it == bi_seen.end()) {
                 bi_seen.emplace(shape_key(op, N, K), fx);
             } else if (it->second != fx) {
                 rc = QLL_ERR_TABLE;
-                *err = "batch-invariant entries vary the K split or orientation with M";
+                *err = "batch-invariant entries vary the K split with M";
                 break;
             }
         }
@@ -235,44 +241,54 @@ int load_table(const char* path, const char* arch, int cus_want, Table** out,
 }
 
 // ------------------------------------------------------------------ heuristic
-// Used when the table has no entry.  Small M: Swap-AB (weights on the MFMA row
-// side) and, for the ordinary ops, Split-K until the grid has about two
-// workgroups per CU; large M: big ordinary tiles.  The batch-invariant op
-// never splits K here and always uses the ordinary orientation.
+// Used when the table has no entry.  M <= 64: the skinny Swap-AB kernel (for
+// the ordinary ops its waves split K inside the workgroup); larger M: ordinary
+// tiles, with Split-K until the grid covers the CUs once.  The batch-invariant
+// op never splits K: every variant it may use accumulates the whole K range
+// of an output element in ascending order in one accumulator.
 qll_cfg heuristic(int op, int64_t M, int64_t N, int64_t K)
 {
     const int cus = device_info().cus;
     const char* name;
-    if (op == OP_BF16 && M <= 128)
-        name = M <= 16 ? "n16x64_w1x4_k" : (M <= 32 ? "n32x128_w1x4_k" : "n64x128_w2x2_k");
-    else if (M <= 16)
-        name = N >= 8192 ? "s256x16_w4x1_k" : (N >= 2048 ? "s128x16_w4x1_k" : "s64x16_w4x1_k");
-    else if (M <= 32)
-        name = "s128x32_w4x1_k";
-    else if (M <= 64)
-        name = "s128x64_w2x2_k";
-    else if (M <= 128)
-        name = "n64x128_w2x2_k";
-    else if (M * N >= (int64_t)cus * 4 * 128 * 256)
-        name = "n128x256_w2x2_k";
-    else
-        name = "n128x128_w2x2_k";
-    // complete the name with the K stage the registry has for it
+    bool exact = true;
+    if (M <= 64) {
+        if (op == OP_BF16)
+            name = M <= 16 ? "r16x16_w4" : (M <= 32 ? "r16x32_w4" : "r16x64_w4");
+        else if (M <= 16)
+            name = (N + 15) / 16 >= 2 * cus ? "k16x16_w8" : "k16x16_w16";
+        else
+            name = M <= 32 ? "k16x32_w8" : "k16x64_w8";
+    } else if (op == OP_BLOCK) {
+        exact = false;
+        if (M <= 128)
+            name = "n64x128_w2x2_k";
+        else if (M * N >= (int64_t)cus * 4 * 128 * 256)
+            name = "n128x256_w2x2_k";
+        else
+            name = "n128x128_w2x2_k";
+    } else if (M <= 128) {
+        name = "p64x128_w2x2_k128_s4";
+    } else if (((M + 255) / 256) * ((N + 127) / 128) >= cus) {
+        name = "p256x128_w4x2_k128_s3";
+    } else {
+        name = "p128x128_w2x2_k128_s4";
+    }
     int n = 0;
     const Variant* v = variants(op, &n);
     int vi = 0;
     for (int i = 0; i < n; ++i)
-        if (std::strncmp(v[i].name, name, std::strlen(name)) == 0) {
+        if (exact ? std::strcmp(v[i].name, name) == 0
+                  : std::strncmp(v[i].name, name, std::strlen(name)) == 0) {
             vi = i;
             break;
         }
-    if (op == OP_BF16)
+    if (op == OP_BF16 || M <= 64)
         return qll_cfg{vi, 1};
     const int64_t tiles = ((v[vi].swap ? N : M) + v[vi].bp - 1) / v[vi].bp *
                           (((v[vi].swap ? M : N) + v[vi].bq - 1) / v[vi].bq);
     const int64_t kbytes = K * op_esz(op);
     int s = 1;
-    while (tiles * s < 2 * cus && (int64_t)s * 2 * 1024 <= kbytes && s < 16)
+    while (tiles * s < cus && (int64_t)s * 2 * 1024 <= kbytes && s < 16)
         s *= 2;
     return qll_cfg{vi, s};
 }
@@ -289,17 +305,8 @@ qll_cfg select_cfg(int op, int64_t M, int64_t N, int64_t K)
             // every M
             auto fx = t->bi_fixed.find(shape_key(op, N, K));
             if (fx != t->bi_fixed.end()) {
+                // a covered (N, K) keeps its table's K split at every M
                 qll_cfg c = heuristic(op, M, N, K);
-                int n = 0;
-                const Variant* v = variants(op, &n);
-                if (v[c.variant].swap != fx->second.second) {
-                    const char* alt = fx->second.second ? "s128x16_w4x1_k" : "n128x128_w2x2_k";
-                    for (int i = 0; i < n; ++i)
-                        if (std::strncmp(v[i].name, alt, std::strlen(alt)) == 0)
-                            c.variant = i;
-                }
-                // the table stores the requested split; recover one that
-                // yields the same effective split
                 c.splits = fx->second.first;
                 return c;
             }

@@ -1,15 +1,21 @@
 // Kernel instantiations and variant registry of the block GEMM.
+#include "gemm_pipe.h"
+#include "gemm_skinny.h"
 #include "gemm_tile.h"
 #include "variant_list.h"
 
 QLL_FOR_EACH_VARIANT(QLL_INSTANTIATE, qll::OP_BLOCK, 256, 128)
+QLL_FOR_EACH_SKINNY(QLL_SKINNY_INSTANTIATE, qll::OP_BLOCK, 1)
 template __global__ void qll::splitk_reduce_kernel<qll::OP_BLOCK>(qll::GemmArgs);
 
 namespace qll {
 
 // host-side registry (the device pass only needs the kernels above)
 #if !defined(__HIP_DEVICE_COMPILE__)
-extern const Variant kVariantsBlock[] = {QLL_FOR_EACH_VARIANT(QLL_ENTRY, OP_BLOCK, 256, 128)};
+extern const Variant kVariantsBlock[] = {
+    QLL_FOR_EACH_VARIANT(QLL_ENTRY, OP_BLOCK, 256, 128)
+    QLL_FOR_EACH_SKINNY(QLL_SKINNY_ENTRY, OP_BLOCK, 1)
+};
 extern const int kNumVariantsBlock = sizeof(kVariantsBlock) / sizeof(Variant);
 #endif
 

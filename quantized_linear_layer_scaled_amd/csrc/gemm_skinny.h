@@ -1,0 +1,179 @@
+// Skinny-M ("decode") scaled GEMM for gfx950, Swap-AB orientation: weights
+// occupy the MFMA row side and the few tokens the column side, which is the
+// Swap-AB strategy of "Helion in vLLM: A Unified Route to Tunable Linear
+// Kernels" ("What the integration changes") for small M.
+//
+// For M <= 64 the GEMM streams the weight matrix once and reuses every byte
+// M times only, so it is bound by HBM bandwidth and by how many loads are in
+// flight.  The tiled kernel's LDS staging buys nothing here, so this kernel:
+//   * loads both operands straight from global memory into registers in MFMA
+//     operand layout (each lane: a contiguous 16/32-byte run of one K-major
+//     row -- the weights are read exactly once, coalesced per row);
+//   * gives each workgroup 16 weight rows and lets its W waves split the K
+//     range among themselves (KSPLIT), so that even N = 2048 yields W x 128
+//     independent streams; D MFMA steps of loads are issued before their
+//     MFMAs to keep many bytes in flight per wave;
+//   * adds the W partial tiles through LDS in a fixed order (wave 0, 1, ...,
+//     W-1), so the result is deterministic and needs no second kernel.
+//   Without KSPLIT each wave owns 16 weight rows and the whole K range (used
+//   by the batch-invariant op, whose K reduction must not change with M).
+// Cross-workgroup Split-K (blockIdx.z) composes with this exactly as in the
+// tiled kernel: each piece is reduced in-workgroup, then the pieces are added
+// in ascending order by the second-stage kernel.
+#pragma once
+
+#include "gemm_tile.h"
+
+namespace qll {
+
+template <int OP, int RQ, int W, bool KSPLIT, int D>
+__global__ __launch_bounds__(W * 64) void gemm_skinny_kernel(GemmArgs a)
+{
+    using Tr = OpTraits<OP>;
+    using acc_t = typename Tr::acc_t;
+    using elem_t = typename Tr::elem_t;
+    constexpr int KB = Tr::kb;
+    constexpr int KSTEP = 4 * KB;
+    constexpr int NJ = KB / 16;  // 16-byte loads per operand per step
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int N = a.N, M = a.M;
+    const int n0 = KSPLIT ? blockIdx.x * 16 : (blockIdx.x * W + wave) * 16;
+    const int m0 = blockIdx.y * (16 * RQ);
+    const int z = blockIdx.z;
+    const int kbeg = z * a.kchunk;
+    const int kend = min(a.kbytes, kbeg + a.kchunk);
+    const int T = (kend - kbeg + KSTEP - 1) / KSTEP;
+    const int s0 = KSPLIT ? wave * T / W : 0;
+    const int s1 = KSPLIT ? (wave + 1) * T / W : T;
+    const size_t ldk = (size_t)a.kbytes;
+
+    // rows this lane loads (clamped: out-of-range rows are masked at the store)
+    const int nrow = min(n0 + (lane & 15), N - 1);
+    const uint8_t* __restrict__ bp =
+        (const uint8_t*)a.B + (size_t)nrow * ldk + kbeg + (lane >> 4) * KB;
+    const uint8_t* __restrict__ ap[RQ];
+#pragma unroll
+    for (int r = 0; r < RQ; ++r) {
+        const int mrow = min(m0 + r * 16 + (lane & 15), M - 1);
+        ap[r] = (const uint8_t*)a.A + (size_t)mrow * ldk + kbeg + (lane >> 4) * KB;
+    }
+    const int klim = kend - kbeg - (lane >> 4) * KB;  // bytes this lane may read
+
+    acc_t acc[RQ];
+#pragma unroll
+    for (int r = 0; r < RQ; ++r)
+        acc[r] = acc_t{0, 0, 0, 0};
+
+    const int KG = a.K / 128;
+    const int nb = (min(n0, N - 1) >> 7);  // 16 weight rows share one 128-row block
+
+    for (int s = s0; s < s1; s += D) {
+        uint4 fb[D][NJ], fa[D][RQ][NJ];
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            const int off = (s + d) * KSTEP;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const bool ok = (s + d < s1) && (off + 16 * j < klim);
+                fb[d][j] = ok ? *(const uint4*)(bp + off + 16 * j) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+                for (int r = 0; r < RQ; ++r)
+                    fa[d][r][j] = ok ? *(const uint4*)(ap[r] + off + 16 * j)
+                                     : make_uint4(0, 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            if (s + d >= s1)
+                break;
+            if constexpr (OP == OP_BLOCK) {
+                const int g = (kbeg >> 7) + s + d;
+                const float sbv = a.sb[nb * KG + g];
+#pragma unroll
+                for (int r = 0; r < RQ; ++r) {
+                    const int m = min(m0 + r * 16 + (lane & 15), M - 1);
+                    const float sc = sbv * a.sa[m * KG + g];
+                    v4f pg = mfma_step<OP>(fb[d], fa[d][r], v4f{0, 0, 0, 0});
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        acc[r][v] = __builtin_fmaf(sc, pg[v], acc[r][v]);
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < RQ; ++r)
+                    acc[r] = mfma_step<OP>(fb[d], fa[d][r], acc[r]);
+            }
+        }
+    }
+
+    // Output element (r, lane, v): n = n0 + (lane >> 4) * 4 + v,
+    //                              m = m0 + r * 16 + (lane & 15).
+    auto emit = [&](int r, int ln, int v, elem_t e) {
+        const int n = n0 + (ln >> 4) * 4 + v;
+        const int m = m0 + r * 16 + (ln & 15);
+        if (m < M && n < N) {
+            if (a.splits > 1)
+                ((elem_t*)a.ws)[((size_t)z * M + m) * N + n] = e;
+            else
+                store_one<OP>(a, (size_t)m * N + n, e, m, n);
+        }
+    };
+
+    if constexpr (!KSPLIT) {
+#pragma unroll
+        for (int r = 0; r < RQ; ++r)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                emit(r, lane, v, acc[r][v]);
+    } else {
+        __shared__ elem_t red[W][RQ * 256];
+#pragma unroll
+        for (int r = 0; r < RQ; ++r)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                red[wave][r * 256 + lane * 4 + v] = acc[r][v];
+        __syncthreads();
+        for (int e = threadIdx.x; e < RQ * 256; e += W * 64) {
+            elem_t sum = red[0][e];
+#pragma unroll
+            for (int w = 1; w < W; ++w)
+                sum += red[w][e];
+            emit(e >> 8, (e & 255) >> 2, e & 3, sum);
+        }
+    }
+}
+
+template <int OP, int RQ, int W, bool KSPLIT, int D>
+hipError_t launch_skinny(const GemmArgs& a, hipStream_t stream)
+{
+    const int rows = KSPLIT ? 16 : 16 * W;
+    dim3 grid((a.N + rows - 1) / rows, (a.M + 16 * RQ - 1) / (16 * RQ), a.splits);
+    if (grid.y > 65535 || grid.z > 65535)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemm_skinny_kernel<OP, RQ, W, KSPLIT, D>), grid, dim3(W * 64), 0,
+                       stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace qll
+
+// Registry entries of the skinny kernel.  Name: "k" (waves split K) or "r"
+// (waves split rows), weight rows x tokens per workgroup, waves.
+// X(OP, RQ, TOKENS, W, KSPLIT, D) is applied to every entry.
+#define QLL_FOR_EACH_SKINNY(X, OP, DM)     \
+    X(OP, 1, 16, 8, true, 4 * (DM))        \
+    X(OP, 2, 32, 8, true, 2 * (DM))        \
+    X(OP, 4, 64, 8, true, 2 * (DM))        \
+    X(OP, 1, 16, 16, true, 2 * (DM))       \
+    X(OP, 1, 16, 4, false, 4 * (DM))       \
+    X(OP, 2, 32, 4, false, 4 * (DM))       \
+    X(OP, 4, 64, 4, false, 2 * (DM))
+
+#define QLL_SKINNY_INSTANTIATE(OP, RQ, TOK, W, KS, D) \
+    template __global__ void qll::gemm_skinny_kernel<OP, RQ, W, KS, D>(qll::GemmArgs);
+#define QLL_SKINNY_ENTRY(OP, RQ, TOK, W, KS, D)                                     \
+    {(KS) ? "k16x" #TOK "_w" #W : "r16x" #TOK "_w" #W, OP, 1, (KS) ? 16 : 16 * (W), \
+     TOK, (KS) ? 1 : (W), 1, 0, (KS) ? (W) * (RQ) * 1024 : 0,                        \
+     &qll::launch_skinny<OP, RQ, W, KS, D>},

@@ -56,6 +56,28 @@ template <> struct OpTraits<OP_BF16> {
     using elem_t = float;
 };
 
+// Workgroup -> output tile, XCD-aware.  The dispatcher hands consecutive
+// workgroup ids to the 8 XCDs in turn, and each XCD has its own L2.  The
+// tiles are numbered so that the workgroups one XCD receives form one
+// contiguous run t = xcd * per + local, and that run is laid out in groups of
+// `group` tile rows (tile_p fastest), so an XCD works on a compact block of
+// tiles that share A rows and B rows in its L2.  The map is a bijection of
+// [0, tp * tq) for any tile count; only locality depends on the dispatch
+// order.
+__device__ __forceinline__ void xcd_tile(int bid, int tp, int tq, int group,
+                                         int& tile_p, int& tile_q)
+{
+    const int T = tp * tq;
+    const int per = T >> 3, rem = T & 7;
+    const int xcd = bid & 7, loc = bid >> 3;
+    const int t = xcd < rem ? xcd * (per + 1) + loc : rem * (per + 1) + (xcd - rem) * per + loc;
+    const int span = group * tq;
+    const int first = (t / span) * group;
+    const int gsize = min(tp - first, group);
+    tile_p = first + (t % span) % gsize;
+    tile_q = (t % span) / gsize;
+}
+
 template <int OP>
 __device__ __forceinline__ typename OpTraits<OP>::acc_t
 mfma_step(const uint4* a, const uint4* b, typename OpTraits<OP>::acc_t c)
@@ -80,6 +102,18 @@ mfma_step(const uint4* a, const uint4* b, typename OpTraits<OP>::acc_t c)
         return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 0, 0,
                                                                 0, 0, 0, 0);
     }
+}
+
+// XOR swizzle of the 16-byte chunks of one staged LDS row.  A fragment read
+// has 16 lanes reading the same logical chunk of 16 consecutive rows; with
+// NC chunks per row the physical chunk is c ^ swz(row), and swz makes both
+// the first 8 and the first 16 rows of every 16-row group hit distinct
+// 16-byte bank groups whether the LDS serves 8 or 16 lanes of a b128 read per
+// cycle (NC = 8: swz = (row ^ row / 8) mod 8; NC = 16: swz = row mod 16).
+template <int NC>
+__device__ __forceinline__ int swz(int row)
+{
+    return (row ^ (row / NC)) & (NC - 1);
 }
 
 __device__ __forceinline__ uint16_t bf16_rne(float f)
@@ -196,7 +230,7 @@ __global__ __launch_bounds__(WP* WQ * 64) void gemm_tile_kernel(GemmArgs a)
             const int c = tid + i * THREADS;
             if (BP * NC % THREADS == 0 || c < BP * NC) {
                 const int row = c / NC, ch = c % NC;
-                *(uint4*)(sp + row * KSTAGE + ((ch ^ (row & (NC - 1))) << 4)) = rp[i];
+                *(uint4*)(sp + row * KSTAGE + ((ch ^ swz<NC>(row)) << 4)) = rp[i];
             }
         }
 #pragma unroll
@@ -204,7 +238,7 @@ __global__ __launch_bounds__(WP* WQ * 64) void gemm_tile_kernel(GemmArgs a)
             const int c = tid + i * THREADS;
             if (BQ * NC % THREADS == 0 || c < BQ * NC) {
                 const int row = c / NC, ch = c % NC;
-                *(uint4*)(sq + row * KSTAGE + ((ch ^ (row & (NC - 1))) << 4)) = rq[i];
+                *(uint4*)(sq + row * KSTAGE + ((ch ^ swz<NC>(row)) << 4)) = rq[i];
             }
         }
     };
@@ -236,10 +270,10 @@ __global__ __launch_bounds__(WP* WQ * 64) void gemm_tile_kernel(GemmArgs a)
         const uint8_t* sq = sp + BP * KSTAGE;
 #pragma unroll
         for (int ks = 0; ks < NSTEP; ++ks) {
-            if constexpr (OP == OP_BLOCK) {
-                if (kbeg + kt * KSTAGE + ks * KSTEP >= kend)
-                    break;
-            }
+            // steps wholly past the end of this K piece are skipped, so every
+            // variant issues the same MFMA sequence for an output element
+            if (kbeg + kt * KSTAGE + ks * KSTEP >= kend)
+                break;
             uint4 fa[RP][KB / 16], fb[RQ][KB / 16];
             const int off = ks * KSTEP + (lane >> 4) * KB;
 #pragma unroll
@@ -248,7 +282,7 @@ __global__ __launch_bounds__(WP* WQ * 64) void gemm_tile_kernel(GemmArgs a)
 #pragma unroll
                 for (int j = 0; j < KB / 16; ++j) {
                     const int ch = (off >> 4) + j;
-                    fa[i][j] = *(const uint4*)(sp + row * KSTAGE + ((ch ^ (row & (NC - 1))) << 4));
+                    fa[i][j] = *(const uint4*)(sp + row * KSTAGE + ((ch ^ swz<NC>(row)) << 4));
                 }
             }
 #pragma unroll
@@ -257,7 +291,7 @@ __global__ __launch_bounds__(WP* WQ * 64) void gemm_tile_kernel(GemmArgs a)
 #pragma unroll
                 for (int j = 0; j < KB / 16; ++j) {
                     const int ch = (off >> 4) + j;
-                    fb[i][j] = *(const uint4*)(sq + row * KSTAGE + ((ch ^ (row & (NC - 1))) << 4));
+                    fb[i][j] = *(const uint4*)(sq + row * KSTAGE + ((ch ^ swz<NC>(row)) << 4));
                 }
             }
             if constexpr (OP == OP_BLOCK) {

@@ -79,12 +79,13 @@ def test_negative_control_m_dependent_split_is_caught(qll):
     assert not torch.equal(small.view(torch.int32), full[:16].view(torch.int32))
 
 
-def test_selected_configs_keep_split_and_orientation(qll):
-    # what the dispatch picks for the BI op: one K split and one orientation
-    # per (N, K), at every M
-    vs = {v["name"]: v for v in qll.variants("bf16_bi")}
+def test_selected_configs_keep_the_k_split(qll):
+    # what the dispatch picks for the BI op: one K split per (N, K) at every
+    # M, and never a variant whose waves split K inside the workgroup (the
+    # orientation may change with M: Swap-AB reproduces the ordinary tiles bit
+    # for bit, see test_swap_equals_ordinary_bitwise)
     for N, K in workloads.BI_SHAPES + [workloads.VOCAB_SHAPE]:
         picks = [qll.select("bf16_bi", M, N, K) for M in range(1, 4097, 37)]
         eff = {qll.effective_splits("bf16_bi", K, s) for _, s in picks}
-        ori = {vs[n]["swap"] for n, _ in picks}
-        assert len(eff) == 1 and len(ori) == 1, (N, K, eff, ori)
+        assert len(eff) == 1, (N, K, eff)
+        assert not any(n.startswith("k16x") for n, _ in picks), (N, K)

@@ -260,7 +260,10 @@ def test_swap_equals_ordinary_bitwise(qll, op, fp8_cases, bf16_cases):
         A, B, _, _ = bf16_cases[(37, 300, 2056)]
         args = (dev_bf16(A), dev_bf16(B))
         fn = qll.gemm_bf16_batch_invariant
-    outs = {n: fn(*args, out_dtype="fp32", cfg=(n, 1)) for n in names(qll, op)}
+    # the "k16x" skinny variants split K across waves (another summation
+    # order by design); every other variant accumulates K in one accumulator
+    single = [n for n in names(qll, op) if not n.startswith("k16x")]
+    outs = {n: fn(*args, out_dtype="fp32", cfg=(n, 1)) for n in single}
     torch.cuda.synchronize()
     ref = outs["n128x128_w2x2_k128"].view(torch.int32)
     diff = [n for n, y in outs.items() if not torch.equal(y.view(torch.int32), ref)]
