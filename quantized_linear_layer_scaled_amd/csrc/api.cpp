@@ -208,10 +208,10 @@ int load_table(const char* path, const char* arch, int cus_want, Table** out,
         if (op == OP_BF16) {
             int n = 0;
             const Variant* v = variants(op, &n);
-            // waves that split K inside the workgroup change the reduction
-            if (std::strncmp(v[vi].name, "k16x", 4) == 0) {
+            // a variant whose waves split K must split it into the kBiFold chunks
+            if (std::strncmp(v[vi].name, "k16x", 4) == 0 && v[vi].wp != kBiFold) {
                 rc = QLL_ERR_TABLE;
-                *err = "batch-invariant entry uses a variant that splits K across waves";
+                *err = "batch-invariant entry splits K across a number of waves other than the fixed chunk count";
                 break;
             }
             const std::pair<int, int> fx(seff, 0);
@@ -244,16 +244,17 @@ int load_table(const char* path, const char* arch, int cus_want, Table** out,
 // Used when the table has no entry.  M <= 64: the skinny Swap-AB kernel (for
 // the ordinary ops its waves split K inside the workgroup); larger M: ordinary
 // tiles, with Split-K until the grid covers the CUs once.  The batch-invariant
-// op never splits K: every variant it may use accumulates the whole K range
-// of an output element in ascending order in one accumulator.
+// op never splits K across workgroups, and every variant it uses sums K in
+// the same kBiFold chunks (the skinny kernel with eight waves does so by
+// construction, the others fold their accumulator at the chunk boundaries).
 qll_cfg heuristic(int op, int64_t M, int64_t N, int64_t K)
 {
     const int cus = device_info().cus;
     const char* name;
     bool exact = true;
     if (M <= 64) {
-        if (op == OP_BF16)
-            name = M <= 16 ? "r16x16_w4" : (M <= 32 ? "r16x32_w4" : "r16x64_w4");
+        if (op == OP_BF16)  // eight waves = the kBiFold chunks
+            name = M <= 16 ? "k16x16_w8" : (M <= 32 ? "k16x32_w8" : "k16x64_w8");
         else if (M <= 16)
             name = (N + 15) / 16 >= 2 * cus ? "k16x16_w8" : "k16x16_w16";
         else
@@ -393,6 +394,7 @@ int run_gemm(int op, const void* A, const void* B, const float* sa,
     a.kbytes = (int)(K * op_esz(op));
     a.splits = effective_splits(op, K, cfg.splits);
     a.kchunk = (int)split_chunk(op, K, cfg.splits);
+    a.kfold = op == OP_BF16 ? kBiFold : 1;
     if (a.splits > 1) {
         const uint64_t need = (uint64_t)a.splits * M * N * 4;
         if (!ws || ws_bytes < need)

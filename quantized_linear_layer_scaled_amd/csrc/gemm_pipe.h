@@ -84,7 +84,7 @@ __global__ __launch_bounds__(WP* WQ * 64) void gemm_pipe_kernel(GemmArgs a)
     __shared__ __attribute__((aligned(1024))) uint8_t lds2[STAGES >= 3 ? STAGE_BYTES : 16];
     __shared__ __attribute__((aligned(1024))) uint8_t lds3[STAGES >= 4 ? STAGE_BYTES : 16];
     static_assert(STAGES <= 4, "at most four ring slots");
-    auto slot = [&](auto J) -> uint8_t* {
+    auto slot = [&](auto J) __attribute__((always_inline)) -> uint8_t* {
         constexpr int j = decltype(J)::value;
         if constexpr (j == 0)
             return lds0;
@@ -130,7 +130,7 @@ __global__ __launch_bounds__(WP* WQ * 64) void gemm_pipe_kernel(GemmArgs a)
         src[i] = base + kbeg + c * 16;
     }
 
-    auto issue = [&](int kt, uint8_t* buf) {
+    auto issue = [&](int kt, uint8_t* buf) __attribute__((always_inline)) {
         const int kb0 = kt * KSTAGE;  // relative to kbeg
 #pragma unroll
         for (int i = 0; i < LPT; ++i) {
@@ -148,7 +148,14 @@ __global__ __launch_bounds__(WP* WQ * 64) void gemm_pipe_kernel(GemmArgs a)
         for (int j = 0; j < RQ; ++j)
             acc[i][j] = acc_t{0, 0, 0, 0};
 
-    auto compute = [&](const uint8_t* sp, int kt) {
+    constexpr bool FOLD = OP == OP_BF16;
+    KFold<acc_t, RP, RQ> fold(FOLD ? a.kfold : 1, (kend - kbeg + KSTEP - 1) / KSTEP,
+                              kFoldUnit / KSTEP);
+    static_assert(!FOLD || (kFoldUnit / KSTEP) % NSTEP == 0, "fold grid must align to stages");
+
+    auto compute = [&](const uint8_t* sp, int kt) __attribute__((always_inline)) {
+        if constexpr (FOLD)
+            fold.before(kt * NSTEP, acc);  // chunk boundaries fall on stage starts
         const uint8_t* sq = sp + BP * KSTAGE;
 #pragma unroll
         for (int ks = 0; ks < NSTEP; ++ks) {
@@ -181,7 +188,6 @@ __global__ __launch_bounds__(WP* WQ * 64) void gemm_pipe_kernel(GemmArgs a)
                     acc[i][j] = mfma_step<OP>(fa[i], fb[j], acc[i][j]);
         }
     };
-
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
@@ -198,7 +204,7 @@ __global__ __launch_bounds__(WP* WQ * 64) void gemm_pipe_kernel(GemmArgs a)
             issue(2, slot(I2{}));
 
     // one K stage in ring slot J
-    auto stage = [&](auto J, int kt) {
+    auto stage = [&](auto J, int kt) __attribute__((always_inline)) {
         constexpr int j = decltype(J)::value;
         // stage kt must have landed; younger stages may stay in flight
         const int younger = min(STAGES - 2, nk - 1 - kt);
@@ -234,6 +240,9 @@ __global__ __launch_bounds__(WP* WQ * 64) void gemm_pipe_kernel(GemmArgs a)
             if (kt + 3 < nk)
                 stage(I3{}, kt + 3);
     }
+
+    if constexpr (FOLD)
+        fold.finish(acc);
 
     // Epilogue through LDS: each wave writes one 16-row block of its tile at a
     // time into a private LDS scratch, then every lane emits 8 consecutive

@@ -44,9 +44,13 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny_kernel(GemmArgs a)
     const int z = blockIdx.z;
     const int kbeg = z * a.kchunk;
     const int kend = min(a.kbytes, kbeg + a.kchunk);
+    // the waves split K on the same grid of kFoldUnit-byte units as the
+    // chunked summation of the other bf16 kernels
+    constexpr int U = kFoldUnit / KSTEP;
     const int T = (kend - kbeg + KSTEP - 1) / KSTEP;
-    const int s0 = KSPLIT ? wave * T / W : 0;
-    const int s1 = KSPLIT ? (wave + 1) * T / W : T;
+    const int TU = (T + U - 1) / U;
+    const int s0 = KSPLIT ? min(T, U * (wave * TU / W)) : 0;
+    const int s1 = KSPLIT ? min(T, U * ((wave + 1) * TU / W)) : T;
     const size_t ldk = (size_t)a.kbytes;
 
     // rows this lane loads (clamped: out-of-range rows are masked at the store)
@@ -69,6 +73,11 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny_kernel(GemmArgs a)
     const int KG = a.K / 128;
     const int nb = (min(n0, N - 1) >> 7);  // 16 weight rows share one 128-row block
 
+    // bf16 without the wave split: chunked K summation (kBiFold); with the
+    // wave split the chunks are the waves themselves (W must equal kfold).
+    constexpr bool FOLD = OP == OP_BF16 && !KSPLIT;
+    KFold<acc_t, 1, RQ> fold(FOLD ? a.kfold : 1, T, U);
+
     for (int s = s0; s < s1; s += D) {
         uint4 fb[D][NJ], fa[D][RQ][NJ];
 #pragma unroll
@@ -88,6 +97,8 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny_kernel(GemmArgs a)
         for (int d = 0; d < D; ++d) {
             if (s + d >= s1)
                 break;
+            if constexpr (FOLD)
+                fold.before(s + d, (acc_t(&)[1][RQ])acc);
             if constexpr (OP == OP_BLOCK) {
                 const int g = (kbeg >> 7) + s + d;
                 const float sbv = a.sb[nb * KG + g];
@@ -108,9 +119,12 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny_kernel(GemmArgs a)
         }
     }
 
+    if constexpr (FOLD)
+        fold.finish((acc_t(&)[1][RQ])acc);
+
     // Output element (r, lane, v): n = n0 + (lane >> 4) * 4 + v,
     //                              m = m0 + r * 16 + (lane & 15).
-    auto emit = [&](int r, int ln, int v, elem_t e) {
+    auto emit = [&](int r, int ln, int v, elem_t e) __attribute__((always_inline)) {
         const int n = n0 + (ln >> 4) * 4 + v;
         const int m = m0 + r * 16 + (ln & 15);
         if (m < M && n < N) {
@@ -160,7 +174,8 @@ hipError_t launch_skinny(const GemmArgs& a, hipStream_t stream)
 }  // namespace qll
 
 // Registry entries of the skinny kernel.  Name: "k" (waves split K) or "r"
-// (waves split rows), weight rows x tokens per workgroup, waves.
+// (waves split rows), weight rows x tokens per workgroup, waves (the wp
+// field holds the wave count).
 // X(OP, RQ, TOKENS, W, KSPLIT, D) is applied to every entry.
 #define QLL_FOR_EACH_SKINNY(X, OP, DM)     \
     X(OP, 1, 16, 8, true, 4 * (DM))        \
@@ -175,5 +190,5 @@ hipError_t launch_skinny(const GemmArgs& a, hipStream_t stream)
     template __global__ void qll::gemm_skinny_kernel<OP, RQ, W, KS, D>(qll::GemmArgs);
 #define QLL_SKINNY_ENTRY(OP, RQ, TOK, W, KS, D)                                     \
     {(KS) ? "k16x" #TOK "_w" #W : "r16x" #TOK "_w" #W, OP, 1, (KS) ? 16 : 16 * (W), \
-     TOK, (KS) ? 1 : (W), 1, 0, (KS) ? (W) * (RQ) * 1024 : 0,                        \
+     TOK, W, 1, 0, (KS) ? (W) * (RQ) * 1024 : 0,                                      \
      &qll::launch_skinny<OP, RQ, W, KS, D>},

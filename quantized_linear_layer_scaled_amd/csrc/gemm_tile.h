@@ -25,6 +25,8 @@
 //     batch-invariant entry point relies on.
 #pragma once
 
+#include <type_traits>
+
 #include "qll_internal.h"
 
 namespace qll {
@@ -157,6 +159,58 @@ __device__ __forceinline__ void store_one(const GemmArgs& a, size_t idx,
         ((float*)a.out)[idx] = y;
 }
 
+// Chunked K summation of the bf16 kernels (see kBiFold): the T MFMA steps of
+// a K piece form F chunks on a grid of U-step units (TU = ceil(T / U) units,
+// chunk w = units [w*TU/F, (w+1)*TU/F), clipped to T); each chunk is summed
+// from zero and the chunk sums are added in ascending order.  before(step)
+// closes the running chunk when `step` is a chunk boundary; finish() closes
+// the rest and leaves the result in acc.  With U a multiple of the steps per
+// K stage, every boundary falls on a stage start.
+template <typename acc_t, int RP, int RQ>
+struct KFold {
+    acc_t tot[RP][RQ];
+    int next = 1, at, F, T, U, TU;
+    bool first = true;
+    __device__ __forceinline__ KFold(int f, int t, int u) : F(f), T(t), U(u)
+    {
+        TU = (T + U - 1) / U;
+        at = F > 1 ? min(T, U * (TU / F)) : 0x7FFFFFFF;
+    }
+    __device__ __forceinline__ void close(acc_t (&acc)[RP][RQ])
+    {
+#pragma unroll
+        for (int i = 0; i < RP; ++i)
+#pragma unroll
+            for (int j = 0; j < RQ; ++j) {
+                tot[i][j] = first ? acc[i][j] : tot[i][j] + acc[i][j];
+                acc[i][j] = acc_t{0, 0, 0, 0};
+            }
+        first = false;
+    }
+    __device__ __forceinline__ void before(int step, acc_t (&acc)[RP][RQ])
+    {
+        while (step == at) {
+            close(acc);
+            ++next;
+            at = next < F ? min(T, U * (next * TU / F)) : 0x7FFFFFFF;
+        }
+    }
+    __device__ __forceinline__ void finish(acc_t (&acc)[RP][RQ])
+    {
+        if (F <= 1)
+            return;
+        while (next <= F) {
+            close(acc);
+            ++next;
+        }
+#pragma unroll
+        for (int i = 0; i < RP; ++i)
+#pragma unroll
+            for (int j = 0; j < RQ; ++j)
+                acc[i][j] = tot[i][j];
+    }
+};
+
 template <int OP, int SWAP, int BP, int BQ, int WP, int WQ, int KSTAGE>
 __global__ __launch_bounds__(WP* WQ * 64) void gemm_tile_kernel(GemmArgs a)
 {
@@ -198,7 +252,7 @@ __global__ __launch_bounds__(WP* WQ * 64) void gemm_tile_kernel(GemmArgs a)
 
     uint4 rp[LP], rq[LQ];
 
-    auto gload = [&](int kt) {
+    auto gload = [&](int kt) __attribute__((always_inline)) {
         const int kb0 = kbeg + kt * KSTAGE;
 #pragma unroll
         for (int i = 0; i < LP; ++i) {
@@ -222,7 +276,7 @@ __global__ __launch_bounds__(WP* WQ * 64) void gemm_tile_kernel(GemmArgs a)
         }
     };
 
-    auto sstore = [&](int buf) {
+    auto sstore = [&](int buf) __attribute__((always_inline)) {
         uint8_t* sp = lds + buf * STAGE_BYTES;
         uint8_t* sq = sp + BP * KSTAGE;
 #pragma unroll
@@ -250,6 +304,11 @@ __global__ __launch_bounds__(WP* WQ * 64) void gemm_tile_kernel(GemmArgs a)
         for (int j = 0; j < RQ; ++j)
             acc[i][j] = acc_t{0, 0, 0, 0};
 
+    constexpr bool FOLD = OP == OP_BF16;
+    KFold<acc_t, RP, RQ> fold(FOLD ? a.kfold : 1, (kend - kbeg + KSTEP - 1) / KSTEP,
+                              kFoldUnit / KSTEP);
+    static_assert(!FOLD || (kFoldUnit / KSTEP) % NSTEP == 0, "fold grid must align to stages");
+
     // Block-FP8 scale bookkeeping: the rows/columns of this lane.
     const int KG = a.K / 128;
     int prow[RP][4];
@@ -265,7 +324,9 @@ __global__ __launch_bounds__(WP* WQ * 64) void gemm_tile_kernel(GemmArgs a)
             qcol[j] = min(q0 + wqi * SQ + j * 16 + (lane & 15), Qdim - 1);
     }
 
-    auto compute = [&](int buf, int kt) {
+    auto compute = [&](int buf, int kt) __attribute__((always_inline)) {
+        if constexpr (FOLD)
+            fold.before(kt * NSTEP, acc);  // chunk boundaries fall on stage starts
         const uint8_t* sp = lds + buf * STAGE_BYTES;
         const uint8_t* sq = sp + BP * KSTAGE;
 #pragma unroll
@@ -338,6 +399,9 @@ __global__ __launch_bounds__(WP* WQ * 64) void gemm_tile_kernel(GemmArgs a)
             sstore(cur ^ 1);
         __syncthreads();
     }
+
+    if constexpr (FOLD)
+        fold.finish(acc);
 
     // Epilogue.
     const int M = a.M, N = a.N;

@@ -32,7 +32,17 @@ struct GemmArgs {
     int kbytes;      // K * element size
     int splits;      // effective number of K pieces
     int kchunk;      // bytes of K per piece (multiple of kSplitGranule)
+    int kfold;       // bf16 only: K chunks summed separately, then in order
 };
+
+// The batch-invariant bf16 op sums every K piece as kBiFold contiguous chunks
+// on a grid of kFoldUnit-byte units (with TU units in the piece, chunk w holds
+// units [w*TU/kBiFold, (w+1)*TU/kBiFold)), each from zero, and adds the chunk
+// sums in ascending order.  Every bf16 kernel reproduces that order, so all
+// of them agree bit for bit.  The skinny kernels' waves split K on the same
+// grid for every op.
+constexpr int kBiFold = 8;
+constexpr int kFoldUnit = 256;
 
 using LaunchFn = hipError_t (*)(const GemmArgs&, hipStream_t);
 

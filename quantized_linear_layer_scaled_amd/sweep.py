@@ -14,8 +14,9 @@ normwise 1e-2 otherwise -- the oracle parity is the test suite's job), times
 the whole call (tile kernel plus Split-K reduction) by replaying a HIP graph
 of back-to-back calls that rotate through several copies of the weights, and
 keeps the fastest configuration per bucket.  The batch-invariant op only
-considers configurations that keep one K split (1) and accumulate K in one
-accumulator, so the table it produces is accepted by the loader.
+considers configurations without a cross-workgroup K split and whose waves,
+if they split K, split it into the op's fixed eight chunks, so the table it
+produces is accepted by the loader.
 
     python -m quantized_linear_layer_scaled_amd.sweep --out tables/gfx950.tsv
     python -m quantized_linear_layer_scaled_amd.sweep --ops fp8 --shapes 4096x2048 --report
@@ -94,8 +95,8 @@ def candidates(qll, op, M, N, K):
     out = []
     for v in qll.variants(op):
         name = v["name"]
-        if op == "bf16_bi" and name.startswith("k16x"):
-            continue  # splits K across waves: not batch invariant
+        if op == "bf16_bi" and name.startswith("k16x") and v["wp"] != 8:
+            continue  # its waves split K into other chunks than the fixed eight
         if name.startswith(("k16x", "r16x")) and M > 128:
             continue  # skinny kernels hold all tokens of a tile in registers
         if name[0] in "np" and M <= 8 and v["bp"] >= 64 and not v["swap"]:

@@ -1,0 +1,205 @@
+"""CPU checks of the C ABI of libqll.so (no GPU needed, no kernel runs):
+the library loads, exports every function include/qll.h declares, validates
+arguments before any HIP call, sizes Split-K workspaces, and its dispatch
+table loader enforces the device key and the batch-invariance rule (one K
+split per (N, K), never a variant that splits K across waves).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qll.h")
+
+
+@pytest.fixture(scope="module")
+def qll():
+    import quantized_linear_layer_scaled_amd as q
+    if not os.path.exists(q.LIB_PATH):
+        from quantized_linear_layer_scaled_amd import build
+        build.build()
+    q.load_library()
+    return q
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?(?:int|int64_t|size_t|char|void)\s*\*?\s*(\w+)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_exports_every_declared_symbol(qll):
+    names = declared_functions()
+    assert len(names) >= 19, names
+    lib = qll.load_library()
+    for n in names:
+        assert hasattr(lib, n), f"libqll.so does not export {n}"
+
+
+def test_status_strings(qll):
+    L = qll.load_library()
+    for s in range(8):
+        assert L.qll_status_str(s).decode()
+    assert L.qll_status_str(99).decode() == "unknown status"
+
+
+P = 0x100000  # a fake, 16-byte aligned device address: never dereferenced
+
+
+def gemm(qll, fn, A=P, B=P, sa=P, sb=P, out=P, od=0, M=16, N=64, K=2048, ws=None,
+         wsb=0, cfg=None):
+    L = qll.load_library()
+    if fn == "gemm_bf16_batch_invariant":
+        args = [A, B, out, od, M, N, K, ws, wsb, None]
+    else:
+        args = [A, B, sa, sb, out, od, M, N, K, ws, wsb, None]
+    if cfg is not None:
+        return getattr(L, fn + "_ex")(*args, ctypes.byref(qll._cfg(
+            qll.OPS[{"gemm_w8a8_int8": "int8", "gemm_fp8_scaled": "fp8",
+                     "gemm_block_fp8": "block_fp8",
+                     "gemm_bf16_batch_invariant": "bf16_bi"}[fn]], cfg)))
+    return getattr(L, fn)(*args)
+
+
+GEMMS = ["gemm_w8a8_int8", "gemm_fp8_scaled", "gemm_block_fp8",
+         "gemm_bf16_batch_invariant"]
+
+
+@pytest.mark.parametrize("fn", GEMMS)
+def test_gemm_argument_validation(qll, fn):
+    INVALID, MISALIGNED = 1, 3
+    assert gemm(qll, fn, M=-1) == INVALID
+    assert gemm(qll, fn, N=0) == INVALID
+    assert gemm(qll, fn, K=0) == INVALID
+    assert gemm(qll, fn, K=2048 + 4) == INVALID          # K not a multiple of 8/16
+    assert gemm(qll, fn, A=None) == INVALID
+    assert gemm(qll, fn, out=None) == INVALID
+    assert gemm(qll, fn, od=7) == INVALID
+    assert gemm(qll, fn, A=P + 8) == MISALIGNED
+    assert gemm(qll, fn, out=P + 2) == MISALIGNED
+    assert gemm(qll, fn, M=0, A=None, out=None) == 0     # M == 0 is a no-op
+    if fn != "gemm_w8a8_int8":
+        assert gemm(qll, fn, od=2) == INVALID            # raw int32 out: INT8 only
+    if fn == "gemm_block_fp8":
+        assert gemm(qll, fn, K=2048 + 16) == INVALID     # K % 128
+    if fn != "gemm_bf16_batch_invariant":
+        assert gemm(qll, fn, sa=None) == INVALID
+        assert gemm(qll, fn, sb=P + 2) == MISALIGNED
+
+
+def test_int8_k_limit_and_forced_cfg(qll):
+    assert gemm(qll, "gemm_w8a8_int8", K=131072) == 1
+    assert gemm(qll, "gemm_w8a8_int8", cfg=(0, 0)) == 1                 # splits < 1
+    assert gemm(qll, "gemm_w8a8_int8", cfg=(999, 1)) == 1               # no such variant
+    assert gemm(qll, "gemm_w8a8_int8", cfg=(0, 65)) == 1                # too many splits
+
+
+@pytest.mark.parametrize("fn", GEMMS)
+def test_missing_workspace_is_reported_before_launch(qll, fn):
+    # a 4-way split of K needs S*M*N*4 bytes; nothing is launched
+    assert gemm(qll, fn, cfg=(0, 4), ws=None, wsb=0) == 4
+    assert gemm(qll, fn, cfg=(0, 4), ws=P, wsb=16) == 4
+    assert gemm(qll, fn, cfg=(0, 4), ws=P + 4, wsb=1 << 30) == 3
+
+
+def test_quantizer_validation(qll):
+    L = qll.load_library()
+    q = L.quantize_per_token_fp8
+    assert q(P, P, P, 4, 2048 + 8, 0, None) == 1      # K % 16
+    assert q(P, P, P, 4, 2048, 64, None) == 2         # only per-token and 128 groups
+    assert q(P, P, P, 4, 2048 + 16, 128, None) == 1   # group 128 needs K % 128
+    assert q(None, P, P, 4, 2048, 0, None) == 1
+    assert q(P + 8, P, P, 4, 2048, 0, None) == 3
+    assert q(None, None, None, 0, 2048, 0, None) == 0
+    w = L.quantize_weight_block_fp8
+    assert w(P, P, P, 300, 2048 + 16, None) == 1
+    assert w(P, P + 1, P, 300, 2048, None) == 3
+
+
+def test_effective_splits_and_workspace(qll):
+    # K pieces are multiples of 512 bytes: fp8 K=2048 allows 4, bf16 K=2048 8
+    assert qll.effective_splits("fp8", 2048, 8) == 4
+    assert qll.effective_splits("fp8", 2048, 3) == 2
+    assert qll.effective_splits("bf16_bi", 2048, 8) == 8
+    assert qll.effective_splits("fp8", 6144, 4) == 4
+    assert qll.effective_splits("int8", 2048, 1) == 1
+    name = qll.variants("fp8")[0]["name"]
+    assert qll.workspace_bytes("fp8", 16, 2048, 2048, (name, 4)) == 4 * 16 * 2048 * 4
+    assert qll.workspace_bytes("fp8", 16, 2048, 2048, (name, 1)) == 0
+    # the split is idempotent: applying it to its own result keeps it
+    for K in (2048, 2064, 4096, 6144, 10000 - 10000 % 16):
+        for s in range(1, 17):
+            e = qll.effective_splits("fp8", K, s)
+            assert qll.effective_splits("fp8", K, e) == e
+
+
+def test_variant_registry(qll):
+    for op in ("int8", "fp8", "block_fp8", "bf16_bi"):
+        vs = qll.variants(op)
+        names = [v["name"] for v in vs]
+        assert len(names) == len(set(names)) >= 10
+        for v in vs:
+            assert v["op"] == op and v["lds"] <= 160 * 1024
+            L = qll.load_library()
+            assert L.qll_variant_index(qll.OPS[op], v["name"].encode()) == v["index"]
+    assert qll.load_library().qll_variant_index(1, b"nope") == -1
+
+
+def test_init_without_device(qll):
+    L = qll.load_library()
+    rc = L.qll_init(None)
+    import torch
+    if not torch.cuda.is_available():
+        assert rc == 5  # QLL_ERR_NO_DEVICE
+
+
+# ---------------------------------------------------------------- tables
+def write(tmp_path, text):
+    p = tmp_path / "t.tsv"
+    p.write_text(text)
+    return str(p)
+
+
+def test_shipped_table_is_valid_for_mi355x(qll):
+    path = os.path.join(os.path.dirname(qll.LIB_PATH), "tables", "gfx950.tsv")
+    rc, why = qll.table_validate(path, "gfx950", 256)
+    assert rc == 0, why
+    rc, why = qll.table_validate(path, "gfx942", 304)
+    assert rc == 6 and "another device" in why
+
+
+def test_table_rules(qll, tmp_path):
+    fp8 = qll.variants("fp8")[0]["name"]
+    bi = [v["name"] for v in qll.variants("bf16_bi")]
+    single = [n for n in bi if not n.startswith("k16x")]
+    head = "# test\ndevice gfx950 256\n"
+    ok = write(tmp_path, head + f"fp8 4096 2048 1 {fp8} 2\nfp8 4096 2048 2 {fp8} 1\n")
+    assert qll.table_validate(ok, "gfx950", 256) == (0, "")
+    assert qll.table_validate(ok, "gfx950", 304)[0] == 6
+    assert qll.table_validate(write(tmp_path, f"fp8 4096 2048 1 {fp8} 2\n"), "gfx950", 256)[0] == 6
+    assert qll.table_validate(write(tmp_path, head + "fp8 4096 2048 3 x 1\n"), "gfx950", 256)[0] == 6
+    assert qll.table_validate(write(tmp_path, head + f"fp8 4096 2048 3 {fp8} 1\n"), "gfx950", 256)[0] == 6
+    assert qll.table_validate(write(tmp_path, head + f"int4 4096 2048 4 {fp8} 1\n"), "gfx950", 256)[0] == 6
+    assert qll.table_validate(str(tmp_path / "missing.tsv"), "gfx950", 256)[0] == 6
+    # batch-invariant: one effective K split per (N, K) ...
+    good = write(tmp_path, head + f"bf16_bi 2048 2048 1 {single[0]} 1\n"
+                                   f"bf16_bi 2048 2048 2 {single[1]} 1\n"
+                                   f"bf16_bi 4096 2048 2 {single[1]} 2\n")
+    assert qll.table_validate(good, "gfx950", 256) == (0, "")
+    bad = write(tmp_path, head + f"bf16_bi 2048 2048 1 {single[0]} 1\n"
+                                  f"bf16_bi 2048 2048 2048 {single[1]} 2\n")
+    rc, why = qll.table_validate(bad, "gfx950", 256)
+    assert rc == 6 and "split" in why
+    # ... and no variant whose waves split K into other than the eight chunks
+    vs = qll.variants("bf16_bi")
+    k8 = [v["name"] for v in vs if v["name"].startswith("k16x") and v["wp"] == 8][0]
+    k16 = [v["name"] for v in vs if v["name"].startswith("k16x") and v["wp"] == 16][0]
+    rc, why = qll.table_validate(write(tmp_path, head + f"bf16_bi 2048 2048 1 {k16} 1\n"),
+                                 "gfx950", 256)
+    assert rc == 6 and "waves" in why
+    assert qll.table_validate(write(tmp_path, head + f"bf16_bi 2048 2048 1 {k8} 1\n"),
+                              "gfx950", 256) == (0, "")

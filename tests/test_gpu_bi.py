@@ -81,11 +81,13 @@ def test_negative_control_m_dependent_split_is_caught(qll):
 
 def test_selected_configs_keep_the_k_split(qll):
     # what the dispatch picks for the BI op: one K split per (N, K) at every
-    # M, and never a variant whose waves split K inside the workgroup (the
-    # orientation may change with M: Swap-AB reproduces the ordinary tiles bit
-    # for bit, see test_swap_equals_ordinary_bitwise)
+    # M, and no variant whose waves split K into other than the fixed eight
+    # chunks (orientation and tile may change with M: every other variant
+    # reproduces the same sums bit for bit, see
+    # test_swap_equals_ordinary_bitwise)
     for N, K in workloads.BI_SHAPES + [workloads.VOCAB_SHAPE]:
         picks = [qll.select("bf16_bi", M, N, K) for M in range(1, 4097, 37)]
         eff = {qll.effective_splits("bf16_bi", K, s) for _, s in picks}
         assert len(eff) == 1, (N, K, eff)
-        assert not any(n.startswith("k16x") for n, _ in picks), (N, K)
+        vs = {v["name"]: v for v in qll.variants("bf16_bi")}
+        assert not any(n.startswith("k16x") and vs[n]["wp"] != 8 for n, _ in picks), (N, K)
