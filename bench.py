@@ -10,12 +10,22 @@ output channel on the device once, before timing.  Every (N, K, M) problem
 has its own buffers (about 350 MB touched per step, more than the 256 MB
 Infinity Cache), so a problem's weights come from HBM, not from a cache.
 
-Timing: W untimed warm-up steps, then K timed steps bracketed by
-torch.cuda.synchronize(); each kernel launch is bracketed by HIP events on the
-stream the library launches on, which gives per-kernel durations.  value =
-GEMM flops of a step / step time (TFLOPS).  The line also carries the
-roofline of the dominant kernel (the GEMM kernel with the most time per step)
-and the CPU oracle timed on a bounded sample of the same workload.
+Timing (all on the one stream the library launches on):
+  * value: after W warm-up steps, K steps launched from the host through the
+    C ABI (prebuilt arguments, no per-call Python work) are timed between
+    HIP events; value = GEMM flops of a step / step time (TFLOPS);
+  * graph_value: the same step captured once into a HIP graph and replayed K
+    times (graph-covered execution, the launch mode the pages recommend for
+    tuned kernels);
+  * per call: for every quantizer and GEMM call of the step, a HIP graph of
+    --copies back-to-back launches, each on its own copy of the call's buffers
+    (cold data), timed with HIP events: this gives the per-shape table and the
+    roofline of the dominant kernel (the GEMM kernel with the most time per
+    step among single-kernel calls).
+The line also carries the CPU oracle timed on a bounded sample of the same
+workload, and, when the rocprofv3 counter CSVs are given (--fetch-csv,
+--write-csv), the HBM traffic of the dominant kernel scaled by the same
+counters read on a copy kernel of known size (--calib-copy runs that copy).
 
 Other workloads (--workload int8|block|bi|vocab) print the same JSON shape.
 
@@ -50,8 +60,16 @@ def parse():
                    help="rows per problem the CPU oracle computes")
     p.add_argument("--table", default="default",
                    help="dispatch table ('default', a path, or 'none')")
-    p.add_argument("--traffic", default=None,
-                   help="JSON file with the measured HBM bytes of the dominant kernel")
+    p.add_argument("--fetch-csv", default=None,
+                   help="rocprofv3 --pmc FETCH_SIZE counter_collection.csv of this command")
+    p.add_argument("--write-csv", default=None,
+                   help="rocprofv3 --pmc WRITE_SIZE counter_collection.csv of this command")
+    p.add_argument("--calib-copy", action="store_true",
+                   help="also run a plain device copy of known size (counter calibration)")
+    p.add_argument("--no-graph", action="store_true",
+                   help="no graphs: eager steps only, no per-call timing (counter runs)")
+    p.add_argument("--copies", type=int, default=8,
+                   help="buffer copies per call for the per-call timing graphs")
     return p.parse_args()
 
 
@@ -67,6 +85,7 @@ class Problem:
         self.op, self.M, self.N, self.K = op, M, N, K
         self.calls = []       # [(name, cfunc, args)]
         self.keep = []        # tensors that must stay alive
+        self.tensors = {}     # kind -> (tensor dict, args builder)
 
     @property
     def flops(self):
@@ -105,18 +124,21 @@ def build_problems(torch, qll, workload):
         t = torch.empty(n, dtype=torch.uint8, device="cuda")
         return t, n
 
+    def gemm_args(p, t):
+        wsp = t["ws"].data_ptr() if t["ws"] is not None else None
+        if p.op == "bf16_bi":
+            return (t["A"].data_ptr(), t["B"].data_ptr(), t["out"].data_ptr(), 0, p.M, p.N,
+                    p.K, wsp, t["wsb"], stream)
+        return (t["A"].data_ptr(), t["B"].data_ptr(), t["sa"].data_ptr(), t["sb"].data_ptr(),
+                t["out"].data_ptr(), 0, p.M, p.N, p.K, wsp, t["wsb"], stream)
+
     def add_gemm(p, fn, A, B, sa, sb):
         out = torch.empty((p.M, p.N), dtype=torch.bfloat16, device="cuda")
         ws, wsb = ws_for(p.op, p.M, p.N, p.K)
-        p.keep += [A, B, out] + [t for t in (sa, sb, ws) if t is not None]
-        wsp = ws.data_ptr() if ws is not None else None
-        if p.op == "bf16_bi":
-            args = (A.data_ptr(), B.data_ptr(), out.data_ptr(), 0, p.M, p.N, p.K,
-                    wsp, wsb, stream)
-        else:
-            args = (A.data_ptr(), B.data_ptr(), sa.data_ptr(), sb.data_ptr(),
-                    out.data_ptr(), 0, p.M, p.N, p.K, wsp, wsb, stream)
-        p.calls.append(("gemm", getattr(L, fn), args))
+        t = dict(A=A, B=B, sa=sa, sb=sb, out=out, ws=ws, wsb=wsb)
+        p.keep += [A, B, out] + [x for x in (sa, sb, ws) if x is not None]
+        p.calls.append(("gemm", getattr(L, fn), gemm_args(p, t)))
+        p.tensors["gemm"] = (t, gemm_args)
         p.variant, p.splits = qll.select(p.op, p.M, p.N, p.K)
         p.eff_splits = qll.effective_splits(p.op, p.K, p.splits)
 
@@ -125,8 +147,11 @@ def build_problems(torch, qll, workload):
         G = p.K if group == 0 else group
         s = torch.empty((p.M, p.K // G), dtype=torch.float32, device="cuda")
         p.keep += [x, q, s]
-        p.calls.append(("quant", L.quantize_per_token_fp8,
-                        (x.data_ptr(), q.data_ptr(), s.data_ptr(), p.M, p.K, group, stream)))
+        qargs = lambda p, t: (t["x"].data_ptr(), t["q"].data_ptr(), t["s"].data_ptr(), p.M,
+                              p.K, group, stream)
+        t = dict(x=x, q=q, s=s)
+        p.calls.append(("quant", L.quantize_per_token_fp8, qargs(p, t)))
+        p.tensors["quant"] = (t, qargs)
         return q, s
 
     if workload in ("fp8", "vocab"):
@@ -182,6 +207,38 @@ def build_problems(torch, qll, workload):
 # timing
 # --------------------------------------------------------------------------
 
+def per_call_us(torch, probs, copies, stream):
+    """Average duration of every call, each timed on its own: a HIP graph of
+    `copies` back-to-back launches of the call, launch r on its own copy of
+    the call's buffers (so every launch reads cold data), replayed once to
+    warm up and once between HIP events.  Returns [[us per call kind]]."""
+    out = []
+    for p in probs:
+        row = []
+        for kind, fn, _ in p.calls:
+            base, make = p.tensors[kind]
+            sets = []
+            for _ in range(copies):
+                t = {k: (v.clone() if isinstance(v, torch.Tensor) else v)
+                     for k, v in base.items()}
+                sets.append((t, make(p, t)))
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for _, args in sets:
+                    fn(*args)
+            g.replay()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            row.append(e0.elapsed_time(e1) * 1e3 / copies)
+            del g, sets
+        out.append(row)
+    torch.cuda.empty_cache()
+    return out
+
+
 def run_step(probs, events=None):
     for i, p in enumerate(probs):
         for j, (_, fn, args) in enumerate(p.calls):
@@ -195,9 +252,17 @@ def run_step(probs, events=None):
 
 
 def kernel_symbol(qll, op, variant):
-    """The kernel's name as rocprofv3 prints it."""
+    """The kernel's name as rocprofv3 prints it (for the skinny kernel, whose
+    last template argument the registry does not list, the name up to it)."""
     opn = {"int8": 0, "fp8": 1, "block_fp8": 2, "bf16_bi": 3}[op]
     v = next(x for x in qll.variants(op) if x["name"] == variant)
+    if variant[0] == "p":
+        st = variant.rsplit("_s", 1)[1]
+        return (f"void qll::gemm_pipe_kernel<{opn}, {v['bp']}, {v['bq']}, {v['wp']}, "
+                f"{v['wq']}, {v['kstage']}, {st}, false>(qll::GemmArgs)")
+    if variant[0] in "kr":
+        return (f"void qll::gemm_skinny_kernel<{opn}, {v['bq'] // 16}, {v['wp']}, "
+                f"{'true' if variant[0] == 'k' else 'false'}, ")
     return (f"void qll::gemm_tile_kernel<{opn}, {v['swap']}, {v['bp']}, {v['bq']}, "
             f"{v['wp']}, {v['wq']}, {v['kstage']}>(qll::GemmArgs)")
 
@@ -268,6 +333,40 @@ def cpu_baseline(workload, rows_cap):
             "seconds": round(t_total, 2)}
 
 
+CALIB_BYTES = 512 << 20  # the copy kernel moves this many bytes each way
+
+
+def counter_per_dispatch(csv_path, counter):
+    """{kernel name: [value per dispatch]} from a rocprofv3 counter CSV."""
+    import csv
+    out = {}
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            if r.get("Counter_Name") == counter:
+                out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return out
+
+
+def hbm_traffic(fetch_csv, write_csv, kernel):
+    """HBM bytes per launch of `kernel`: FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch), each scaled by the ratio of known bytes to what the same
+    counter reads for the calibration copy (CALIB_BYTES read and written)."""
+    res = {}
+    for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        d = counter_per_dispatch(path, name)
+        ks = [v for k, v in d.items() if k.startswith(kernel)]
+        cal = [v for k, v in d.items() if "copy" in k.lower() or "elementwise" in k.lower()]
+        if not ks or not cal:
+            return None
+        vals = ks[0]
+        cal_kib = max(max(c) for c in cal)   # the large calibration copy
+        factor = CALIB_BYTES / (cal_kib * 1024.0)
+        res[name] = (sum(vals) / len(vals)) * 1024.0 * factor
+        res[name + "_factor"] = factor
+    res["bytes_per_launch"] = res["FETCH_SIZE"] + res["WRITE_SIZE"]
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -287,44 +386,73 @@ def main():
           f"{props.multi_processor_count} CUs; table entries {table_used} (init rc {rc})",
           file=sys.stderr, flush=True)
 
+    # one stream for everything: the prebuilt calls, the events and the
+    # graph capture all use it (default priority)
+    stream = torch.cuda.Stream()
+    torch.cuda.set_stream(stream)
     probs = build_problems(torch, qll, args.workload)
     print(f"# {len(probs)} problems built", file=sys.stderr, flush=True)
-    def new_events():
-        return [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                 for _ in p.calls] for p in probs]
 
     for _ in range(args.warmup):
         run_step(probs)
     torch.cuda.synchronize()
 
-    # one set of events per timed step, created before the timed region
-    step_events = [new_events() for _ in range(args.steps)]
+    # ---- timed region 1: graph replays of the whole step -> value
+    ms_graph = None
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            run_step(probs)
+        graph.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        g0.record()
+        for _ in range(args.steps):
+            graph.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        ms_graph = g0.elapsed_time(g1) / args.steps
+        print(f"# graph step {ms_graph * 1e3:.1f} us", file=sys.stderr, flush=True)
+
+    # ---- timed region 2: eager steps (host launches, no graph)
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_wall0 = time.perf_counter()
     start.record()
     for step in range(args.steps):
-        run_step(probs, step_events[step])
+        run_step(probs)
     end.record()
     torch.cuda.synchronize()
-    durations = [[[ev[i][j] for ev in step_events] for j in range(len(p.calls))]
-                 for i, p in enumerate(probs)]
     wall = time.perf_counter() - t_wall0
-    total_ms = start.elapsed_time(end)
-    ms_per_step = total_ms / args.steps
+    ms_eager = start.elapsed_time(end) / args.steps
+    ms_per_step = ms_eager
 
-    # per-kernel average durations (ms)
+    # ---- timed region 3: every call on its own (graph of cold copies)
+    if args.no_graph:  # counter-collection runs: launches only, no timing
+        call_us = [[1.0 for _ in p.calls] for p in probs]
+    else:
+        call_us = per_call_us(torch, probs, args.copies, stream)
+
+    if args.calib_copy:
+        # an elementwise kernel that reads CALIB_BYTES and writes CALIB_BYTES
+        src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
+    # per-call average durations (ms)
     per_shape = []
-    kernels = {}  # symbol -> [total_ms, launches, flops, bytes]
+    kernels = {}  # symbol -> [total s, launches, flops, bytes, dtype, bounds, splits]
     gemm_flops_step = 0.0
     for i, p in enumerate(probs):
         rec = {"op": p.op, "M": p.M, "N": p.N, "K": p.K, "variant": p.variant,
                "splits": p.eff_splits}
         for j, (kind, _, _) in enumerate(p.calls):
-            ts = [a.elapsed_time(b) for a, b in durations[i][j]]
-            avg = sum(ts) / len(ts)
-            rec[f"{kind}_us"] = round(avg * 1e3, 3)
+            rec[f"{kind}_us"] = round(call_us[i][j], 3)
         t_gemm = rec["gemm_us"] * 1e-6
         dt = {"fp8": "fp8", "block_fp8": "fp8", "int8": "int8", "bf16_bi": "bf16"}[p.op]
         t_mem = p.algo_bytes() / (HBM_GBS * 1e9)
@@ -337,13 +465,16 @@ def main():
             rec["quant_gbs"] = round(p.quant_bytes() / (rec["quant_us"] * 1e-6) / 1e9, 1)
         per_shape.append(rec)
         gemm_flops_step += p.flops
+        if p.eff_splits > 1:
+            continue  # two kernels per call: not comparable with a kernel trace
         sym = kernel_symbol(qll, p.op, p.variant)
-        k = kernels.setdefault(sym, [0.0, 0, 0.0, 0.0, dt, []])
+        k = kernels.setdefault(sym, [0.0, 0, 0.0, 0.0, dt, [], []])
         k[0] += t_gemm
         k[1] += 1
         k[2] += p.flops
         k[3] += p.algo_bytes()
         k[5].append(rec["bound"])
+        k[6].append(p.eff_splits)
 
     dom_sym, dom = max(kernels.items(), key=lambda kv: kv[1][0])
     avg_dur = dom[0] / dom[1]
@@ -357,16 +488,22 @@ def main():
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_GBS, 4)}
     roof["traffic"] = None
-    if args.traffic and os.path.exists(args.traffic):
-        with open(args.traffic) as f:
-            tr = json.load(f)
-        if tr.get("kernel") == dom_sym:
-            roof["traffic"] = tr.get("bytes_per_launch")
+    if args.fetch_csv and args.write_csv and os.path.exists(args.fetch_csv) \
+            and os.path.exists(args.write_csv):
+        tr = hbm_traffic(args.fetch_csv, args.write_csv, dom_sym)
+        if tr:
+            roof["traffic"] = round(tr["bytes_per_launch"])
+            roof["traffic_detail"] = {k: round(v, 4) for k, v in tr.items()}
     roof["kernel"] = dom_sym
     roof["launches_per_step"] = dom[1]
     roof["avg_us"] = round(avg_dur * 1e6, 3)
     roof["algorithmic_per_launch"] = (round(dom[2] / dom[1]) if bound == "mfma"
                                       else round(dom[3] / dom[1]))
+    roof["algorithmic_bytes_per_launch"] = round(dom[3] / dom[1])
+    roof["timing"] = (f"per call: HIP graph of {args.copies} back-to-back launches on cold "
+                      "buffer copies, timed with HIP events; the dominant kernel is the one "
+                      "with the most time per step among calls that launch a single kernel "
+                      "(no Split-K)")
 
     value = gemm_flops_step / (ms_per_step * 1e-3) / 1e12
     names = {"fp8": "FP8 dynamic per-token sweep: (N,K) in {(4096,2048),(2048,6144)}, "
@@ -392,7 +529,11 @@ def main():
         "config": {"workload": names[args.workload],
                    "problems_per_step": len(probs),
                    "dispatch": "table" if table_used else "heuristic",
+                   "timing": "eager C-ABI launches (graph replay in graph_value)",
                    "cold_weights": True},
+        "graph_ms_per_step": round(ms_graph, 4) if ms_graph is not None else None,
+        "graph_value": (round(gemm_flops_step / (ms_graph * 1e-3) / 1e12, 3)
+                        if ms_graph is not None else None),
         "roofline": roof,
         "cpu_baseline": None,
         "wall_s_timed": round(wall, 3),
@@ -403,6 +544,12 @@ def main():
     if not args.no_cpu_baseline:
         print("# timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_rows)
+    for r in per_shape:
+        print(f"#  {r['op']:9s} M={r['M']:5d} N={r['N']:6d} K={r['K']:5d} {r['variant']:24s} "
+              f"S={r['splits']} gemm {r['gemm_us']:8.2f} us {r['tflops']:8.1f} TFLOPS "
+              f"{r['gbs']:7.0f} GB/s {r['bound']} {100 * r['roof_frac']:5.1f}%"
+              + (f"  quant {r['quant_us']:6.2f} us" if 'quant_us' in r else ""),
+              file=sys.stderr)
     print(json.dumps(line), flush=True)
 
 

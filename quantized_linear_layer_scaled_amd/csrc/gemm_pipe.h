@@ -55,7 +55,9 @@ __device__ __forceinline__ void wait_vm_barrier()
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-template <int OP, int BP, int BQ, int WP, int WQ, int KSTAGE, int STAGES>
+// SPLITK only gives the first stage of a Split-K call its own kernel symbol
+// (the code is the same), so that traces separate the two kinds of launch.
+template <int OP, int BP, int BQ, int WP, int WQ, int KSTAGE, int STAGES, bool SPLITK>
 __global__ __launch_bounds__(WP* WQ * 64) void gemm_pipe_kernel(GemmArgs a)
 {
     using Tr = OpTraits<OP>;
@@ -307,9 +309,13 @@ hipError_t launch_pipe(const GemmArgs& a, hipStream_t stream)
     const long tiles = (long)((a.M + BP - 1) / BP) * ((a.N + BQ - 1) / BQ);
     if (tiles > 0x7FFFFFFFL)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gemm_pipe_kernel<OP, BP, BQ, WP, WQ, KSTAGE, STAGES>),
-                       dim3((unsigned)tiles, (unsigned)a.splits), dim3(WP * WQ * 64), 0,
-                       stream, a);
+    if (a.splits > 1)
+        hipLaunchKernelGGL((gemm_pipe_kernel<OP, BP, BQ, WP, WQ, KSTAGE, STAGES, true>),
+                           dim3((unsigned)tiles, (unsigned)a.splits), dim3(WP * WQ * 64), 0,
+                           stream, a);
+    else
+        hipLaunchKernelGGL((gemm_pipe_kernel<OP, BP, BQ, WP, WQ, KSTAGE, STAGES, false>),
+                           dim3((unsigned)tiles, 1), dim3(WP * WQ * 64), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -325,8 +331,9 @@ hipError_t launch_pipe(const GemmArgs& a, hipStream_t stream)
     X(OP, 128, 64, 2, 2, 128, 4)           \
     X(OP, 64, 128, 2, 2, 128, 4)
 
-#define QLL_PIPE_INSTANTIATE(OP, BP, BQ, WP, WQ, KS, ST) \
-    template __global__ void qll::gemm_pipe_kernel<OP, BP, BQ, WP, WQ, KS, ST>(qll::GemmArgs);
+#define QLL_PIPE_INSTANTIATE(OP, BP, BQ, WP, WQ, KS, ST)                                       \
+    template __global__ void qll::gemm_pipe_kernel<OP, BP, BQ, WP, WQ, KS, ST, false>(qll::GemmArgs); \
+    template __global__ void qll::gemm_pipe_kernel<OP, BP, BQ, WP, WQ, KS, ST, true>(qll::GemmArgs);
 #define QLL_PIPE_ENTRY(OP, BP, BQ, WP, WQ, KS, ST)                                   \
     {"p" #BP "x" #BQ "_w" #WP "x" #WQ "_k" #KS "_s" #ST, OP, 0, BP, BQ, WP, WQ, KS,    \
      (ST) * ((BP) + (BQ)) * (KS), &qll::launch_pipe<OP, BP, BQ, WP, WQ, KS, ST>},
