@@ -178,6 +178,24 @@ int gemm_bf16_batch_invariant_ex(const void* A, const void* B, void* out,
                                  int64_t K, void* ws, size_t ws_bytes,
                                  void* stream, const qll_cfg* cfg);
 
+/* FP8 dynamic linear layer in one call ("FP8 dynamic quantization", same
+ * section): quantize_per_token_fp8(x -> q, sa) followed by
+ * gemm_fp8_scaled(q, B, sa, sb -> out) with the configuration the dispatch
+ * (or cfg) picks, both enqueued on `stream`.  Results, codes and scales are
+ * bitwise those of the two calls.
+ *   x bf16 [M][K] (in); B e4m3 [N][K]; sb fp32 [N];
+ *   q e4m3 [M][K] and sa fp32 [M] (out, required: the quantized activations);
+ *   out bf16 / fp32 [M][N]; ws as for gemm_fp8_scaled (Split-K;
+ *   qll_workspace_bytes(QLL_OP_FP8, ...)).
+ * Errors: those of the two calls; nothing is launched on an invalid argument. */
+int linear_fp8_dynamic(const void* x, const void* B, const float* sb, void* q,
+                       float* sa, void* out, int out_dtype, int64_t M, int64_t N,
+                       int64_t K, void* ws, size_t ws_bytes, void* stream);
+int linear_fp8_dynamic_ex(const void* x, const void* B, const float* sb, void* q,
+                          float* sa, void* out, int out_dtype, int64_t M, int64_t N,
+                          int64_t K, void* ws, size_t ws_bytes, void* stream,
+                          const qll_cfg* cfg);
+
 /* ------------------------------------------------------------------ */
 /* Dispatch, registry and support                                      */
 /* ------------------------------------------------------------------ */

@@ -10,7 +10,8 @@ raises.
 
 Operations (see include/qll.h for the full contract):
   quantize_per_token_fp8, quantize_weight_block_fp8,
-  gemm_w8a8_int8, gemm_fp8_scaled, gemm_block_fp8, gemm_bf16_batch_invariant.
+  gemm_w8a8_int8, gemm_fp8_scaled, gemm_block_fp8, gemm_bf16_batch_invariant,
+  linear_fp8_dynamic (per-token quantization + FP8 GEMM in one call).
 """
 from __future__ import annotations
 
@@ -67,6 +68,9 @@ def load_library():
         getattr(L, name + "_ex").argtypes = _GEMM_ARGS + [ctypes.POINTER(qll_cfg)]
     L.gemm_bf16_batch_invariant.argtypes = _BF16_ARGS
     L.gemm_bf16_batch_invariant_ex.argtypes = _BF16_ARGS + [ctypes.POINTER(qll_cfg)]
+    _LIN = [_P, _P, _P, _P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _P, ctypes.c_size_t, _P]
+    L.linear_fp8_dynamic.argtypes = _LIN
+    L.linear_fp8_dynamic_ex.argtypes = _LIN + [ctypes.POINTER(qll_cfg)]
     L.qll_init.argtypes = [ctypes.c_char_p]
     L.qll_table_validate.argtypes = [ctypes.c_char_p, ctypes.c_char_p, ctypes.c_int,
                                      ctypes.c_char_p, ctypes.c_size_t]
@@ -316,6 +320,35 @@ def gemm_bf16_batch_invariant(A, B, out_dtype="bf16", out=None, cfg=None,
         rc = L.gemm_bf16_batch_invariant(*args)
     _check("gemm_bf16_batch_invariant", rc)
     return out
+
+
+def linear_fp8_dynamic(x, B, sb, out_dtype="bf16", out=None, q=None, sa=None, cfg=None,
+                       workspace=None, stream=None):
+    """bf16 x [M][K] -> (out [M][N], q e4m3 [M][K], sa fp32 [M][1]): per-token
+    quantization of x and the scaled FP8 GEMM with e4m3 B [N][K], sb [N]."""
+    torch = _torch()
+    _ensure_init()
+    if x.dtype != torch.bfloat16 or x.dim() != 2:
+        raise ValueError("x must be a 2-D bfloat16 tensor")
+    M, K = x.shape
+    N, K2 = B.shape
+    if K2 != K:
+        raise ValueError(f"x is [M][{K}] but B is [N][{K2}]")
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.float8_e4m3fn, device=x.device)
+    if sa is None:
+        sa = torch.empty((M, 1), dtype=torch.float32, device=x.device)
+    out = _out(out, M, N, out_dtype, x.device)
+    c = _cfg(1, cfg)
+    ws, wsb = _workspace(1, M, N, K, c, workspace)
+    L = load_library()
+    args = [_dev_ptr(x, "x"), _bytes8(B, "B"), _f32(sb, "sb", (N,)), _bytes8(q, "q"),
+            _f32(sa, "sa", (M,)), _dev_ptr(out, "out"), OUT[out_dtype], M, N, K,
+            ws.data_ptr() if ws is not None else None, wsb, _stream(stream)]
+    rc = L.linear_fp8_dynamic_ex(*args, ctypes.byref(c)) if c else L.linear_fp8_dynamic(*args)
+    _check("linear_fp8_dynamic", rc)
+    return out, q, sa
+
 
 
 # --------------------------------------------------------------------------

@@ -528,6 +528,46 @@ int gemm_bf16_batch_invariant(const void* A, const void* B, void* out,
                     ws, ws_bytes, stream, nullptr);
 }
 
+int linear_fp8_dynamic_ex(const void* x, const void* B, const float* sb, void* q,
+                          float* sa, void* out, int out_dtype, int64_t M, int64_t N,
+                          int64_t K, void* ws, size_t ws_bytes, void* stream,
+                          const qll_cfg* cfg)
+{
+    if (!q || !sa || !x)
+        return M == 0 && N > 0 && K > 0 ? QLL_OK : QLL_ERR_INVALID_ARG;
+    int rc = validate_gemm(OP_FP8, x, B, sa, sb, out, out_dtype, M, N, K);
+    if (rc != QLL_OK)
+        return rc;
+    if (cfg && (rc = validate_cfg(OP_FP8, cfg)) != QLL_OK)
+        return rc;
+    if (misaligned(q, 16))
+        return QLL_ERR_MISALIGNED;
+    if (M == 0)
+        return QLL_OK;
+    const qll_cfg c = cfg ? *cfg : select_cfg(OP_FP8, M, N, K);
+    // the GEMM's own workspace checks, before anything is enqueued
+    const int splits = effective_splits(OP_FP8, K, c.splits);
+    if (splits > 1) {
+        if (!ws || ws_bytes < (uint64_t)splits * M * N * 4)
+            return QLL_ERR_WORKSPACE;
+        if (misaligned(ws, 16))
+            return QLL_ERR_MISALIGNED;
+    }
+    rc = quantize_per_token_fp8(x, q, sa, M, K, 0, stream);
+    if (rc != QLL_OK)
+        return rc;
+    return run_gemm(OP_FP8, q, B, sa, sb, out, out_dtype, M, N, K, ws, ws_bytes, stream,
+                    &c);
+}
+
+int linear_fp8_dynamic(const void* x, const void* B, const float* sb, void* q, float* sa,
+                       void* out, int out_dtype, int64_t M, int64_t N, int64_t K, void* ws,
+                       size_t ws_bytes, void* stream)
+{
+    return linear_fp8_dynamic_ex(x, B, sb, q, sa, out, out_dtype, M, N, K, ws, ws_bytes,
+                                 stream, nullptr);
+}
+
 int qll_init(const char* table_path)
 {
     const char* path = table_path;

@@ -115,14 +115,16 @@ __global__ __launch_bounds__(WP* WQ * 64) void gemm_pipe_kernel(GemmArgs a)
 
     // Source of each of this thread's LPT loads: LDS chunk index
     // L = (i * WAVES + wave) * 64 + lane holds logical chunk
-    // (L % NC) ^ swz(row) of tile row L / NC.
+    // (L % NC) ^ swz(r) of stage row L / NC, r its row within the A or B part.
     const uint8_t* src[LPT];
     int coff[LPT];
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
         const int L = (i * WAVES + wave) * 64 + lane;
         const int row = L / NC;
-        const int c = (L % NC) ^ swz<NC>(row);
+        // the fragment reads swizzle with the row index inside the A part or
+        // the B part of the stage, so the copy must do the same
+        const int c = (L % NC) ^ swz<NC>(row < BP ? row : row - BP);
         coff[i] = c * 16;
         const uint8_t* base;
         if (row < BP)
@@ -329,7 +331,10 @@ hipError_t launch_pipe(const GemmArgs& a, hipStream_t stream)
     X(OP, 128, 256, 2, 2, 128, 3)          \
     X(OP, 256, 128, 4, 2, 128, 3)          \
     X(OP, 128, 64, 2, 2, 128, 4)           \
-    X(OP, 64, 128, 2, 2, 128, 4)
+    X(OP, 64, 128, 2, 2, 128, 4)           \
+    X(OP, 32, 128, 1, 4, 128, 4)           \
+    X(OP, 64, 64, 2, 2, 128, 4)            \
+    X(OP, 128, 32, 4, 1, 128, 4)
 
 #define QLL_PIPE_INSTANTIATE(OP, BP, BQ, WP, WQ, KS, ST)                                       \
     template __global__ void qll::gemm_pipe_kernel<OP, BP, BQ, WP, WQ, KS, ST, false>(qll::GemmArgs); \

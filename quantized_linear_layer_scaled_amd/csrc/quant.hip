@@ -11,9 +11,9 @@
 // round to nearest even) after the clamp.
 //
 // All three kernels are HBM-bound (read 2 bytes, write 1 byte per element):
-//   quant_rows:        one workgroup per row, the row held in registers,
-//                      wave max by cross-lane shuffles, then across the
-//                      workgroup's waves through LDS;
+//   quant_rows:        one wave per row, the row held in registers, max by
+//                      cross-lane shuffles (very long rows: one workgroup
+//                      per row, two passes, max across waves through LDS);
 //   quant_groups128:   16 lanes per 1x128 group (8 bf16 per lane), shuffle
 //                      max inside the 16 lanes; no LDS;
 //   quant_weight_blocks: one workgroup per 128x128 weight block.
@@ -75,46 +75,47 @@ __device__ __forceinline__ float wave_max(float v)
     return v;
 }
 
-// One workgroup of 256 threads per row; the row (K <= 256 * 8 * CH) stays in
-// registers between the max and the conversion.
+// One wave per row, four rows per 256-thread workgroup: the row
+// (K <= 64 * 8 * CH) stays in registers between the max and the conversion,
+// the max is a wave-level shuffle reduction (no LDS, no barrier), and each
+// lane keeps CH 16-byte loads in flight.
 template <int CH>
 __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restrict__ x,
                                                         uint8_t* __restrict__ q,
-                                                        float* __restrict__ s, int K)
+                                                        float* __restrict__ s, int M, int K)
 {
-    const int m = blockIdx.x;
-    const int tid = threadIdx.x;
+    const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (m >= M)
+        return;
     const uint16_t* xr = x + (size_t)m * K;
     uint8_t* qr = q + (size_t)m * K;
     uint4 v[CH];
     float amax = 0.0f;
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-        const int e = (c * 256 + tid) * 8;
+        const int e = (c * 64 + lane) * 8;
         v[c] = make_uint4(0, 0, 0, 0);
         if (e < K)
             v[c] = *(const uint4*)(xr + e);
-        amax = fmaxf(amax, absmax8(v[c]));
     }
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+        amax = fmaxf(amax, absmax8(v[c]));
     amax = wave_max(amax);
-    __shared__ float red[4];
-    if ((tid & 63) == 0)
-        red[tid >> 6] = amax;
-    __syncthreads();
-    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     const float sc = amax / 448.0f;
-    if (tid == 0)
+    if (lane == 0)
         s[m] = sc;
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-        const int e = (c * 256 + tid) * 8;
+        const int e = (c * 64 + lane) * 8;
         if (e < K)
             *(uint2*)(qr + e) = encode8(v[c], sc);
     }
 }
 
-// Rows longer than 256 * 8 * 8 elements: two passes over the row (the second
-// one hits the caches).
+// Rows longer than 64 * 8 * 16 elements: one workgroup per row, two passes
+// over the row (the second one hits the caches).
 __global__ __launch_bounds__(256) void quant_rows_long_kernel(const uint16_t* __restrict__ x,
                                                              uint8_t* __restrict__ q,
                                                              float* __restrict__ s, int K)
@@ -208,20 +209,30 @@ __global__ __launch_bounds__(256) void quant_weight_blocks_kernel(const uint16_t
 hipError_t launch_quant_rows(const void* x, void* q, float* s, int M, int K,
                              hipStream_t stream)
 {
-    const int ch = (K + 2047) / 2048;
+    const int ch = (K + 511) / 512;  // 16-byte chunks per lane, one wave per row
     const uint16_t* xp = (const uint16_t*)x;
     uint8_t* qp = (uint8_t*)q;
-    dim3 grid(M), block(256);
+    dim3 grid((M + 3) / 4), block(256);
     switch (ch) {
-    case 1: hipLaunchKernelGGL(quant_rows_kernel<1>, grid, block, 0, stream, xp, qp, s, K); break;
-    case 2: hipLaunchKernelGGL(quant_rows_kernel<2>, grid, block, 0, stream, xp, qp, s, K); break;
-    case 3: hipLaunchKernelGGL(quant_rows_kernel<3>, grid, block, 0, stream, xp, qp, s, K); break;
-    case 4: hipLaunchKernelGGL(quant_rows_kernel<4>, grid, block, 0, stream, xp, qp, s, K); break;
+    case 1: hipLaunchKernelGGL(quant_rows_kernel<1>, grid, block, 0, stream, xp, qp, s, M, K); break;
+    case 2: hipLaunchKernelGGL(quant_rows_kernel<2>, grid, block, 0, stream, xp, qp, s, M, K); break;
+    case 3:
+    case 4: hipLaunchKernelGGL(quant_rows_kernel<4>, grid, block, 0, stream, xp, qp, s, M, K); break;
     case 5:
-    case 6: hipLaunchKernelGGL(quant_rows_kernel<6>, grid, block, 0, stream, xp, qp, s, K); break;
+    case 6: hipLaunchKernelGGL(quant_rows_kernel<6>, grid, block, 0, stream, xp, qp, s, M, K); break;
     case 7:
-    case 8: hipLaunchKernelGGL(quant_rows_kernel<8>, grid, block, 0, stream, xp, qp, s, K); break;
-    default: hipLaunchKernelGGL(quant_rows_long_kernel, grid, block, 0, stream, xp, qp, s, K); break;
+    case 8: hipLaunchKernelGGL(quant_rows_kernel<8>, grid, block, 0, stream, xp, qp, s, M, K); break;
+    case 9:
+    case 10:
+    case 11:
+    case 12: hipLaunchKernelGGL(quant_rows_kernel<12>, grid, block, 0, stream, xp, qp, s, M, K); break;
+    case 13:
+    case 14:
+    case 15:
+    case 16: hipLaunchKernelGGL(quant_rows_kernel<16>, grid, block, 0, stream, xp, qp, s, M, K); break;
+    default:
+        hipLaunchKernelGGL(quant_rows_long_kernel, dim3(M), block, 0, stream, xp, qp, s, K);
+        break;
     }
     return hipGetLastError();
 }

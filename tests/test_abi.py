@@ -106,6 +106,28 @@ def test_missing_workspace_is_reported_before_launch(qll, fn):
     assert gemm(qll, fn, cfg=(0, 4), ws=P + 4, wsb=1 << 30) == 3
 
 
+def test_linear_fp8_dynamic_validation(qll):
+    # x, B, sb, q, sa, out, out_dtype, M, N, K, ws, ws_bytes, stream
+    L = qll.load_library()
+
+    def lin(x=P, q=P, sa=P, M=16, K=2048, ws=None, wsb=0, cfg=None):
+        args = [x, P, P, q, sa, P, 0, M, 64, K, ws, wsb, None]
+        if cfg is None:
+            return L.linear_fp8_dynamic(*args)
+        return L.linear_fp8_dynamic_ex(*args, ctypes.byref(qll._cfg(qll.OPS["fp8"], cfg)))
+
+    assert lin(q=None) == 1
+    assert lin(sa=None) == 1
+    assert lin(x=None) == 1
+    assert lin(K=2048 + 8, cfg=(0, 1)) == 1
+    assert lin(x=P + 8, cfg=(0, 1)) == 3
+    assert lin(q=P + 8, cfg=(0, 1)) == 3
+    assert lin(M=0, x=None, q=None, sa=None) == 0
+    # the GEMM's workspace is checked before the quantizer is enqueued
+    assert lin(cfg=(0, 4)) == 4
+    assert lin(cfg=(0, 4), ws=P + 4, wsb=1 << 30) == 3
+
+
 def test_quantizer_validation(qll):
     L = qll.load_library()
     q = L.quantize_per_token_fp8
