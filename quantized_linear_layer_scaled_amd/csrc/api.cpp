@@ -66,6 +66,13 @@ const char* const kOpNames[OP_COUNT] = {"int8", "fp8", "block_fp8", "bf16_bi"};
 
 int op_esz(int op) { return op == OP_BF16 ? 2 : 1; }
 
+// The pipelined kernels address a tile's rows with 32-bit buffer offsets:
+// their tile rows times the row length in bytes must stay below 2^31.
+bool variant_fits(const Variant& v, int64_t kbytes)
+{
+    return v.name[0] != 'p' || (int64_t)v.bp * kbytes <= 0x7FFFFFFF;
+}
+
 // ------------------------------------------------------------------ device
 struct DeviceInfo {
     bool ok = false;
@@ -204,6 +211,14 @@ int load_table(const char* path, const char* arch, int cus_want, Table** out,
             *err = std::string("bad entry: ") + p;
             break;
         }
+        {
+            int n = 0;
+            if (!variant_fits(variants(op, &n)[vi], K * op_esz(op))) {
+                rc = QLL_ERR_TABLE;
+                *err = std::string("entry's variant does not support this K: ") + p;
+                break;
+            }
+        }
         const int seff = effective_splits(op, K, splits);
         if (op == OP_BF16) {
             int n = 0;
@@ -242,8 +257,9 @@ int load_table(const char* path, const char* arch, int cus_want, Table** out,
 
 // ------------------------------------------------------------------ heuristic
 // Used when the table has no entry.  M <= 64: the skinny Swap-AB kernel (for
-// the ordinary ops its waves split K inside the workgroup); larger M: ordinary
-// tiles, with Split-K until the grid covers the CUs once.  The batch-invariant
+// the ordinary ops its waves split K inside the workgroup); larger M: the
+// pipelined ordinary tiles with two-stage rings (several workgroups per CU),
+// growing with M, with Split-K until the grid covers the CUs once.  The batch-invariant
 // op never splits K across workgroups, and every variant it uses sums K in
 // the same kBiFold chunks (the skinny kernel with eight waves does so by
 // construction, the others fold their accumulator at the chunk boundaries).
@@ -267,12 +283,12 @@ qll_cfg heuristic(int op, int64_t M, int64_t N, int64_t K)
             name = "n128x256_w2x2_k";
         else
             name = "n128x128_w2x2_k";
-    } else if (M <= 128) {
-        name = "p64x128_w2x2_k128_s4";
-    } else if (((M + 255) / 256) * ((N + 127) / 128) >= cus) {
-        name = "p256x128_w4x2_k128_s3";
+    } else if (M <= 512) {
+        name = "p64x64_w2x2_k128_s2";
+    } else if (M <= 1024) {
+        name = "p128x64_w2x2_k128_s2";
     } else {
-        name = "p128x128_w2x2_k128_s4";
+        name = "p128x128_w2x2_k128_s2";
     }
     int n = 0;
     const Variant* v = variants(op, &n);
@@ -283,11 +299,17 @@ qll_cfg heuristic(int op, int64_t M, int64_t N, int64_t K)
             vi = i;
             break;
         }
+    const int64_t kbytes = K * op_esz(op);
+    if (!variant_fits(v[vi], kbytes))  // very long rows: the plain tiled kernel
+        for (int i = 0; i < n; ++i)
+            if (std::strncmp(v[i].name, "n128x128_w2x2_k", 15) == 0) {
+                vi = i;
+                break;
+            }
     if (op == OP_BF16 || M <= 64)
         return qll_cfg{vi, 1};
     const int64_t tiles = ((v[vi].swap ? N : M) + v[vi].bp - 1) / v[vi].bp *
                           (((v[vi].swap ? M : N) + v[vi].bq - 1) / v[vi].bq);
-    const int64_t kbytes = K * op_esz(op);
     int s = 1;
     while (tiles * s < cus && (int64_t)s * 2 * 1024 <= kbytes && s < 16)
         s *= 2;
@@ -380,6 +402,8 @@ int run_gemm(int op, const void* A, const void* B, const float* sa,
     int nv = 0;
     const Variant* vs = variants(op, &nv);
     const Variant& v = vs[cfg.variant];
+    if (!variant_fits(v, K * op_esz(op)))
+        return QLL_ERR_UNSUPPORTED;
     GemmArgs a;
     a.A = A;
     a.B = B;
@@ -545,7 +569,10 @@ int linear_fp8_dynamic_ex(const void* x, const void* B, const float* sb, void* q
     if (M == 0)
         return QLL_OK;
     const qll_cfg c = cfg ? *cfg : select_cfg(OP_FP8, M, N, K);
-    // the GEMM's own workspace checks, before anything is enqueued
+    // the GEMM's own checks, before anything is enqueued
+    int nv = 0;
+    if (!variant_fits(variants(OP_FP8, &nv)[c.variant], K))
+        return QLL_ERR_UNSUPPORTED;
     const int splits = effective_splits(OP_FP8, K, c.splits);
     if (splits > 1) {
         if (!ws || ws_bytes < (uint64_t)splits * M * N * 4)

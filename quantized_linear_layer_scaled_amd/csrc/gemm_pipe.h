@@ -6,20 +6,28 @@
 // The plain tiled kernel prefetches one stage into registers, so every K step
 // waits for a full global-memory round trip.  Here:
 //   * operands go from global memory straight into LDS with
-//     global_load_lds_dwordx4 (no VGPR staging, no ds_write), STAGES-1 stages
-//     ahead, in a ring of STAGES LDS buffers (the K loop is unrolled by
-//     STAGES so that every slot is a compile-time LDS object);
+//     buffer_load_dwordx4 ... lds (no VGPR staging, no ds_write) into a ring
+//     of STAGES LDS buffers, every buffer holding a stage in flight;
+//   * the MFMA fragments of a stage are read from LDS into one of two
+//     register sets while the MFMAs of the previous stage run on the other,
+//     so a ring slot is free as soon as its fragments are in registers (the
+//     K loop is unrolled by lcm(STAGES, 2) so that every slot is a
+//     compile-time LDS object and every register set a fixed set);
 //   * a wave waits only for its own oldest stage (s_waitcnt vmcnt(N) with N
-//     the loads of the younger stages still allowed in flight) and then meets
-//     the other waves at one s_barrier per stage -- the barrier also frees the
-//     buffer that the next prefetch overwrites;
+//     the loads of the younger stages still allowed in flight) and for its
+//     LDS reads, and then meets the other waves at one s_barrier per stage --
+//     the barrier also frees the buffer that the next prefetch overwrites;
 //   * each lane's 64 destination bytes are fixed by the hardware (lane i of a
 //     wave writes bytes 16i..16i+15 of the wave's 1 KiB block), so the XOR
 //     swizzle of 16-byte chunks is applied on the global side: the lane that
 //     fills LDS chunk (row, j) fetches logical chunk j ^ swz(row);
-//   * loads past the end of the K range read a 16-byte zero block, so the
-//     K tail needs no masking in the MFMA loop; rows past M or N are clamped
-//     (their outputs are discarded at the store).
+//   * the A and B tiles are addressed through buffer resources whose range
+//     ends at the last row of the matrix, with one 32-bit offset per load:
+//     rows past M or N fall outside the range, and a load past the end of
+//     the K range gets an offset outside it, so the hardware fills both with
+//     zeros and the MFMA loop needs no masking (outputs of rows past M or N
+//     are discarded at the store).  This needs BP * K bytes < 2^31, which the
+//     host checks.
 // Output element accumulation is the same ascending sequence of MFMA K steps
 // as in the other kernels, so results are bitwise equal to theirs for the
 // same K split.
@@ -31,34 +39,68 @@
 
 namespace qll {
 
-// 16 zero bytes that loads past the K range read (one copy per translation
-// unit; never written).
-static __device__ __attribute__((aligned(16))) uint4 g_zero16[1];
+// Raw buffer resource (GFX9 layout): 48-bit base, stride 0, num_records
+// bytes, 32-bit data format; loads at offsets past num_records return zeros.
+__device__ __forceinline__ v4i buffer_rsrc(const void* base, uint32_t bytes)
+{
+    const uint64_t b = (uint64_t)(uintptr_t)base;
+    v4i r;
+    r.x = (int)(uint32_t)b;
+    r.y = (int)(uint32_t)(b >> 32) & 0xFFFF;
+    r.z = (int)bytes;
+    r.w = 0x00020000;
+    return r;
+}
 
-// One 16-byte global -> LDS copy per lane (global_load_lds_dwordx4): lane i
-// of the wave writes LDS bytes lds_base + 16 i .. + 15.  Issued from inline
+// Offset that lies outside every resource built here (num_records < 2^31).
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+// One 16-byte buffer -> LDS copy per lane (buffer_load_dwordx4 ... lds): lane
+// i of the wave writes LDS bytes lds_base + 16 i .. + 15.  Issued from inline
 // asm so that the compiler, which cannot tell the ring slots apart, does not
 // add a wait for every copy in flight before each LDS read; the only
 // synchronization is the explicit vmcnt wait + barrier below.  The asm has no
 // register outputs; M0 is set inside the same block.
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds_base)
+__device__ __forceinline__ void dma16(uint32_t voff, v4i rsrc, uint32_t lds_base)
 {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 ::"v"(g), "s"(lds_base)
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 ::"v"(voff), "s"(rsrc), "s"(lds_base)
                  : "memory", "m0");
 }
 
+// Wait until at most N of this wave's global->LDS copies are in flight and
+// all of its LDS reads have returned, then meet the other waves.  The wait is
+// the s_waitcnt builtin (vmcnt(N) lgkmcnt(0), GFX9 encoding) so that the
+// compiler knows the LDS reads issued before it are complete and does not
+// make later MFMAs wait for reads issued after it.
 template <int N>
 __device__ __forceinline__ void wait_vm_barrier()
 {
     static_assert(N >= 0 && N < 64, "vmcnt out of range");
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+    asm volatile("s_barrier" ::: "memory");
+}
+
+// Waves per SIMD the register allocation has to allow: as many workgroups
+// as the LDS ring lets share a CU (160 KiB of LDS, at most four), each with
+// WP x WQ waves over the CU's four SIMDs.  Several resident workgroups are
+// what keeps the global->LDS copies of one overlapping the barrier waits and
+// MFMAs of another.
+template <int BP, int BQ, int WP, int WQ, int KSTAGE, int STAGES>
+constexpr int pipe_waves_per_eu()
+{
+    constexpr int lds = STAGES * (BP + BQ) * KSTAGE;
+    constexpr int wgs = 163840 / lds < 4 ? 163840 / lds : 4;
+    constexpr int w = wgs * WP * WQ / 4;
+    return w < 1 ? 1 : (w > 8 ? 8 : w);
 }
 
 // SPLITK only gives the first stage of a Split-K call its own kernel symbol
 // (the code is the same), so that traces separate the two kinds of launch.
 template <int OP, int BP, int BQ, int WP, int WQ, int KSTAGE, int STAGES, bool SPLITK>
-__global__ __launch_bounds__(WP* WQ * 64) void gemm_pipe_kernel(GemmArgs a)
+__global__ __launch_bounds__(WP* WQ * 64)
+__attribute__((amdgpu_waves_per_eu(pipe_waves_per_eu<BP, BQ, WP, WQ, KSTAGE, STAGES>())))
+void gemm_pipe_kernel(GemmArgs a)
 {
     using Tr = OpTraits<OP>;
     using acc_t = typename Tr::acc_t;
@@ -76,7 +118,7 @@ __global__ __launch_bounds__(WP* WQ * 64) void gemm_pipe_kernel(GemmArgs a)
     constexpr int STAGE_BYTES = ROWS * KSTAGE;
     static_assert(ROWS * NC % THREADS == 0, "stage must split evenly over the waves");
     static_assert((NC & (NC - 1)) == 0 && KSTAGE % KSTEP == 0, "bad K stage");
-    static_assert(STAGES >= 2 && (STAGES - 2) * LPT < 64, "bad pipeline depth");
+    static_assert(STAGES >= 2 && (STAGES - 1) * LPT < 64, "bad pipeline depth");
     static_assert(OP != OP_BLOCK, "block scaling is not pipelined here");
 
     // One LDS object per ring slot, the slot known at compile time in the
@@ -100,7 +142,7 @@ __global__ __launch_bounds__(WP* WQ * 64) void gemm_pipe_kernel(GemmArgs a)
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int wpi = wave % WP, wqi = wave / WP;
     const int M = a.M, N = a.N;
     const int tp = (M + BP - 1) / BP, tq = (N + BQ - 1) / BQ;
@@ -111,37 +153,48 @@ __global__ __launch_bounds__(WP* WQ * 64) void gemm_pipe_kernel(GemmArgs a)
     const int kbeg = z * a.kchunk;
     const int kend = min(a.kbytes, kbeg + a.kchunk);
     const int nk = (kend - kbeg + KSTAGE - 1) / KSTAGE;
-    const size_t ldk = (size_t)a.kbytes;
+    const uint32_t ldk = (uint32_t)a.kbytes;
+
+    // The tile's A rows and B rows as two buffers, each ending at the last
+    // row of its matrix.
+    const v4i rsA = buffer_rsrc((const uint8_t*)a.A + (size_t)p0 * ldk,
+                                (uint32_t)min((uint64_t)(M - p0) * ldk, (uint64_t)0x7FFFFFFF));
+    const v4i rsB = buffer_rsrc((const uint8_t*)a.B + (size_t)q0 * ldk,
+                                (uint32_t)min((uint64_t)(N - q0) * ldk, (uint64_t)0x7FFFFFFF));
 
     // Source of each of this thread's LPT loads: LDS chunk index
     // L = (i * WAVES + wave) * 64 + lane holds logical chunk
-    // (L % NC) ^ swz(r) of stage row L / NC, r its row within the A or B part.
-    const uint8_t* src[LPT];
-    int coff[LPT];
-#pragma unroll
-    for (int i = 0; i < LPT; ++i) {
+    // (L % NC) ^ swz(r) of stage row L / NC, r its row within the A or B
+    // part (the fragment reads swizzle with that row index).  One load
+    // instruction fills 1024 / KSTAGE whole rows of one part, so the part is
+    // wave-uniform.
+    auto chunk_of = [&](int i) __attribute__((always_inline)) {
         const int L = (i * WAVES + wave) * 64 + lane;
         const int row = L / NC;
-        // the fragment reads swizzle with the row index inside the A part or
-        // the B part of the stage, so the copy must do the same
-        const int c = (L % NC) ^ swz<NC>(row < BP ? row : row - BP);
-        coff[i] = c * 16;
-        const uint8_t* base;
-        if (row < BP)
-            base = (const uint8_t*)a.A + (size_t)min(p0 + row, M - 1) * ldk;
-        else
-            base = (const uint8_t*)a.B + (size_t)min(q0 + row - BP, N - 1) * ldk;
-        src[i] = base + kbeg + c * 16;
+        return (L % NC) ^ swz<NC>(row < BP ? row : row - BP);
+    };
+    auto in_a = [&](int i) __attribute__((always_inline)) {
+        return (i * WAVES + wave) * 64 / NC < BP;
+    };
+    uint32_t voff[LPT];
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+        const int row = ((i * WAVES + wave) * 64 + lane) / NC;
+        const int r = in_a(i) ? row : row - BP;
+        voff[i] = (uint32_t)r * ldk + (uint32_t)kbeg + (uint32_t)chunk_of(i) * 16u;
     }
 
     auto issue = [&](int kt, uint8_t* buf) __attribute__((always_inline)) {
         const int kb0 = kt * KSTAGE;  // relative to kbeg
+        const bool full = kbeg + kb0 + KSTAGE <= kend;
 #pragma unroll
         for (int i = 0; i < LPT; ++i) {
-            const bool live = kbeg + kb0 + coff[i] < kend;
-            const void* g = live ? (const void*)(src[i] + kb0) : (const void*)g_zero16;
-            dma16(g, __builtin_amdgcn_readfirstlane(
-                         (uint32_t)(uintptr_t)(buf + (i * WAVES + wave) * 1024)));
+            uint32_t vo = voff[i] + (uint32_t)kb0;
+            if (!full && kbeg + kb0 + chunk_of(i) * 16 >= kend)
+                vo = kOutOfRange;  // past the K range: zeros
+            dma16(vo, in_a(i) ? rsA : rsB,
+                  __builtin_amdgcn_readfirstlane(
+                      (uint32_t)(uintptr_t)(buf + (i * WAVES + wave) * 1024)));
         }
     };
 
@@ -157,93 +210,133 @@ __global__ __launch_bounds__(WP* WQ * 64) void gemm_pipe_kernel(GemmArgs a)
                               kFoldUnit / KSTEP);
     static_assert(!FOLD || (kFoldUnit / KSTEP) % NSTEP == 0, "fold grid must align to stages");
 
-    auto compute = [&](const uint8_t* sp, int kt) __attribute__((always_inline)) {
-        if constexpr (FOLD)
-            fold.before(kt * NSTEP, acc);  // chunk boundaries fall on stage starts
+    // The MFMA fragments of one K step (the wave's RP A blocks and RQ B
+    // blocks) are read from LDS into one of two register sets while the
+    // MFMAs of the previous step run on the other, so the LDS latency hides
+    // behind the matrix cores.  Global step g = kt * NSTEP + ks uses set g % 2.
+    struct Frag {
+        uint4 a[RP][KB / 16];
+        uint4 b[RQ][KB / 16];
+    };
+    Frag fr[2];
+    auto load_step = [&](const uint8_t* sp, int ks, Frag& f) __attribute__((always_inline)) {
         const uint8_t* sq = sp + BP * KSTAGE;
+        const int off = ks * KSTEP + (lane >> 4) * KB;
 #pragma unroll
-        for (int ks = 0; ks < NSTEP; ++ks) {
-            if (kbeg + kt * KSTAGE + ks * KSTEP >= kend)
-                break;
-            uint4 fa[RP][KB / 16], fb[RQ][KB / 16];
-            const int off = ks * KSTEP + (lane >> 4) * KB;
+        for (int i = 0; i < RP; ++i) {
+            const int row = wpi * SP + i * 16 + (lane & 15);
 #pragma unroll
-            for (int i = 0; i < RP; ++i) {
-                const int row = wpi * SP + i * 16 + (lane & 15);
-#pragma unroll
-                for (int j = 0; j < KB / 16; ++j) {
-                    const int ch = (off >> 4) + j;
-                    fa[i][j] = *(const uint4*)(sp + row * KSTAGE + ((ch ^ swz<NC>(row)) << 4));
-                }
+            for (int j = 0; j < KB / 16; ++j) {
+                const int ch = (off >> 4) + j;
+                f.a[i][j] = *(const uint4*)(sp + row * KSTAGE + ((ch ^ swz<NC>(row)) << 4));
             }
-#pragma unroll
-            for (int i = 0; i < RQ; ++i) {
-                const int row = wqi * SQ + i * 16 + (lane & 15);
-#pragma unroll
-                for (int j = 0; j < KB / 16; ++j) {
-                    const int ch = (off >> 4) + j;
-                    fb[i][j] = *(const uint4*)(sq + row * KSTAGE + ((ch ^ swz<NC>(row)) << 4));
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < RP; ++i)
-#pragma unroll
-                for (int j = 0; j < RQ; ++j)
-                    acc[i][j] = mfma_step<OP>(fa[i], fb[j], acc[i][j]);
         }
+#pragma unroll
+        for (int i = 0; i < RQ; ++i) {
+            const int row = wqi * SQ + i * 16 + (lane & 15);
+#pragma unroll
+            for (int j = 0; j < KB / 16; ++j) {
+                const int ch = (off >> 4) + j;
+                f.b[i][j] = *(const uint4*)(sq + row * KSTAGE + ((ch ^ swz<NC>(row)) << 4));
+            }
+        }
+    };
+    auto compute_step = [&](const Frag& f, int kt, int ks) __attribute__((always_inline)) {
+        if (kbeg + kt * KSTAGE + ks * KSTEP >= kend)
+            return;  // steps past the K range (zero-filled) are skipped
+#pragma unroll
+        for (int i = 0; i < RP; ++i)
+#pragma unroll
+            for (int j = 0; j < RQ; ++j)
+                acc[i][j] = mfma_step<OP>(f.a[i], f.b[j], acc[i][j]);
+    };
+    // wait for the oldest stage in flight with `younger` later stages still
+    // allowed in flight
+    auto wait_stage = [&](int younger) __attribute__((always_inline)) {
+        if (STAGES >= 4 && younger >= 3)
+            wait_vm_barrier<(STAGES >= 4 ? 3 : 0) * LPT>();
+        else if (STAGES >= 3 && younger >= 2)
+            wait_vm_barrier<(STAGES >= 3 ? 2 : 0) * LPT>();
+        else if (younger >= 1)
+            wait_vm_barrier<LPT>();
+        else
+            wait_vm_barrier<0>();
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
     using I3 = std::integral_constant<int, 3>;
 
-    // prologue: stages 0 .. STAGES-2 in flight
+    // prologue: every ring slot receives a stage (0 .. STAGES-1); the
+    // fragments of step 0 go to register set 0
     if (0 < nk)
         issue(0, slot(I0{}));
+    if (1 < nk)
+        issue(1, slot(I1{}));
     if constexpr (STAGES >= 3)
-        if (1 < nk)
-            issue(1, slot(I1{}));
-    if constexpr (STAGES >= 4)
         if (2 < nk)
             issue(2, slot(I2{}));
+    if constexpr (STAGES >= 4)
+        if (3 < nk)
+            issue(3, slot(I3{}));
+    if (0 < nk) {
+        wait_stage(min(STAGES - 1, nk - 1));
+        load_step(slot(I0{}), 0, fr[0]);
+    }
 
-    // one K stage in ring slot J
+    // stage kt (J = kt mod U, U a multiple of STAGES with U * NSTEP even, so
+    // that ring slot and register set are compile-time constants): the steps
+    // of the stage run one after the other, each reading the next step's
+    // fragments first.  Before the last step, once stage kt+1 has landed for
+    // every wave and every wave holds its stage-kt fragments in registers,
+    // slot kt % STAGES takes stage kt + STAGES and the first step of stage
+    // kt+1 is read from the next slot.
+    constexpr int U = (NSTEP % 2 == 0 || STAGES % 2 == 0) ? STAGES : 2 * STAGES;
     auto stage = [&](auto J, int kt) __attribute__((always_inline)) {
         constexpr int j = decltype(J)::value;
-        // stage kt must have landed; younger stages may stay in flight
-        const int younger = min(STAGES - 2, nk - 1 - kt);
-        if constexpr (STAGES >= 4) {
-            if (younger >= 2)
-                wait_vm_barrier<2 * LPT>();
-            else if (younger == 1)
-                wait_vm_barrier<LPT>();
-            else
-                wait_vm_barrier<0>();
-        } else if constexpr (STAGES == 3) {
-            if (younger >= 1)
-                wait_vm_barrier<LPT>();
-            else
-                wait_vm_barrier<0>();
-        } else {
-            wait_vm_barrier<0>();
+        constexpr int cs = j % STAGES, ns = (j + 1) % STAGES;
+        if constexpr (FOLD)
+            fold.before(kt * NSTEP, acc);  // chunk boundaries fall on stage starts
+#pragma unroll
+        for (int ks = 0; ks < NSTEP; ++ks) {
+            const int cp = (j * NSTEP + ks) & 1;
+            if (ks + 1 < NSTEP) {
+                load_step(slot(std::integral_constant<int, cs>{}), ks + 1, fr[cp ^ 1]);
+            } else {
+                // the fragments of this step are in registers on every path
+                // from here on, so the compiler never holds the MFMAs for the
+                // reads issued below
+                __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+                if (kt + 1 < nk) {
+                    wait_stage(min(STAGES - 2, nk - 2 - kt));
+                    if (kt + STAGES < nk)
+                        issue(kt + STAGES, slot(std::integral_constant<int, cs>{}));
+                    load_step(slot(std::integral_constant<int, ns>{}), 0, fr[cp ^ 1]);
+                }
+            }
+            compute_step(fr[cp], kt, ks);
         }
-        // the slot consumed one stage ago is free again for all waves
-        if (kt + STAGES - 1 < nk)
-            issue(kt + STAGES - 1, slot(std::integral_constant<int, (j + STAGES - 1) % STAGES>{}));
-        compute(slot(J), kt);
     };
-
-    for (int kt = 0; kt < nk; kt += STAGES) {
+    for (int kt = 0; kt < nk; kt += U) {
         stage(I0{}, kt);
         if (kt + 1 < nk)
             stage(I1{}, kt + 1);
-        if constexpr (STAGES >= 3)
+        if constexpr (U >= 3) {
             if (kt + 2 < nk)
                 stage(I2{}, kt + 2);
-        if constexpr (STAGES >= 4)
+        }
+        if constexpr (U >= 4) {
             if (kt + 3 < nk)
                 stage(I3{}, kt + 3);
+        }
+        if constexpr (U >= 6) {
+            if (kt + 4 < nk)
+                stage(std::integral_constant<int, 4>{}, kt + 4);
+            if (kt + 5 < nk)
+                stage(std::integral_constant<int, 5>{}, kt + 5);
+        }
     }
+    static_assert(U <= 6 && U != 5, "unroll factor");
 
     if constexpr (FOLD)
         fold.finish(acc);
@@ -309,8 +402,8 @@ template <int OP, int BP, int BQ, int WP, int WQ, int KSTAGE, int STAGES>
 hipError_t launch_pipe(const GemmArgs& a, hipStream_t stream)
 {
     const long tiles = (long)((a.M + BP - 1) / BP) * ((a.N + BQ - 1) / BQ);
-    if (tiles > 0x7FFFFFFFL)
-        return hipErrorInvalidValue;
+    if (tiles > 0x7FFFFFFFL || (long)BP * a.kbytes > 0x7FFFFFFFL)
+        return hipErrorInvalidValue;  // 32-bit buffer offsets within a tile
     if (a.splits > 1)
         hipLaunchKernelGGL((gemm_pipe_kernel<OP, BP, BQ, WP, WQ, KSTAGE, STAGES, true>),
                            dim3((unsigned)tiles, (unsigned)a.splits), dim3(WP * WQ * 64), 0,
@@ -325,15 +418,21 @@ hipError_t launch_pipe(const GemmArgs& a, hipStream_t stream)
 
 // X(OP, BP, BQ, WP, WQ, KSTAGE, STAGES) for every pipelined variant.
 #define QLL_FOR_EACH_PIPE(X, OP)           \
-    X(OP, 128, 128, 2, 2, 128, 4)          \
+    X(OP, 128, 128, 2, 2, 128, 2)          \
     X(OP, 128, 128, 2, 2, 128, 3)          \
+    X(OP, 128, 128, 2, 2, 128, 4)          \
+    X(OP, 256, 128, 4, 2, 128, 2)          \
+    X(OP, 256, 128, 4, 2, 128, 3)          \
+    X(OP, 128, 256, 2, 4, 128, 2)          \
     X(OP, 256, 128, 2, 2, 128, 3)          \
     X(OP, 128, 256, 2, 2, 128, 3)          \
-    X(OP, 256, 128, 4, 2, 128, 3)          \
-    X(OP, 128, 64, 2, 2, 128, 4)           \
+    X(OP, 64, 128, 2, 2, 128, 2)           \
     X(OP, 64, 128, 2, 2, 128, 4)           \
+    X(OP, 128, 64, 2, 2, 128, 2)           \
+    X(OP, 128, 64, 2, 2, 128, 4)           \
+    X(OP, 64, 64, 2, 2, 128, 2)            \
+    X(OP, 64, 64, 2, 2, 128, 3)            \
     X(OP, 32, 128, 1, 4, 128, 4)           \
-    X(OP, 64, 64, 2, 2, 128, 4)            \
     X(OP, 128, 32, 4, 1, 128, 4)
 
 #define QLL_PIPE_INSTANTIATE(OP, BP, BQ, WP, WQ, KS, ST)                                       \

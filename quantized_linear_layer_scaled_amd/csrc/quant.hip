@@ -5,15 +5,29 @@
 // integration changes"; scale rule absmax / 448 of the FP8 per-token
 // workload): for each group of values
 //     amax = max |x|,  s = amax / 448,  q = e4m3_rne(clamp(x / s, -448, 448))
-// with a correctly rounded fp32 division (not a reciprocal multiply), s = 0
-// and zero codes for an all-zero group, and the sign kept when a value rounds
-// to zero.  The conversion uses gfx950's v_cvt_pk_fp8_f32 (OCP e4m3,
-// round to nearest even) after the clamp.
+// with the correctly rounded fp32 quotient x / s, s = 0 and zero codes for an
+// all-zero group, and the sign kept when a value rounds to zero.  The
+// conversion uses gfx950's v_cvt_pk_fp8_f32 (OCP e4m3, round to nearest even)
+// after the clamp.
 //
-// All three kernels are HBM-bound (read 2 bytes, write 1 byte per element):
-//   quant_rows:        one wave per row, the row held in registers, max by
-//                      cross-lane shuffles (very long rows: one workgroup
-//                      per row, two passes, max across waves through LDS);
+// The quotient.  A correctly rounded fp32 division costs about ten
+// instructions (one of them quarter rate), which dominates the arithmetic of
+// these kernels.  Every value of a group shares s, so the kernels take the
+// reciprocal y = 1 / s once (correctly rounded) and per value form
+//     q0 = x * y,  r = fma(-q0, s, x),  q = fma(r, y, q0)
+// (one correction step from the exactly computed residual, Markstein's
+// division scheme).  For bf16 x and s = amax / 448 with amax a bf16 value,
+// s in [2^-64, 2^64], this q equals the correctly rounded x / s whenever
+// either of them is at least 2^-10, and both are below 2^-10 otherwise, so
+// the e4m3 code (+-0 below 2^-10, sign from x) is the same; this was checked
+// exhaustively over all such (x, amax) pairs.  Groups with s outside that
+// range take the division.
+//
+// All kernels are HBM-bound (read 2 bytes, write 1 byte per element):
+//   quant_rows:        TPR threads (64, 128 or 256) per row, the row held in
+//                      registers, max by cross-lane shuffles and, across the
+//                      waves of a row, through LDS (very long rows: one
+//                      workgroup per row, two passes);
 //   quant_groups128:   16 lanes per 1x128 group (8 bf16 per lane), shuffle
 //                      max inside the 16 lanes; no LDS;
 //   quant_weight_blocks: one workgroup per 128x128 weight block.
@@ -50,16 +64,35 @@ __device__ __forceinline__ float clamp448(float v)
     return fminf(fmaxf(v, -448.0f), 448.0f);
 }
 
+// The quotient x / s of one group (see the header comment).
+struct Quot {
+    float s, y;
+    bool fast;
+    __device__ __forceinline__ explicit Quot(float sc) : s(sc)
+    {
+        fast = sc >= 0x1p-64f && sc <= 0x1p64f;
+        y = fast ? 1.0f / sc : 0.0f;
+    }
+    __device__ __forceinline__ float operator()(float x) const
+    {
+        if (!fast)
+            return x / s;
+        const float q0 = x * y;
+        const float r = __builtin_fmaf(-q0, s, x);
+        return __builtin_copysignf(__builtin_fmaf(r, y, q0), x);
+    }
+};
+
 // 8 bf16 values -> 8 e4m3 codes (little-endian in a uint2).
-__device__ __forceinline__ uint2 encode8(const uint4& v, float s)
+__device__ __forceinline__ uint2 encode8(const uint4& v, const Quot& d)
 {
     float f[8];
     unpack8(v, f);
-    if (s == 0.0f)
+    if (d.s == 0.0f)
         return make_uint2(0, 0);
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-        f[i] = clamp448(f[i] / s);
+        f[i] = clamp448(d(f[i]));
     int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
     w0 = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], w0, true);
     int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(f[4], f[5], 0, false);
@@ -75,46 +108,60 @@ __device__ __forceinline__ float wave_max(float v)
     return v;
 }
 
-// One wave per row, four rows per 256-thread workgroup: the row
-// (K <= 64 * 8 * CH) stays in registers between the max and the conversion,
-// the max is a wave-level shuffle reduction (no LDS, no barrier), and each
-// lane keeps CH 16-byte loads in flight.
-template <int CH>
+// TPR threads per row, 256 / TPR rows per 256-thread workgroup: each thread
+// holds CH 16-byte chunks of its row (chunk c of thread t covers elements
+// 8 (c TPR + t) .. + 7) in registers between the max and the conversion.
+// The max is a wave shuffle reduction, then (TPR > 64) a max over the row's
+// waves through LDS.
+template <int TPR, int CH>
 __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restrict__ x,
                                                         uint8_t* __restrict__ q,
                                                         float* __restrict__ s, int M, int K)
 {
-    const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
-    if (m >= M)
-        return;
+    constexpr int WPR = TPR / 64;
+    const int tid = threadIdx.x;
+    const int sub = tid / TPR, t = tid % TPR;
+    const int m = blockIdx.x * (256 / TPR) + sub;
+    const bool live = m < M;
     const uint16_t* xr = x + (size_t)m * K;
     uint8_t* qr = q + (size_t)m * K;
     uint4 v[CH];
     float amax = 0.0f;
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-        const int e = (c * 64 + lane) * 8;
+        const int e = (c * TPR + t) * 8;
         v[c] = make_uint4(0, 0, 0, 0);
-        if (e < K)
+        if (live && e < K)
             v[c] = *(const uint4*)(xr + e);
     }
 #pragma unroll
     for (int c = 0; c < CH; ++c)
         amax = fmaxf(amax, absmax8(v[c]));
     amax = wave_max(amax);
+    if constexpr (WPR > 1) {
+        __shared__ float red[4];
+        if ((tid & 63) == 0)
+            red[tid >> 6] = amax;
+        __syncthreads();
+#pragma unroll
+        for (int w = 0; w < WPR; ++w)
+            amax = fmaxf(amax, red[sub * WPR + w]);
+    }
+    if (!live)
+        return;
     const float sc = amax / 448.0f;
-    if (lane == 0)
+    if (t == 0)
         s[m] = sc;
+    const Quot d(sc);
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-        const int e = (c * 64 + lane) * 8;
+        const int e = (c * TPR + t) * 8;
         if (e < K)
-            *(uint2*)(qr + e) = encode8(v[c], sc);
+            *(uint2*)(qr + e) = encode8(v[c], d);
     }
 }
 
-// Rows longer than 64 * 8 * 16 elements: one workgroup per row, two passes
+// Rows longer than 256 * 8 * 16 elements: one workgroup per row, two passes
 // over the row (the second one hits the caches).
 __global__ __launch_bounds__(256) void quant_rows_long_kernel(const uint16_t* __restrict__ x,
                                                              uint8_t* __restrict__ q,
@@ -136,8 +183,9 @@ __global__ __launch_bounds__(256) void quant_rows_long_kernel(const uint16_t* __
     const float sc = amax / 448.0f;
     if (tid == 0)
         s[m] = sc;
+    const Quot d(sc);
     for (int e = tid * 8; e < K; e += 256 * 8)
-        *(uint2*)(qr + e) = encode8(*(const uint4*)(xr + e), sc);
+        *(uint2*)(qr + e) = encode8(*(const uint4*)(xr + e), d);
 }
 
 // 1x128 groups: the flattened [M][K] array is a sequence of M*K/128 groups
@@ -160,7 +208,7 @@ __global__ __launch_bounds__(256) void quant_groups128_kernel(const uint16_t* __
     if (live) {
         if ((threadIdx.x & 15) == 0)
             s[e >> 7] = sc;
-        *(uint2*)(q + e) = encode8(v, sc);
+        *(uint2*)(q + e) = encode8(v, Quot(sc));
     }
 }
 
@@ -194,45 +242,64 @@ __global__ __launch_bounds__(256) void quant_weight_blocks_kernel(const uint16_t
     const float sc = amax / 448.0f;
     if (tid == 0)
         s[nb * KG + kb] = sc;
+    const Quot d(sc);
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
         const int idx = c * 256 + tid;
         const int r = nb * 128 + (idx >> 4);
         const int col = kb * 128 + (idx & 15) * 8;
         if (r < N)
-            *(uint2*)(q + (size_t)r * K + col) = encode8(v[c], sc);
+            *(uint2*)(q + (size_t)r * K + col) = encode8(v[c], d);
     }
 }
 
 }  // namespace
 
+template <int TPR, int CH>
+static void launch_rows(const uint16_t* x, uint8_t* q, float* s, int M, int K,
+                        hipStream_t stream)
+{
+    hipLaunchKernelGGL((quant_rows_kernel<TPR, CH>), dim3((M + 256 / TPR - 1) / (256 / TPR)),
+                       dim3(256), 0, stream, x, q, s, M, K);
+}
+
 hipError_t launch_quant_rows(const void* x, void* q, float* s, int M, int K,
                              hipStream_t stream)
 {
-    const int ch = (K + 511) / 512;  // 16-byte chunks per lane, one wave per row
     const uint16_t* xp = (const uint16_t*)x;
     uint8_t* qp = (uint8_t*)q;
-    dim3 grid((M + 3) / 4), block(256);
-    switch (ch) {
-    case 1: hipLaunchKernelGGL(quant_rows_kernel<1>, grid, block, 0, stream, xp, qp, s, M, K); break;
-    case 2: hipLaunchKernelGGL(quant_rows_kernel<2>, grid, block, 0, stream, xp, qp, s, M, K); break;
-    case 3:
-    case 4: hipLaunchKernelGGL(quant_rows_kernel<4>, grid, block, 0, stream, xp, qp, s, M, K); break;
-    case 5:
-    case 6: hipLaunchKernelGGL(quant_rows_kernel<6>, grid, block, 0, stream, xp, qp, s, M, K); break;
-    case 7:
-    case 8: hipLaunchKernelGGL(quant_rows_kernel<8>, grid, block, 0, stream, xp, qp, s, M, K); break;
-    case 9:
-    case 10:
-    case 11:
-    case 12: hipLaunchKernelGGL(quant_rows_kernel<12>, grid, block, 0, stream, xp, qp, s, M, K); break;
-    case 13:
-    case 14:
-    case 15:
-    case 16: hipLaunchKernelGGL(quant_rows_kernel<16>, grid, block, 0, stream, xp, qp, s, M, K); break;
-    default:
-        hipLaunchKernelGGL(quant_rows_long_kernel, dim3(M), block, 0, stream, xp, qp, s, K);
-        break;
+    // a whole workgroup per row from 2048 elements on (short per-thread
+    // chains, no idle lanes), narrower rows share a workgroup
+    const int chunks = (K + 7) / 8;
+    if (chunks <= 64)
+        launch_rows<64, 1>(xp, qp, s, M, K, stream);
+    else if (chunks <= 128)
+        launch_rows<64, 2>(xp, qp, s, M, K, stream);
+    else if (chunks < 256)
+        launch_rows<128, 2>(xp, qp, s, M, K, stream);
+    else {
+        switch ((chunks + 255) / 256) {
+        case 1: launch_rows<256, 1>(xp, qp, s, M, K, stream); break;
+        case 2: launch_rows<256, 2>(xp, qp, s, M, K, stream); break;
+        case 3: launch_rows<256, 3>(xp, qp, s, M, K, stream); break;
+        case 4: launch_rows<256, 4>(xp, qp, s, M, K, stream); break;
+        case 5:
+        case 6: launch_rows<256, 6>(xp, qp, s, M, K, stream); break;
+        case 7:
+        case 8: launch_rows<256, 8>(xp, qp, s, M, K, stream); break;
+        case 9:
+        case 10:
+        case 11:
+        case 12: launch_rows<256, 12>(xp, qp, s, M, K, stream); break;
+        case 13:
+        case 14:
+        case 15:
+        case 16: launch_rows<256, 16>(xp, qp, s, M, K, stream); break;
+        default:
+            hipLaunchKernelGGL(quant_rows_long_kernel, dim3(M), dim3(256), 0, stream, xp, qp, s,
+                               K);
+            break;
+        }
     }
     return hipGetLastError();
 }

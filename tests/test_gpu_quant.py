@@ -39,8 +39,11 @@ def assert_same(q, s, qr, sr, what):
                              f"gpu {q[i]:#04x} oracle {qr[i]:#04x}")
 
 
-@pytest.mark.parametrize("M,K", [(1, 16), (3, 2048), (5, 6144), (2048, 2048),
-                                 (7, 4112), (2, 16400), (64, 20000)])
+# K spans every row-kernel shape: 64, 128 and 256 threads per row, one to
+# sixteen 16-byte chunks per thread, and the two-pass kernel past 32768
+@pytest.mark.parametrize("M,K", [(1, 16), (4, 608), (9, 1024), (301, 1040), (3, 2048),
+                                 (5, 6144), (2048, 2048), (7, 4112), (2, 16400),
+                                 (64, 20000), (3, 32768), (2, 40000)])
 def test_per_token_bit_exact(qll, M, K):
     x = workloads.bf16_normal((M, K), (workloads.W_TEST, 20, M, K), outlier_frac=0.01)
     q, s = run_quant(qll, x)
@@ -80,7 +83,8 @@ def test_edge_values_bit_exact(qll):
     r[:] = 0x8000
     rows.append(r.copy())                            # all -0.0
     big = workloads.to_bf16_bits(np.float32([448.0]))[0]
-    for scale in (1.0, 1e-3, 1e-30, 1e37):
+    # scales on both sides of the reciprocal path's range of s, [2^-64, 2^64]
+    for scale in (1.0, 1e-3, 2.0**-55, 2.0**-58, 2.0**-61, 1e-30, 2.0**68, 2.0**71, 1e37):
         v = (g.standard_normal(K) * scale).astype(np.float32)
         v[::7] *= np.float32(1e-6)
         b = workloads.to_bf16_bits(v)
