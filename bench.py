@@ -168,8 +168,8 @@ def build_problems(torch, qll, workload):
             del w
             for M in mlist:
                 p = Problem("fp8", M, N, K)
-                q, s = add_quant(p, x_all[:M].clone(), 0)
                 # own copy of the weights per problem (cold for every problem)
+                q, s = add_quant(p, x_all[:M].clone(), 0)
                 add_gemm(p, "gemm_fp8_scaled", q, qw.clone(), s, sw.clone())
                 probs.append(p)
     elif workload == "int8":

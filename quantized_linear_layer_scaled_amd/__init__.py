@@ -351,6 +351,7 @@ def linear_fp8_dynamic(x, B, sb, out_dtype="bf16", out=None, q=None, sa=None, cf
 
 
 
+
 # --------------------------------------------------------------------------
 # registry / dispatch introspection
 # --------------------------------------------------------------------------

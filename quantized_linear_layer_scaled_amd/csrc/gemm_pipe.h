@@ -68,6 +68,15 @@ __device__ __forceinline__ void dma16(uint32_t voff, v4i rsrc, uint32_t lds_base
                  : "memory", "m0");
 }
 
+// One 4-byte buffer -> LDS copy per lane: lane i writes LDS bytes
+// lds_base + 4 i .. + 3.
+__device__ __forceinline__ void dma4(uint32_t voff, v4i rsrc, uint32_t lds_base)
+{
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
+                 ::"v"(voff), "s"(rsrc), "s"(lds_base)
+                 : "memory", "m0");
+}
+
 // Wait until at most N of this wave's global->LDS copies are in flight and
 // all of its LDS reads have returned, then meet the other waves.  The wait is
 // the s_waitcnt builtin (vmcnt(N) lgkmcnt(0), GFX9 encoding) so that the
@@ -86,10 +95,10 @@ __device__ __forceinline__ void wait_vm_barrier()
 // WP x WQ waves over the CU's four SIMDs.  Several resident workgroups are
 // what keeps the global->LDS copies of one overlapping the barrier waits and
 // MFMAs of another.
-template <int BP, int BQ, int WP, int WQ, int KSTAGE, int STAGES>
+template <int OP, int BP, int BQ, int WP, int WQ, int KSTAGE, int STAGES>
 constexpr int pipe_waves_per_eu()
 {
-    constexpr int lds = STAGES * (BP + BQ) * KSTAGE;
+    constexpr int lds = STAGES * (BP + BQ) * KSTAGE + (OP == OP_BLOCK ? (STAGES + 1) * 1280 : 0);
     constexpr int wgs = 163840 / lds < 4 ? 163840 / lds : 4;
     constexpr int w = wgs * WP * WQ / 4;
     return w < 1 ? 1 : (w > 8 ? 8 : w);
@@ -99,7 +108,7 @@ constexpr int pipe_waves_per_eu()
 // (the code is the same), so that traces separate the two kinds of launch.
 template <int OP, int BP, int BQ, int WP, int WQ, int KSTAGE, int STAGES, bool SPLITK>
 __global__ __launch_bounds__(WP* WQ * 64)
-__attribute__((amdgpu_waves_per_eu(pipe_waves_per_eu<BP, BQ, WP, WQ, KSTAGE, STAGES>())))
+__attribute__((amdgpu_waves_per_eu(pipe_waves_per_eu<OP, BP, BQ, WP, WQ, KSTAGE, STAGES>())))
 void gemm_pipe_kernel(GemmArgs a)
 {
     using Tr = OpTraits<OP>;
@@ -114,12 +123,15 @@ void gemm_pipe_kernel(GemmArgs a)
     constexpr int SP = BP / WP, SQ = BQ / WQ;
     constexpr int RP = SP / 16, RQ = SQ / 16;
     constexpr int ROWS = BP + BQ;
-    constexpr int LPT = ROWS * NC / THREADS;  // loads per thread per stage
+    constexpr bool BLK = OP == OP_BLOCK;
+    constexpr int LPT0 = ROWS * NC / THREADS;      // operand loads per thread per stage
+    constexpr int LPT = LPT0 + (BLK ? 2 : 0);      // + the two group-scale loads
     constexpr int STAGE_BYTES = ROWS * KSTAGE;
     static_assert(ROWS * NC % THREADS == 0, "stage must split evenly over the waves");
     static_assert((NC & (NC - 1)) == 0 && KSTAGE % KSTEP == 0, "bad K stage");
     static_assert(STAGES >= 2 && (STAGES - 1) * LPT < 64, "bad pipeline depth");
-    static_assert(OP != OP_BLOCK, "block scaling is not pipelined here");
+    static_assert(!BLK || (KSTAGE == 128 && NSTEP == 1 && BP <= 256 && WAVES >= BP / 64),
+                  "block scaling: one 128-wide K group per stage");
 
     // One LDS object per ring slot, the slot known at compile time in the
     // unrolled K loop (constant LDS addresses for the fragment reads).
@@ -127,6 +139,13 @@ void gemm_pipe_kernel(GemmArgs a)
     __shared__ __attribute__((aligned(1024))) uint8_t lds1[STAGE_BYTES];
     __shared__ __attribute__((aligned(1024))) uint8_t lds2[STAGES >= 3 ? STAGE_BYTES : 16];
     __shared__ __attribute__((aligned(1024))) uint8_t lds3[STAGES >= 4 ? STAGE_BYTES : 16];
+    // Block-FP8: the K group's activation scales of the tile rows (256
+    // floats) and its weight-block scales (64) per stage, in a ring of
+    // STAGES + 1 entries, so that a stage's scales outlive the reuse of its
+    // operand slot while its MFMAs run.
+    constexpr int SC_SLOTS = BLK ? STAGES + 1 : 1;
+    constexpr int SC_FLOATS = 320;
+    __shared__ __attribute__((aligned(16))) float lsc[SC_SLOTS][BLK ? SC_FLOATS : 4];
     static_assert(STAGES <= 4, "at most four ring slots");
     auto slot = [&](auto J) __attribute__((always_inline)) -> uint8_t* {
         constexpr int j = decltype(J)::value;
@@ -176,25 +195,55 @@ void gemm_pipe_kernel(GemmArgs a)
     auto in_a = [&](int i) __attribute__((always_inline)) {
         return (i * WAVES + wave) * 64 / NC < BP;
     };
-    uint32_t voff[LPT];
+    uint32_t voff[LPT0];
 #pragma unroll
-    for (int i = 0; i < LPT; ++i) {
+    for (int i = 0; i < LPT0; ++i) {
         const int row = ((i * WAVES + wave) * 64 + lane) / NC;
         const int r = in_a(i) ? row : row - BP;
         voff[i] = (uint32_t)r * ldk + (uint32_t)kbeg + (uint32_t)chunk_of(i) * 16u;
+    }
+
+    // Block-FP8 scale sources: sa [M][KG] from the tile's first row, sb
+    // [ceil(N/128)][KG] from the tile's first column block.  Each wave loads
+    // one 64-row chunk of the tile's activation scales (chunks repeat when
+    // there are more waves than chunks: the copies write equal values) and
+    // the (at most four) weight-block scales, so that every wave issues the
+    // same number of loads per stage.
+    const int KG = a.K / 128;
+    v4i rsSa{}, rsSb{};
+    uint32_t sa_off = 0, sb_off = kOutOfRange;
+    constexpr int SA_CHUNKS = BP >= 64 ? BP / 64 : 1;
+    const int sa_chunk = wave % SA_CHUNKS;
+    if constexpr (BLK) {
+        rsSa = buffer_rsrc(a.sa + (size_t)p0 * KG,
+                           (uint32_t)min((uint64_t)(M - p0) * KG * 4, (uint64_t)0x7FFFFFFF));
+        const int nb0 = q0 >> 7, nbs = (N + 127) >> 7;
+        rsSb = buffer_rsrc(a.sb + (size_t)nb0 * KG,
+                           (uint32_t)min((uint64_t)(nbs - nb0) * KG * 4, (uint64_t)0x7FFFFFFF));
+        sa_off = (uint32_t)((sa_chunk * 64 + lane) * KG) * 4u;
+        if (lane < 4)
+            sb_off = (uint32_t)(lane * KG) * 4u;
     }
 
     auto issue = [&](int kt, uint8_t* buf) __attribute__((always_inline)) {
         const int kb0 = kt * KSTAGE;  // relative to kbeg
         const bool full = kbeg + kb0 + KSTAGE <= kend;
 #pragma unroll
-        for (int i = 0; i < LPT; ++i) {
+        for (int i = 0; i < LPT0; ++i) {
             uint32_t vo = voff[i] + (uint32_t)kb0;
             if (!full && kbeg + kb0 + chunk_of(i) * 16 >= kend)
                 vo = kOutOfRange;  // past the K range: zeros
             dma16(vo, in_a(i) ? rsA : rsB,
                   __builtin_amdgcn_readfirstlane(
                       (uint32_t)(uintptr_t)(buf + (i * WAVES + wave) * 1024)));
+        }
+        if constexpr (BLK) {
+            const uint32_t g4 = (uint32_t)((kbeg + kb0) >> 7) * 4u;
+            float* sc = lsc[kt % SC_SLOTS];
+            dma4(sa_off + g4, rsSa,
+                 __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(sc + sa_chunk * 64)));
+            dma4(sb_off == kOutOfRange ? kOutOfRange : sb_off + g4, rsSb,
+                 __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(sc + 256)));
         }
     };
 
@@ -244,11 +293,41 @@ void gemm_pipe_kernel(GemmArgs a)
     auto compute_step = [&](const Frag& f, int kt, int ks) __attribute__((always_inline)) {
         if (kbeg + kt * KSTAGE + ks * KSTEP >= kend)
             return;  // steps past the K range (zero-filled) are skipped
+        if constexpr (BLK) {
+            // promotion: a fresh MFMA partial per K group, scaled by
+            // sa[m][g] * sb[n / 128][g] into the fp32 accumulator
+            // The wave's SQ columns start at a multiple of SQ <= 128, so
+            // they lie in one 128-column weight block: one weight scale per
+            // step, and the scale product sa * sb is formed once per row.
+            static_assert(SQ <= 128, "a wave's columns must share one weight block");
+            const float* sc = lsc[kt % SC_SLOTS];
+            const float qs = sc[256 + (((q0 & 127) + wqi * SQ) >> 7)];
+            float4 ps[RP];
 #pragma unroll
-        for (int i = 0; i < RP; ++i)
+            for (int i = 0; i < RP; ++i) {
+                ps[i] = *(const float4*)(sc + wpi * SP + i * 16 + (lane >> 4) * 4);
+                ps[i].x *= qs;
+                ps[i].y *= qs;
+                ps[i].z *= qs;
+                ps[i].w *= qs;
+            }
 #pragma unroll
-            for (int j = 0; j < RQ; ++j)
-                acc[i][j] = mfma_step<OP>(f.a[i], f.b[j], acc[i][j]);
+            for (int i = 0; i < RP; ++i)
+#pragma unroll
+                for (int j = 0; j < RQ; ++j) {
+                    const v4f pg = mfma_step<OP>(f.a[i], f.b[j], v4f{0, 0, 0, 0});
+                    acc[i][j][0] = __builtin_fmaf(ps[i].x, pg[0], acc[i][j][0]);
+                    acc[i][j][1] = __builtin_fmaf(ps[i].y, pg[1], acc[i][j][1]);
+                    acc[i][j][2] = __builtin_fmaf(ps[i].z, pg[2], acc[i][j][2]);
+                    acc[i][j][3] = __builtin_fmaf(ps[i].w, pg[3], acc[i][j][3]);
+                }
+        } else {
+#pragma unroll
+            for (int i = 0; i < RP; ++i)
+#pragma unroll
+                for (int j = 0; j < RQ; ++j)
+                    acc[i][j] = mfma_step<OP>(f.a[i], f.b[j], acc[i][j]);
+        }
     };
     // wait for the oldest stage in flight with `younger` later stages still
     // allowed in flight
@@ -350,7 +429,37 @@ void gemm_pipe_kernel(GemmArgs a)
     elem_t* scr = (elem_t*)(lds0 + wave * 16 * SQ * 4);
     constexpr int CPR = SQ / 8;          // 8-column groups per row
     constexpr int RPP = 64 / CPR;        // rows per pass
+    constexpr int PASSES = 16 / RPP;
     const bool vec_ok = (N & 7) == 0;
+    const int c = (lane % CPR) * 8;      // this lane's 8 columns, fixed
+    const int n = q0 + wqi * SQ + c;
+    // The per-token and per-channel scales this lane applies, loaded together
+    // before the stores instead of one dependent load per element.
+    constexpr bool SCALED = OP == OP_INT8 || OP == OP_FP8;
+    const bool scaled = SCALED && a.splits == 1 && a.out_dtype != OUT_INT32;
+    float sbv[8], sav[RP][PASSES];
+    if (SCALED && scaled) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+            sbv[t] = n + t < N ? a.sb[n + t] : 0.0f;
+#pragma unroll
+        for (int i = 0; i < RP; ++i)
+#pragma unroll
+            for (int pass = 0; pass < PASSES; ++pass) {
+                const int m = p0 + wpi * SP + i * 16 + pass * RPP + lane / CPR;
+                sav[i][pass] = m < M ? a.sa[m] : 0.0f;
+            }
+    }
+    // the epilogue value of an accumulator element: (acc * sa[m]) * sb[n]
+    // for the per-token x per-channel ops, the accumulator otherwise
+    auto value = [&](elem_t e, int i, int pass, int t) __attribute__((always_inline)) -> float {
+        if constexpr (SCALED) {
+            const float u = (float)e * sav[i][pass];
+            return u * sbv[t];
+        } else {
+            return (float)e;
+        }
+    };
 #pragma unroll
     for (int i = 0; i < RP; ++i) {
 #pragma unroll
@@ -359,39 +468,56 @@ void gemm_pipe_kernel(GemmArgs a)
             for (int v = 0; v < 4; ++v)
                 scr[((lane >> 4) * 4 + v) * SQ + j * 16 + (lane & 15)] = acc[i][j][v];
 #pragma unroll
-        for (int pass = 0; pass < 16 / RPP; ++pass) {
+        for (int pass = 0; pass < PASSES; ++pass) {
             const int r = pass * RPP + lane / CPR;
-            const int c = (lane % CPR) * 8;
             const int m = p0 + wpi * SP + i * 16 + r;
-            const int n = q0 + wqi * SQ + c;
             elem_t e[8];
 #pragma unroll
             for (int t = 0; t < 8; ++t)
                 e[t] = scr[r * SQ + c + t];
-            if (m < M) {
-                if (a.splits > 1) {
-                    elem_t* dst = (elem_t*)a.ws + ((size_t)z * M + m) * N + n;
-                    if (vec_ok && n + 7 < N) {
-                        ((uint4*)dst)[0] = make_uint4(__builtin_bit_cast(uint32_t, e[0]), __builtin_bit_cast(uint32_t, e[1]),
-                                                      __builtin_bit_cast(uint32_t, e[2]), __builtin_bit_cast(uint32_t, e[3]));
-                        ((uint4*)dst)[1] = make_uint4(__builtin_bit_cast(uint32_t, e[4]), __builtin_bit_cast(uint32_t, e[5]),
-                                                      __builtin_bit_cast(uint32_t, e[6]), __builtin_bit_cast(uint32_t, e[7]));
-                    } else {
-                        for (int t = 0; t < 8; ++t)
-                            if (n + t < N)
-                                dst[t] = e[t];
-                    }
-                } else if (vec_ok && n + 7 < N && a.out_dtype == OUT_BF16) {
-                    uint32_t w[4];
-#pragma unroll
-                    for (int t = 0; t < 4; ++t)
-                        w[t] = (uint32_t)bf16_rne(epilogue_value<OP>(e[2 * t], a, m, n + 2 * t)) |
-                               ((uint32_t)bf16_rne(epilogue_value<OP>(e[2 * t + 1], a, m, n + 2 * t + 1)) << 16);
-                    *(uint4*)((uint16_t*)a.out + (size_t)m * N + n) = make_uint4(w[0], w[1], w[2], w[3]);
+            if (m >= M)
+                continue;
+            if (a.splits > 1 || (OP == OP_INT8 && a.out_dtype == OUT_INT32)) {
+                // raw accumulators: Split-K partials or the INT8 int32 output
+                elem_t* dst = a.splits > 1 ? (elem_t*)a.ws + ((size_t)z * M + m) * N + n
+                                           : (elem_t*)a.out + (size_t)m * N + n;
+                if (vec_ok && n + 7 < N) {
+                    ((uint4*)dst)[0] = make_uint4(__builtin_bit_cast(uint32_t, e[0]), __builtin_bit_cast(uint32_t, e[1]),
+                                                  __builtin_bit_cast(uint32_t, e[2]), __builtin_bit_cast(uint32_t, e[3]));
+                    ((uint4*)dst)[1] = make_uint4(__builtin_bit_cast(uint32_t, e[4]), __builtin_bit_cast(uint32_t, e[5]),
+                                                  __builtin_bit_cast(uint32_t, e[6]), __builtin_bit_cast(uint32_t, e[7]));
                 } else {
                     for (int t = 0; t < 8; ++t)
                         if (n + t < N)
-                            store_one<OP>(a, (size_t)m * N + n + t, e[t], m, n + t);
+                            dst[t] = e[t];
+                }
+            } else if (a.out_dtype == OUT_BF16) {
+                uint16_t* dst = (uint16_t*)a.out + (size_t)m * N + n;
+                if (vec_ok && n + 7 < N) {
+                    uint32_t w[4];
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        w[t] = (uint32_t)bf16_rne(value(e[2 * t], i, pass, 2 * t)) |
+                               ((uint32_t)bf16_rne(value(e[2 * t + 1], i, pass, 2 * t + 1)) << 16);
+                    *(uint4*)dst = make_uint4(w[0], w[1], w[2], w[3]);
+                } else {
+                    for (int t = 0; t < 8; ++t)
+                        if (n + t < N)
+                            dst[t] = bf16_rne(value(e[t], i, pass, t));
+                }
+            } else {
+                float* dst = (float*)a.out + (size_t)m * N + n;
+                float y[8];
+#pragma unroll
+                for (int t = 0; t < 8; ++t)
+                    y[t] = value(e[t], i, pass, t);
+                if (vec_ok && n + 7 < N) {
+                    ((float4*)dst)[0] = make_float4(y[0], y[1], y[2], y[3]);
+                    ((float4*)dst)[1] = make_float4(y[4], y[5], y[6], y[7]);
+                } else {
+                    for (int t = 0; t < 8; ++t)
+                        if (n + t < N)
+                            dst[t] = y[t];
                 }
             }
         }
@@ -427,11 +553,14 @@ hipError_t launch_pipe(const GemmArgs& a, hipStream_t stream)
     X(OP, 256, 128, 2, 2, 128, 3)          \
     X(OP, 128, 256, 2, 2, 128, 3)          \
     X(OP, 64, 128, 2, 2, 128, 2)           \
+    X(OP, 64, 128, 2, 2, 128, 3)           \
     X(OP, 64, 128, 2, 2, 128, 4)           \
     X(OP, 128, 64, 2, 2, 128, 2)           \
+    X(OP, 128, 64, 2, 2, 128, 3)           \
     X(OP, 128, 64, 2, 2, 128, 4)           \
     X(OP, 64, 64, 2, 2, 128, 2)            \
     X(OP, 64, 64, 2, 2, 128, 3)            \
+    X(OP, 64, 64, 2, 2, 128, 4)            \
     X(OP, 32, 128, 1, 4, 128, 4)           \
     X(OP, 128, 32, 4, 1, 128, 4)
 

@@ -177,11 +177,14 @@ hipError_t launch_skinny(const GemmArgs& a, hipStream_t stream)
 // (waves split rows), weight rows x tokens per workgroup, waves (the wp
 // field holds the wave count).
 // X(OP, RQ, TOKENS, W, KSPLIT, D) is applied to every entry.
+// D is the number of K steps whose loads are in flight together: enough for
+// a wave's whole K chunk at K = 6144 (fp8) for the wave-split kernels, so the
+// weight stream costs one memory round trip.
 #define QLL_FOR_EACH_SKINNY(X, OP, DM)     \
-    X(OP, 1, 16, 8, true, 4 * (DM))        \
-    X(OP, 2, 32, 8, true, 2 * (DM))        \
-    X(OP, 4, 64, 8, true, 2 * (DM))        \
-    X(OP, 1, 16, 16, true, 2 * (DM))       \
+    X(OP, 1, 16, 8, true, 6 * (DM))        \
+    X(OP, 2, 32, 8, true, 4 * (DM))        \
+    X(OP, 4, 64, 8, true, 4 * (DM))        \
+    X(OP, 1, 16, 16, true, 4 * (DM))       \
     X(OP, 1, 16, 4, false, 4 * (DM))       \
     X(OP, 2, 32, 4, false, 4 * (DM))       \
     X(OP, 4, 64, 4, false, 2 * (DM))

@@ -10,18 +10,8 @@
 // conversion uses gfx950's v_cvt_pk_fp8_f32 (OCP e4m3, round to nearest even)
 // after the clamp.
 //
-// The quotient.  A correctly rounded fp32 division costs about ten
-// instructions (one of them quarter rate), which dominates the arithmetic of
-// these kernels.  Every value of a group shares s, so the kernels take the
-// reciprocal y = 1 / s once (correctly rounded) and per value form
-//     q0 = x * y,  r = fma(-q0, s, x),  q = fma(r, y, q0)
-// (one correction step from the exactly computed residual, Markstein's
-// division scheme).  For bf16 x and s = amax / 448 with amax a bf16 value,
-// s in [2^-64, 2^64], this q equals the correctly rounded x / s whenever
-// either of them is at least 2^-10, and both are below 2^-10 otherwise, so
-// the e4m3 code (+-0 below 2^-10, sign from x) is the same; this was checked
-// exhaustively over all such (x, amax) pairs.  Groups with s outside that
-// range take the division.
+// The quotient x / s uses the reciprocal of s with one fma correction
+// (quant_encode.h), equal in effect to the correctly rounded division.
 //
 // All kernels are HBM-bound (read 2 bytes, write 1 byte per element):
 //   quant_rows:        TPR threads (64, 128 or 256) per row, the row held in
@@ -32,73 +22,11 @@
 //                      max inside the 16 lanes; no LDS;
 //   quant_weight_blocks: one workgroup per 128x128 weight block.
 #include "qll_internal.h"
+#include "quant_encode.h"
 
 namespace qll {
 
 namespace {
-
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-
-__device__ __forceinline__ void unpack8(const uint4& v, float* f)
-{
-    f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
-    f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
-    f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
-    f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
-}
-
-__device__ __forceinline__ float absmax8(const uint4& v)
-{
-    float f[8];
-    unpack8(v, f);
-    float m = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-        m = fmaxf(m, fabsf(f[i]));
-    return m;
-}
-
-__device__ __forceinline__ float clamp448(float v)
-{
-    return fminf(fmaxf(v, -448.0f), 448.0f);
-}
-
-// The quotient x / s of one group (see the header comment).
-struct Quot {
-    float s, y;
-    bool fast;
-    __device__ __forceinline__ explicit Quot(float sc) : s(sc)
-    {
-        fast = sc >= 0x1p-64f && sc <= 0x1p64f;
-        y = fast ? 1.0f / sc : 0.0f;
-    }
-    __device__ __forceinline__ float operator()(float x) const
-    {
-        if (!fast)
-            return x / s;
-        const float q0 = x * y;
-        const float r = __builtin_fmaf(-q0, s, x);
-        return __builtin_copysignf(__builtin_fmaf(r, y, q0), x);
-    }
-};
-
-// 8 bf16 values -> 8 e4m3 codes (little-endian in a uint2).
-__device__ __forceinline__ uint2 encode8(const uint4& v, const Quot& d)
-{
-    float f[8];
-    unpack8(v, f);
-    if (d.s == 0.0f)
-        return make_uint2(0, 0);
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-        f[i] = clamp448(d(f[i]));
-    int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
-    w0 = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], w0, true);
-    int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(f[4], f[5], 0, false);
-    w1 = __builtin_amdgcn_cvt_pk_fp8_f32(f[6], f[7], w1, true);
-    return make_uint2((uint32_t)w0, (uint32_t)w1);
-}
 
 __device__ __forceinline__ float wave_max(float v)
 {

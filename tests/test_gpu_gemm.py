@@ -37,7 +37,7 @@ def names(qll, op):
 
 INT8_SHAPES = [(1, 520, 1040), (37, 300, 2064), (130, 264, 512)]
 FP8_SHAPES = [(1, 520, 1040), (37, 300, 2064), (130, 264, 512)]
-BLOCK_SHAPES = [(1, 520, 1024), (37, 300, 2048), (130, 264, 512)]
+BLOCK_SHAPES = [(1, 520, 1024), (37, 300, 2048), (130, 264, 512), (300, 648, 1024)]
 BF16_SHAPES = [(1, 520, 1032), (37, 300, 2056), (130, 264, 512)]
 SPLITS = [1, 3]
 
@@ -247,8 +247,8 @@ def test_workspace_too_small_is_rejected(qll):
     assert e.value.status == 4
 
 
-@pytest.mark.parametrize("op", ["bf16_bi", "fp8"])
-def test_swap_equals_ordinary_bitwise(qll, op, fp8_cases, bf16_cases):
+@pytest.mark.parametrize("op", ["bf16_bi", "fp8", "block_fp8"])
+def test_swap_equals_ordinary_bitwise(qll, op, fp8_cases, bf16_cases, block_cases):
     # whether the Swap-AB orientation reproduces the ordinary one bit for bit
     # (same MFMA, operands exchanged); the batch-invariant dispatch only mixes
     # orientations if this holds
@@ -256,15 +256,20 @@ def test_swap_equals_ordinary_bitwise(qll, op, fp8_cases, bf16_cases):
         A, B, sa, sb, _, _ = fp8_cases[(37, 300, 2064)]
         args = (dev_e4m3(A), dev_e4m3(B), dev(sa), dev(sb))
         fn = qll.gemm_fp8_scaled
+    elif op == "block_fp8":
+        A, B, sa, sb, _, _ = block_cases[(37, 300, 2048)]
+        args = (dev_e4m3(A), dev_e4m3(B), dev(sa), dev(sb))
+        fn = qll.gemm_block_fp8
     else:
         A, B, _, _ = bf16_cases[(37, 300, 2056)]
         args = (dev_bf16(A), dev_bf16(B))
         fn = qll.gemm_bf16_batch_invariant
-    # fp8: the "k16x" skinny variants split K across waves (another summation
-    # order by design), every other variant accumulates K in one accumulator.
+    # fp8 and Block-FP8: the "k16x" skinny variants split K across waves
+    # (another summation order by design), every other variant accumulates K
+    # in one accumulator (Block-FP8: one promotion per K group, in order).
     # bf16: every variant sums K in the same eight chunks, so all agree except
     # a skinny variant whose waves split K into another number of chunks.
-    if op == "fp8":
+    if op != "bf16_bi":
         single = [n for n in names(qll, op) if not n.startswith("k16x")]
     else:
         single = [v["name"] for v in qll.variants(op)

@@ -38,7 +38,8 @@ def test_linear_equals_two_calls_and_oracle(qll, N, K):
         qr, sr = oracle.quantize_fp8(x)
         ref, absref = oracle.gemm_fp8(qr, B, sr[:, 0].copy(), sb[:, 0].copy(), with_abs=True)
         dx = dev_bf16(x)
-        for cfg in (None, ("k16x16_w8", 1), ("k16x16_w8", 2), ("p64x128_w2x2_k128_s4", 1)):
+        for cfg in (None, ("k16x16_w8", 1), ("k16x16_w16", 1), ("k16x32_w8", 1),
+                    ("k16x64_w8", 1), ("k16x16_w8", 2), ("p64x128_w2x2_k128_s4", 1)):
             for od in ("bf16", "fp32"):
                 y, q, sa = qll.linear_fp8_dynamic(dx, dB, dsb, out_dtype=od, cfg=cfg)
                 q2, sa2 = qll.quantize_per_token_fp8(dx)
@@ -64,3 +65,4 @@ def test_linear_large_m_sampled(qll):
     torch.cuda.synchronize()
     assert np.array_equal(host_codes(q), qr)
     check_fp(host_f64(y)[rows], ref, absref, K, "bf16", "linear M=512")
+
