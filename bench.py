@@ -21,7 +21,9 @@ Timing (all on the one stream the library launches on):
     --copies back-to-back launches, each on its own copy of the call's buffers
     (cold data), timed with HIP events: this gives the per-shape table and the
     roofline of the dominant kernel (the GEMM kernel with the most time per
-    step among single-kernel calls).
+    step among single-kernel calls);
+  * dispatch: host-side costs of the C-ABI path (table load, the first step
+    of the process, host enqueue time per call).
 The line also carries the CPU oracle timed on a bounded sample of the same
 workload, and, when the rocprofv3 counter CSVs are given (--fetch-csv,
 --write-csv), the HBM traffic of the dominant kernel scaled by the same
@@ -379,7 +381,9 @@ def main():
     import quantized_linear_layer_scaled_amd as qll
 
     qll.load_library()
+    t_init = time.perf_counter()
     rc = qll.init(None if args.table == "none" else args.table)
+    init_ms = (time.perf_counter() - t_init) * 1e3
     table_used = qll.table_entries()
     props = torch.cuda.get_device_properties(0)
     print(f"# device {props.name} {getattr(props, 'gcnArchName', '?')} "
@@ -393,6 +397,12 @@ def main():
     probs = build_problems(torch, qll, args.workload)
     print(f"# {len(probs)} problems built", file=sys.stderr, flush=True)
 
+    # first step of the process: includes loading the kernels' code objects
+    torch.cuda.synchronize()
+    t_first = time.perf_counter()
+    run_step(probs)
+    torch.cuda.synchronize()
+    first_step_ms = (time.perf_counter() - t_first) * 1e3
     for _ in range(args.warmup):
         run_step(probs)
     torch.cuda.synchronize()
@@ -424,9 +434,11 @@ def main():
     for step in range(args.steps):
         run_step(probs)
     end.record()
+    host_enqueue_s = time.perf_counter() - t_wall0  # host time to enqueue K steps
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall0
     ms_eager = start.elapsed_time(end) / args.steps
+    n_calls = sum(len(p.calls) for p in probs)
     ms_per_step = ms_eager
 
     # ---- timed region 3: every call on its own (graph of cold copies)
@@ -536,6 +548,14 @@ def main():
                         if ms_graph is not None else None),
         "roofline": roof,
         "cpu_baseline": None,
+        # host side of the C-ABI path: table load, the first step of the
+        # process (code-object loading included), and the host time to
+        # enqueue one call (ctypes + argument checks + dispatch + launch)
+        "dispatch": {"init_ms": round(init_ms, 3),
+                     "first_step_ms": round(first_step_ms, 3),
+                     "calls_per_step": n_calls,
+                     "host_us_per_call": round(host_enqueue_s * 1e6 / (args.steps * n_calls), 2),
+                     "host_us_per_step": round(host_enqueue_s * 1e6 / args.steps, 1)},
         "wall_s_timed": round(wall, 3),
         "device": {"name": props.name, "cus": props.multi_processor_count,
                    "arch": getattr(props, "gcnArchName", "?")},

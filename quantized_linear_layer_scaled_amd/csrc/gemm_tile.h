@@ -64,8 +64,10 @@ template <> struct OpTraits<OP_BF16> {
 // contiguous run t = xcd * per + local, and that run is laid out in groups of
 // `group` tile rows (tile_p fastest), so an XCD works on a compact block of
 // tiles that share A rows and B rows in its L2.  The map is a bijection of
-// [0, tp * tq) for any tile count; only locality depends on the dispatch
-// order.
+// [0, tp * tq) for any tile count and group; only locality depends on the
+// dispatch order.  (Groups chosen to make an XCD's block square measured
+// slower than four tile rows: the workgroups running at the same time share
+// rows better in the taller-than-wide arrangement.)
 __device__ __forceinline__ void xcd_tile(int bid, int tp, int tq, int group,
                                          int& tile_p, int& tile_q)
 {
