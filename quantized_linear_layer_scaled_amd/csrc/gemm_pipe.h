@@ -564,6 +564,14 @@ hipError_t launch_pipe(const GemmArgs& a, hipStream_t stream)
     X(OP, 32, 128, 1, 4, 128, 4)           \
     X(OP, 128, 32, 4, 1, 128, 4)
 
+// Variants with 256-byte K stages (two fp8 / four bf16 MFMA steps per stage:
+// half the barriers per K); not for Block-FP8, whose stage is one K group.
+#define QLL_FOR_EACH_PIPE_K256(X, OP)      \
+    X(OP, 64, 64, 2, 2, 256, 2)            \
+    X(OP, 128, 64, 2, 2, 256, 2)           \
+    X(OP, 64, 128, 2, 2, 256, 2)           \
+    X(OP, 128, 128, 2, 2, 256, 2)
+
 #define QLL_PIPE_INSTANTIATE(OP, BP, BQ, WP, WQ, KS, ST)                                       \
     template __global__ void qll::gemm_pipe_kernel<OP, BP, BQ, WP, WQ, KS, ST, false>(qll::GemmArgs); \
     template __global__ void qll::gemm_pipe_kernel<OP, BP, BQ, WP, WQ, KS, ST, true>(qll::GemmArgs);
