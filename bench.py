@@ -29,7 +29,9 @@ workload, and, when the rocprofv3 counter CSVs are given (--fetch-csv,
 --write-csv), the HBM traffic of the dominant kernel scaled by the same
 counters read on a copy kernel of known size (--calib-copy runs that copy).
 
-Other workloads (--workload int8|block|bi|vocab) print the same JSON shape.
+Other workloads (--workload int8|block|bi|vocab|moe) print the same JSON
+shape; moe is the grouped (per-expert) FP8 GEMM of a 64-expert layer with
+synthetic top-8 routing (per-token quantization + gemm_fp8_grouped).
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload fp8]
 """
@@ -56,7 +58,7 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="fp8",
-                   choices=["fp8", "int8", "block", "bi", "vocab"])
+                   choices=["fp8", "int8", "block", "bi", "vocab", "moe"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=128,
                    help="rows per problem the CPU oracle computes")
@@ -100,6 +102,8 @@ class Problem:
             return 2 * M * K + 2 * N * K + 2 * M * N
         if self.op == "block_fp8":
             return M * K + N * K + 4 * M * (K // 128) + 4 * ((N + 127) // 128) * (K // 128) + 2 * M * N
+        if self.op == "fp8_grouped":  # the weights of every expert that has rows
+            return M * K + self.experts_used * (N * K + 4 * N) + 4 * M + 2 * M * N
         return M * K + N * K + 4 * M + 4 * N + 2 * M * N
 
     def quant_bytes(self):
@@ -192,6 +196,32 @@ def build_problems(torch, qll, workload):
                 q, s = add_quant(p, x_all[:M].clone(), 128)
                 add_gemm(p, "gemm_block_fp8", q, qw.clone(), s, sw.clone())
                 probs.append(p)
+    elif workload == "moe":
+        N, K = W.MOE_SHAPE
+        E = W.MOE_E
+        w = dev_bf16(torch, W.moe_weights(E, N, K).reshape(E * N, K))
+        qw, sw = qll.quantize_per_token_fp8(w)
+        del w
+
+        def grouped_args(p, t):
+            return (t["A"].data_ptr(), t["B"].data_ptr(), t["sa"].data_ptr(),
+                    t["sb"].data_ptr(), t["off"].data_ptr(), t["out"].data_ptr(), 0,
+                    p.M, p.N, p.K, E, stream)
+
+        for T in W.MOE_T:
+            off = W.moe_routing(T)
+            M = int(off[-1])
+            p = Problem("fp8_grouped", M, N, K)
+            p.experts_used = int((np.diff(off) > 0).sum())
+            q, s = add_quant(p, dev_bf16(torch, W.moe_activations(M, K)), 0)
+            out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+            t = dict(A=q, B=qw.clone().view(E, N, K), sa=s, sb=sw.clone().view(E, N),
+                     off=torch.from_numpy(off).cuda(), out=out)
+            p.keep += list(t.values())
+            p.calls.append(("gemm", L.gemm_fp8_grouped, grouped_args(p, t)))
+            p.tensors["gemm"] = (t, grouped_args)
+            p.variant, p.splits, p.eff_splits = qll.grouped_select(M, E), 1, 1
+            probs.append(p)
     elif workload == "bi":
         for N, K in W.BI_SHAPES:
             d = W.bi_inputs(N, K)
@@ -256,12 +286,16 @@ def run_step(probs, events=None):
 def kernel_symbol(qll, op, variant):
     """The kernel's name as rocprofv3 prints it (for the skinny kernel, whose
     last template argument the registry does not list, the name up to it)."""
+    grouped = op == "fp8_grouped"
+    if grouped:
+        op = "fp8"
     opn = {"int8": 0, "fp8": 1, "block_fp8": 2, "bf16_bi": 3}[op]
     v = next(x for x in qll.variants(op) if x["name"] == variant)
     if variant[0] == "p":
         st = variant.rsplit("_s", 1)[1]
         return (f"void qll::gemm_pipe_kernel<{opn}, {v['bp']}, {v['bq']}, {v['wp']}, "
-                f"{v['wq']}, {v['kstage']}, {st}, false>(qll::GemmArgs)")
+                f"{v['wq']}, {v['kstage']}, {st}, false{', true' if grouped else ''}>"
+                "(qll::GemmArgs)")
     if variant[0] in "kr":
         return (f"void qll::gemm_skinny_kernel<{opn}, {v['bq'] // 16}, {v['wp']}, "
                 f"{'true' if variant[0] == 'k' else 'false'}, ")
@@ -320,6 +354,24 @@ def cpu_baseline(workload, rows_cap):
                 t_total += time.perf_counter() - t0
                 flops += 2.0 * r * N * K
         desc = f"first min(M,{rows_cap}) rows of every Block-FP8 problem"
+    elif workload == "moe":
+        N, K = W.MOE_SHAPE
+        E = W.MOE_E
+        w = W.moe_weights(E, N, K).reshape(E * N, K)
+        B, sb = oracle.quantize_fp8(w)
+        B, sb = B.reshape(E, N, K), sb[:, 0].reshape(E, N).copy()
+        for T in W.MOE_T:
+            off = W.moe_routing(T)
+            M = int(off[-1])
+            x = W.moe_activations(M, K)
+            rows = np.arange(0, M, max(1, M // min(M, rows_cap)))[:rows_cap]
+            t0 = time.perf_counter()
+            A, sa = oracle.quantize_fp8(x)
+            oracle.gemm_fp8_grouped(A, B, sa[:, 0].copy(), sb, off, rows=rows)
+            t_total += time.perf_counter() - t0
+            flops += 2.0 * rows.size * N * K
+        desc = (f"min(M,{rows_cap}) evenly spaced rows of every grouped problem "
+                "(all experts), per-token quantization of all rows + grouped FP8 GEMM")
     else:
         for N, K in W.BI_SHAPES:
             d = W.bi_inputs(N, K)
@@ -466,7 +518,8 @@ def main():
         for j, (kind, _, _) in enumerate(p.calls):
             rec[f"{kind}_us"] = round(call_us[i][j], 3)
         t_gemm = rec["gemm_us"] * 1e-6
-        dt = {"fp8": "fp8", "block_fp8": "fp8", "int8": "int8", "bf16_bi": "bf16"}[p.op]
+        dt = {"fp8": "fp8", "fp8_grouped": "fp8", "block_fp8": "fp8", "int8": "int8",
+              "bf16_bi": "bf16"}[p.op]
         t_mem = p.algo_bytes() / (HBM_GBS * 1e9)
         t_mfma = p.flops / (PEAK[dt] * 1e12)
         rec["tflops"] = round(p.flops / t_gemm / 1e12, 2)
@@ -526,9 +579,13 @@ def main():
                       "M in {1,16,64,256,2048}; 1x128 quantization + GEMM, bf16 out",
              "bi": "batch-invariant bf16 sweep: (N,K) in {(2048,2048),(4096,2048)}, "
                    "M in {1,4,...,2048}, bf16 out",
+             "moe": "grouped FP8 GEMM (per-expert weights): 64 experts of N=1536 K=2048, "
+                    "T in {16,128,1024} tokens routed to 8 experts each (skewed synthetic "
+                    "routing); per-token quantization + gemm_fp8_grouped, bf16 out",
              "vocab": "large-vocab FP8 dynamic projection N=151936 K=2048, "
                       "M in {1,8,64,512,2048}"}
     dtype = {"fp8": "fp8e4m3", "vocab": "fp8e4m3", "block": "fp8e4m3", "int8": "int8",
+             "moe": "fp8e4m3",
              "bi": "bf16"}[args.workload]
     line = {
         "metric": "TFLOPS/TOPS + % of HBM or MFMA roofline per (M,N,K), FP8/INT8 scaled_mm",

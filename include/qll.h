@@ -196,6 +196,38 @@ int linear_fp8_dynamic_ex(const void* x, const void* B, const float* sb, void* q
                           int64_t K, void* ws, size_t ws_bytes, void* stream,
                           const qll_cfg* cfg);
 
+/* Grouped (per-expert) FP8 GEMM, the expert layer of an FP8 mixture of
+ * experts built from the same scaled FP8 GEMM ("FP8 dynamic quantization"
+ * of "Helion in vLLM: A Unified Route to Tunable Linear Kernels", "What the
+ * integration changes"; the FP8 MoE pipeline of the Hunyuan MoE backend
+ * pages).  The M rows of A are sorted by expert: rows
+ * [offsets[e], offsets[e+1]) go to expert e, whose weights are B + e*N*K
+ * and whose per-channel scales are sb + e*N:
+ *   out[m][n] = bf16_rne((acc * sa[m]) * sb[e][n]),
+ *   acc = sum_k e4m3(A[m][k]) * e4m3(B[e][n][k]) in fp32.
+ *   A e4m3 [M][K]; B e4m3 [E][N][K]; sa fp32 [M]; sb fp32 [E][N];
+ *   offsets: DEVICE int32 [E + 1], offsets[0] = 0, offsets[E] = M,
+ *   non-decreasing (other values give unspecified output rows but never an
+ *   access outside A, B, sa, sb or out: the kernel clamps them to [0, M] and
+ *   takes their running maximum);
+ *   out bf16 / fp32 [M][N].  K % 16 == 0, 1 <= E <= 65536.  No workspace.
+ * variant (the _ex form): one of the pipelined variant names
+ * ("p<BP>x<BQ>_w<WP>x<WQ>_k128_s<S>", as listed by qll_variant_info for the
+ * FP8 op), or NULL for the built-in rule.  M == 0 is a no-op.
+ * Errors: INVALID_ARG (shapes, pointers, unknown variant), MISALIGNED,
+ * UNSUPPORTED (K too long for the variant), HIP. */
+int gemm_fp8_grouped(const void* A, const void* B, const float* sa, const float* sb,
+                     const int32_t* offsets, void* out, int out_dtype, int64_t M,
+                     int64_t N, int64_t K, int64_t E, void* stream);
+int gemm_fp8_grouped_ex(const void* A, const void* B, const float* sa, const float* sb,
+                        const int32_t* offsets, void* out, int out_dtype, int64_t M,
+                        int64_t N, int64_t K, int64_t E, void* stream,
+                        const char* variant);
+/* The variant gemm_fp8_grouped picks for M rows over E experts, written as
+ * a NUL-terminated name into buf (cap bytes).  INVALID_ARG on bad arguments
+ * or a too small buffer. */
+int qll_grouped_select(int64_t M, int64_t E, char* buf, size_t cap);
+
 /* ------------------------------------------------------------------ */
 /* Dispatch, registry and support                                      */
 /* ------------------------------------------------------------------ */

@@ -242,6 +242,36 @@ def gemm_fp8(A, B, sa, sb, rows=None, with_abs=False):
     return (ref, absref) if with_abs else ref
 
 
+def gemm_fp8_grouped(A, B, sa, sb, offsets, rows=None, with_abs=False):
+    """Grouped (per-expert) FP8 GEMM in fp64: row m of A, with
+    offsets[e] <= m < offsets[e+1], is multiplied by expert e's weights
+    B[e] ([N][K]) and scaled by sa[m] and sb[e] ([N]) -- the per-channel FP8
+    product of gemm_fp8, one expert at a time."""
+    A = np.ascontiguousarray(A, dtype=np.uint8)
+    B = np.ascontiguousarray(B, dtype=np.uint8)
+    sa = np.asarray(sa, dtype=np.float32).reshape(-1)
+    sb = np.asarray(sb, dtype=np.float32)
+    offsets = np.asarray(offsets, dtype=np.int64)
+    M, K = A.shape
+    E, N, K2 = B.shape
+    assert K2 == K and sa.size == M and sb.shape == (E, N) and offsets.shape == (E + 1,)
+    assert offsets[0] == 0 and offsets[E] == M and np.all(np.diff(offsets) >= 0)
+    r = _rows(M, rows)
+    ref = np.empty((r.size, N), dtype=np.float64)
+    absref = np.empty((r.size, N), dtype=np.float64) if with_abs else None
+    expert = np.searchsorted(offsets, r, side="right") - 1
+    for e in range(E):
+        sel = np.nonzero(expert == e)[0]
+        if sel.size == 0:
+            continue
+        res = gemm_fp8(A, B[e], sa, sb[e], rows=r[sel], with_abs=with_abs)
+        if with_abs:
+            ref[sel], absref[sel] = res
+        else:
+            ref[sel] = res
+    return (ref, absref) if with_abs else ref
+
+
 def gemm_block_fp8(A, B, sa, sb, rows=None, with_abs=False, group: int = 128):
     """Block-FP8 GEMM (1 x group activation scales, group x group weight
     scales) in fp64."""

@@ -11,7 +11,8 @@ raises.
 Operations (see include/qll.h for the full contract):
   quantize_per_token_fp8, quantize_weight_block_fp8,
   gemm_w8a8_int8, gemm_fp8_scaled, gemm_block_fp8, gemm_bf16_batch_invariant,
-  linear_fp8_dynamic (per-token quantization + FP8 GEMM in one call).
+  linear_fp8_dynamic (per-token quantization + FP8 GEMM in one call),
+  gemm_fp8_grouped (per-expert FP8 GEMM over rows sorted by expert).
 """
 from __future__ import annotations
 
@@ -71,6 +72,10 @@ def load_library():
     _LIN = [_P, _P, _P, _P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _P, ctypes.c_size_t, _P]
     L.linear_fp8_dynamic.argtypes = _LIN
     L.linear_fp8_dynamic_ex.argtypes = _LIN + [ctypes.POINTER(qll_cfg)]
+    _GRP = [_P, _P, _P, _P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _I64, _P]
+    L.gemm_fp8_grouped.argtypes = _GRP
+    L.gemm_fp8_grouped_ex.argtypes = _GRP + [ctypes.c_char_p]
+    L.qll_grouped_select.argtypes = [_I64, _I64, ctypes.c_char_p, ctypes.c_size_t]
     L.qll_init.argtypes = [ctypes.c_char_p]
     L.qll_table_validate.argtypes = [ctypes.c_char_p, ctypes.c_char_p, ctypes.c_int,
                                      ctypes.c_char_p, ctypes.c_size_t]
@@ -355,6 +360,37 @@ def linear_fp8_dynamic(x, B, sb, out_dtype="bf16", out=None, q=None, sa=None, cf
 # --------------------------------------------------------------------------
 # registry / dispatch introspection
 # --------------------------------------------------------------------------
+
+def gemm_fp8_grouped(A, B, sa, sb, offsets, out_dtype="bf16", out=None, variant=None,
+                     stream=None):
+    """Grouped (per-expert) FP8 GEMM: A e4m3 [M][K] with rows sorted by
+    expert, B e4m3 [E][N][K], sa fp32 [M], sb fp32 [E][N], offsets int32
+    [E + 1] on the GPU (rows [offsets[e], offsets[e+1]) use expert e)."""
+    torch = _torch()
+    _ensure_init()
+    M, K = A.shape
+    E, N, K2 = B.shape
+    if K2 != K:
+        raise ValueError(f"A is [M][{K}] but B is [E][N][{K2}]")
+    if offsets.dtype != torch.int32 or tuple(offsets.shape) != (E + 1,):
+        raise ValueError(f"offsets must be int32 of shape ({E + 1},)")
+    out = _out(out, M, N, out_dtype, A.device)
+    args = [_bytes8(A, "A"), _bytes8(B, "B"), _f32(sa, "sa", (M,)),
+            _f32(sb, "sb", (E, N)), _dev_ptr(offsets, "offsets"), _dev_ptr(out, "out"),
+            OUT[out_dtype], M, N, K, E, _stream(stream)]
+    L = load_library()
+    rc = (L.gemm_fp8_grouped_ex(*args, variant.encode()) if variant
+          else L.gemm_fp8_grouped(*args))
+    _check("gemm_fp8_grouped", rc)
+    return out
+
+
+def grouped_select(M: int, E: int) -> str:
+    """The variant gemm_fp8_grouped picks for M rows over E experts."""
+    buf = ctypes.create_string_buffer(64)
+    _check("qll_grouped_select", load_library().qll_grouped_select(M, E, buf, 64))
+    return buf.value.decode()
+
 
 def variants(op: str | int) -> list[dict]:
     L = load_library()

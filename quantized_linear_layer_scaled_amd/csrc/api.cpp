@@ -30,6 +30,8 @@ extern const Variant kVariantsInt8[];
 extern const int kNumVariantsInt8;
 extern const Variant kVariantsFp8[];
 extern const int kNumVariantsFp8;
+extern const Variant kVariantsFp8Grouped[];
+extern const int kNumVariantsFp8Grouped;
 extern const Variant kVariantsBlock[];
 extern const int kNumVariantsBlock;
 extern const Variant kVariantsBf16[];
@@ -48,6 +50,12 @@ const Variant* variants(int op, int* count)
     case OP_BF16: *count = kNumVariantsBf16; return kVariantsBf16;
     default: *count = 0; return nullptr;
     }
+}
+
+const Variant* grouped_variants(int* count)
+{
+    *count = kNumVariantsFp8Grouped;
+    return kVariantsFp8Grouped;
 }
 
 hipError_t launch_splitk_reduce(int op, const GemmArgs& a, hipStream_t stream)
@@ -419,6 +427,8 @@ int run_gemm(int op, const void* A, const void* B, const float* sa,
     a.splits = effective_splits(op, K, cfg.splits);
     a.kchunk = (int)split_chunk(op, K, cfg.splits);
     a.kfold = op == OP_BF16 ? kBiFold : 1;
+    a.offsets = nullptr;
+    a.E = 0;
     if (a.splits > 1) {
         const uint64_t need = (uint64_t)a.splits * M * N * 4;
         if (!ws || ws_bytes < need)
@@ -432,6 +442,15 @@ int run_gemm(int op, const void* A, const void* B, const float* sa,
     if (a.splits > 1 && launch_splitk_reduce(op, a, s) != hipSuccess)
         return QLL_ERR_HIP;
     return QLL_OK;
+}
+
+// Built-in tile rule of the grouped GEMM: few rows per expert take small
+// tiles, many rows the 128x128 tile with two workgroups per CU.
+const char* grouped_rule(int64_t M, int64_t E)
+{
+    const int64_t per = M / (E > 0 ? E : 1);
+    return per <= 128 ? "p64x64_w2x2_k128_s3"
+                      : (per <= 512 ? "p128x64_w2x2_k128_s3" : "p128x128_w2x2_k128_s2");
 }
 
 }  // namespace
@@ -593,6 +612,73 @@ int linear_fp8_dynamic(const void* x, const void* B, const float* sb, void* q, f
 {
     return linear_fp8_dynamic_ex(x, B, sb, q, sa, out, out_dtype, M, N, K, ws, ws_bytes,
                                  stream, nullptr);
+}
+
+int qll_grouped_select(int64_t M, int64_t E, char* buf, size_t cap)
+{
+    if (M < 0 || E < 1 || !buf || cap == 0)
+        return QLL_ERR_INVALID_ARG;
+    const char* name = grouped_rule(M, E);
+    if (std::strlen(name) + 1 > cap)
+        return QLL_ERR_INVALID_ARG;
+    std::memcpy(buf, name, std::strlen(name) + 1);
+    return QLL_OK;
+}
+
+int gemm_fp8_grouped_ex(const void* A, const void* B, const float* sa, const float* sb,
+                        const int32_t* offsets, void* out, int out_dtype, int64_t M,
+                        int64_t N, int64_t K, int64_t E, void* stream, const char* variant)
+{
+    if (M < 0 || N <= 0 || K <= 0 || K % 16 || E < 1 || E > 65536 || M > 0x7FFFFFFF ||
+        N > 0x7FFFFFFF || K > 0x3FFFFFFF || M * K > ((int64_t)1 << 40) ||
+        E * N * K > ((int64_t)1 << 42) || M * N > ((int64_t)1 << 40))
+        return QLL_ERR_INVALID_ARG;
+    if (out_dtype != QLL_OUT_BF16 && out_dtype != QLL_OUT_FP32)
+        return QLL_ERR_INVALID_ARG;
+    int nv = 0;
+    const Variant* vs = grouped_variants(&nv);
+    const char* name = variant ? variant : grouped_rule(M, E);
+    int vi = -1;
+    for (int i = 0; i < nv; ++i)
+        if (std::strcmp(vs[i].name, name) == 0)
+            vi = i;
+    if (vi < 0)
+        return QLL_ERR_INVALID_ARG;
+    if (M == 0)
+        return QLL_OK;
+    if (!A || !B || !sa || !sb || !offsets || !out)
+        return QLL_ERR_INVALID_ARG;
+    if (misaligned(A, 16) || misaligned(B, 16) || misaligned(out, 16) || misaligned(sa, 4) ||
+        misaligned(sb, 4) || misaligned(offsets, 4))
+        return QLL_ERR_MISALIGNED;
+    if (!variant_fits(vs[vi], K))
+        return QLL_ERR_UNSUPPORTED;
+    GemmArgs a;
+    a.A = A;
+    a.B = B;
+    a.sa = sa;
+    a.sb = sb;
+    a.out = out;
+    a.ws = nullptr;
+    a.out_dtype = out_dtype;
+    a.M = (int)M;
+    a.N = (int)N;
+    a.K = (int)K;
+    a.kbytes = (int)K;
+    a.splits = 1;
+    a.kchunk = (int)K;
+    a.kfold = 1;
+    a.offsets = offsets;
+    a.E = (int)E;
+    return vs[vi].launch(a, (hipStream_t)stream) == hipSuccess ? QLL_OK : QLL_ERR_HIP;
+}
+
+int gemm_fp8_grouped(const void* A, const void* B, const float* sa, const float* sb,
+                     const int32_t* offsets, void* out, int out_dtype, int64_t M, int64_t N,
+                     int64_t K, int64_t E, void* stream)
+{
+    return gemm_fp8_grouped_ex(A, B, sa, sb, offsets, out, out_dtype, M, N, K, E, stream,
+                               nullptr);
 }
 
 int qll_init(const char* table_path)

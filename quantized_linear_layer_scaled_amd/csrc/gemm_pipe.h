@@ -104,9 +104,59 @@ constexpr int pipe_waves_per_eu()
     return w < 1 ? 1 : (w > 8 ? 8 : w);
 }
 
+// Grouped GEMM: the expert that owns virtual row tile t (tiles of BP rows,
+// numbered expert by expert) and its row range [m0, m1) for that tile.
+// Offsets are clamped to [0, M] and made non-decreasing, so no access leaves
+// the A rows whatever the offsets hold.  Lane-parallel over 64 experts at a
+// time (prefix sum by shuffles); every lane gets the same answer, e = -1 past
+// the last tile.
+__device__ __forceinline__ void group_tile(const int* __restrict__ off, int E, int M, int t,
+                                           int BP, int lane, int& e, int& m0, int& m1)
+{
+    int before = 0;   // tiles of the experts already scanned
+    int carry = 0;    // running maximum of the offsets already scanned
+    for (int base = 0; base < E; base += 64) {
+        const int j = base + lane;
+        const bool live = j < E;
+        // c[j] = max(clamp(off[0..j])): expert j owns rows [c[j], c[j+1])
+        int lo = live ? min(max(off[j], 0), M) : 0;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int v = __shfl_up(lo, d, 64);
+            if (lane >= d)
+                lo = max(lo, v);
+        }
+        lo = max(lo, carry);
+        const int hi = live ? max(lo, min(max(off[j + 1], 0), M)) : lo;
+        const int tiles = live ? (hi - lo + BP - 1) / BP : 0;
+        int incl = tiles;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int v = __shfl_up(incl, d, 64);
+            if (lane >= d)
+                incl += v;
+        }
+        const unsigned long long hit = __ballot(live && before + incl > t);
+        if (hit) {
+            const int L = __ffsll((long long)hit) - 1;
+            const int first = before + __shfl(incl - tiles, L, 64);
+            e = base + L;
+            m0 = __shfl(lo, L, 64) + (t - first) * BP;
+            m1 = __shfl(hi, L, 64);
+            return;
+        }
+        before += __shfl(incl, 63, 64);
+        carry = __shfl(hi, 63, 64);
+    }
+    e = -1;
+    m0 = m1 = 0;
+}
+
 // SPLITK only gives the first stage of a Split-K call its own kernel symbol
 // (the code is the same), so that traces separate the two kinds of launch.
-template <int OP, int BP, int BQ, int WP, int WQ, int KSTAGE, int STAGES, bool SPLITK>
+// GROUPED: the per-expert GEMM over rows sorted by expert (no Split-K).
+template <int OP, int BP, int BQ, int WP, int WQ, int KSTAGE, int STAGES, bool SPLITK,
+          bool GROUPED = false>
 __global__ __launch_bounds__(WP* WQ * 64)
 __attribute__((amdgpu_waves_per_eu(pipe_waves_per_eu<OP, BP, BQ, WP, WQ, KSTAGE, STAGES>())))
 void gemm_pipe_kernel(GemmArgs a)
@@ -130,6 +180,8 @@ void gemm_pipe_kernel(GemmArgs a)
     static_assert(ROWS * NC % THREADS == 0, "stage must split evenly over the waves");
     static_assert((NC & (NC - 1)) == 0 && KSTAGE % KSTEP == 0, "bad K stage");
     static_assert(STAGES >= 2 && (STAGES - 1) * LPT < 64, "bad pipeline depth");
+    static_assert(!GROUPED || (!SPLITK && (OP == OP_FP8 || OP == OP_INT8)),
+                  "grouped: per-token x per-channel ops, no Split-K");
     static_assert(!BLK || (KSTAGE == 128 && NSTEP == 1 && BP <= 256 && WAVES >= BP / 64),
                   "block scaling: one 128-wide K group per stage");
 
@@ -163,11 +215,35 @@ void gemm_pipe_kernel(GemmArgs a)
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int wpi = wave % WP, wqi = wave / WP;
-    const int M = a.M, N = a.N;
-    const int tp = (M + BP - 1) / BP, tq = (N + BQ - 1) / BQ;
-    int tile_p, tile_q;
-    xcd_tile(blockIdx.x, tp, tq, 4, tile_p, tile_q);
-    const int p0 = tile_p * BP, q0 = tile_q * BQ;
+    const int N = a.N;
+    const int tq = (N + BQ - 1) / BQ;
+    int M = a.M;  // the tile's row limit (grouped: the end of its expert's rows)
+    int tile_p, tile_q, p0;
+    const uint8_t* Bp = (const uint8_t*)a.B;
+    const float* sbp = a.sb;
+    if constexpr (GROUPED) {
+        // virtual row tiles: at most one partial tile per expert
+        const int tpv = (a.M + BP - 1) / BP + a.E;
+        xcd_tile(blockIdx.x, tpv, tq, 4, tile_p, tile_q);
+        int e, m0, m1;
+        group_tile(a.offsets, a.E, a.M, tile_p, BP, lane, e, m0, m1);
+        // equal in every lane: make them scalar (the buffer resources below
+        // must live in scalar registers)
+        e = __builtin_amdgcn_readfirstlane(e);
+        m0 = __builtin_amdgcn_readfirstlane(m0);
+        m1 = __builtin_amdgcn_readfirstlane(m1);
+        if (e < 0)
+            return;  // past the last tile (the same for every wave)
+        p0 = m0;
+        M = m1;
+        Bp += (size_t)e * N * (size_t)a.kbytes;
+        sbp += (size_t)e * N;
+    } else {
+        const int tp = (M + BP - 1) / BP;
+        xcd_tile(blockIdx.x, tp, tq, 4, tile_p, tile_q);
+        p0 = tile_p * BP;
+    }
+    const int q0 = tile_q * BQ;
     const int z = blockIdx.y;
     const int kbeg = z * a.kchunk;
     const int kend = min(a.kbytes, kbeg + a.kchunk);
@@ -178,7 +254,7 @@ void gemm_pipe_kernel(GemmArgs a)
     // row of its matrix.
     const v4i rsA = buffer_rsrc((const uint8_t*)a.A + (size_t)p0 * ldk,
                                 (uint32_t)min((uint64_t)(M - p0) * ldk, (uint64_t)0x7FFFFFFF));
-    const v4i rsB = buffer_rsrc((const uint8_t*)a.B + (size_t)q0 * ldk,
+    const v4i rsB = buffer_rsrc(Bp + (size_t)q0 * ldk,
                                 (uint32_t)min((uint64_t)(N - q0) * ldk, (uint64_t)0x7FFFFFFF));
 
     // Source of each of this thread's LPT loads: LDS chunk index
@@ -441,7 +517,7 @@ void gemm_pipe_kernel(GemmArgs a)
     if (SCALED && scaled) {
 #pragma unroll
         for (int t = 0; t < 8; ++t)
-            sbv[t] = n + t < N ? a.sb[n + t] : 0.0f;
+            sbv[t] = n + t < N ? sbp[n + t] : 0.0f;
 #pragma unroll
         for (int i = 0; i < RP; ++i)
 #pragma unroll
@@ -540,6 +616,17 @@ hipError_t launch_pipe(const GemmArgs& a, hipStream_t stream)
     return hipGetLastError();
 }
 
+template <int OP, int BP, int BQ, int WP, int WQ, int KSTAGE, int STAGES>
+hipError_t launch_pipe_grouped(const GemmArgs& a, hipStream_t stream)
+{
+    const long tiles = (long)((a.M + BP - 1) / BP + a.E) * ((a.N + BQ - 1) / BQ);
+    if (a.splits != 1 || tiles > 0x7FFFFFFFL || (long)BP * a.kbytes > 0x7FFFFFFFL)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemm_pipe_kernel<OP, BP, BQ, WP, WQ, KSTAGE, STAGES, false, true>),
+                       dim3((unsigned)tiles, 1), dim3(WP * WQ * 64), 0, stream, a);
+    return hipGetLastError();
+}
+
 }  // namespace qll
 
 // X(OP, BP, BQ, WP, WQ, KSTAGE, STAGES) for every pipelined variant.
@@ -575,6 +662,11 @@ hipError_t launch_pipe(const GemmArgs& a, hipStream_t stream)
 #define QLL_PIPE_INSTANTIATE(OP, BP, BQ, WP, WQ, KS, ST)                                       \
     template __global__ void qll::gemm_pipe_kernel<OP, BP, BQ, WP, WQ, KS, ST, false>(qll::GemmArgs); \
     template __global__ void qll::gemm_pipe_kernel<OP, BP, BQ, WP, WQ, KS, ST, true>(qll::GemmArgs);
+#define QLL_PIPE_GROUPED_INSTANTIATE(OP, BP, BQ, WP, WQ, KS, ST) \
+    template __global__ void qll::gemm_pipe_kernel<OP, BP, BQ, WP, WQ, KS, ST, false, true>(qll::GemmArgs);
+#define QLL_PIPE_GROUPED_ENTRY(OP, BP, BQ, WP, WQ, KS, ST)                           \
+    {"p" #BP "x" #BQ "_w" #WP "x" #WQ "_k" #KS "_s" #ST, OP, 0, BP, BQ, WP, WQ, KS,    \
+     (ST) * ((BP) + (BQ)) * (KS), &qll::launch_pipe_grouped<OP, BP, BQ, WP, WQ, KS, ST>},
 #define QLL_PIPE_ENTRY(OP, BP, BQ, WP, WQ, KS, ST)                                   \
     {"p" #BP "x" #BQ "_w" #WP "x" #WQ "_k" #KS "_s" #ST, OP, 0, BP, BQ, WP, WQ, KS,    \
      (ST) * ((BP) + (BQ)) * (KS), &qll::launch_pipe<OP, BP, BQ, WP, WQ, KS, ST>},

@@ -33,6 +33,10 @@ struct GemmArgs {
     int splits;      // effective number of K pieces
     int kchunk;      // bytes of K per piece (multiple of kSplitGranule)
     int kfold;       // bf16 only: K chunks summed separately, then in order
+    // grouped (per-expert) GEMM only: A rows [offsets[e], offsets[e+1]) use
+    // weights B + e * N * K and scales sb + e * N (device int32 [E + 1])
+    const int* offsets;
+    int E;
 };
 
 // The batch-invariant bf16 op sums every K piece as kBiFold contiguous chunks
@@ -59,6 +63,8 @@ struct Variant {
 
 // Registries, one per op (defined in the kernel translation units).
 const Variant* variants(int op, int* count);
+// Grouped FP8 GEMM: the pipelined variants launched over experts.
+const Variant* grouped_variants(int* count);
 
 // Second Split-K stage: out = epilogue(sum_{s ascending} ws[s]).
 hipError_t launch_splitk_reduce(int op, const GemmArgs& a, hipStream_t stream);

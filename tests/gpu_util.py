@@ -5,11 +5,17 @@ Acceptance rule for floating-point outputs (the GPU accumulates in fp32 on the
 matrix cores in an order of its own, so several results are correct):
   * normwise:  max|y - ref| / max|ref| <= 1e-2 (bf16 out) or 2e-3 (fp32 out);
   * elementwise a-priori bound, for every output element:
-        |y - ref| <= c_out * |ref| + (K + K/128 + 4) * 2^-23 * absref
+        |y - ref| <= c_out * |ref| + ((K + K/128 + 4) * 2^-23 + 2^-12) * absref
     where absref = sum_k |scale * a_k * b_k| (from the oracle), c_out = 2^-8
     (one bf16 rounding) or 2^-22 (the fp32 epilogue products), and 2^-23 is
     the fp32 unit roundoff doubled so that accumulation by truncation is
-    covered as well as by rounding.
+    covered as well as by rounding.  The 2^-12 term covers the matrix core's
+    own sum inside one MFMA: gfx950's e4m3 x e4m3 MFMA (128 products per
+    lane group) adds its products more coarsely than step-by-step fp32 -- at
+    K = 256 every kernel, the plain tiled one included, showed errors up to
+    2^-14 of absref, about twice the fp32-only term, and independent of K.
+    The per-step errors add up to at most that fraction of absref, since the
+    steps partition the K range.
 """
 import numpy as np
 import torch
@@ -52,7 +58,7 @@ def check_fp(y: np.ndarray, ref: np.ndarray, absref: np.ndarray, K: int,
     tol = 1e-2 if out_dtype == "bf16" else 2e-3
     assert normwise <= tol, f"{what}: normwise error {normwise:.3e} > {tol}"
     c_out = 2.0 ** -8 if out_dtype == "bf16" else 2.0 ** -22
-    bound = c_out * np.abs(ref) + (K + K // 128 + 4) * 2.0 ** -23 * absref
+    bound = c_out * np.abs(ref) + ((K + K // 128 + 4) * 2.0 ** -23 + 2.0 ** -12) * absref
     bad = err > bound * (1 + 1e-12) + 1e-30
     assert not np.any(bad), (
         f"{what}: {int(bad.sum())} elements outside the a-priori bound; worst "

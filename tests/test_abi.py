@@ -128,6 +128,32 @@ def test_linear_fp8_dynamic_validation(qll):
     assert lin(cfg=(0, 4), ws=P + 4, wsb=1 << 30) == 3
 
 
+def test_grouped_validation(qll):
+    # A, B, sa, sb, offsets, out, out_dtype, M, N, K, E, stream
+    L = qll.load_library()
+
+    def grp(A=P, sa=P, off=P, od=0, M=64, N=128, K=256, E=4, variant=None):
+        args = [A, P, sa, P, off, P, od, M, N, K, E, None]
+        if variant is None:
+            return L.gemm_fp8_grouped(*args)
+        return L.gemm_fp8_grouped_ex(*args, variant.encode())
+
+    assert grp(E=0) == 1
+    assert grp(K=264) == 1                    # K % 16
+    assert grp(od=2) == 1                     # no raw int32 out
+    assert grp(off=None) == 1
+    assert grp(sa=P + 2) == 3
+    assert grp(off=P + 2) == 3
+    assert grp(A=P + 8) == 3
+    assert grp(variant="no_such_tile") == 1
+    assert grp(variant="k16x16_w8") == 1      # only the pipelined tiles
+    assert grp(M=0, A=None, sa=None, off=None) == 0
+    assert qll.grouped_select(128, 64) == "p64x64_w2x2_k128_s3"
+    assert qll.grouped_select(8192, 8) == "p128x128_w2x2_k128_s2"
+    names = [v["name"] for v in qll.variants("fp8")]
+    assert all(qll.grouped_select(M, 64) in names for M in (0, 1, 5000, 1 << 20))
+
+
 def test_quantizer_validation(qll):
     L = qll.load_library()
     q = L.quantize_per_token_fp8

@@ -117,6 +117,41 @@ def test_fp8_fraction_bruteforce(M, N, K):
             assert absref[m, n] == float(aex)
 
 
+def test_fp8_grouped_fraction_bruteforce():
+    # three experts, one of them empty; rows sorted by expert
+    g = np.random.default_rng([17])
+    counts = [2, 0, 3]
+    off = np.concatenate([[0], np.cumsum(counts)])
+    M, N, K, E = int(off[-1]), 4, 24, 3
+    A, B = rand_e4m3((M, K), g), rand_e4m3((E, N, K), g)
+    sa = g.uniform(1e-3, 1e-1, M).astype(np.float32)
+    sb = g.uniform(1e-3, 1e-1, (E, N)).astype(np.float32)
+    ref, absref = oracle.gemm_fp8_grouped(A, B, sa, sb, off, with_abs=True)
+    da, db = torch_dec_e4m3(A), torch_dec_e4m3(B)
+    owner = [0, 0, 2, 2, 2]
+    for m in range(M):
+        e = owner[m]
+        for n in range(N):
+            s = sum(Fraction(da[m, k]) * Fraction(db[e, n, k]) for k in range(K))
+            assert ref[m, n] == float(Fraction(float(sa[m])) * Fraction(float(sb[e, n])) * s)
+            aex = abs(Fraction(float(sa[m])) * Fraction(float(sb[e, n]))) * sum(
+                abs(Fraction(da[m, k]) * Fraction(db[e, n, k])) for k in range(K))
+            assert absref[m, n] == float(aex)
+    # sampled rows give the same values as the full product
+    rows = [4, 0, 3]
+    assert np.array_equal(oracle.gemm_fp8_grouped(A, B, sa, sb, off, rows=rows), ref[rows])
+
+
+def test_fp8_grouped_single_expert_is_the_dense_product():
+    g = np.random.default_rng([18])
+    M, N, K = 7, 5, 40
+    A, B = rand_e4m3((M, K), g), rand_e4m3((1, N, K), g)
+    sa = g.uniform(1e-3, 1e-1, M).astype(np.float32)
+    sb = g.uniform(1e-3, 1e-1, (1, N)).astype(np.float32)
+    dense = oracle.gemm_fp8(A, B[0], sa, sb[0])
+    assert np.array_equal(oracle.gemm_fp8_grouped(A, B, sa, sb, [0, M]), dense)
+
+
 def test_fp8_matches_numpy_dequantized():
     g = np.random.default_rng(8)
     M, N, K = 19, 41, 512

@@ -26,6 +26,11 @@ vocabulary N=151936 and a square N=K=2048 weight):
                N(0, 1) / sqrt(K); each M uses the first M rows of a 2048-row A.
   Vocab        N=151936, K=2048, M in VOCAB_M; A bf16 N(0, 1), W bf16
                N(0, 0.02); both the bf16 and the FP8 path on the same data.
+  Grouped FP8  MOE_E = 64 experts of N=1536 x K=2048 weights (bf16 N(0, 0.02),
+               quantized per output channel), T in MOE_T tokens routed to
+               MOE_TOPK = 8 experts each with a skewed synthetic routing; the
+               routed rows (bf16 N(0, 1) with outliers) are quantized per
+               token.
 """
 from __future__ import annotations
 
@@ -43,9 +48,14 @@ BI_M = [1, 4, 8, 16, 32, 64, 256, 512, 1024, 2048]
 VOCAB_SHAPE = (151936, 2048)
 VOCAB_M = [1, 8, 64, 512, 2048]
 MAX_M = 2048
+# grouped (per-expert) FP8 GEMM: E experts of [N][K] weights, T tokens each
+# routed to TOPK distinct experts
+MOE_E, MOE_TOPK = 64, 8
+MOE_SHAPE = (1536, 2048)  # (N, K)
+MOE_T = [16, 128, 1024]
 
 # workload ids used in the seeds
-W_INT8, W_FP8, W_BLOCK, W_BI, W_VOCAB, W_TEST = 1, 2, 3, 4, 5, 9
+W_INT8, W_FP8, W_BLOCK, W_BI, W_VOCAB, W_MOE, W_TEST = 1, 2, 3, 4, 5, 6, 9
 
 
 def rng(*key) -> np.random.Generator:
@@ -154,3 +164,30 @@ def vocab_activations(K=2048, key=(W_VOCAB,)):
 
 def vocab_weights(N=151936, K=2048, key=(W_VOCAB,)):
     return bf16_normal((N, K), (*key, N, K, 1), std=0.02)
+
+
+def moe_routing(T, E=MOE_E, topk=MOE_TOPK, key=(W_MOE,)):
+    """Synthetic routing: each of T tokens picks `topk` distinct experts with
+    probabilities proportional to 1 / (rank + 1) over a seeded random order of
+    the experts (a skewed load, some experts empty at small T).  Returns the
+    expert offsets (int32 [E + 1]) of the rows sorted by expert: T * topk rows."""
+    g = rng(*key, T, E, topk)
+    order = g.permutation(E)
+    p = 1.0 / (np.arange(E) + 1.0)
+    p = p / p.sum()
+    counts = np.zeros(E, dtype=np.int64)
+    for _ in range(T):
+        pick = g.choice(E, size=topk, replace=False, p=p)
+        counts[order[pick]] += 1
+    return np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+
+
+def moe_activations(rows, K, key=(W_MOE,)):
+    """bf16 activations of the routed rows, distributed like the FP8 dynamic
+    workload (N(0, 1) with outlier channels)."""
+    return bf16_normal((rows, K), (*key, 1, rows, K), outlier_frac=0.01)
+
+
+def moe_weights(E, N, K, key=(W_MOE,)):
+    """bf16 expert weights [E][N][K], N(0, 0.02)."""
+    return bf16_normal((E * N, K), (*key, 2, E, N, K), std=0.02).reshape(E, N, K)
