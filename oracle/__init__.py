@@ -15,6 +15,9 @@ the design notes):
   * vLLM PR #53446, sections "Summary" and "Test Plan": the batch-invariant
     bf16 matmul, i.e. the plain bf16 product whose rows must not depend on the
     batch size.
+  * The 4-bit formats named in the introduction of "Helion in vLLM", in their
+    block-scaled form MXFP4, whose encodings and conversion rule come from the
+    OCP Microscaling Formats (MX) v1.0 specification (the pages define none).
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 against something other than itself (torch's own e4m3/bf16 casts, Python
@@ -89,6 +92,17 @@ def _load():
     lib.oracle_e4m3_encode_array.argtypes = [_P, _I64, _P]
     lib.oracle_e4m3_decode_array.restype = None
     lib.oracle_e4m3_decode_array.argtypes = [_P, _I64, _P]
+    lib.oracle_e2m1_decode.restype = ctypes.c_double
+    lib.oracle_e2m1_decode.argtypes = [ctypes.c_uint8]
+    lib.oracle_e8m0_decode.restype = ctypes.c_double
+    lib.oracle_e8m0_decode.argtypes = [ctypes.c_uint8]
+    lib.oracle_e2m1_encode_array.restype = None
+    lib.oracle_e2m1_encode_array.argtypes = [_P, _I64, _P]
+    lib.oracle_quantize_mxfp4.restype = ctypes.c_int
+    lib.oracle_quantize_mxfp4.argtypes = [_P, _I64, _I64, _P, _P]
+    lib.oracle_gemm_mxfp4.restype = None
+    lib.oracle_gemm_mxfp4.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _P, _I64,
+                                      _P, _P]
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     _lib = lib
@@ -149,6 +163,41 @@ def bf16_decode(bits) -> np.ndarray:
     return (b.astype(np.uint32) << 16).view(np.float32)
 
 
+def e2m1_decode(codes) -> np.ndarray:
+    """E2M1 codes (low 4 bits of uint8) -> float64 values."""
+    c = np.asarray(codes, dtype=np.uint8)
+    lib = _load()
+    return np.vectorize(lambda v: lib.oracle_e2m1_decode(int(v) & 15),
+                        otypes=[np.float64])(c)
+
+
+def e2m1_encode(values) -> np.ndarray:
+    """float64 values -> E2M1 codes, nearest with ties to even, saturating
+    at 6, sign kept for zeros."""
+    v = np.ascontiguousarray(np.asarray(values, dtype=np.float64))
+    out = np.empty(v.shape, dtype=np.uint8)
+    _load().oracle_e2m1_encode_array(_ptr(v), v.size, _ptr(out))
+    return out
+
+
+def e8m0_decode(codes) -> np.ndarray:
+    """E8M0 scale codes -> float64 powers of two (NaN for 0xFF)."""
+    c = np.asarray(codes, dtype=np.uint8)
+    lib = _load()
+    return np.vectorize(lambda v: lib.oracle_e8m0_decode(int(v)),
+                        otypes=[np.float64])(c)
+
+
+def unpack_fp4(packed: np.ndarray) -> np.ndarray:
+    """Packed E2M1 codes [..][K/2] -> one code per element [..][K] (element
+    2j from bits 0-3 of byte j, element 2j+1 from bits 4-7)."""
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(p.shape[:-1] + (p.shape[-1] * 2,), dtype=np.uint8)
+    out[..., 0::2] = p & 15
+    out[..., 1::2] = p >> 4
+    return out
+
+
 # --------------------------------------------------------------------------
 # Quantizers
 # --------------------------------------------------------------------------
@@ -182,6 +231,21 @@ def quantize_fp8_block(w_bf16_bits: np.ndarray, block: int = 128):
                                            _ptr(s))
     if rc != 0:
         raise ValueError(f"oracle_quantize_fp8_block failed ({rc})")
+    return q, s
+
+
+def quantize_mxfp4(x_bf16_bits: np.ndarray):
+    """MXFP4 quantization of bf16 [M][K] (uint16 bits), one E8M0 scale per
+    32 consecutive elements of a row.  Returns (packed codes uint8 [M][K/2],
+    scale codes uint8 [M][K/32])."""
+    x = np.ascontiguousarray(x_bf16_bits, dtype=np.uint16)
+    M, K = x.shape
+    q = np.empty((M, K // 2), dtype=np.uint8)
+    s = np.empty((M, K // 32), dtype=np.uint8)
+    rc = _load().oracle_quantize_mxfp4(_ptr(x), M, K, _ptr(q), _ptr(s))
+    if rc != 0:
+        raise ValueError(f"oracle_quantize_mxfp4 failed ({rc}): non-finite input "
+                         "or K not a multiple of 32")
     return q, s
 
 
@@ -305,4 +369,26 @@ def gemm_bf16(A_bits, B_bits, rows=None, with_abs=False):
     absref = np.empty((r.size, N), dtype=np.float64) if with_abs else None
     _load().oracle_gemm_bf16(_ptr(A), _ptr(B), M, N, K, _ptr(r), r.size,
                              _ptr(ref), _ptr(absref) if with_abs else None)
+    return (ref, absref) if with_abs else ref
+
+
+def gemm_mxfp4(A, B, sa, sb, rows=None, with_abs=False):
+    """MXFP4 GEMM in fp64: A [M][K/2], B [N][K/2] packed E2M1 codes, sa
+    [M][K/32], sb [N][K/32] E8M0 scale codes; every element is its code's
+    value times its block's power of two."""
+    A = np.ascontiguousarray(A, dtype=np.uint8)
+    B = np.ascontiguousarray(B, dtype=np.uint8)
+    sa = np.ascontiguousarray(sa, dtype=np.uint8)
+    sb = np.ascontiguousarray(sb, dtype=np.uint8)
+    M, K2 = A.shape
+    N = B.shape[0]
+    K = 2 * K2
+    assert B.shape[1] == K2 and K % 32 == 0
+    assert sa.shape == (M, K // 32) and sb.shape == (N, K // 32)
+    r = _rows(M, rows)
+    ref = np.empty((r.size, N), dtype=np.float64)
+    absref = np.empty((r.size, N), dtype=np.float64) if with_abs else None
+    _load().oracle_gemm_mxfp4(_ptr(A), _ptr(B), _ptr(sa), _ptr(sb), M, N, K,
+                              _ptr(r), r.size, _ptr(ref),
+                              _ptr(absref) if with_abs else None)
     return (ref, absref) if with_abs else ref

@@ -1,7 +1,8 @@
 /*
  * oracle.c -- plain, slow, obviously correct CPU reference for the scaled_mm
  * hot path (per-token dynamic FP8 quantization, W8A8 INT8, FP8 with
- * per-token x per-channel scales, Block-FP8, bf16 GEMM).
+ * per-token x per-channel scales, Block-FP8, bf16 GEMM, and the MXFP4
+ * quantizer and GEMM).
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, includes or
  * calls this file; only the tests, the smoke check and the CPU-baseline leg of
@@ -375,6 +376,158 @@ void oracle_gemm_bf16(const uint16_t* A, const uint16_t* B, int64_t M, int64_t N
             if (absref)
                 absref[r * N + n] = asum;
         }
+}
+
+/* ------------------------------------------------------------------------ */
+/* MXFP4: 4-bit E2M1 elements sharing one power-of-two E8M0 scale per block  */
+/* of 32 consecutive K elements.  The pages name 4-bit formats (INT4, NVFP4) */
+/* among those vLLM serves (introduction of "Helion in vLLM: A Unified Route */
+/* to Tunable Linear Kernels") but define none; MXFP4 is the block-scaled    */
+/* 4-bit format the CDNA4 matrix cores take natively, and its element and    */
+/* scale encodings and its conversion rule are those of the OCP Microscaling */
+/* Formats (MX) v1.0 specification (sections on the E2M1 element type, the   */
+/* E8M0 scale type and the conversion of a vector to an MX block).           */
+/* Packing (a reading: the specification leaves it to the implementation):   */
+/* element 2j of a row in bits 0-3 of byte j, element 2j+1 in bits 4-7.      */
+/* ------------------------------------------------------------------------ */
+
+/* E2M1: bit 3 sign, bits 2-1 exponent (bias 1), bit 0 mantissa.  Exponent
+ * field 0 is subnormal (m * 2^-1).  No infinity, no NaN; largest value 6. */
+double oracle_e2m1_decode(uint8_t c)
+{
+    int sign = (c >> 3) & 1;
+    int e = (c >> 1) & 3;
+    int m = c & 1;
+    double mag = e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return sign ? -mag : mag;
+}
+
+/* E8M0 scale: the power of two 2^(c - 127); code 0xFF is NaN. */
+double oracle_e8m0_decode(uint8_t c)
+{
+    return c == 0xFF ? NAN : ldexp(1.0, (int)c - 127);
+}
+
+/* Nearest E2M1 code to v, ties to the code whose last bit is 0; magnitudes
+ * above the largest value 6 give 6 (the MX conversion saturates to the
+ * largest normal).  The sign bit is the sign of v, also for a magnitude that
+ * rounds to zero.  Codes 0..7 have increasing magnitudes. */
+uint8_t oracle_e2m1_encode_rne(double v)
+{
+    uint8_t sign = signbit(v) ? 8 : 0;
+    double a = fabs(v);
+    int lo = 0, best;
+    if (isnan(v))
+        return 0xFF;
+    while (lo < 7 && oracle_e2m1_decode((uint8_t)(lo + 1)) <= a)
+        ++lo;
+    best = lo;
+    if (lo < 7) {
+        double dlo = a - oracle_e2m1_decode((uint8_t)lo);
+        double dhi = oracle_e2m1_decode((uint8_t)(lo + 1)) - a;
+        if (dhi < dlo || (dhi == dlo && ((lo + 1) & 1) == 0))
+            best = lo + 1;
+    }
+    return (uint8_t)(sign | best);
+}
+
+/* MXFP4 quantization of bf16 x [M][K] (K a multiple of 32), one block of 32
+ * consecutive elements of a row at a time:
+ *   amax = max |x_i|;
+ *   shared exponent E = floor(log2(amax)) - 2 (2 = the exponent of E2M1's
+ *   largest normal, 6 = 1.5 * 2^2), clamped to the E8M0 range [-127, 127];
+ *   an all-zero block has no logarithm and takes the lower end -127;
+ *   scale code s = E + 127;
+ *   element code = e2m1_rne(x_i / 2^E), saturating at 6.
+ * q: packed codes [M][K/2]; s: [M][K/32].  Returns 0, or -1 on a non-finite
+ * input, -2 when 32 does not divide K. */
+int oracle_quantize_mxfp4(const uint16_t* x, int64_t M, int64_t K, uint8_t* q,
+                          uint8_t* s)
+{
+    int64_t m, b, nb;
+    int bad = 0;
+    if (K % 32 != 0)
+        return -2;
+    nb = K / 32;
+#pragma omp parallel for private(b) reduction(| : bad) schedule(static)
+    for (m = 0; m < M; ++m)
+        for (b = 0; b < nb; ++b) {
+            const uint16_t* xb = x + m * K + b * 32;
+            uint8_t codes[32];
+            double amax = 0.0;
+            int i, E;
+            for (i = 0; i < 32; ++i) {
+                double xi = (double)oracle_bf16_decode(xb[i]);
+                if (!isfinite(xi))
+                    bad = 1;
+                else if (fabs(xi) > amax)
+                    amax = fabs(xi);
+            }
+            if (amax == 0.0) {
+                E = -127;
+            } else {
+                int p;
+                (void)frexp(amax, &p); /* amax = f * 2^p, 0.5 <= f < 1 */
+                E = (p - 1) - 2;
+                if (E < -127)
+                    E = -127;
+                if (E > 127)
+                    E = 127;
+            }
+            s[m * nb + b] = (uint8_t)(E + 127);
+            for (i = 0; i < 32; ++i)
+                codes[i] = oracle_e2m1_encode_rne(
+                    ldexp((double)oracle_bf16_decode(xb[i]), -E));
+            for (i = 0; i < 16; ++i)
+                q[m * (K / 2) + b * 16 + i] =
+                    (uint8_t)((codes[2 * i] & 15) | ((codes[2 * i + 1] & 15) << 4));
+        }
+    return bad ? -1 : 0;
+}
+
+/* MXFP4 GEMM in fp64: with A [M][K/2], B [N][K/2] packed codes and
+ * sa [M][K/32], sb [N][K/32] scale codes,
+ *   ref[r][n] = sum_k dec(A[m][k]) * 2^(sa[m][k/32]-127)
+ *                     * dec(B[n][k]) * 2^(sb[n][k/32]-127),
+ * absref the same sum of magnitudes. */
+void oracle_gemm_mxfp4(const uint8_t* A, const uint8_t* B, const uint8_t* sa,
+                       const uint8_t* sb, int64_t M, int64_t N, int64_t K,
+                       const int64_t* rows, int64_t nrows, double* ref,
+                       double* absref)
+{
+    int64_t r, n, k;
+    double dec[16], sdec[256];
+    (void)M;
+    for (k = 0; k < 16; ++k)
+        dec[k] = oracle_e2m1_decode((uint8_t)k);
+    for (k = 0; k < 256; ++k)
+        sdec[k] = oracle_e8m0_decode((uint8_t)k);
+#pragma omp parallel for private(n, k) collapse(2) schedule(static)
+    for (r = 0; r < nrows; ++r)
+        for (n = 0; n < N; ++n) {
+            const int64_t m = rows[r];
+            const uint8_t* a = A + m * (K / 2);
+            const uint8_t* b = B + n * (K / 2);
+            double sum = 0.0, asum = 0.0;
+            for (k = 0; k < K; ++k) {
+                int ca = (a[k / 2] >> (4 * (k & 1))) & 15;
+                int cb = (b[k / 2] >> (4 * (k & 1))) & 15;
+                double p = dec[ca] * sdec[sa[m * (K / 32) + k / 32]] * dec[cb] *
+                           sdec[sb[n * (K / 32) + k / 32]];
+                sum += p;
+                asum += fabs(p);
+            }
+            ref[r * N + n] = sum;
+            if (absref)
+                absref[r * N + n] = asum;
+        }
+}
+
+void oracle_e2m1_encode_array(const double* v, int64_t n, uint8_t* out)
+{
+    int64_t i;
+    for (i = 0; i < n; ++i)
+        out[i] = oracle_e2m1_encode_rne(v[i]);
 }
 
 /* Elementwise helpers exposed for tests: fp32 -> bf16 bits, fp32 -> e4m3. */
