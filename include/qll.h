@@ -12,6 +12,9 @@
  *   gemm_fp8_scaled             FP8 GEMM, per-token x per-channel scales
  *   gemm_block_fp8              Block-FP8 GEMM (1x128 and 128x128 scales)
  *   gemm_bf16_batch_invariant   bf16 GEMM whose rows do not depend on M
+ *   quantize_mxfp4, gemm_mxfp4  MXFP4 (4-bit E2M1, E8M0 scale per 32) quantizer
+ *                               and GEMM, the block-scaled 4-bit format of the
+ *                               CDNA4 matrix cores (see below)
  * Each GEMM runs as an ordinary tiled GEMM, as Split-K or as Swap-AB (the
  * three strategies of "What the integration changes"), chosen per (M, N, K)
  * by a dispatch table that an on-device sweep fills, or forced with the _ex
@@ -70,7 +73,8 @@ typedef enum {
     QLL_OP_INT8 = 0,
     QLL_OP_FP8 = 1,
     QLL_OP_BLOCK_FP8 = 2,
-    QLL_OP_BF16_BI = 3
+    QLL_OP_BF16_BI = 3,
+    QLL_OP_MXFP4 = 4
 } qll_op;
 
 /* A GEMM configuration: which registered kernel variant (tile shape, wave
@@ -177,6 +181,44 @@ int gemm_bf16_batch_invariant_ex(const void* A, const void* B, void* out,
                                  int out_dtype, int64_t M, int64_t N,
                                  int64_t K, void* ws, size_t ws_bytes,
                                  void* stream, const qll_cfg* cfg);
+
+/* MXFP4.  The page "Helion in vLLM: A Unified Route to Tunable Linear
+ * Kernels" names 4-bit formats (INT4, NVFP4) among those vLLM serves
+ * (introduction) without defining them; MXFP4 is the block-scaled 4-bit
+ * format gfx950's matrix cores read natively.  Encodings and conversion rule
+ * follow the OCP Microscaling Formats (MX) v1.0 specification:
+ *   E2M1 codes (sign bit 3, values 0, 0.5, 1, 1.5, 2, 3, 4, 6), two per byte:
+ *   element 2j of a row in bits 0-3 of byte j, element 2j+1 in bits 4-7;
+ *   E8M0 scale bytes, value 2^(s - 127), one per 32 consecutive elements of
+ *   a row (0xFF = NaN is never produced here).
+ *
+ * Quantizer, for each block of 32 elements of a row of bf16 x [M][K]:
+ *   amax = max |x|;  E = floor(log2 amax) - 2 clamped to [-127, 127]
+ *   (-127 for an all-zero block);  scale byte = E + 127;
+ *   code = round-to-nearest-even of x / 2^E on the E2M1 values, saturating
+ *   at 6, sign bit = sign of x (also when the magnitude rounds to zero).
+ *   x bf16 [M][K] (16-byte aligned); q [M][K/2] bytes (4-byte aligned);
+ *   scales [M][K/32] bytes.  K % 32 == 0.  Non-finite inputs give
+ *   unspecified codes.  Used for activations (per call) and weights. */
+int quantize_mxfp4(const void* x, void* q, void* scales, int64_t M, int64_t K,
+                   void* stream);
+
+/* MXFP4 GEMM:
+ *   out[m][n] = sum_k a(m,k) * b(n,k),
+ *   a(m,k) = e2m1(A[m][k]) * 2^(sa[m][k/32] - 127), b likewise with sb,
+ *   accumulated in fp32 on the matrix cores (each 32-element block product
+ *   is exact; the block scales are applied inside the instruction);
+ *   out = bf16_rne (or fp32).
+ *   A [M][K/2], B [N][K/2] packed codes (16-byte aligned); sa [M][K/32],
+ *   sb [N][K/32] scale bytes (4-byte aligned); K % 128 == 0, K <= 2^23.
+ *   ws as for the other GEMMs (Split-K, qll_workspace_bytes(QLL_OP_MXFP4,...)).
+ * gemm_mxfp4_ex forces a configuration like the other _ex entry points. */
+int gemm_mxfp4(const void* A, const void* B, const void* sa, const void* sb,
+               void* out, int out_dtype, int64_t M, int64_t N, int64_t K,
+               void* ws, size_t ws_bytes, void* stream);
+int gemm_mxfp4_ex(const void* A, const void* B, const void* sa, const void* sb,
+                  void* out, int out_dtype, int64_t M, int64_t N, int64_t K,
+                  void* ws, size_t ws_bytes, void* stream, const qll_cfg* cfg);
 
 /* FP8 dynamic linear layer in one call ("FP8 dynamic quantization", same
  * section): quantize_per_token_fp8(x -> q, sa) followed by

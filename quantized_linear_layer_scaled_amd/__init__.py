@@ -12,7 +12,9 @@ Operations (see include/qll.h for the full contract):
   quantize_per_token_fp8, quantize_weight_block_fp8,
   gemm_w8a8_int8, gemm_fp8_scaled, gemm_block_fp8, gemm_bf16_batch_invariant,
   linear_fp8_dynamic (per-token quantization + FP8 GEMM in one call),
-  gemm_fp8_grouped (per-expert FP8 GEMM over rows sorted by expert).
+  gemm_fp8_grouped (per-expert FP8 GEMM over rows sorted by expert),
+  quantize_mxfp4, gemm_mxfp4 (MXFP4: E2M1 codes packed two per byte, one
+  E8M0 scale byte per 32 elements of a row; tensors as uint8).
 """
 from __future__ import annotations
 
@@ -29,7 +31,7 @@ STATUS = {0: "QLL_OK", 1: "QLL_ERR_INVALID_ARG", 2: "QLL_ERR_UNSUPPORTED",
           3: "QLL_ERR_MISALIGNED", 4: "QLL_ERR_WORKSPACE", 5: "QLL_ERR_NO_DEVICE",
           6: "QLL_ERR_TABLE", 7: "QLL_ERR_HIP"}
 OUT = {"bf16": 0, "fp32": 1, "int32": 2}
-OPS = {"int8": 0, "fp8": 1, "block_fp8": 2, "bf16_bi": 3}
+OPS = {"int8": 0, "fp8": 1, "block_fp8": 2, "bf16_bi": 3, "mxfp4": 4}
 
 
 class QllError(RuntimeError):
@@ -67,6 +69,9 @@ def load_library():
     for name in ("gemm_w8a8_int8", "gemm_fp8_scaled", "gemm_block_fp8"):
         getattr(L, name).argtypes = _GEMM_ARGS
         getattr(L, name + "_ex").argtypes = _GEMM_ARGS + [ctypes.POINTER(qll_cfg)]
+    L.quantize_mxfp4.argtypes = [_P, _P, _P, _I64, _I64, _P]
+    L.gemm_mxfp4.argtypes = _GEMM_ARGS
+    L.gemm_mxfp4_ex.argtypes = _GEMM_ARGS + [ctypes.POINTER(qll_cfg)]
     L.gemm_bf16_batch_invariant.argtypes = _BF16_ARGS
     L.gemm_bf16_batch_invariant_ex.argtypes = _BF16_ARGS + [ctypes.POINTER(qll_cfg)]
     _LIN = [_P, _P, _P, _P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _P, ctypes.c_size_t, _P]
@@ -327,6 +332,56 @@ def gemm_bf16_batch_invariant(A, B, out_dtype="bf16", out=None, cfg=None,
     return out
 
 
+def _u8(t, name, shape):
+    torch = _torch()
+    if t.dtype != torch.uint8 or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be uint8 of shape {tuple(shape)}")
+    return _dev_ptr(t, name)
+
+
+def quantize_mxfp4(x, q=None, scales=None, stream=None):
+    """bf16 [M][K] -> (packed E2M1 codes uint8 [M][K/2], E8M0 scale bytes
+    uint8 [M][K/32]); K % 32 == 0."""
+    torch = _torch()
+    if x.dtype != torch.bfloat16 or x.dim() != 2:
+        raise ValueError("x must be a 2-D bfloat16 tensor")
+    M, K = x.shape
+    if K % 32:
+        raise ValueError("K must be a multiple of 32")
+    if q is None:
+        q = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((M, K // 32), dtype=torch.uint8, device=x.device)
+    rc = load_library().quantize_mxfp4(
+        _dev_ptr(x, "x"), _u8(q, "q", (M, K // 2)), _u8(scales, "scales", (M, K // 32)),
+        M, K, _stream(stream))
+    _check("quantize_mxfp4", rc)
+    return q, scales
+
+
+def gemm_mxfp4(A, B, sa, sb, out_dtype="bf16", out=None, cfg=None, workspace=None,
+               stream=None):
+    """MXFP4 A [M][K/2] x B [N][K/2] (packed codes, uint8) with E8M0 scale
+    bytes sa [M][K/32], sb [N][K/32] (uint8)."""
+    _ensure_init()
+    M, K2 = A.shape
+    N, K2b = B.shape
+    if K2b != K2:
+        raise ValueError(f"A is [M][{K2}] but B is [N][{K2b}] bytes")
+    K = 2 * K2
+    pa, pb = _u8(A, "A", (M, K2)), _u8(B, "B", (N, K2))
+    psa, psb = _u8(sa, "sa", (M, K // 32)), _u8(sb, "sb", (N, K // 32))
+    out = _out(out, M, N, out_dtype, A.device)
+    c = _cfg(4, cfg)
+    ws, wsb = _workspace(4, M, N, K, c, workspace)
+    L = load_library()
+    args = [pa, pb, psa, psb, _dev_ptr(out, "out"), OUT[out_dtype], M, N, K,
+            ws.data_ptr() if ws is not None else None, wsb, _stream(stream)]
+    rc = L.gemm_mxfp4_ex(*args, ctypes.byref(c)) if c else L.gemm_mxfp4(*args)
+    _check("gemm_mxfp4", rc)
+    return out
+
+
 def linear_fp8_dynamic(x, B, sb, out_dtype="bf16", out=None, q=None, sa=None, cfg=None,
                        workspace=None, stream=None):
     """bf16 x [M][K] -> (out [M][N], q e4m3 [M][K], sa fp32 [M][1]): per-token
@@ -354,12 +409,6 @@ def linear_fp8_dynamic(x, B, sb, out_dtype="bf16", out=None, q=None, sa=None, cf
     _check("linear_fp8_dynamic", rc)
     return out, q, sa
 
-
-
-
-# --------------------------------------------------------------------------
-# registry / dispatch introspection
-# --------------------------------------------------------------------------
 
 def gemm_fp8_grouped(A, B, sa, sb, offsets, out_dtype="bf16", out=None, variant=None,
                      stream=None):
@@ -391,6 +440,10 @@ def grouped_select(M: int, E: int) -> str:
     _check("qll_grouped_select", load_library().qll_grouped_select(M, E, buf, 64))
     return buf.value.decode()
 
+
+# --------------------------------------------------------------------------
+# registry / dispatch introspection
+# --------------------------------------------------------------------------
 
 def variants(op: str | int) -> list[dict]:
     L = load_library()

@@ -36,10 +36,13 @@ extern const Variant kVariantsBlock[];
 extern const int kNumVariantsBlock;
 extern const Variant kVariantsBf16[];
 extern const int kNumVariantsBf16;
+extern const Variant kVariantsMxfp4[];
+extern const int kNumVariantsMxfp4;
 hipError_t launch_reduce_int8(const GemmArgs&, hipStream_t);
 hipError_t launch_reduce_fp8(const GemmArgs&, hipStream_t);
 hipError_t launch_reduce_block(const GemmArgs&, hipStream_t);
 hipError_t launch_reduce_bf16(const GemmArgs&, hipStream_t);
+hipError_t launch_reduce_mxfp4(const GemmArgs&, hipStream_t);
 
 const Variant* variants(int op, int* count)
 {
@@ -48,6 +51,7 @@ const Variant* variants(int op, int* count)
     case OP_FP8: *count = kNumVariantsFp8; return kVariantsFp8;
     case OP_BLOCK: *count = kNumVariantsBlock; return kVariantsBlock;
     case OP_BF16: *count = kNumVariantsBf16; return kVariantsBf16;
+    case OP_MXFP4: *count = kNumVariantsMxfp4; return kVariantsMxfp4;
     default: *count = 0; return nullptr;
     }
 }
@@ -64,15 +68,24 @@ hipError_t launch_splitk_reduce(int op, const GemmArgs& a, hipStream_t stream)
     case OP_INT8: return launch_reduce_int8(a, stream);
     case OP_FP8: return launch_reduce_fp8(a, stream);
     case OP_BLOCK: return launch_reduce_block(a, stream);
+    case OP_MXFP4: return launch_reduce_mxfp4(a, stream);
     default: return launch_reduce_bf16(a, stream);
     }
 }
 
 namespace {
 
-const char* const kOpNames[OP_COUNT] = {"int8", "fp8", "block_fp8", "bf16_bi"};
+const char* const kOpNames[OP_COUNT] = {"int8", "fp8", "block_fp8", "bf16_bi", "mxfp4"};
 
-int op_esz(int op) { return op == OP_BF16 ? 2 : 1; }
+// Bytes of one K-row of A or B: bf16 2 per element, packed MXFP4 one per two.
+int64_t op_kbytes(int op, int64_t K)
+{
+    return op == OP_BF16 ? 2 * K : (op == OP_MXFP4 ? K / 2 : K);
+}
+
+// Longest MXFP4 K: every pipelined variant's tile rows times the row bytes
+// stay below 2^31 (there is no tiled fallback for this op).
+constexpr int64_t kMaxKMxfp4 = (int64_t)1 << 23;
 
 // The pipelined kernels address a tile's rows with 32-bit buffer offsets:
 // their tile rows times the row length in bytes must stay below 2^31.
@@ -152,7 +165,7 @@ int find_variant(int op, const char* name)
 
 int effective_splits(int op, int64_t K, int splits)
 {
-    const int64_t kbytes = K * op_esz(op);
+    const int64_t kbytes = op_kbytes(op, K);
     if (splits <= 1)
         return 1;
     int64_t chunk = (kbytes + splits - 1) / splits;
@@ -162,7 +175,7 @@ int effective_splits(int op, int64_t K, int splits)
 
 int64_t split_chunk(int op, int64_t K, int splits)
 {
-    const int64_t kbytes = K * op_esz(op);
+    const int64_t kbytes = op_kbytes(op, K);
     if (splits <= 1)
         return kbytes;
     int64_t chunk = (kbytes + splits - 1) / splits;
@@ -221,7 +234,7 @@ int load_table(const char* path, const char* arch, int cus_want, Table** out,
         }
         {
             int n = 0;
-            if (!variant_fits(variants(op, &n)[vi], K * op_esz(op))) {
+            if (!variant_fits(variants(op, &n)[vi], op_kbytes(op, K))) {
                 rc = QLL_ERR_TABLE;
                 *err = std::string("entry's variant does not support this K: ") + p;
                 break;
@@ -307,7 +320,7 @@ qll_cfg heuristic(int op, int64_t M, int64_t N, int64_t K)
             vi = i;
             break;
         }
-    const int64_t kbytes = K * op_esz(op);
+    const int64_t kbytes = op_kbytes(op, K);
     if (!variant_fits(v[vi], kbytes))  // very long rows: the plain tiled kernel
         for (int i = 0; i < n; ++i)
             if (std::strncmp(v[i].name, "n128x128_w2x2_k", 15) == 0) {
@@ -369,6 +382,9 @@ int validate_gemm(int op, const void* A, const void* B, const float* sa,
     } else if (op == OP_BLOCK) {
         if (K % 128)
             return QLL_ERR_INVALID_ARG;
+    } else if (op == OP_MXFP4) {
+        if (K % 128 || K > kMaxKMxfp4)
+            return QLL_ERR_INVALID_ARG;
     } else if (K % 16) {
         return QLL_ERR_INVALID_ARG;
     }
@@ -410,7 +426,7 @@ int run_gemm(int op, const void* A, const void* B, const float* sa,
     int nv = 0;
     const Variant* vs = variants(op, &nv);
     const Variant& v = vs[cfg.variant];
-    if (!variant_fits(v, K * op_esz(op)))
+    if (!variant_fits(v, op_kbytes(op, K)))
         return QLL_ERR_UNSUPPORTED;
     GemmArgs a;
     a.A = A;
@@ -423,7 +439,7 @@ int run_gemm(int op, const void* A, const void* B, const float* sa,
     a.M = (int)M;
     a.N = (int)N;
     a.K = (int)K;
-    a.kbytes = (int)(K * op_esz(op));
+    a.kbytes = (int)op_kbytes(op, K);
     a.splits = effective_splits(op, K, cfg.splits);
     a.kchunk = (int)split_chunk(op, K, cfg.splits);
     a.kfold = op == OP_BF16 ? kBiFold : 1;
@@ -576,6 +592,38 @@ int gemm_bf16_batch_invariant(const void* A, const void* B, void* out,
 {
     return run_gemm(OP_BF16, A, B, nullptr, nullptr, out, out_dtype, M, N, K,
                     ws, ws_bytes, stream, nullptr);
+}
+
+int quantize_mxfp4(const void* x, void* q, void* scales, int64_t M, int64_t K, void* stream)
+{
+    if (M < 0 || K <= 0 || K % 32 || M > 0x7FFFFFFF || K > 0x3FFFFFFF ||
+        M * K > ((int64_t)1 << 40))
+        return QLL_ERR_INVALID_ARG;
+    if (M == 0)
+        return QLL_OK;
+    if (!x || !q || !scales)
+        return QLL_ERR_INVALID_ARG;
+    if (misaligned(x, 16) || misaligned(q, 4))
+        return QLL_ERR_MISALIGNED;
+    return launch_quant_mxfp4(x, q, scales, M * K, (hipStream_t)stream) == hipSuccess
+               ? QLL_OK
+               : QLL_ERR_HIP;
+}
+
+int gemm_mxfp4_ex(const void* A, const void* B, const void* sa, const void* sb, void* out,
+                  int out_dtype, int64_t M, int64_t N, int64_t K, void* ws, size_t ws_bytes,
+                  void* stream, const qll_cfg* cfg)
+{
+    return run_gemm(OP_MXFP4, A, B, (const float*)sa, (const float*)sb, out, out_dtype, M, N,
+                    K, ws, ws_bytes, stream, cfg);
+}
+
+int gemm_mxfp4(const void* A, const void* B, const void* sa, const void* sb, void* out,
+               int out_dtype, int64_t M, int64_t N, int64_t K, void* ws, size_t ws_bytes,
+               void* stream)
+{
+    return run_gemm(OP_MXFP4, A, B, (const float*)sa, (const float*)sb, out, out_dtype, M, N,
+                    K, ws, ws_bytes, stream, nullptr);
 }
 
 int linear_fp8_dynamic_ex(const void* x, const void* B, const float* sb, void* q,

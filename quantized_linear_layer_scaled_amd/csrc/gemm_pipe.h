@@ -95,10 +95,19 @@ __device__ __forceinline__ void wait_vm_barrier()
 // WP x WQ waves over the CU's four SIMDs.  Several resident workgroups are
 // what keeps the global->LDS copies of one overlapping the barrier waits and
 // MFMAs of another.
+// MXFP4 stages carry the tile rows' E8M0 block scales (KSTAGE / 16 bytes per
+// row) behind the codes, in whole 256-byte copy units.
+template <int OP, int BP, int BQ, int KSTAGE>
+constexpr int pipe_scale_bytes()
+{
+    return OP == OP_MXFP4 ? ((BP + BQ) * (KSTAGE / 16) + 255) / 256 * 256 : 0;
+}
+
 template <int OP, int BP, int BQ, int WP, int WQ, int KSTAGE, int STAGES>
 constexpr int pipe_waves_per_eu()
 {
-    constexpr int lds = STAGES * (BP + BQ) * KSTAGE + (OP == OP_BLOCK ? (STAGES + 1) * 1280 : 0);
+    constexpr int lds = STAGES * ((BP + BQ) * KSTAGE + pipe_scale_bytes<OP, BP, BQ, KSTAGE>()) +
+                        (OP == OP_BLOCK ? (STAGES + 1) * 1280 : 0);
     constexpr int wgs = 163840 / lds < 4 ? 163840 / lds : 4;
     constexpr int w = wgs * WP * WQ / 4;
     return w < 1 ? 1 : (w > 8 ? 8 : w);
@@ -174,9 +183,17 @@ void gemm_pipe_kernel(GemmArgs a)
     constexpr int RP = SP / 16, RQ = SQ / 16;
     constexpr int ROWS = BP + BQ;
     constexpr bool BLK = OP == OP_BLOCK;
+    constexpr bool MX = OP == OP_MXFP4;
     constexpr int LPT0 = ROWS * NC / THREADS;      // operand loads per thread per stage
-    constexpr int LPT = LPT0 + (BLK ? 2 : 0);      // + the two group-scale loads
-    constexpr int STAGE_BYTES = ROWS * KSTAGE;
+    // MXFP4: SCB scale bytes per tile row per stage, copied in NSC units of
+    // 256 bytes (64 lanes x 4), LPS per wave (units repeat when there are
+    // more waves than units: the copies write equal values)
+    constexpr int SCB = MX ? KSTAGE / 16 : 0;
+    constexpr int SC_REGION = pipe_scale_bytes<OP, BP, BQ, KSTAGE>();
+    constexpr int NSC = SC_REGION / 256;
+    constexpr int LPS = MX ? (NSC + WAVES - 1) / WAVES : 0;
+    constexpr int LPT = LPT0 + (BLK ? 2 : 0) + LPS;  // + the scale loads
+    constexpr int STAGE_BYTES = ROWS * KSTAGE + SC_REGION;
     static_assert(ROWS * NC % THREADS == 0, "stage must split evenly over the waves");
     static_assert((NC & (NC - 1)) == 0 && KSTAGE % KSTEP == 0, "bad K stage");
     static_assert(STAGES >= 2 && (STAGES - 1) * LPT < 64, "bad pipeline depth");
@@ -184,6 +201,8 @@ void gemm_pipe_kernel(GemmArgs a)
                   "grouped: per-token x per-channel ops, no Split-K");
     static_assert(!BLK || (KSTAGE == 128 && NSTEP == 1 && BP <= 256 && WAVES >= BP / 64),
                   "block scaling: one 128-wide K group per stage");
+    static_assert(!MX || ((SCB == 8 || SCB == 16) && BP % (256 / (SCB ? SCB : 1)) == 0),
+                  "MXFP4: a scale copy unit must not straddle the A and B rows");
 
     // One LDS object per ring slot, the slot known at compile time in the
     // unrolled K loop (constant LDS addresses for the fragment reads).
@@ -301,6 +320,33 @@ void gemm_pipe_kernel(GemmArgs a)
             sb_off = (uint32_t)(lane * KG) * 4u;
     }
 
+    // MXFP4 scale sources: [M][K/32] and [N][K/32] bytes from the tile's
+    // first row; unit c of a stage holds the bytes c*256 + 4*lane .. + 3 of
+    // the stage's [ROWS][SCB] scale block.
+    v4i rsXA{}, rsXB{};
+    uint32_t xoff[LPS > 0 ? LPS : 1];
+    int xj[LPS > 0 ? LPS : 1];
+    bool xin_a[LPS > 0 ? LPS : 1];
+    uint32_t xdst[LPS > 0 ? LPS : 1];
+    const uint32_t srow = (uint32_t)a.kbytes / 16u;
+    if constexpr (MX) {
+        rsXA = buffer_rsrc((const uint8_t*)a.sa + (size_t)p0 * srow,
+                           (uint32_t)min((uint64_t)(M - p0) * srow, (uint64_t)0x7FFFFFFF));
+        rsXB = buffer_rsrc((const uint8_t*)a.sb + (size_t)q0 * srow,
+                           (uint32_t)min((uint64_t)(N - q0) * srow, (uint64_t)0x7FFFFFFF));
+#pragma unroll
+        for (int i = 0; i < LPS; ++i) {
+            const int c = (i * WAVES + wave) % NSC;
+            const int b = c * 256 + lane * 4;
+            const int row = b / SCB, j = b % SCB;
+            xin_a[i] = c * 256 / SCB < BP;  // wave-uniform
+            const int r = row < BP ? row : row - BP;
+            xoff[i] = row < ROWS ? (uint32_t)r * srow + (uint32_t)(kbeg / 16 + j) : kOutOfRange;
+            xj[i] = j;
+            xdst[i] = (uint32_t)(ROWS * KSTAGE + c * 256);
+        }
+    }
+
     auto issue = [&](int kt, uint8_t* buf) __attribute__((always_inline)) {
         const int kb0 = kt * KSTAGE;  // relative to kbeg
         const bool full = kbeg + kb0 + KSTAGE <= kend;
@@ -312,6 +358,17 @@ void gemm_pipe_kernel(GemmArgs a)
             dma16(vo, in_a(i) ? rsA : rsB,
                   __builtin_amdgcn_readfirstlane(
                       (uint32_t)(uintptr_t)(buf + (i * WAVES + wave) * 1024)));
+        }
+        if constexpr (MX) {
+#pragma unroll
+            for (int i = 0; i < LPS; ++i) {
+                // scale byte j covers code bytes 16 j .. 16 j + 15 of the stage
+                uint32_t xo = xoff[i] + (uint32_t)(kt * SCB);
+                if (xoff[i] == kOutOfRange || (!full && kbeg + kb0 + xj[i] * 16 >= kend))
+                    xo = kOutOfRange;
+                dma4(xo, xin_a[i] ? rsXA : rsXB,
+                     __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(buf + xdst[i])));
+            }
         }
         if constexpr (BLK) {
             const uint32_t g4 = (uint32_t)((kbeg + kb0) >> 7) * 4u;
@@ -342,6 +399,8 @@ void gemm_pipe_kernel(GemmArgs a)
     struct Frag {
         uint4 a[RP][KB / 16];
         uint4 b[RQ][KB / 16];
+        int xa[MX ? RP : 1];  // MXFP4: this lane's block scale per fragment
+        int xb[MX ? RQ : 1];
     };
     Frag fr[2];
     auto load_step = [&](const uint8_t* sp, int ks, Frag& f) __attribute__((always_inline)) {
@@ -364,6 +423,16 @@ void gemm_pipe_kernel(GemmArgs a)
                 const int ch = (off >> 4) + j;
                 f.b[i][j] = *(const uint4*)(sq + row * KSTAGE + ((ch ^ swz<NC>(row)) << 4));
             }
+        }
+        if constexpr (MX) {
+            // scale byte of step ks, block lane >> 4, of each fragment row
+            const uint8_t* sc = sp + ROWS * KSTAGE + ks * 4 + (lane >> 4);
+#pragma unroll
+            for (int i = 0; i < RP; ++i)
+                f.xa[i] = sc[(wpi * SP + i * 16 + (lane & 15)) * SCB];
+#pragma unroll
+            for (int i = 0; i < RQ; ++i)
+                f.xb[i] = sc[(BP + wqi * SQ + i * 16 + (lane & 15)) * SCB];
         }
     };
     auto compute_step = [&](const Frag& f, int kt, int ks) __attribute__((always_inline)) {
@@ -397,6 +466,12 @@ void gemm_pipe_kernel(GemmArgs a)
                     acc[i][j][2] = __builtin_fmaf(ps[i].z, pg[2], acc[i][j][2]);
                     acc[i][j][3] = __builtin_fmaf(ps[i].w, pg[3], acc[i][j][3]);
                 }
+        } else if constexpr (MX) {
+#pragma unroll
+            for (int i = 0; i < RP; ++i)
+#pragma unroll
+                for (int j = 0; j < RQ; ++j)
+                    acc[i][j] = mfma_mx(f.a[i][0], f.b[j][0], acc[i][j], f.xa[i], f.xb[j]);
         } else {
 #pragma unroll
             for (int i = 0; i < RP; ++i)
@@ -669,4 +744,5 @@ hipError_t launch_pipe_grouped(const GemmArgs& a, hipStream_t stream)
      (ST) * ((BP) + (BQ)) * (KS), &qll::launch_pipe_grouped<OP, BP, BQ, WP, WQ, KS, ST>},
 #define QLL_PIPE_ENTRY(OP, BP, BQ, WP, WQ, KS, ST)                                   \
     {"p" #BP "x" #BQ "_w" #WP "x" #WQ "_k" #KS "_s" #ST, OP, 0, BP, BQ, WP, WQ, KS,    \
-     (ST) * ((BP) + (BQ)) * (KS), &qll::launch_pipe<OP, BP, BQ, WP, WQ, KS, ST>},
+     (ST) * (((BP) + (BQ)) * (KS) + qll::pipe_scale_bytes<OP, BP, BQ, KS>()),          \
+     &qll::launch_pipe<OP, BP, BQ, WP, WQ, KS, ST>},

@@ -65,6 +65,21 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny_kernel(GemmArgs a)
     }
     const int klim = kend - kbeg - (lane >> 4) * KB;  // bytes this lane may read
 
+    // MXFP4: each row's E8M0 scales, one byte per 32 K elements (16 bytes of
+    // codes); the scale dword of step t holds the four blocks of that step,
+    // and this lane's block is byte lane >> 4 of it.
+    constexpr bool MX = OP == OP_MXFP4;
+    const int srow = a.kbytes / 16;  // scale bytes per row
+    const uint8_t* __restrict__ sbp =
+        (const uint8_t*)a.sb + (size_t)nrow * srow + kbeg / 16;
+    const uint8_t* __restrict__ sap[RQ];
+#pragma unroll
+    for (int r = 0; r < RQ; ++r) {
+        const int mrow = min(m0 + r * 16 + (lane & 15), M - 1);
+        sap[r] = (const uint8_t*)a.sa + (size_t)mrow * srow + kbeg / 16;
+    }
+    const int sshift = 8 * (lane >> 4);
+
     acc_t acc[RQ];
 #pragma unroll
     for (int r = 0; r < RQ; ++r)
@@ -80,6 +95,7 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny_kernel(GemmArgs a)
 
     for (int s = s0; s < s1; s += D) {
         uint4 fb[D][NJ], fa[D][RQ][NJ];
+        uint32_t xb[MX ? D : 1], xa[MX ? D : 1][RQ];
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             const int off = (s + d) * KSTEP;
@@ -92,11 +108,19 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny_kernel(GemmArgs a)
                     fa[d][r][j] = ok ? *(const uint4*)(ap[r] + off + 16 * j)
                                      : make_uint4(0, 0, 0, 0);
             }
+            if constexpr (MX) {
+                // a whole step is in range or not (K is a multiple of 128)
+                const bool ok = (s + d < s1) && (off < klim);
+                xb[d] = ok ? *(const uint32_t*)(sbp + 4 * (s + d)) : 0u;
+#pragma unroll
+                for (int r = 0; r < RQ; ++r)
+                    xa[d][r] = ok ? *(const uint32_t*)(sap[r] + 4 * (s + d)) : 0u;
+            }
         }
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             if (s + d >= s1)
-                break;
+                continue;  // (every later step is past s1 too)
             if constexpr (FOLD)
                 fold.before(s + d, (acc_t(&)[1][RQ])acc);
             if constexpr (OP == OP_BLOCK) {
@@ -111,6 +135,12 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny_kernel(GemmArgs a)
                     for (int v = 0; v < 4; ++v)
                         acc[r][v] = __builtin_fmaf(sc, pg[v], acc[r][v]);
                 }
+            } else if constexpr (MX) {
+                const int xw = (int)__builtin_amdgcn_ubfe(xb[d], sshift, 8);
+#pragma unroll
+                for (int r = 0; r < RQ; ++r)
+                    acc[r] = mfma_mx(fb[d][0], fa[d][r][0], acc[r], xw,
+                                     (int)__builtin_amdgcn_ubfe(xa[d][r], sshift, 8));
             } else {
 #pragma unroll
                 for (int r = 0; r < RQ; ++r)

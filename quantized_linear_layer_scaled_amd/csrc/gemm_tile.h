@@ -57,6 +57,13 @@ template <> struct OpTraits<OP_BF16> {
     using acc_t = v4f;
     using elem_t = float;
 };
+// MXFP4: two E2M1 codes per byte, 32 codes (16 bytes) per lane per MFMA,
+// E8M0 block scales applied inside the matrix core
+template <> struct OpTraits<OP_MXFP4> {
+    static constexpr int esz = 1, kb = 16;
+    using acc_t = v4f;
+    using elem_t = float;
+};
 
 // Workgroup -> output tile, XCD-aware.  The dispatcher hands consecutive
 // workgroup ids to the 8 XCDs in turn, and each XCD has its own L2.  The
@@ -106,6 +113,21 @@ mfma_step(const uint4* a, const uint4* b, typename OpTraits<OP>::acc_t c)
         return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 0, 0,
                                                                 0, 0, 0, 0);
     }
+}
+
+// One block-scaled MXFP4 step, 16 x 16 x 128 (format code 4 = E2M1 for both
+// operands; only the first four dwords of each operand carry codes).  Lane l
+// supplies the 32 K elements (l >> 4) * 32 .. + 31 of row l & 15 of each
+// operand and, in bits 0-7 of sa / sb (byte select 0), the E8M0 scale of
+// exactly that block of 32: v_mfma_scale_f32_16x16x128_f8f6f4.
+__device__ __forceinline__ v4f mfma_mx(const uint4& a, const uint4& b, v4f c, int sa, int sb)
+{
+    v8i av, bv;
+    av.lo = __builtin_bit_cast(v4i, a);
+    av.hi = v4i{0, 0, 0, 0};
+    bv.lo = __builtin_bit_cast(v4i, b);
+    bv.hi = v4i{0, 0, 0, 0};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 4, 0, sa, 0, sb);
 }
 
 // XOR swizzle of the 16-byte chunks of one staged LDS row.  A fragment read

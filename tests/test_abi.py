@@ -61,12 +61,13 @@ def gemm(qll, fn, A=P, B=P, sa=P, sb=P, out=P, od=0, M=16, N=64, K=2048, ws=None
         return getattr(L, fn + "_ex")(*args, ctypes.byref(qll._cfg(
             qll.OPS[{"gemm_w8a8_int8": "int8", "gemm_fp8_scaled": "fp8",
                      "gemm_block_fp8": "block_fp8",
-                     "gemm_bf16_batch_invariant": "bf16_bi"}[fn]], cfg)))
+                     "gemm_bf16_batch_invariant": "bf16_bi",
+                     "gemm_mxfp4": "mxfp4"}[fn]], cfg)))
     return getattr(L, fn)(*args)
 
 
 GEMMS = ["gemm_w8a8_int8", "gemm_fp8_scaled", "gemm_block_fp8",
-         "gemm_bf16_batch_invariant"]
+         "gemm_bf16_batch_invariant", "gemm_mxfp4"]
 
 
 @pytest.mark.parametrize("fn", GEMMS)
@@ -84,11 +85,43 @@ def test_gemm_argument_validation(qll, fn):
     assert gemm(qll, fn, M=0, A=None, out=None) == 0     # M == 0 is a no-op
     if fn != "gemm_w8a8_int8":
         assert gemm(qll, fn, od=2) == INVALID            # raw int32 out: INT8 only
-    if fn == "gemm_block_fp8":
+    if fn in ("gemm_block_fp8", "gemm_mxfp4"):
         assert gemm(qll, fn, K=2048 + 16) == INVALID     # K % 128
+    if fn == "gemm_mxfp4":
+        assert gemm(qll, fn, K=(1 << 23) + 128) == INVALID   # longest K 2^23
     if fn != "gemm_bf16_batch_invariant":
         assert gemm(qll, fn, sa=None) == INVALID
         assert gemm(qll, fn, sb=P + 2) == MISALIGNED
+
+
+def test_quantize_mxfp4_validation(qll):
+    L = qll.load_library()
+
+    def qz(x=P, q=P, s=P, M=4, K=256):
+        return L.quantize_mxfp4(x, q, s, M, K, None)
+
+    assert qz(K=48) == 1                  # K % 32
+    assert qz(K=0) == 1
+    assert qz(M=-1) == 1
+    assert qz(x=None) == 1
+    assert qz(s=None) == 1
+    assert qz(x=P + 4) == 3               # x 16-byte aligned
+    assert qz(q=P + 2) == 3               # q 4-byte aligned
+    assert qz(M=0, x=None, q=None, s=None) == 0
+
+
+def test_mxfp4_registry_and_dispatch(qll):
+    names = [v["name"] for v in qll.variants("mxfp4")]
+    # skinny Swap-AB kernels for few tokens, pipelined tiles for many; no
+    # tiled fallback
+    assert "k16x16_w8" in names and "p128x128_w2x2_k128_s2" in names
+    assert not any(n.startswith(("n", "s")) for n in names)
+    assert qll.select("mxfp4", 8, 4096, 4096)[0].startswith("k16x")
+    assert qll.select("mxfp4", 2048, 4096, 4096)[0].startswith("p")
+    # K bytes are K / 2: a 2-way split of K = 2048 (1024 bytes) is allowed,
+    # a 4-way one rounds to 512-byte pieces, i.e. 2
+    assert qll.effective_splits("mxfp4", 2048, 4) == 2
+    assert qll.workspace_bytes("mxfp4", 64, 128, 2048, ("p64x64_w2x2_k128_s2", 2)) == 2 * 64 * 128 * 4
 
 
 def test_int8_k_limit_and_forced_cfg(qll):

@@ -31,6 +31,11 @@ vocabulary N=151936 and a square N=K=2048 weight):
                MOE_TOPK = 8 experts each with a skewed synthetic routing; the
                routed rows (bf16 N(0, 1) with outliers) are quantized per
                token.
+  MXFP4        the FP8 dynamic shapes and M values on the same kind of data
+               (A bf16 N(0, 1) with outlier channels, W bf16 N(0, 0.02)),
+               both quantized to MXFP4; parity cases also draw packed codes
+               uniformly over all 256 bytes and scale bytes uniform in a
+               band around 2^0.
 """
 from __future__ import annotations
 
@@ -53,9 +58,12 @@ MAX_M = 2048
 MOE_E, MOE_TOPK = 64, 8
 MOE_SHAPE = (1536, 2048)  # (N, K)
 MOE_T = [16, 128, 1024]
+# MXFP4: the FP8 dynamic (N, K) shapes and M values
+MX_SHAPES = FP8_SHAPES
+MX_M = FP8_M
 
 # workload ids used in the seeds
-W_INT8, W_FP8, W_BLOCK, W_BI, W_VOCAB, W_MOE, W_TEST = 1, 2, 3, 4, 5, 6, 9
+W_INT8, W_FP8, W_BLOCK, W_BI, W_VOCAB, W_MOE, W_MX, W_TEST = 1, 2, 3, 4, 5, 6, 7, 9
 
 
 def rng(*key) -> np.random.Generator:
@@ -191,3 +199,24 @@ def moe_activations(rows, K, key=(W_MOE,)):
 def moe_weights(E, N, K, key=(W_MOE,)):
     """bf16 expert weights [E][N][K], N(0, 0.02)."""
     return bf16_normal((E * N, K), (*key, 2, E, N, K), std=0.02).reshape(E, N, K)
+
+
+def mx_activations(M, K, key=(W_MX,)):
+    """bf16 activations of the MXFP4 workload (first M rows of a MAX_M-row
+    draw, 1% outlier channels x20, like the FP8 dynamic workload)."""
+    rows = max(M, MAX_M)
+    return bf16_normal((rows, K), (*key, K, 0), outlier_frac=0.01)[:M].copy()
+
+
+def mx_weights(N, K, key=(W_MX,)):
+    return bf16_normal((N, K), (*key, N, K, 1), std=0.02)
+
+
+def mx_codes(rows, K, key) -> np.ndarray:
+    """Packed E2M1 codes [rows][K/2]: every byte uniform over 0..255."""
+    return rng(*key).integers(0, 256, size=(rows, K // 2), dtype=np.uint8)
+
+
+def mx_scale_bytes(rows, K, key, lo=118, hi=136) -> np.ndarray:
+    """E8M0 scale bytes [rows][K/32] uniform in [lo, hi]."""
+    return rng(*key).integers(lo, hi + 1, size=(rows, K // 32), dtype=np.uint8)
