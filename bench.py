@@ -29,9 +29,10 @@ workload, and, when the rocprofv3 counter CSVs are given (--fetch-csv,
 --write-csv), the HBM traffic of the dominant kernel scaled by the same
 counters read on a copy kernel of known size (--calib-copy runs that copy).
 
-Other workloads (--workload int8|block|bi|vocab|moe) print the same JSON
-shape; moe is the grouped (per-expert) FP8 GEMM of a 64-expert layer with
-synthetic top-8 routing (per-token quantization + gemm_fp8_grouped).
+Other workloads (--workload int8|block|bi|vocab|moe|mxfp4) print the same
+JSON shape; moe is the grouped (per-expert) FP8 GEMM of a 64-expert layer with
+synthetic top-8 routing (per-token quantization + gemm_fp8_grouped); mxfp4 is
+the FP8 sweep's shapes and data in MXFP4 (quantize_mxfp4 + gemm_mxfp4).
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload fp8]
 """
@@ -48,7 +49,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-PEAK = {"fp8": 5000.0, "int8": 5000.0, "bf16": 2500.0}  # dense TFLOP/s (TOP/s)
+PEAK = {"fp8": 5000.0, "int8": 5000.0, "bf16": 2500.0, "fp4": 10100.0}  # dense TFLOP/s (TOP/s)
 HBM_GBS = 8000.0
 
 
@@ -58,7 +59,7 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="fp8",
-                   choices=["fp8", "int8", "block", "bi", "vocab", "moe"])
+                   choices=["fp8", "int8", "block", "bi", "vocab", "moe", "mxfp4"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=128,
                    help="rows per problem the CPU oracle computes")
@@ -104,9 +105,13 @@ class Problem:
             return M * K + N * K + 4 * M * (K // 128) + 4 * ((N + 127) // 128) * (K // 128) + 2 * M * N
         if self.op == "fp8_grouped":  # the weights of every expert that has rows
             return M * K + self.experts_used * (N * K + 4 * N) + 4 * M + 2 * M * N
+        if self.op == "mxfp4":  # packed codes + one scale byte per 32 + bf16 out
+            return (M + N) * (K // 2 + K // 32) + 2 * M * N
         return M * K + N * K + 4 * M + 4 * N + 2 * M * N
 
     def quant_bytes(self):
+        if self.op == "mxfp4":
+            return 2 * self.M * self.K + self.M * (self.K // 2 + self.K // 32)
         return 3 * self.M * self.K + 4 * self.M * max(1, self.K // (128 if self.op == "block_fp8" else self.K))
 
 
@@ -177,6 +182,23 @@ def build_problems(torch, qll, workload):
                 # own copy of the weights per problem (cold for every problem)
                 q, s = add_quant(p, x_all[:M].clone(), 0)
                 add_gemm(p, "gemm_fp8_scaled", q, qw.clone(), s, sw.clone())
+                probs.append(p)
+    elif workload == "mxfp4":
+        for N, K in W.MX_SHAPES:
+            qw, sw = qll.quantize_mxfp4(dev_bf16(torch, W.mx_weights(N, K)))
+            x_all = dev_bf16(torch, W.mx_activations(W.MAX_M, K))
+            for M in W.MX_M:
+                p = Problem("mxfp4", M, N, K)
+                x = x_all[:M].clone()
+                q = torch.empty((M, K // 2), dtype=torch.uint8, device="cuda")
+                s = torch.empty((M, K // 32), dtype=torch.uint8, device="cuda")
+                p.keep += [x, q, s]
+                qargs = lambda p, t: (t["x"].data_ptr(), t["q"].data_ptr(), t["s"].data_ptr(),
+                                      p.M, p.K, stream)
+                t = dict(x=x, q=q, s=s)
+                p.calls.append(("quant", L.quantize_mxfp4, qargs(p, t)))
+                p.tensors["quant"] = (t, qargs)
+                add_gemm(p, "gemm_mxfp4", q, qw.clone(), s, sw.clone())
                 probs.append(p)
     elif workload == "int8":
         M, N, K = W.INT8_SHAPE
@@ -289,7 +311,7 @@ def kernel_symbol(qll, op, variant):
     grouped = op == "fp8_grouped"
     if grouped:
         op = "fp8"
-    opn = {"int8": 0, "fp8": 1, "block_fp8": 2, "bf16_bi": 3}[op]
+    opn = {"int8": 0, "fp8": 1, "block_fp8": 2, "bf16_bi": 3, "mxfp4": 4}[op]
     v = next(x for x in qll.variants(op) if x["name"] == variant)
     if variant[0] == "p":
         st = variant.rsplit("_s", 1)[1]
@@ -332,6 +354,19 @@ def cpu_baseline(workload, rows_cap):
             sample.append(f"N={N},K={K}")
         desc = (f"first min(M,{rows_cap}) rows of every (N,K,M) problem "
                 f"({', '.join(sample)}), per-token quantization + FP8 GEMM")
+    elif workload == "mxfp4":
+        for N, K in W.MX_SHAPES:
+            B, sb = oracle.quantize_mxfp4(W.mx_weights(N, K))
+            x_all = W.mx_activations(W.MAX_M, K)
+            for M in W.MX_M:
+                r = min(M, rows_cap)
+                t0 = time.perf_counter()
+                A, sa = oracle.quantize_mxfp4(np.ascontiguousarray(x_all[:r]))
+                oracle.gemm_mxfp4(A, B, sa, sb)
+                t_total += time.perf_counter() - t0
+                flops += 2.0 * r * N * K
+        desc = (f"first min(M,{rows_cap}) rows of every MXFP4 problem, "
+                "MXFP4 quantization + GEMM")
     elif workload == "int8":
         M, N, K = W.INT8_SHAPE
         d = W.int8_inputs(M, N, K)
@@ -519,7 +554,7 @@ def main():
             rec[f"{kind}_us"] = round(call_us[i][j], 3)
         t_gemm = rec["gemm_us"] * 1e-6
         dt = {"fp8": "fp8", "fp8_grouped": "fp8", "block_fp8": "fp8", "int8": "int8",
-              "bf16_bi": "bf16"}[p.op]
+              "bf16_bi": "bf16", "mxfp4": "fp4"}[p.op]
         t_mem = p.algo_bytes() / (HBM_GBS * 1e9)
         t_mfma = p.flops / (PEAK[dt] * 1e12)
         rec["tflops"] = round(p.flops / t_gemm / 1e12, 2)
@@ -583,9 +618,12 @@ def main():
                     "T in {16,128,1024} tokens routed to 8 experts each (skewed synthetic "
                     "routing); per-token quantization + gemm_fp8_grouped, bf16 out",
              "vocab": "large-vocab FP8 dynamic projection N=151936 K=2048, "
-                      "M in {1,8,64,512,2048}"}
+                      "M in {1,8,64,512,2048}",
+             "mxfp4": "MXFP4 sweep: (N,K) in {(4096,2048),(2048,6144)}, "
+                      "M in {1,4,8,16,32,64,256,512,1024,2048}; MXFP4 quantization of the "
+                      "activations + MXFP4 GEMM (E8M0 scale per 32), bf16 out"}
     dtype = {"fp8": "fp8e4m3", "vocab": "fp8e4m3", "block": "fp8e4m3", "int8": "int8",
-             "moe": "fp8e4m3",
+             "moe": "fp8e4m3", "mxfp4": "fp4e2m1",
              "bi": "bf16"}[args.workload]
     line = {
         "metric": "TFLOPS/TOPS + % of HBM or MFMA roofline per (M,N,K), FP8/INT8 scaled_mm",

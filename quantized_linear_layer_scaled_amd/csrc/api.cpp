@@ -289,7 +289,11 @@ qll_cfg heuristic(int op, int64_t M, int64_t N, int64_t K)
     const int cus = device_info().cus;
     const char* name;
     bool exact = true;
-    if (M <= 64) {
+    if (op == OP_MXFP4 && M > 32) {
+        // 256-byte K stages (four MFMA steps of 128 elements per barrier):
+        // fastest from 64 tokens up on the sweep shapes
+        name = M <= 1024 ? "p64x64_w2x2_k256_s2" : "p128x128_w2x2_k256_s2";
+    } else if (M <= 64) {
         if (op == OP_BF16)  // eight waves = the kBiFold chunks
             name = M <= 16 ? "k16x16_w8" : (M <= 32 ? "k16x32_w8" : "k16x64_w8");
         else if (M <= 16)
