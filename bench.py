@@ -61,8 +61,9 @@ def parse():
     p.add_argument("--workload", default="fp8",
                    choices=["fp8", "int8", "block", "bi", "vocab", "moe", "mxfp4"])
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-rows", type=int, default=128,
-                   help="rows per problem the CPU oracle computes")
+    p.add_argument("--cpu-rows", type=int, default=2048,
+                   help="rows per problem the CPU oracle computes (the default covers "
+                        "every row of the FP8 and MXFP4 sweeps)")
     p.add_argument("--table", default="default",
                    help="dispatch table ('default', a path, or 'none')")
     p.add_argument("--fetch-csv", default=None,
@@ -316,7 +317,7 @@ def kernel_symbol(qll, op, variant):
     if variant[0] == "p":
         st = variant.rsplit("_s", 1)[1]
         return (f"void qll::gemm_pipe_kernel<{opn}, {v['bp']}, {v['bq']}, {v['wp']}, "
-                f"{v['wq']}, {v['kstage']}, {st}, false{', true' if grouped else ''}>"
+                f"{v['wq']}, {v['kstage']}, {st}, false, {'true' if grouped else 'false'}>"
                 "(qll::GemmArgs)")
     if variant[0] in "kr":
         return (f"void qll::gemm_skinny_kernel<{opn}, {v['bq'] // 16}, {v['wp']}, "
