@@ -17,7 +17,8 @@ the design notes):
     batch size.
   * The 4-bit formats named in the introduction of "Helion in vLLM", in their
     block-scaled form MXFP4, whose encodings and conversion rule come from the
-    OCP Microscaling Formats (MX) v1.0 specification (the pages define none).
+    OCP Microscaling Formats (MX) v1.0 specification (the pages define none),
+    and INT4 weight-only (symmetric, one scale per 128-element group).
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 against something other than itself (torch's own e4m3/bf16 casts, Python
@@ -103,6 +104,12 @@ def _load():
     lib.oracle_gemm_mxfp4.restype = None
     lib.oracle_gemm_mxfp4.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _P, _I64,
                                       _P, _P]
+    lib.oracle_int4_decode.restype = ctypes.c_int
+    lib.oracle_int4_decode.argtypes = [ctypes.c_uint8]
+    lib.oracle_quantize_int4.restype = ctypes.c_int
+    lib.oracle_quantize_int4.argtypes = [_P, _I64, _I64, _P, _P]
+    lib.oracle_gemm_w4a16.restype = None
+    lib.oracle_gemm_w4a16.argtypes = [_P, _P, _P, _I64, _I64, _I64, _P, _I64, _P, _P]
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     _lib = lib
@@ -249,6 +256,29 @@ def quantize_mxfp4(x_bf16_bits: np.ndarray):
     return q, s
 
 
+def int4_decode(codes) -> np.ndarray:
+    """4-bit two's complement codes (low 4 bits) -> int64 values."""
+    c = np.asarray(codes, dtype=np.uint8)
+    lib = _load()
+    return np.vectorize(lambda v: lib.oracle_int4_decode(int(v) & 15),
+                        otypes=[np.int64])(c)
+
+
+def quantize_int4(w_bf16_bits: np.ndarray):
+    """INT4 weight quantization of bf16 [N][K] (uint16 bits), one fp32 scale
+    per 128 consecutive elements of a row.  Returns (packed codes uint8
+    [N][K/2], scales float32 [N][K/128])."""
+    w = np.ascontiguousarray(w_bf16_bits, dtype=np.uint16)
+    N, K = w.shape
+    q = np.empty((N, K // 2), dtype=np.uint8)
+    s = np.empty((N, K // 128), dtype=np.float32)
+    rc = _load().oracle_quantize_int4(_ptr(w), N, K, _ptr(q), _ptr(s))
+    if rc != 0:
+        raise ValueError(f"oracle_quantize_int4 failed ({rc}): non-finite input "
+                         "or K not a multiple of 128")
+    return q, s
+
+
 # --------------------------------------------------------------------------
 # GEMMs (A [M][K], B [N][K]; outputs [len(rows)][N])
 # --------------------------------------------------------------------------
@@ -391,4 +421,22 @@ def gemm_mxfp4(A, B, sa, sb, rows=None, with_abs=False):
     _load().oracle_gemm_mxfp4(_ptr(A), _ptr(B), _ptr(sa), _ptr(sb), M, N, K,
                               _ptr(r), r.size, _ptr(ref),
                               _ptr(absref) if with_abs else None)
+    return (ref, absref) if with_abs else ref
+
+
+def gemm_w4a16(A_bits, B, s, rows=None, with_abs=False):
+    """INT4 weight-only GEMM in fp64: A bf16 [M][K] (uint16 bits), B packed
+    int4 [N][K/2], s fp32 [N][K/128]; per 128-wide group the exact partial
+    sum times the group scale."""
+    A = np.ascontiguousarray(A_bits, dtype=np.uint16)
+    B = np.ascontiguousarray(B, dtype=np.uint8)
+    s = np.ascontiguousarray(s, dtype=np.float32)
+    M, K = A.shape
+    N = B.shape[0]
+    assert B.shape[1] == K // 2 and K % 128 == 0 and s.shape == (N, K // 128)
+    r = _rows(M, rows)
+    ref = np.empty((r.size, N), dtype=np.float64)
+    absref = np.empty((r.size, N), dtype=np.float64) if with_abs else None
+    _load().oracle_gemm_w4a16(_ptr(A), _ptr(B), _ptr(s), M, N, K, _ptr(r), r.size,
+                              _ptr(ref), _ptr(absref) if with_abs else None)
     return (ref, absref) if with_abs else ref

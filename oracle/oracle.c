@@ -1,8 +1,8 @@
 /*
  * oracle.c -- plain, slow, obviously correct CPU reference for the scaled_mm
  * hot path (per-token dynamic FP8 quantization, W8A8 INT8, FP8 with
- * per-token x per-channel scales, Block-FP8, bf16 GEMM, and the MXFP4
- * quantizer and GEMM).
+ * per-token x per-channel scales, Block-FP8, bf16 GEMM, the MXFP4 quantizer
+ * and GEMM, and the INT4 weight-only quantizer and GEMM).
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, includes or
  * calls this file; only the tests, the smoke check and the CPU-baseline leg of
@@ -528,6 +528,108 @@ void oracle_e2m1_encode_array(const double* v, int64_t n, uint8_t* out)
     int64_t i;
     for (i = 0; i < n; ++i)
         out[i] = oracle_e2m1_encode_rne(v[i]);
+}
+
+/* ------------------------------------------------------------------------ */
+/* INT4 weight-only (W4A16): signed 4-bit weights with one fp32 scale per    */
+/* output channel and 128-element K group, bf16 activations.  The pages name */
+/* INT4 among vLLM's formats (introduction of "Helion in vLLM: A Unified     */
+/* Route to Tunable Linear Kernels") without defining it; the reading here   */
+/* is the symmetric per-group form of the FP8 rule above: scale = amax / 7,  */
+/* codes in [-8, 7] (two's complement nibbles, packed like MXFP4: element 2j */
+/* in bits 0-3 of byte j).                                                    */
+/* ------------------------------------------------------------------------ */
+
+/* Two's complement value of a 4-bit code. */
+int oracle_int4_decode(uint8_t c)
+{
+    int v = c & 15;
+    return v >= 8 ? v - 16 : v;
+}
+
+/* Weight quantization of bf16 w [N][K] (K a multiple of 128), one group of
+ * 128 consecutive elements of a row at a time:
+ *   amax = max |w|;  s = amax / 7 (fp32);  q = clamp(rne(w / s), -8, 7)
+ * with w / s the correctly rounded fp32 quotient; an all-zero group gets
+ * s = 0 and zero codes.  q: packed [N][K/2]; s: fp32 [N][K/128].
+ * Returns 0, -1 on a non-finite input, -2 when 128 does not divide K. */
+int oracle_quantize_int4(const uint16_t* w, int64_t N, int64_t K, uint8_t* q,
+                         float* s)
+{
+    int64_t n, g, ng;
+    int bad = 0;
+    if (K % 128 != 0)
+        return -2;
+    ng = K / 128;
+#pragma omp parallel for private(g) reduction(| : bad) schedule(static)
+    for (n = 0; n < N; ++n)
+        for (g = 0; g < ng; ++g) {
+            const uint16_t* wg = w + n * K + g * 128;
+            float amax = 0.0f, sc;
+            int i;
+            for (i = 0; i < 128; ++i) {
+                float x = oracle_bf16_decode(wg[i]);
+                if (!isfinite(x))
+                    bad = 1;
+                else if (fabsf(x) > amax)
+                    amax = fabsf(x);
+            }
+            sc = amax / 7.0f;
+            s[n * ng + g] = sc;
+            for (i = 0; i < 128; i += 2) {
+                int c[2], j;
+                for (j = 0; j < 2; ++j) {
+                    float v, r;
+                    if (sc == 0.0f) {
+                        c[j] = 0;
+                        continue;
+                    }
+                    v = oracle_bf16_decode(wg[i + j]) / sc;
+                    r = nearbyintf(v); /* default rounding: to nearest, ties to even */
+                    if (r > 7.0f)
+                        r = 7.0f;
+                    if (r < -8.0f)
+                        r = -8.0f;
+                    c[j] = (int)r & 15;
+                }
+                q[n * (K / 2) + (g * 128 + i) / 2] = (uint8_t)(c[0] | (c[1] << 4));
+            }
+        }
+    return bad ? -1 : 0;
+}
+
+/* W4A16 GEMM in fp64: with A bf16 [M][K], B packed int4 [N][K/2] and
+ * s fp32 [N][K/128],
+ *   P_g = sum_{k in group g} A[m][k] * q[n][k]        (exact)
+ *   ref[r][n] = sum_g s[n][g] * P_g,
+ * absref the same with magnitudes. */
+void oracle_gemm_w4a16(const uint16_t* A, const uint8_t* B, const float* s,
+                       int64_t M, int64_t N, int64_t K, const int64_t* rows,
+                       int64_t nrows, double* ref, double* absref)
+{
+    int64_t r, n, k, g, ng = K / 128;
+    (void)M;
+#pragma omp parallel for private(n, k, g) collapse(2) schedule(static)
+    for (r = 0; r < nrows; ++r)
+        for (n = 0; n < N; ++n) {
+            const uint16_t* a = A + rows[r] * K;
+            const uint8_t* b = B + n * (K / 2);
+            double sum = 0.0, asum = 0.0;
+            for (g = 0; g < ng; ++g) {
+                double pg = 0.0, apg = 0.0, sc = (double)s[n * ng + g];
+                for (k = g * 128; k < (g + 1) * 128; ++k) {
+                    double p = (double)oracle_bf16_decode(a[k]) *
+                               (double)oracle_int4_decode((uint8_t)(b[k / 2] >> (4 * (k & 1))));
+                    pg += p;
+                    apg += fabs(p);
+                }
+                sum += sc * pg;
+                asum += fabs(sc) * apg;
+            }
+            ref[r * N + n] = sum;
+            if (absref)
+                absref[r * N + n] = asum;
+        }
 }
 
 /* Elementwise helpers exposed for tests: fp32 -> bf16 bits, fp32 -> e4m3. */
