@@ -29,10 +29,12 @@ workload, and, when the rocprofv3 counter CSVs are given (--fetch-csv,
 --write-csv), the HBM traffic of the dominant kernel scaled by the same
 counters read on a copy kernel of known size (--calib-copy runs that copy).
 
-Other workloads (--workload int8|block|bi|vocab|moe|mxfp4) print the same
-JSON shape; moe is the grouped (per-expert) FP8 GEMM of a 64-expert layer with
-synthetic top-8 routing (per-token quantization + gemm_fp8_grouped); mxfp4 is
-the FP8 sweep's shapes and data in MXFP4 (quantize_mxfp4 + gemm_mxfp4).
+Other workloads (--workload int8|block|bi|vocab|moe|mxfp4|w4a16) print the
+same JSON shape; moe is the grouped (per-expert) FP8 GEMM of a 64-expert layer
+with synthetic top-8 routing (per-token quantization + gemm_fp8_grouped);
+mxfp4 is the FP8 sweep's shapes and data in MXFP4 (quantize_mxfp4 +
+gemm_mxfp4); w4a16 is the same sweep with int4 weights and bf16 activations
+(gemm_w4a16; the weights are quantized once, before timing).
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload fp8]
 """
@@ -50,6 +52,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK = {"fp8": 5000.0, "int8": 5000.0, "bf16": 2500.0, "fp4": 10100.0}  # dense TFLOP/s (TOP/s)
+# (W4A16 runs on the bf16 matrix cores: its peak is the bf16 one)
 HBM_GBS = 8000.0
 
 
@@ -59,7 +62,7 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="fp8",
-                   choices=["fp8", "int8", "block", "bi", "vocab", "moe", "mxfp4"])
+                   choices=["fp8", "int8", "block", "bi", "vocab", "moe", "mxfp4", "w4a16"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=2048,
                    help="rows per problem the CPU oracle computes (the default covers "
@@ -108,6 +111,8 @@ class Problem:
             return M * K + self.experts_used * (N * K + 4 * N) + 4 * M + 2 * M * N
         if self.op == "mxfp4":  # packed codes + one scale byte per 32 + bf16 out
             return (M + N) * (K // 2 + K // 32) + 2 * M * N
+        if self.op == "w4a16":  # bf16 A + packed int4 B + fp32 group scales + bf16 out
+            return 2 * M * K + N * K // 2 + 4 * N * (K // 128) + 2 * M * N
         return M * K + N * K + 4 * M + 4 * N + 2 * M * N
 
     def quant_bytes(self):
@@ -138,6 +143,9 @@ def build_problems(torch, qll, workload):
 
     def gemm_args(p, t):
         wsp = t["ws"].data_ptr() if t["ws"] is not None else None
+        if p.op == "w4a16":
+            return (t["A"].data_ptr(), t["B"].data_ptr(), t["sb"].data_ptr(),
+                    t["out"].data_ptr(), 0, p.M, p.N, p.K, wsp, t["wsb"], stream)
         if p.op == "bf16_bi":
             return (t["A"].data_ptr(), t["B"].data_ptr(), t["out"].data_ptr(), 0, p.M, p.N,
                     p.K, wsp, t["wsb"], stream)
@@ -200,6 +208,14 @@ def build_problems(torch, qll, workload):
                 p.calls.append(("quant", L.quantize_mxfp4, qargs(p, t)))
                 p.tensors["quant"] = (t, qargs)
                 add_gemm(p, "gemm_mxfp4", q, qw.clone(), s, sw.clone())
+                probs.append(p)
+    elif workload == "w4a16":
+        for N, K in W.W4_SHAPES:
+            qw, sw = qll.quantize_int4_weights(dev_bf16(torch, W.w4_weights(N, K)))
+            x_all = dev_bf16(torch, W.w4_activations(W.MAX_M, K))
+            for M in W.W4_M:
+                p = Problem("w4a16", M, N, K)
+                add_gemm(p, "gemm_w4a16", x_all[:M].clone(), qw.clone(), None, sw.clone())
                 probs.append(p)
     elif workload == "int8":
         M, N, K = W.INT8_SHAPE
@@ -312,7 +328,7 @@ def kernel_symbol(qll, op, variant):
     grouped = op == "fp8_grouped"
     if grouped:
         op = "fp8"
-    opn = {"int8": 0, "fp8": 1, "block_fp8": 2, "bf16_bi": 3, "mxfp4": 4}[op]
+    opn = {"int8": 0, "fp8": 1, "block_fp8": 2, "bf16_bi": 3, "mxfp4": 4, "w4a16": 5}[op]
     v = next(x for x in qll.variants(op) if x["name"] == variant)
     if variant[0] == "p":
         st = variant.rsplit("_s", 1)[1]
@@ -368,6 +384,17 @@ def cpu_baseline(workload, rows_cap):
                 flops += 2.0 * r * N * K
         desc = (f"first min(M,{rows_cap}) rows of every MXFP4 problem, "
                 "MXFP4 quantization + GEMM")
+    elif workload == "w4a16":
+        for N, K in W.W4_SHAPES:
+            B, sb = oracle.quantize_int4(W.w4_weights(N, K))
+            x_all = W.w4_activations(W.MAX_M, K)
+            for M in W.W4_M:
+                r = min(M, rows_cap)
+                t0 = time.perf_counter()
+                oracle.gemm_w4a16(np.ascontiguousarray(x_all[:r]), B, sb)
+                t_total += time.perf_counter() - t0
+                flops += 2.0 * r * N * K
+        desc = f"first min(M,{rows_cap}) rows of every W4A16 problem (GEMM only)"
     elif workload == "int8":
         M, N, K = W.INT8_SHAPE
         d = W.int8_inputs(M, N, K)
@@ -555,7 +582,7 @@ def main():
             rec[f"{kind}_us"] = round(call_us[i][j], 3)
         t_gemm = rec["gemm_us"] * 1e-6
         dt = {"fp8": "fp8", "fp8_grouped": "fp8", "block_fp8": "fp8", "int8": "int8",
-              "bf16_bi": "bf16", "mxfp4": "fp4"}[p.op]
+              "bf16_bi": "bf16", "mxfp4": "fp4", "w4a16": "bf16"}[p.op]
         t_mem = p.algo_bytes() / (HBM_GBS * 1e9)
         t_mfma = p.flops / (PEAK[dt] * 1e12)
         rec["tflops"] = round(p.flops / t_gemm / 1e12, 2)
@@ -620,11 +647,14 @@ def main():
                     "routing); per-token quantization + gemm_fp8_grouped, bf16 out",
              "vocab": "large-vocab FP8 dynamic projection N=151936 K=2048, "
                       "M in {1,8,64,512,2048}",
+             "w4a16": "INT4 weight-only sweep: (N,K) in {(4096,2048),(2048,6144)}, "
+                      "M in {1,4,8,16,32,64,256,512,1024,2048}; bf16 activations x int4 "
+                      "weights (scale per 128-element group), bf16 out",
              "mxfp4": "MXFP4 sweep: (N,K) in {(4096,2048),(2048,6144)}, "
                       "M in {1,4,8,16,32,64,256,512,1024,2048}; MXFP4 quantization of the "
                       "activations + MXFP4 GEMM (E8M0 scale per 32), bf16 out"}
     dtype = {"fp8": "fp8e4m3", "vocab": "fp8e4m3", "block": "fp8e4m3", "int8": "int8",
-             "moe": "fp8e4m3", "mxfp4": "fp4e2m1",
+             "moe": "fp8e4m3", "mxfp4": "fp4e2m1", "w4a16": "bf16 x int4",
              "bi": "bf16"}[args.workload]
     line = {
         "metric": "TFLOPS/TOPS + % of HBM or MFMA roofline per (M,N,K), FP8/INT8 scaled_mm",

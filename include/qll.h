@@ -15,6 +15,8 @@
  *   quantize_mxfp4, gemm_mxfp4  MXFP4 (4-bit E2M1, E8M0 scale per 32) quantizer
  *                               and GEMM, the block-scaled 4-bit format of the
  *                               CDNA4 matrix cores (see below)
+ *   quantize_int4_weights,      INT4 weight-only: symmetric int4 weights with a
+ *   gemm_w4a16                  scale per 128-element group, bf16 activations
  * Each GEMM runs as an ordinary tiled GEMM, as Split-K or as Swap-AB (the
  * three strategies of "What the integration changes"), chosen per (M, N, K)
  * by a dispatch table that an on-device sweep fills, or forced with the _ex
@@ -74,7 +76,8 @@ typedef enum {
     QLL_OP_FP8 = 1,
     QLL_OP_BLOCK_FP8 = 2,
     QLL_OP_BF16_BI = 3,
-    QLL_OP_MXFP4 = 4
+    QLL_OP_MXFP4 = 4,
+    QLL_OP_W4A16 = 5
 } qll_op;
 
 /* A GEMM configuration: which registered kernel variant (tile shape, wave
@@ -219,6 +222,31 @@ int gemm_mxfp4(const void* A, const void* B, const void* sa, const void* sb,
 int gemm_mxfp4_ex(const void* A, const void* B, const void* sa, const void* sb,
                   void* out, int out_dtype, int64_t M, int64_t N, int64_t K,
                   void* ws, size_t ws_bytes, void* stream, const qll_cfg* cfg);
+
+/* INT4 weight-only (W4A16).  The same page names INT4 among vLLM's formats
+ * without defining it; the reading is the symmetric per-group form of the
+ * FP8 rule:
+ *   weights: for each output channel n and group g of 128 consecutive K
+ *   elements, amax = max |w|, s[n][g] = amax / 7 (fp32), q = clamp(
+ *   rne(w / s), -8, 7) with the correctly rounded fp32 quotient (an all-zero
+ *   group: s = 0, zero codes); codes are 4-bit two's complement nibbles,
+ *   element 2j of a row in bits 0-3 of byte j, element 2j+1 in bits 4-7.
+ *     w bf16 [N][K] (16-byte aligned); q [N][K/2] bytes (4-byte aligned);
+ *     scales fp32 [N][K/128]; K % 128 == 0.  Weight preparation (offline).
+ *   GEMM: out[m][n] = sum_g s[n][g] * P_g,  P_g = sum_{k in g} A[m][k] q[n][k]
+ *   with each P_g a fresh fp32 matrix-core sum (bf16 x int4 products are
+ *   exact) promoted by one fma per group; out bf16_rne (or fp32).
+ *     A bf16 [M][K]; B packed int4 [N][K/2]; scales fp32 [N][K/128];
+ *     K % 128 == 0; ws as for the other GEMMs (Split-K pieces are whole
+ *     multiples of 8 groups: qll_workspace_bytes(QLL_OP_W4A16, ...)). */
+int quantize_int4_weights(const void* w, void* q, float* scales, int64_t N,
+                          int64_t K, void* stream);
+int gemm_w4a16(const void* A, const void* B, const float* scales, void* out,
+               int out_dtype, int64_t M, int64_t N, int64_t K, void* ws,
+               size_t ws_bytes, void* stream);
+int gemm_w4a16_ex(const void* A, const void* B, const float* scales, void* out,
+                  int out_dtype, int64_t M, int64_t N, int64_t K, void* ws,
+                  size_t ws_bytes, void* stream, const qll_cfg* cfg);
 
 /* FP8 dynamic linear layer in one call ("FP8 dynamic quantization", same
  * section): quantize_per_token_fp8(x -> q, sa) followed by

@@ -14,7 +14,9 @@ Operations (see include/qll.h for the full contract):
   linear_fp8_dynamic (per-token quantization + FP8 GEMM in one call),
   gemm_fp8_grouped (per-expert FP8 GEMM over rows sorted by expert),
   quantize_mxfp4, gemm_mxfp4 (MXFP4: E2M1 codes packed two per byte, one
-  E8M0 scale byte per 32 elements of a row; tensors as uint8).
+  E8M0 scale byte per 32 elements of a row; tensors as uint8),
+  quantize_int4_weights, gemm_w4a16 (INT4 weight-only: int4 codes packed two
+  per byte, an fp32 scale per 128-element group, bf16 activations).
 """
 from __future__ import annotations
 
@@ -31,7 +33,7 @@ STATUS = {0: "QLL_OK", 1: "QLL_ERR_INVALID_ARG", 2: "QLL_ERR_UNSUPPORTED",
           3: "QLL_ERR_MISALIGNED", 4: "QLL_ERR_WORKSPACE", 5: "QLL_ERR_NO_DEVICE",
           6: "QLL_ERR_TABLE", 7: "QLL_ERR_HIP"}
 OUT = {"bf16": 0, "fp32": 1, "int32": 2}
-OPS = {"int8": 0, "fp8": 1, "block_fp8": 2, "bf16_bi": 3, "mxfp4": 4}
+OPS = {"int8": 0, "fp8": 1, "block_fp8": 2, "bf16_bi": 3, "mxfp4": 4, "w4a16": 5}
 
 
 class QllError(RuntimeError):
@@ -70,6 +72,9 @@ def load_library():
         getattr(L, name).argtypes = _GEMM_ARGS
         getattr(L, name + "_ex").argtypes = _GEMM_ARGS + [ctypes.POINTER(qll_cfg)]
     L.quantize_mxfp4.argtypes = [_P, _P, _P, _I64, _I64, _P]
+    L.quantize_int4_weights.argtypes = [_P, _P, _P, _I64, _I64, _P]
+    L.gemm_w4a16.argtypes = _BF16_ARGS[:2] + [_P] + _BF16_ARGS[2:]
+    L.gemm_w4a16_ex.argtypes = _BF16_ARGS[:2] + [_P] + _BF16_ARGS[2:] + [ctypes.POINTER(qll_cfg)]
     L.gemm_mxfp4.argtypes = _GEMM_ARGS
     L.gemm_mxfp4_ex.argtypes = _GEMM_ARGS + [ctypes.POINTER(qll_cfg)]
     L.gemm_bf16_batch_invariant.argtypes = _BF16_ARGS
@@ -379,6 +384,49 @@ def gemm_mxfp4(A, B, sa, sb, out_dtype="bf16", out=None, cfg=None, workspace=Non
             ws.data_ptr() if ws is not None else None, wsb, _stream(stream)]
     rc = L.gemm_mxfp4_ex(*args, ctypes.byref(c)) if c else L.gemm_mxfp4(*args)
     _check("gemm_mxfp4", rc)
+    return out
+
+
+def quantize_int4_weights(w, q=None, scales=None, stream=None):
+    """bf16 weights [N][K] -> (packed int4 codes uint8 [N][K/2], fp32 scales
+    [N][K/128]); K % 128 == 0."""
+    torch = _torch()
+    if w.dtype != torch.bfloat16 or w.dim() != 2:
+        raise ValueError("w must be a 2-D bfloat16 tensor")
+    N, K = w.shape
+    if K % 128:
+        raise ValueError("K must be a multiple of 128")
+    if q is None:
+        q = torch.empty((N, K // 2), dtype=torch.uint8, device=w.device)
+    if scales is None:
+        scales = torch.empty((N, K // 128), dtype=torch.float32, device=w.device)
+    rc = load_library().quantize_int4_weights(
+        _dev_ptr(w, "w"), _u8(q, "q", (N, K // 2)), _f32(scales, "scales", (N, K // 128)),
+        N, K, _stream(stream))
+    _check("quantize_int4_weights", rc)
+    return q, scales
+
+
+def gemm_w4a16(A, B, scales, out_dtype="bf16", out=None, cfg=None, workspace=None,
+               stream=None):
+    """bf16 A [M][K] x packed int4 B [N][K/2] (uint8) with fp32 group scales
+    [N][K/128]."""
+    torch = _torch()
+    _ensure_init()
+    if A.dtype != torch.bfloat16 or A.dim() != 2:
+        raise TypeError("A must be a 2-D bfloat16 tensor")
+    M, K = A.shape
+    N = B.shape[0]
+    pb = _u8(B, "B", (N, K // 2))
+    ps = _f32(scales, "scales", (N, K // 128))
+    out = _out(out, M, N, out_dtype, A.device)
+    c = _cfg(5, cfg)
+    ws, wsb = _workspace(5, M, N, K, c, workspace)
+    L = load_library()
+    args = [_dev_ptr(A, "A"), pb, ps, _dev_ptr(out, "out"), OUT[out_dtype], M, N, K,
+            ws.data_ptr() if ws is not None else None, wsb, _stream(stream)]
+    rc = L.gemm_w4a16_ex(*args, ctypes.byref(c)) if c else L.gemm_w4a16(*args)
+    _check("gemm_w4a16", rc)
     return out
 
 

@@ -38,11 +38,14 @@ extern const Variant kVariantsBf16[];
 extern const int kNumVariantsBf16;
 extern const Variant kVariantsMxfp4[];
 extern const int kNumVariantsMxfp4;
+extern const Variant kVariantsW4a16[];
+extern const int kNumVariantsW4a16;
 hipError_t launch_reduce_int8(const GemmArgs&, hipStream_t);
 hipError_t launch_reduce_fp8(const GemmArgs&, hipStream_t);
 hipError_t launch_reduce_block(const GemmArgs&, hipStream_t);
 hipError_t launch_reduce_bf16(const GemmArgs&, hipStream_t);
 hipError_t launch_reduce_mxfp4(const GemmArgs&, hipStream_t);
+hipError_t launch_reduce_w4a16(const GemmArgs&, hipStream_t);
 
 const Variant* variants(int op, int* count)
 {
@@ -52,6 +55,7 @@ const Variant* variants(int op, int* count)
     case OP_BLOCK: *count = kNumVariantsBlock; return kVariantsBlock;
     case OP_BF16: *count = kNumVariantsBf16; return kVariantsBf16;
     case OP_MXFP4: *count = kNumVariantsMxfp4; return kVariantsMxfp4;
+    case OP_W4A16: *count = kNumVariantsW4a16; return kVariantsW4a16;
     default: *count = 0; return nullptr;
     }
 }
@@ -69,18 +73,22 @@ hipError_t launch_splitk_reduce(int op, const GemmArgs& a, hipStream_t stream)
     case OP_FP8: return launch_reduce_fp8(a, stream);
     case OP_BLOCK: return launch_reduce_block(a, stream);
     case OP_MXFP4: return launch_reduce_mxfp4(a, stream);
+    case OP_W4A16: return launch_reduce_w4a16(a, stream);
     default: return launch_reduce_bf16(a, stream);
     }
 }
 
 namespace {
 
-const char* const kOpNames[OP_COUNT] = {"int8", "fp8", "block_fp8", "bf16_bi", "mxfp4"};
+const char* const kOpNames[OP_COUNT] = {"int8", "fp8", "block_fp8", "bf16_bi", "mxfp4",
+                                         "w4a16"};
 
-// Bytes of one K-row of A or B: bf16 2 per element, packed MXFP4 one per two.
+// Bytes of one K-row of A or B: bf16 2 per element, packed MXFP4 one per two;
+// W4A16 counts the packed weight row (its Split-K pieces are cut on those
+// bytes, 512 of them = 8 groups of 128).
 int64_t op_kbytes(int op, int64_t K)
 {
-    return op == OP_BF16 ? 2 * K : (op == OP_MXFP4 ? K / 2 : K);
+    return op == OP_BF16 ? 2 * K : (op == OP_MXFP4 || op == OP_W4A16 ? K / 2 : K);
 }
 
 // Longest MXFP4 K: every pipelined variant's tile rows times the row bytes
@@ -289,7 +297,13 @@ qll_cfg heuristic(int op, int64_t M, int64_t N, int64_t K)
     const int cus = device_info().cus;
     const char* name;
     bool exact = true;
-    if (op == OP_MXFP4 && M > 32) {
+    if (op == OP_W4A16) {
+        // few tokens: the wave-split decode kernel; more: LDS tiles (the
+        // fastest variants of the on-device sweep of the two sweep shapes)
+        name = M <= 16 ? "k16x16_w16"
+             : M <= 64 ? "k16x32_w8"
+             : M <= 512 ? "t64x64_w2x2" : "t128x64_w2x2";
+    } else if (op == OP_MXFP4 && M > 32) {
         // 256-byte K stages (four MFMA steps of 128 elements per barrier):
         // fastest from 64 tokens up on the sweep shapes
         name = M <= 1024 ? "p64x64_w2x2_k256_s2" : "p128x128_w2x2_k256_s2";
@@ -389,6 +403,9 @@ int validate_gemm(int op, const void* A, const void* B, const float* sa,
     } else if (op == OP_MXFP4) {
         if (K % 128 || K > kMaxKMxfp4)
             return QLL_ERR_INVALID_ARG;
+    } else if (op == OP_W4A16) {
+        if (K % 128)
+            return QLL_ERR_INVALID_ARG;
     } else if (K % 16) {
         return QLL_ERR_INVALID_ARG;
     }
@@ -396,11 +413,12 @@ int validate_gemm(int op, const void* A, const void* B, const float* sa,
         return QLL_ERR_INVALID_ARG;
     if (M == 0)
         return QLL_OK;
-    if (!A || !B || !out || (op != OP_BF16 && (!sa || !sb)))
+    const bool has_sa = op != OP_BF16 && op != OP_W4A16;
+    if (!A || !B || !out || (has_sa && !sa) || (op != OP_BF16 && !sb))
         return QLL_ERR_INVALID_ARG;
     if (misaligned(A, 16) || misaligned(B, 16) || misaligned(out, 16))
         return QLL_ERR_MISALIGNED;
-    if (op != OP_BF16 && (misaligned(sa, 4) || misaligned(sb, 4)))
+    if ((has_sa && misaligned(sa, 4)) || (op != OP_BF16 && misaligned(sb, 4)))
         return QLL_ERR_MISALIGNED;
     return QLL_OK;
 }
@@ -612,6 +630,38 @@ int quantize_mxfp4(const void* x, void* q, void* scales, int64_t M, int64_t K, v
     return launch_quant_mxfp4(x, q, scales, M * K, (hipStream_t)stream) == hipSuccess
                ? QLL_OK
                : QLL_ERR_HIP;
+}
+
+int quantize_int4_weights(const void* w, void* q, float* scales, int64_t N, int64_t K,
+                          void* stream)
+{
+    if (N < 0 || K <= 0 || K % 128 || N > 0x7FFFFFFF || K > 0x3FFFFFFF ||
+        N * K > ((int64_t)1 << 40))
+        return QLL_ERR_INVALID_ARG;
+    if (N == 0)
+        return QLL_OK;
+    if (!w || !q || !scales)
+        return QLL_ERR_INVALID_ARG;
+    if (misaligned(w, 16) || misaligned(q, 4) || misaligned(scales, 4))
+        return QLL_ERR_MISALIGNED;
+    return launch_quant_int4(w, q, scales, N * K, (hipStream_t)stream) == hipSuccess
+               ? QLL_OK
+               : QLL_ERR_HIP;
+}
+
+int gemm_w4a16_ex(const void* A, const void* B, const float* scales, void* out, int out_dtype,
+                  int64_t M, int64_t N, int64_t K, void* ws, size_t ws_bytes, void* stream,
+                  const qll_cfg* cfg)
+{
+    return run_gemm(OP_W4A16, A, B, nullptr, scales, out, out_dtype, M, N, K, ws, ws_bytes,
+                    stream, cfg);
+}
+
+int gemm_w4a16(const void* A, const void* B, const float* scales, void* out, int out_dtype,
+               int64_t M, int64_t N, int64_t K, void* ws, size_t ws_bytes, void* stream)
+{
+    return run_gemm(OP_W4A16, A, B, nullptr, scales, out, out_dtype, M, N, K, ws, ws_bytes,
+                    stream, nullptr);
 }
 
 int gemm_mxfp4_ex(const void* A, const void* B, const void* sa, const void* sb, void* out,

@@ -64,6 +64,13 @@ template <> struct OpTraits<OP_MXFP4> {
     using acc_t = v4f;
     using elem_t = float;
 };
+// W4A16: bf16 activations (16 bytes per lane per bf16 MFMA), int4 weights
+// widened to bf16 in registers
+template <> struct OpTraits<OP_W4A16> {
+    static constexpr int esz = 2, kb = 16;
+    using acc_t = v4f;
+    using elem_t = float;
+};
 
 // Workgroup -> output tile, XCD-aware.  The dispatcher hands consecutive
 // workgroup ids to the 8 XCDs in turn, and each XCD has its own L2.  The

@@ -8,7 +8,15 @@
 
 namespace qll {
 
-enum Op : int { OP_INT8 = 0, OP_FP8 = 1, OP_BLOCK = 2, OP_BF16 = 3, OP_MXFP4 = 4, OP_COUNT = 5 };
+enum Op : int {
+    OP_INT8 = 0,
+    OP_FP8 = 1,
+    OP_BLOCK = 2,
+    OP_BF16 = 3,
+    OP_MXFP4 = 4,
+    OP_W4A16 = 5,
+    OP_COUNT = 6
+};
 enum Out : int { OUT_BF16 = 0, OUT_FP32 = 1, OUT_INT32 = 2 };
 
 // The K range of one Split-K piece is a multiple of this many bytes, for every
@@ -25,12 +33,14 @@ struct GemmArgs {
     const void* B;   // [N][K]
     const float* sa; // per-token [M] or per-group [M][K/128]
     const float* sb; // per-channel [N] or per-block [ceil(N/128)][K/128]
-                     // (MXFP4: E8M0 bytes [M][K/32] and [N][K/32])
+                     // (MXFP4: E8M0 bytes [M][K/32] and [N][K/32];
+                     // W4A16: sb fp32 [N][K/128], sa unused)
     void* out;       // [M][N]
     void* ws;        // [splits][M][N] int32 / fp32 partials (splits > 1)
     int out_dtype;
     int M, N, K;     // K in elements
-    int kbytes;      // bytes of one row of A or B (K / 2 for packed MXFP4)
+    int kbytes;      // bytes of one row of A or B (K / 2 for packed MXFP4;
+                     // W4A16: of B, the packed int4 weights)
     int splits;      // effective number of K pieces
     int kchunk;      // bytes of K per piece (multiple of kSplitGranule)
     int kfold;       // bf16 only: K chunks summed separately, then in order
@@ -79,5 +89,7 @@ hipError_t launch_quant_weight_blocks(const void* w, void* q, float* s, int N,
                                       int K, hipStream_t stream);
 hipError_t launch_quant_mxfp4(const void* x, void* q, void* s, int64_t elems,
                               hipStream_t stream);
+hipError_t launch_quant_int4(const void* w, void* q, float* s, int64_t elems,
+                             hipStream_t stream);
 
 }  // namespace qll

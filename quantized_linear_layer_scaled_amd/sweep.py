@@ -41,6 +41,7 @@ DEFAULT_SHAPES = {
     "block_fp8": [(12288, 2048), (2048, 6144)],
     "bf16_bi": [(2048, 2048), (4096, 2048), (151936, 2048)],
     "mxfp4": [(4096, 2048), (2048, 6144)],
+    "w4a16": [(4096, 2048), (2048, 6144)],
 }
 SPLITS = [1, 2, 4, 8]
 WS_LIMIT = 1 << 30
@@ -74,6 +75,12 @@ def _inputs(torch, op, M, N, K, copies):
               for _ in range(copies)]
         sa = torch.randint(120, 134, (M, K // 32), device="cuda", dtype=torch.uint8, generator=g)
         sb = torch.randint(120, 134, (N, K // 32), device="cuda", dtype=torch.uint8, generator=g)
+    elif op == "w4a16":
+        A = (torch.randn((M, K), device="cuda", generator=g)).to(torch.bfloat16)
+        Bs = [torch.randint(0, 256, (N, K // 2), device="cuda", dtype=torch.uint8, generator=g)
+              for _ in range(copies)]
+        sa = None
+        sb = torch.rand((N, K // 128), device="cuda", generator=g) * 9e-3 + 1e-3
     elif op == "block_fp8":
         A = e4m3((M, K))
         Bs = [e4m3((N, K)) for _ in range(copies)]
@@ -97,6 +104,8 @@ def _call(qll, op, A, B, sa, sb, out_dtype, cfg, ws, out=None):
         return qll.gemm_block_fp8(A, B, sa, sb, **kw)
     if op == "mxfp4":
         return qll.gemm_mxfp4(A, B, sa, sb, **kw)
+    if op == "w4a16":
+        return qll.gemm_w4a16(A, B, sb, **kw)
     return qll.gemm_bf16_batch_invariant(A, B, **kw)
 
 
@@ -148,7 +157,7 @@ def time_config(torch, qll, op, A, Bs, sa, sb, cfg, ws, reps):
 
 
 def sweep_shape(torch, qll, op, N, K, mlist, reps, log):
-    row_bytes = {"bf16_bi": 2 * K, "mxfp4": K // 2}.get(op, K)
+    row_bytes = {"bf16_bi": 2 * K, "mxfp4": K // 2, "w4a16": K // 2}.get(op, K)
     copies = max(2, min(8, (512 << 20) // max(1, N * row_bytes)))
     Mmax = max(mlist)
     A_all, Bs, sa_all, sb = _inputs(torch, op, Mmax, N, K, copies)
@@ -192,7 +201,7 @@ def sweep_shape(torch, qll, op, N, K, mlist, reps, log):
 
 def main(argv=None):
     ap = argparse.ArgumentParser(description="fill the scaled_mm dispatch table")
-    ap.add_argument("--ops", default="int8,fp8,block_fp8,bf16_bi,mxfp4")
+    ap.add_argument("--ops", default="int8,fp8,block_fp8,bf16_bi,mxfp4,w4a16")
     ap.add_argument("--shapes", default=None, help="NxK[,NxK...] (default: the shipped set)")
     ap.add_argument("--m", default=None, help="M values (default: 1..2048 powers of two)")
     ap.add_argument("--reps", type=int, default=20)

@@ -55,6 +55,8 @@ def gemm(qll, fn, A=P, B=P, sa=P, sb=P, out=P, od=0, M=16, N=64, K=2048, ws=None
     L = qll.load_library()
     if fn == "gemm_bf16_batch_invariant":
         args = [A, B, out, od, M, N, K, ws, wsb, None]
+    elif fn == "gemm_w4a16":
+        args = [A, B, sb, out, od, M, N, K, ws, wsb, None]
     else:
         args = [A, B, sa, sb, out, od, M, N, K, ws, wsb, None]
     if cfg is not None:
@@ -62,12 +64,12 @@ def gemm(qll, fn, A=P, B=P, sa=P, sb=P, out=P, od=0, M=16, N=64, K=2048, ws=None
             qll.OPS[{"gemm_w8a8_int8": "int8", "gemm_fp8_scaled": "fp8",
                      "gemm_block_fp8": "block_fp8",
                      "gemm_bf16_batch_invariant": "bf16_bi",
-                     "gemm_mxfp4": "mxfp4"}[fn]], cfg)))
+                     "gemm_mxfp4": "mxfp4", "gemm_w4a16": "w4a16"}[fn]], cfg)))
     return getattr(L, fn)(*args)
 
 
 GEMMS = ["gemm_w8a8_int8", "gemm_fp8_scaled", "gemm_block_fp8",
-         "gemm_bf16_batch_invariant", "gemm_mxfp4"]
+         "gemm_bf16_batch_invariant", "gemm_mxfp4", "gemm_w4a16"]
 
 
 @pytest.mark.parametrize("fn", GEMMS)
@@ -85,12 +87,14 @@ def test_gemm_argument_validation(qll, fn):
     assert gemm(qll, fn, M=0, A=None, out=None) == 0     # M == 0 is a no-op
     if fn != "gemm_w8a8_int8":
         assert gemm(qll, fn, od=2) == INVALID            # raw int32 out: INT8 only
-    if fn in ("gemm_block_fp8", "gemm_mxfp4"):
+    if fn in ("gemm_block_fp8", "gemm_mxfp4", "gemm_w4a16"):
         assert gemm(qll, fn, K=2048 + 16) == INVALID     # K % 128
     if fn == "gemm_mxfp4":
         assert gemm(qll, fn, K=(1 << 23) + 128) == INVALID   # longest K 2^23
-    if fn != "gemm_bf16_batch_invariant":
+    if fn not in ("gemm_bf16_batch_invariant", "gemm_w4a16"):
         assert gemm(qll, fn, sa=None) == INVALID
+    if fn != "gemm_bf16_batch_invariant":
+        assert gemm(qll, fn, sb=None) == INVALID
         assert gemm(qll, fn, sb=P + 2) == MISALIGNED
 
 
@@ -108,6 +112,31 @@ def test_quantize_mxfp4_validation(qll):
     assert qz(x=P + 4) == 3               # x 16-byte aligned
     assert qz(q=P + 2) == 3               # q 4-byte aligned
     assert qz(M=0, x=None, q=None, s=None) == 0
+
+
+def test_quantize_int4_validation(qll):
+    L = qll.load_library()
+
+    def qz(w=P, q=P, s=P, N=4, K=256):
+        return L.quantize_int4_weights(w, q, s, N, K, None)
+
+    assert qz(K=192) == 1                 # K % 128
+    assert qz(N=-1) == 1
+    assert qz(w=None) == 1
+    assert qz(s=None) == 1
+    assert qz(w=P + 8) == 3
+    assert qz(s=P + 2) == 3
+    assert qz(N=0, w=None, q=None, s=None) == 0
+
+
+def test_w4a16_registry_and_dispatch(qll):
+    names = [v["name"] for v in qll.variants("w4a16")]
+    assert "k16x16_w8" in names and "t128x128_w2x2" in names
+    assert qll.select("w4a16", 1, 4096, 4096)[0] == "k16x16_w16"
+    assert qll.select("w4a16", 2048, 4096, 4096)[0].startswith("t")
+    # Split-K pieces on the packed weight bytes: 512 bytes = 8 groups
+    assert qll.effective_splits("w4a16", 2048, 2) == 2
+    assert qll.effective_splits("w4a16", 2048, 4) == 2
 
 
 def test_mxfp4_registry_and_dispatch(qll):

@@ -36,6 +36,10 @@ vocabulary N=151936 and a square N=K=2048 weight):
                both quantized to MXFP4; parity cases also draw packed codes
                uniformly over all 256 bytes and scale bytes uniform in a
                band around 2^0.
+  INT4 W4A16   the FP8 dynamic shapes and M values: A bf16 N(0, 1) with
+               outlier channels, W bf16 N(0, 0.02) quantized to int4 per
+               128-element group; parity cases also draw packed codes over all
+               256 bytes and fp32 group scales uniform in [1e-3, 1e-2].
 """
 from __future__ import annotations
 
@@ -58,12 +62,14 @@ MAX_M = 2048
 MOE_E, MOE_TOPK = 64, 8
 MOE_SHAPE = (1536, 2048)  # (N, K)
 MOE_T = [16, 128, 1024]
-# MXFP4: the FP8 dynamic (N, K) shapes and M values
+# MXFP4 and INT4 weight-only: the FP8 dynamic (N, K) shapes and M values
 MX_SHAPES = FP8_SHAPES
 MX_M = FP8_M
+W4_SHAPES = FP8_SHAPES
+W4_M = FP8_M
 
 # workload ids used in the seeds
-W_INT8, W_FP8, W_BLOCK, W_BI, W_VOCAB, W_MOE, W_MX, W_TEST = 1, 2, 3, 4, 5, 6, 7, 9
+W_INT8, W_FP8, W_BLOCK, W_BI, W_VOCAB, W_MOE, W_MX, W_W4, W_TEST = 1, 2, 3, 4, 5, 6, 7, 8, 9
 
 
 def rng(*key) -> np.random.Generator:
@@ -220,3 +226,14 @@ def mx_codes(rows, K, key) -> np.ndarray:
 def mx_scale_bytes(rows, K, key, lo=118, hi=136) -> np.ndarray:
     """E8M0 scale bytes [rows][K/32] uniform in [lo, hi]."""
     return rng(*key).integers(lo, hi + 1, size=(rows, K // 32), dtype=np.uint8)
+
+
+def w4_activations(M, K, key=(W_W4,)):
+    """bf16 activations of the INT4 weight-only workload (first M rows of a
+    MAX_M-row draw, 1% outlier channels x20)."""
+    rows = max(M, MAX_M)
+    return bf16_normal((rows, K), (*key, K, 0), outlier_frac=0.01)[:M].copy()
+
+
+def w4_weights(N, K, key=(W_W4,)):
+    return bf16_normal((N, K), (*key, N, K, 1), std=0.02)
