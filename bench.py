@@ -330,6 +330,11 @@ def kernel_symbol(qll, op, variant):
         op = "fp8"
     opn = {"int8": 0, "fp8": 1, "block_fp8": 2, "bf16_bi": 3, "mxfp4": 4, "w4a16": 5}[op]
     v = next(x for x in qll.variants(op) if x["name"] == variant)
+    if op == "w4a16":
+        if variant[0] == "t":
+            return (f"void qll::gemm_w4_tile_kernel<{v['bp']}, {v['bq']}, {v['wp']}, "
+                    f"{v['wq']}>(qll::GemmArgs)")
+        return f"void qll::gemm_w4_skinny_kernel<{v['bq'] // 16}, {v['wp']}, "
     if variant[0] == "p":
         st = variant.rsplit("_s", 1)[1]
         return (f"void qll::gemm_pipe_kernel<{opn}, {v['bp']}, {v['bq']}, {v['wp']}, "

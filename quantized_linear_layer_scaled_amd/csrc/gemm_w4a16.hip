@@ -103,6 +103,8 @@ __device__ __forceinline__ void piece_groups(const GemmArgs& a, int z, int& g0, 
     g1 = min(G, g0 + a.kchunk / 64);
 }
 
+}  // namespace
+
 // ---------------------------------------------------------------- decode
 
 // 16 output channels per workgroup, 16 * RQ tokens; the W waves split the
@@ -403,7 +405,6 @@ template __global__ void gemm_w4_tile_kernel<64, 128, 2, 2>(GemmArgs);
 template __global__ void gemm_w4_tile_kernel<128, 128, 2, 2>(GemmArgs);
 template __global__ void gemm_w4_tile_kernel<256, 64, 4, 1>(GemmArgs);
 
-}  // namespace
 
 hipError_t launch_quant_int4(const void* w, void* q, float* s, int64_t elems,
                              hipStream_t stream)

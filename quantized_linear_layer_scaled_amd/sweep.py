@@ -12,8 +12,11 @@ point with a forced configuration, checks the result against a reference
 configuration of the same op (bit-exact for the INT8 int32 accumulators,
 normwise 1e-2 otherwise -- the oracle parity is the test suite's job), times
 the whole call (tile kernel plus Split-K reduction) by replaying a HIP graph
-of back-to-back calls that rotate through several copies of the weights, and
-keeps the fastest configuration per bucket.  The batch-invariant op only
+of back-to-back calls that rotate through enough copies of the weights to
+exceed the 256 MB Infinity Cache (cold weights, as in serving, where every
+layer's weights come from HBM; the activations stay the same, as when the
+previous kernel has just written them), and keeps the fastest configuration
+per bucket.  The batch-invariant op only
 considers configurations without a cross-workgroup K split and whose waves,
 if they split K, split it into the op's fixed eight chunks, so the table it
 produces is accepted by the loader.
@@ -45,6 +48,7 @@ DEFAULT_SHAPES = {
 }
 SPLITS = [1, 2, 4, 8]
 WS_LIMIT = 1 << 30
+COLD_BYTES = 384 << 20  # weights touched per timing replay: > the 256 MB Infinity Cache
 
 
 def _inputs(torch, op, M, N, K, copies):
@@ -158,7 +162,9 @@ def time_config(torch, qll, op, A, Bs, sa, sb, cfg, ws, reps):
 
 def sweep_shape(torch, qll, op, N, K, mlist, reps, log):
     row_bytes = {"bf16_bi": 2 * K, "mxfp4": K // 2, "w4a16": K // 2}.get(op, K)
-    copies = max(2, min(8, (512 << 20) // max(1, N * row_bytes)))
+    # rotate through at least COLD_BYTES of weights per graph replay
+    copies = max(2, min(64, -(-COLD_BYTES // max(1, N * row_bytes))))
+    reps = max(reps, copies)
     Mmax = max(mlist)
     A_all, Bs, sa_all, sb = _inputs(torch, op, Mmax, N, K, copies)
     results = {}
