@@ -18,10 +18,14 @@ Timing (all on the one stream the library launches on):
     times (graph-covered execution, the launch mode the pages recommend for
     tuned kernels);
   * per call: for every quantizer and GEMM call of the step, a HIP graph of
-    --copies back-to-back launches, each on its own copy of the call's buffers
-    (cold data), timed with HIP events: this gives the per-shape table and the
-    roofline of the dominant kernel (the GEMM kernel with the most time per
-    step among single-kernel calls);
+    back-to-back launches, each on its own copy of the call's buffers, with
+    enough copies (>= 1 GiB per replay) that every launch reads from HBM,
+    replayed --replays times between HIP events (median, p10, p90 of the
+    per-launch time; the same call on one warm set of buffers as context):
+    this gives the per-shape table and the roofline of the dominant kernel
+    (the GEMM kernel with the most time per step among single-kernel calls);
+  * eager per call: HIP events around each C-ABI call of a few extra eager
+    steps (launch included);
   * dispatch: host-side costs of the C-ABI path (table load, the first step
     of the process, host enqueue time per call).
 The line also carries the CPU oracle timed on a bounded sample of the same
@@ -77,8 +81,8 @@ def parse():
                    help="also run a plain device copy of known size (counter calibration)")
     p.add_argument("--no-graph", action="store_true",
                    help="no graphs: eager steps only, no per-call timing (counter runs)")
-    p.add_argument("--copies", type=int, default=8,
-                   help="buffer copies per call for the per-call timing graphs")
+    p.add_argument("--replays", type=int, default=5,
+                   help="timed replays of each per-call timing graph (median, p10/p90)")
     return p.parse_args()
 
 
@@ -278,36 +282,93 @@ def build_problems(torch, qll, workload):
 # timing
 # --------------------------------------------------------------------------
 
-def per_call_us(torch, probs, copies, stream):
-    """Average duration of every call, each timed on its own: a HIP graph of
-    `copies` back-to-back launches of the call, launch r on its own copy of
-    the call's buffers (so every launch reads cold data), replayed once to
-    warm up and once between HIP events.  Returns [[us per call kind]]."""
-    out = []
+COLD_BYTES = 1 << 30  # buffers one per-call timing replay rotates through
+
+
+def _graph_us(torch, fn, arg_sets, replays, stream):
+    """A HIP graph of one launch per argument set, replayed once to warm up,
+    then `replays` times, each replay between HIP events on the stream the
+    graph runs on: the per-launch mean of every replay."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for args in arg_sets:
+            fn(*args)
+    g.replay()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(replays)]
+    for e0, e1 in evs:
+        e0.record()
+        g.replay()
+        e1.record()
+    torch.cuda.synchronize()
+    del g
+    return [e0.elapsed_time(e1) * 1e3 / len(arg_sets) for e0, e1 in evs]
+
+
+def _stats(xs):
+    import numpy as np
+    a = np.asarray(xs, dtype=np.float64)
+    return {"median": float(np.median(a)), "p10": float(np.percentile(a, 10)),
+            "p90": float(np.percentile(a, 90)), "n": int(a.size)}
+
+
+def per_call_us(torch, probs, replays, stream, max_copies=256):
+    """Every call timed on its own, cold: a HIP graph of back-to-back launches
+    of the call, launch r on its own copy of all the call's buffers, with
+    enough copies that one replay touches at least COLD_BYTES (more than the
+    256 MB Infinity Cache and the L2s, so every launch reads from HBM); the
+    median and p10/p90 over `replays` timed replays of the per-launch time
+    (the GPU time of a replay divided by its launches: kernel time plus the
+    in-graph gap between consecutive launches).  Context: the same number of
+    launches on one warm set of buffers.  Returns ([[stats]], [[copies]])."""
+    out, plan = [], []
     for p in probs:
-        row = []
+        row, prow = [], []
         for kind, fn, _ in p.calls:
             base, make = p.tensors[kind]
+            nbytes = sum(v.numel() * v.element_size() for v in base.values()
+                         if isinstance(v, torch.Tensor))
+            copies = max(8, min(max_copies, -(-COLD_BYTES // max(1, nbytes))))
             sets = []
             for _ in range(copies):
                 t = {k: (v.clone() if isinstance(v, torch.Tensor) else v)
                      for k, v in base.items()}
                 sets.append((t, make(p, t)))
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=stream):
-                for _, args in sets:
-                    fn(*args)
-            g.replay()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            g.replay()
-            e1.record()
-            torch.cuda.synchronize()
-            row.append(e0.elapsed_time(e1) * 1e3 / copies)
-            del g, sets
+            st = _stats(_graph_us(torch, fn, [a for _, a in sets], replays, stream))
+            del sets
+            st["warm"] = _stats(_graph_us(torch, fn, [make(p, base)] * copies, replays,
+                                          stream))["median"]
+            st["copies"] = copies
+            row.append(st)
+            prow.append(copies)
+            torch.cuda.empty_cache()
         out.append(row)
-    torch.cuda.empty_cache()
-    return out
+        plan.append(prow)
+    return out, plan
+
+
+def env_info():
+    """ROCm version and the GPU clocks as the SMI tool reports them (best
+    effort: empty when the tool is missing or slow)."""
+    import subprocess
+    info = {}
+    try:
+        info["rocm"] = open("/opt/rocm/.info/version").read().strip()
+    except OSError:
+        info["rocm"] = None
+    clocks = None
+    for cmd in (["amd-smi", "metric", "-g", "0", "-c"], ["rocm-smi", "--showclocks"]):
+        try:
+            r = subprocess.run(cmd, capture_output=True, text=True, timeout=20)
+            if r.returncode == 0 and r.stdout.strip():
+                lines = [l.strip() for l in r.stdout.splitlines()
+                         if any(w in l.lower() for w in ("sclk", "mclk", "gfx_0", "mem_0", "clk"))]
+                clocks = " | ".join(lines)[:600]
+                break
+        except (OSError, subprocess.SubprocessError):
+            continue
+    info["clocks"] = clocks
+    return info
 
 
 def run_step(probs, events=None):
@@ -450,9 +511,32 @@ def cpu_baseline(workload, rows_cap):
                 t_total += time.perf_counter() - t0
                 flops += 2.0 * r * N * K
         desc = f"first min(M,{rows_cap}) rows of every bf16 problem"
+    cores = oracle.num_threads()
+    # one single-thread timing on the W8A8 INT8 shape (median of 3 runs)
+    M, N, K = W.INT8_SHAPE
+    d = W.int8_inputs(M, N, K)
+    oracle.set_threads(1)
+    ts = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        oracle.gemm_w8a8_int8(d["A"], d["B"], d["sa"], d["sb"])
+        ts.append(time.perf_counter() - t0)
+    oracle.set_threads(cores)
+    single = 2.0 * M * N * K / sorted(ts)[1] / 1e9
+    cpu_model = None
+    try:
+        for l in open("/proc/cpuinfo"):
+            if l.startswith("model name"):
+                cpu_model = l.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": round(flops / t_total / 1e12, 6), "unit": "TFLOPS",
-            "cores": oracle.num_threads(), "kind": "oracle", "sample": desc,
-            "seconds": round(t_total, 2)}
+            "cores": cores, "kind": "oracle", "sample": desc,
+            "seconds": round(t_total, 2), "cpu_model": cpu_model,
+            "cores_available": len(os.sched_getaffinity(0)),
+            "single_thread_int8_gops": round(single, 3),
+            "single_thread_shape": f"W8A8 INT8 M={M} N={N} K={K}, median of 3"}
 
 
 CALIB_BYTES = 512 << 20  # the copy kernel moves this many bytes each way
@@ -515,6 +599,7 @@ def main():
     stream = torch.cuda.Stream()
     torch.cuda.set_stream(stream)
     probs = build_problems(torch, qll, args.workload)
+    env_before = env_info()
     print(f"# {len(probs)} problems built", file=sys.stderr, flush=True)
 
     # first step of the process: includes loading the kernels' code objects
@@ -561,11 +646,27 @@ def main():
     n_calls = sum(len(p.calls) for p in probs)
     ms_per_step = ms_eager
 
+    # ---- eager per-call wall time: HIP events around each C-ABI call
+    eager_call = [[[] for _ in p.calls] for p in probs]
+    if not args.no_graph:
+        for _ in range(5):
+            evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                    for _ in p.calls] for p in probs]
+            run_step(probs, evs)
+            torch.cuda.synchronize()
+            for i, p in enumerate(probs):
+                for j in range(len(p.calls)):
+                    eager_call[i][j].append(evs[i][j][0].elapsed_time(evs[i][j][1]) * 1e3)
+
     # ---- timed region 3: every call on its own (graph of cold copies)
     if args.no_graph:  # counter-collection runs: launches only, no timing
-        call_us = [[1.0 for _ in p.calls] for p in probs]
+        call_st = [[{"median": 1.0, "p10": 1.0, "p90": 1.0, "n": 1, "warm": 1.0, "copies": 1}
+                    for _ in p.calls] for p in probs]
+        call_plan = [[1 for _ in p.calls] for p in probs]
     else:
-        call_us = per_call_us(torch, probs, args.copies, stream)
+        call_st, call_plan = per_call_us(torch, probs, args.replays, stream)
+    call_us = [[st["median"] for st in row] for row in call_st]
+    env_after = env_info()
 
     if args.calib_copy:
         # an elementwise kernel that reads CALIB_BYTES and writes CALIB_BYTES
@@ -584,7 +685,13 @@ def main():
         rec = {"op": p.op, "M": p.M, "N": p.N, "K": p.K, "variant": p.variant,
                "splits": p.eff_splits}
         for j, (kind, _, _) in enumerate(p.calls):
-            rec[f"{kind}_us"] = round(call_us[i][j], 3)
+            st = call_st[i][j]
+            rec[f"{kind}_us"] = round(st["median"], 3)
+            rec[f"{kind}_us_p10_p90"] = [round(st["p10"], 3), round(st["p90"], 3)]
+            rec[f"{kind}_warm_us"] = round(st["warm"], 3)
+            rec[f"{kind}_copies"] = st["copies"]
+            if eager_call[i][j]:
+                rec[f"{kind}_eager_us"] = round(sorted(eager_call[i][j])[len(eager_call[i][j]) // 2], 3)
         t_gemm = rec["gemm_us"] * 1e-6
         dt = {"fp8": "fp8", "fp8_grouped": "fp8", "block_fp8": "fp8", "int8": "int8",
               "bf16_bi": "bf16", "mxfp4": "fp4", "w4a16": "bf16"}[p.op]
@@ -601,13 +708,14 @@ def main():
         if p.eff_splits > 1:
             continue  # two kernels per call: not comparable with a kernel trace
         sym = kernel_symbol(qll, p.op, p.variant)
-        k = kernels.setdefault(sym, [0.0, 0, 0.0, 0.0, dt, [], []])
+        k = kernels.setdefault(sym, [0.0, 0, 0.0, 0.0, dt, [], [], []])
         k[0] += t_gemm
         k[1] += 1
         k[2] += p.flops
         k[3] += p.algo_bytes()
         k[5].append(rec["bound"])
         k[6].append(p.eff_splits)
+        k[7].append(rec["gemm_copies"])
 
     dom_sym, dom = max(kernels.items(), key=lambda kv: kv[1][0])
     avg_dur = dom[0] / dom[1]
@@ -633,10 +741,16 @@ def main():
     roof["algorithmic_per_launch"] = (round(dom[2] / dom[1]) if bound == "mfma"
                                       else round(dom[3] / dom[1]))
     roof["algorithmic_bytes_per_launch"] = round(dom[3] / dom[1])
-    roof["timing"] = (f"per call: HIP graph of {args.copies} back-to-back launches on cold "
-                      "buffer copies, timed with HIP events; the dominant kernel is the one "
-                      "with the most time per step among calls that launch a single kernel "
-                      "(no Split-K)")
+    roof["timing"] = ("per call: HIP graph of back-to-back launches, each on its own copy "
+                      "of the call's buffers (>= 1 GiB per replay: cold, from HBM), "
+                      f"{args.replays} replays between HIP events, median per-launch time "
+                      "(kernel time plus the in-graph gap to the next launch); the dominant "
+                      "kernel is the one with the most time per step among calls that "
+                      "launch a single kernel (no Split-K)")
+    # the per-call timing launches of the dominant kernel, in trace order: for
+    # each problem that uses it, (1 + replays) replays of `copies` cold
+    # launches, then (1 + replays) replays of `copies` warm launches
+    roof["per_call_plan"] = {"copies": dom[7], "replays": args.replays}
 
     value = gemm_flops_step / (ms_per_step * 1e-3) / 1e12
     names = {"fp8": "FP8 dynamic per-token sweep: (N,K) in {(4096,2048),(2048,6144)}, "
@@ -689,12 +803,16 @@ def main():
                      "host_us_per_step": round(host_enqueue_s * 1e6 / args.steps, 1)},
         "wall_s_timed": round(wall, 3),
         "device": {"name": props.name, "cus": props.multi_processor_count,
-                   "arch": getattr(props, "gcnArchName", "?")},
+                   "arch": getattr(props, "gcnArchName", "?"), "rocm": env_before["rocm"],
+                   "torch": torch.__version__, "clocks_before": env_before["clocks"],
+                   "clocks_after": env_after["clocks"]},
         "per_shape": per_shape,
     }
     if not args.no_cpu_baseline:
         print("# timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_rows)
+        cb = cpu_baseline(args.workload, args.cpu_rows)
+        cb["gpu_over_cpu"] = round(value / cb["value"], 1) if cb["value"] else None
+        line["cpu_baseline"] = cb
     for r in per_shape:
         print(f"#  {r['op']:9s} M={r['M']:5d} N={r['N']:6d} K={r['K']:5d} {r['variant']:24s} "
               f"S={r['splits']} gemm {r['gemm_us']:8.2f} us {r['tflops']:8.1f} TFLOPS "

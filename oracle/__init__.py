@@ -110,6 +110,8 @@ def _load():
     lib.oracle_quantize_int4.argtypes = [_P, _I64, _I64, _P, _P]
     lib.oracle_gemm_w4a16.restype = None
     lib.oracle_gemm_w4a16.argtypes = [_P, _P, _P, _I64, _I64, _I64, _P, _I64, _P, _P]
+    lib.oracle_set_threads.restype = None
+    lib.oracle_set_threads.argtypes = [ctypes.c_int]
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     _lib = lib
@@ -133,6 +135,11 @@ def _rows(M: int, rows) -> np.ndarray:
 def num_threads() -> int:
     """OpenMP threads the oracle runs with."""
     return int(_load().oracle_num_threads())
+
+
+def set_threads(n: int) -> None:
+    """OpenMP threads for the oracle's loops from now on (timing runs)."""
+    _load().oracle_set_threads(int(n))
 
 
 # --------------------------------------------------------------------------

@@ -656,6 +656,17 @@ void oracle_e4m3_decode_array(const uint8_t* c, int64_t n, double* out)
         out[i] = oracle_e4m3_decode(c[i]);
 }
 
+/* Threads the OpenMP loops use from now on (n >= 1); timing only. */
+void oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    extern void omp_set_num_threads(int);
+    omp_set_num_threads(n > 0 ? n : 1);
+#else
+    (void)n;
+#endif
+}
+
 int oracle_num_threads(void)
 {
     int n = 1;
