@@ -81,6 +81,8 @@ def parse():
                    help="also run a plain device copy of known size (counter calibration)")
     p.add_argument("--no-graph", action="store_true",
                    help="no graphs: eager steps only, no per-call timing (counter runs)")
+    p.add_argument("--vendor", action="store_true",
+                   help="also time the vendor library's GEMM on the same problems (context)")
     p.add_argument("--replays", type=int, default=5,
                    help="timed replays of each per-call timing graph (median, p10/p90)")
     return p.parse_args()
@@ -347,27 +349,60 @@ def per_call_us(torch, probs, replays, stream, max_copies=256):
     return out, plan
 
 
+def vendor_us(torch, probs, replays, stream, max_copies=256):
+    """Context only (not the product, not a target): the vendor library's
+    GEMM on the same problems, timed like per_call_us (cold copies, graph
+    replays, median per launch): torch._scaled_mm (hipBLASLt) with row-wise
+    scales for the FP8 problems, torch.matmul for the bf16 ones; None where
+    the op has no vendor counterpart or the call fails."""
+    out = []
+    for p in probs:
+        t = p.tensors["gemm"][0]
+        if p.op == "fp8":
+            def call(A, B, sa, sb):
+                return torch._scaled_mm(A, B.t(), scale_a=sa.view(-1, 1), scale_b=sb.view(1, -1),
+                                        out_dtype=torch.bfloat16)
+            base = (t["A"], t["B"], t["sa"], t["sb"])
+        elif p.op == "bf16_bi":
+            def call(A, Bt):
+                return torch.matmul(A, Bt)
+            base = (t["A"], t["B"].t().contiguous())  # [K][N], no transposed view
+        else:
+            out.append(None)
+            continue
+        nbytes = sum(x.numel() * x.element_size() for x in base) + 2 * p.M * p.N
+        copies = max(8, min(max_copies, -(-COLD_BYTES // max(1, nbytes))))
+        try:
+            sets = [tuple(x.clone() for x in base) for _ in range(copies)]
+            call(*sets[0])
+            out.append(_stats(_graph_us(torch, call, sets, replays, stream))["median"])
+        except Exception as ex:  # the library may not take this shape
+            print(f"# vendor GEMM failed for M={p.M} N={p.N} K={p.K}: {ex}", file=sys.stderr)
+            out.append(None)
+        sets = None
+        torch.cuda.empty_cache()
+    return out
+
+
 def env_info():
-    """ROCm version and the GPU clocks as the SMI tool reports them (best
-    effort: empty when the tool is missing or slow)."""
-    import subprocess
+    """ROCm version and the GPU's current shader and memory clocks as the
+    driver's sysfs files report them (read, no program is started)."""
+    import glob
     info = {}
     try:
         info["rocm"] = open("/opt/rocm/.info/version").read().strip()
     except OSError:
         info["rocm"] = None
-    clocks = None
-    for cmd in (["amd-smi", "metric", "-g", "0", "-c"], ["rocm-smi", "--showclocks"]):
-        try:
-            r = subprocess.run(cmd, capture_output=True, text=True, timeout=20)
-            if r.returncode == 0 and r.stdout.strip():
-                lines = [l.strip() for l in r.stdout.splitlines()
-                         if any(w in l.lower() for w in ("sclk", "mclk", "gfx_0", "mem_0", "clk"))]
-                clocks = " | ".join(lines)[:600]
-                break
-        except (OSError, subprocess.SubprocessError):
-            continue
-    info["clocks"] = clocks
+    clocks = {}
+    for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+        for name in ("pp_dpm_sclk", "pp_dpm_mclk"):
+            try:
+                cur = [l.strip() for l in open(f"{dev}/{name}") if l.strip().endswith("*")]
+            except OSError:
+                continue
+            if cur:
+                clocks.setdefault(dev.split("/")[4], {})[name[-4:]] = cur[0]
+    info["clocks"] = clocks or None
     return info
 
 
@@ -666,6 +701,7 @@ def main():
     else:
         call_st, call_plan = per_call_us(torch, probs, args.replays, stream)
     call_us = [[st["median"] for st in row] for row in call_st]
+    vend = vendor_us(torch, probs, args.replays, stream) if args.vendor else None
     env_after = env_info()
 
     if args.calib_copy:
@@ -692,6 +728,8 @@ def main():
             rec[f"{kind}_copies"] = st["copies"]
             if eager_call[i][j]:
                 rec[f"{kind}_eager_us"] = round(sorted(eager_call[i][j])[len(eager_call[i][j]) // 2], 3)
+        if vend is not None:
+            rec["vendor_gemm_us"] = round(vend[i], 3) if vend[i] is not None else None
         t_gemm = rec["gemm_us"] * 1e-6
         dt = {"fp8": "fp8", "fp8_grouped": "fp8", "block_fp8": "fp8", "int8": "int8",
               "bf16_bi": "bf16", "mxfp4": "fp4", "w4a16": "bf16"}[p.op]
@@ -808,6 +846,17 @@ def main():
                    "clocks_after": env_after["clocks"]},
         "per_shape": per_shape,
     }
+    if vend is not None:
+        both = [(r["gemm_us"], r["vendor_gemm_us"]) for r in per_shape
+                if r.get("vendor_gemm_us")]
+        line["vendor_context"] = {
+            "library": "torch._scaled_mm (hipBLASLt), row-wise scales" if args.workload != "bi"
+                       else "torch.matmul (hipBLASLt)",
+            "problems": len(both),
+            "sum_gemm_us_ours": round(sum(a for a, _ in both), 2),
+            "sum_gemm_us_vendor": round(sum(b for _, b in both), 2),
+            "note": "context only: the same per-call method (cold copies, graph replays); "
+                    "GEMM only, the quantizer is not part of the vendor call"}
     if not args.no_cpu_baseline:
         print("# timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         cb = cpu_baseline(args.workload, args.cpu_rows)
