@@ -164,8 +164,8 @@ int gemm_bf16_batch_invariant(const void* A, const void* B, void* out,
                               int out_dtype, int64_t M, int64_t N, int64_t K,
                               void* ws, size_t ws_bytes, void* stream);
 
-/* The same five GEMMs with a forced configuration (the sweep and the tests
- * use these).  cfg == NULL behaves like the plain entry point.  For the
+/* The four GEMMs above with a forced configuration (the sweep and the tests
+ * use these; the MXFP4 and W4A16 GEMMs below have _ex forms too).  cfg == NULL behaves like the plain entry point.  For the
  * batch-invariant entry a forced cfg is the caller's responsibility: only
  * the table / heuristic choice is guaranteed M-independent. */
 int gemm_w8a8_int8_ex(const void* A, const void* B, const float* sa,
