@@ -384,6 +384,32 @@ def vendor_us(torch, probs, replays, stream, max_copies=256):
     return out
 
 
+def xcd_fill_bytes(M, N, kbytes, bp, bq, group=4):
+    """Bytes the 8 XCD L2 caches must fetch for one pipelined launch when each
+    XCD reads every A and B row its tiles touch once: the workgroup -> tile
+    map of the kernel (consecutive workgroup ids go to the XCDs in turn; the
+    tiles of one XCD form a contiguous run laid out `group` tile rows at a
+    time) applied to every workgroup."""
+    tp, tq = -(-M // bp), -(-N // bq)
+    T = tp * tq
+    per, rem = T >> 3, T & 7
+    rows = [(set(), set()) for _ in range(8)]
+    for bid in range(T):
+        xcd, loc = bid & 7, bid >> 3
+        t = xcd * (per + 1) + loc if xcd < rem else rem * (per + 1) + (xcd - rem) * per + loc
+        span = group * tq
+        first = (t // span) * group
+        gsize = min(tp - first, group)
+        p, q = first + (t % span) % gsize, (t % span) // gsize
+        rows[xcd][0].add(p)
+        rows[xcd][1].add(q)
+    total = 0
+    for a, b in rows:
+        total += sum(min(bp, M - p * bp) for p in a) * kbytes
+        total += sum(min(bq, N - q * bq) for q in b) * kbytes
+    return total
+
+
 def env_info():
     """ROCm version and the GPU's current shader and memory clocks as the
     driver's sysfs files report them (read, no program is started)."""
@@ -773,6 +799,17 @@ def main():
         if tr:
             roof["traffic"] = round(tr["bytes_per_launch"])
             roof["traffic_detail"] = {k: round(v, 4) for k, v in tr.items()}
+    if dom_sym.startswith("void qll::gemm_pipe_kernel") and "true>" not in dom_sym:
+        # the fetch the XCD structure implies (each XCD's L2 reads the rows
+        # of its tiles once), per launch, plus the bf16 output
+        dp = [p for p in probs if p.eff_splits == 1 and
+              kernel_symbol(qll, p.op, p.variant) == dom_sym]
+        if dp:
+            vv = {v["name"]: v for v in qll.variants(dp[0].op)}[dp[0].variant]
+            kb = {"bf16_bi": 2, "mxfp4": 0.5}.get(dp[0].op, 1)
+            model = [xcd_fill_bytes(p.M, p.N, int(p.K * kb), vv["bp"], vv["bq"]) + 2 * p.M * p.N
+                     for p in dp]
+            roof["traffic_xcd_model"] = round(sum(model) / len(model))
     roof["kernel"] = dom_sym
     roof["launches_per_step"] = dom[1]
     roof["avg_us"] = round(avg_dur * 1e6, 3)

@@ -8,6 +8,8 @@ QLL_FOR_EACH_VARIANT(QLL_INSTANTIATE, qll::OP_BF16, 256, 128)
 QLL_FOR_EACH_SKINNY(QLL_SKINNY_INSTANTIATE, qll::OP_BF16, 2)
 QLL_FOR_EACH_PIPE(QLL_PIPE_INSTANTIATE, qll::OP_BF16)
 QLL_FOR_EACH_PIPE_K256(QLL_PIPE_INSTANTIATE, qll::OP_BF16)
+QLL_FOR_EACH_PIPE_W8(QLL_PIPE_INSTANTIATE, qll::OP_BF16)
+QLL_FOR_EACH_PIPE_W8_K256(QLL_PIPE_INSTANTIATE, qll::OP_BF16)
 template __global__ void qll::splitk_reduce_kernel<qll::OP_BF16>(qll::GemmArgs);
 
 namespace qll {
@@ -19,6 +21,8 @@ extern const Variant kVariantsBf16[] = {
     QLL_FOR_EACH_SKINNY(QLL_SKINNY_ENTRY, OP_BF16, 2)
     QLL_FOR_EACH_PIPE(QLL_PIPE_ENTRY, OP_BF16)
     QLL_FOR_EACH_PIPE_K256(QLL_PIPE_ENTRY, OP_BF16)
+    QLL_FOR_EACH_PIPE_W8(QLL_PIPE_ENTRY, OP_BF16)
+    QLL_FOR_EACH_PIPE_W8_K256(QLL_PIPE_ENTRY, OP_BF16)
 };
 extern const int kNumVariantsBf16 = sizeof(kVariantsBf16) / sizeof(Variant);
 #endif

@@ -7,6 +7,7 @@
 QLL_FOR_EACH_VARIANT(QLL_INSTANTIATE, qll::OP_BLOCK, 256, 128)
 QLL_FOR_EACH_SKINNY(QLL_SKINNY_INSTANTIATE, qll::OP_BLOCK, 1)
 QLL_FOR_EACH_PIPE(QLL_PIPE_INSTANTIATE, qll::OP_BLOCK)
+QLL_FOR_EACH_PIPE_W8(QLL_PIPE_INSTANTIATE, qll::OP_BLOCK)
 template __global__ void qll::splitk_reduce_kernel<qll::OP_BLOCK>(qll::GemmArgs);
 
 namespace qll {
@@ -17,6 +18,7 @@ extern const Variant kVariantsBlock[] = {
     QLL_FOR_EACH_VARIANT(QLL_ENTRY, OP_BLOCK, 256, 128)
     QLL_FOR_EACH_SKINNY(QLL_SKINNY_ENTRY, OP_BLOCK, 1)
     QLL_FOR_EACH_PIPE(QLL_PIPE_ENTRY, OP_BLOCK)
+    QLL_FOR_EACH_PIPE_W8(QLL_PIPE_ENTRY, OP_BLOCK)
 };
 extern const int kNumVariantsBlock = sizeof(kVariantsBlock) / sizeof(Variant);
 #endif

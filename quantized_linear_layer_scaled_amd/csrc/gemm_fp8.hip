@@ -8,7 +8,10 @@ QLL_FOR_EACH_VARIANT(QLL_INSTANTIATE, qll::OP_FP8, 256, 128)
 QLL_FOR_EACH_SKINNY(QLL_SKINNY_INSTANTIATE, qll::OP_FP8, 1)
 QLL_FOR_EACH_PIPE(QLL_PIPE_INSTANTIATE, qll::OP_FP8)
 QLL_FOR_EACH_PIPE_K256(QLL_PIPE_INSTANTIATE, qll::OP_FP8)
+QLL_FOR_EACH_PIPE_W8(QLL_PIPE_INSTANTIATE, qll::OP_FP8)
+QLL_FOR_EACH_PIPE_W8_K256(QLL_PIPE_INSTANTIATE, qll::OP_FP8)
 QLL_FOR_EACH_PIPE(QLL_PIPE_GROUPED_INSTANTIATE, qll::OP_FP8)
+QLL_FOR_EACH_PIPE_W8(QLL_PIPE_GROUPED_INSTANTIATE, qll::OP_FP8)
 template __global__ void qll::splitk_reduce_kernel<qll::OP_FP8>(qll::GemmArgs);
 
 namespace qll {
@@ -20,11 +23,14 @@ extern const Variant kVariantsFp8[] = {
     QLL_FOR_EACH_SKINNY(QLL_SKINNY_ENTRY, OP_FP8, 1)
     QLL_FOR_EACH_PIPE(QLL_PIPE_ENTRY, OP_FP8)
     QLL_FOR_EACH_PIPE_K256(QLL_PIPE_ENTRY, OP_FP8)
+    QLL_FOR_EACH_PIPE_W8(QLL_PIPE_ENTRY, OP_FP8)
+    QLL_FOR_EACH_PIPE_W8_K256(QLL_PIPE_ENTRY, OP_FP8)
 };
 extern const int kNumVariantsFp8 = sizeof(kVariantsFp8) / sizeof(Variant);
 // the grouped (per-expert) GEMM runs the pipelined tiles over experts
 extern const Variant kVariantsFp8Grouped[] = {
     QLL_FOR_EACH_PIPE(QLL_PIPE_GROUPED_ENTRY, OP_FP8)
+    QLL_FOR_EACH_PIPE_W8(QLL_PIPE_GROUPED_ENTRY, OP_FP8)
 };
 extern const int kNumVariantsFp8Grouped = sizeof(kVariantsFp8Grouped) / sizeof(Variant);
 #endif

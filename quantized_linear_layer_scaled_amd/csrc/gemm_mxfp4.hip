@@ -9,6 +9,8 @@
 QLL_FOR_EACH_SKINNY(QLL_SKINNY_INSTANTIATE, qll::OP_MXFP4, 2)
 QLL_FOR_EACH_PIPE(QLL_PIPE_INSTANTIATE, qll::OP_MXFP4)
 QLL_FOR_EACH_PIPE_K256(QLL_PIPE_INSTANTIATE, qll::OP_MXFP4)
+QLL_FOR_EACH_PIPE_W8(QLL_PIPE_INSTANTIATE, qll::OP_MXFP4)
+QLL_FOR_EACH_PIPE_W8_K256(QLL_PIPE_INSTANTIATE, qll::OP_MXFP4)
 template __global__ void qll::splitk_reduce_kernel<qll::OP_MXFP4>(qll::GemmArgs);
 
 namespace qll {
@@ -19,6 +21,8 @@ extern const Variant kVariantsMxfp4[] = {
     QLL_FOR_EACH_SKINNY(QLL_SKINNY_ENTRY, OP_MXFP4, 2)
     QLL_FOR_EACH_PIPE(QLL_PIPE_ENTRY, OP_MXFP4)
     QLL_FOR_EACH_PIPE_K256(QLL_PIPE_ENTRY, OP_MXFP4)
+    QLL_FOR_EACH_PIPE_W8(QLL_PIPE_ENTRY, OP_MXFP4)
+    QLL_FOR_EACH_PIPE_W8_K256(QLL_PIPE_ENTRY, OP_MXFP4)
 };
 extern const int kNumVariantsMxfp4 = sizeof(kVariantsMxfp4) / sizeof(Variant);
 #endif

@@ -103,12 +103,49 @@ constexpr int pipe_scale_bytes()
     return OP == OP_MXFP4 ? ((BP + BQ) * (KSTAGE / 16) + 255) / 256 * 256 : 0;
 }
 
+// LDS of the operand ring (and the Block-FP8 scale ring).
+template <int OP, int BP, int BQ, int KSTAGE, int STAGES>
+constexpr int pipe_ring_bytes()
+{
+    return STAGES * ((BP + BQ) * KSTAGE + pipe_scale_bytes<OP, BP, BQ, KSTAGE>()) +
+           (OP == OP_BLOCK ? (STAGES + 1) * 1280 : 0);
+}
+
+constexpr int pipe_wgs_per_cu(int lds)
+{
+    return 163840 / lds < 4 ? 163840 / lds : 4;
+}
+
+// The per-token x per-channel ops copy the tile's activation and weight
+// scales into LDS at the start, so that the epilogue does not wait a memory
+// round trip for them after the K loop -- unless the extra bytes (whole
+// 64-float units per operand) would lower the number of resident workgroups.
+template <int BP, int BQ>
+constexpr int pipe_prescale_bytes()
+{
+    return ((BP + 63) / 64 + (BQ + 63) / 64) * 256;
+}
+
+template <int OP, int BP, int BQ, int KSTAGE, int STAGES>
+constexpr bool pipe_prescale()
+{
+    return (OP == OP_INT8 || OP == OP_FP8) &&
+           pipe_wgs_per_cu(pipe_ring_bytes<OP, BP, BQ, KSTAGE, STAGES>() +
+                           pipe_prescale_bytes<BP, BQ>()) ==
+               pipe_wgs_per_cu(pipe_ring_bytes<OP, BP, BQ, KSTAGE, STAGES>());
+}
+
+template <int OP, int BP, int BQ, int KSTAGE, int STAGES>
+constexpr int pipe_lds_bytes()
+{
+    return pipe_ring_bytes<OP, BP, BQ, KSTAGE, STAGES>() +
+           (pipe_prescale<OP, BP, BQ, KSTAGE, STAGES>() ? pipe_prescale_bytes<BP, BQ>() : 0);
+}
+
 template <int OP, int BP, int BQ, int WP, int WQ, int KSTAGE, int STAGES>
 constexpr int pipe_waves_per_eu()
 {
-    constexpr int lds = STAGES * ((BP + BQ) * KSTAGE + pipe_scale_bytes<OP, BP, BQ, KSTAGE>()) +
-                        (OP == OP_BLOCK ? (STAGES + 1) * 1280 : 0);
-    constexpr int wgs = 163840 / lds < 4 ? 163840 / lds : 4;
+    constexpr int wgs = pipe_wgs_per_cu(pipe_lds_bytes<OP, BP, BQ, KSTAGE, STAGES>());
     constexpr int w = wgs * WP * WQ / 4;
     return w < 1 ? 1 : (w > 8 ? 8 : w);
 }
@@ -497,6 +534,29 @@ void gemm_pipe_kernel(GemmArgs a)
     using I2 = std::integral_constant<int, 2>;
     using I3 = std::integral_constant<int, 3>;
 
+    // The tile's scales, into LDS ahead of the operand stages (the stage
+    // waits, which count only the younger copies, also cover these): unit u
+    // holds sa of tile rows 64u .. 64u + 63 (u < UA), then sb of the tile
+    // columns; entries past M or N read as zero.
+    constexpr bool SCALED = OP == OP_INT8 || OP == OP_FP8;
+    constexpr bool PRE = pipe_prescale<OP, BP, BQ, KSTAGE, STAGES>();
+    constexpr int UA = (BP + 63) / 64, UB = (BQ + 63) / 64;
+    __shared__ __attribute__((aligned(16))) float lpre[PRE ? (UA + UB) * 64 : 1];
+    const bool scaled = SCALED && a.splits == 1 && a.out_dtype != OUT_INT32;
+    if constexpr (PRE) {
+        if (scaled) {
+            const v4i rsPa = buffer_rsrc(
+                a.sa + p0, (uint32_t)min((uint64_t)(M - p0) * 4, (uint64_t)0x7FFFFFFF));
+            const v4i rsPb = buffer_rsrc(
+                sbp + q0, (uint32_t)min((uint64_t)(N - q0) * 4, (uint64_t)0x7FFFFFFF));
+            for (int u = wave; u < UA + UB; u += WAVES) {
+                const bool ua = u < UA;
+                dma4((uint32_t)((ua ? u : u - UA) * 64 + lane) * 4u, ua ? rsPa : rsPb,
+                     __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lpre + u * 64)));
+            }
+        }
+    }
+
     // prologue: every ring slot receives a stage (0 .. STAGES-1); the
     // fragments of step 0 go to register set 0
     if (0 < nk)
@@ -584,21 +644,27 @@ void gemm_pipe_kernel(GemmArgs a)
     const bool vec_ok = (N & 7) == 0;
     const int c = (lane % CPR) * 8;      // this lane's 8 columns, fixed
     const int n = q0 + wqi * SQ + c;
-    // The per-token and per-channel scales this lane applies, loaded together
-    // before the stores instead of one dependent load per element.
-    constexpr bool SCALED = OP == OP_INT8 || OP == OP_FP8;
-    const bool scaled = SCALED && a.splits == 1 && a.out_dtype != OUT_INT32;
+    // The per-token and per-channel scales this lane applies, read together
+    // before the stores (from the LDS copy when there is one) instead of one
+    // dependent load per element.
     float sbv[8], sav[RP][PASSES];
     if (SCALED && scaled) {
 #pragma unroll
-        for (int t = 0; t < 8; ++t)
-            sbv[t] = n + t < N ? sbp[n + t] : 0.0f;
+        for (int t = 0; t < 8; ++t) {
+            if constexpr (PRE)
+                sbv[t] = lpre[UA * 64 + wqi * SQ + c + t];
+            else
+                sbv[t] = n + t < N ? sbp[n + t] : 0.0f;
+        }
 #pragma unroll
         for (int i = 0; i < RP; ++i)
 #pragma unroll
             for (int pass = 0; pass < PASSES; ++pass) {
-                const int m = p0 + wpi * SP + i * 16 + pass * RPP + lane / CPR;
-                sav[i][pass] = m < M ? a.sa[m] : 0.0f;
+                const int r = wpi * SP + i * 16 + pass * RPP + lane / CPR;
+                if constexpr (PRE)
+                    sav[i][pass] = lpre[r];
+                else
+                    sav[i][pass] = p0 + r < M ? a.sa[p0 + r] : 0.0f;
             }
     }
     // the epilogue value of an accumulator element: (acc * sa[m]) * sb[n]
@@ -726,6 +792,21 @@ hipError_t launch_pipe_grouped(const GemmArgs& a, hipStream_t stream)
     X(OP, 32, 128, 1, 4, 128, 4)           \
     X(OP, 128, 32, 4, 1, 128, 4)
 
+// Tiles over 8 and 16 waves (32x32 to 64x32 per wave): more independent
+// copy streams per CU for grids of about one tile per CU.
+#define QLL_FOR_EACH_PIPE_W8(X, OP)        \
+    X(OP, 128, 128, 2, 4, 128, 3)          \
+    X(OP, 128, 128, 4, 2, 128, 3)          \
+    X(OP, 128, 128, 4, 4, 128, 3)          \
+    X(OP, 128, 128, 4, 4, 128, 4)          \
+    X(OP, 128, 64, 4, 2, 128, 3)           \
+    X(OP, 128, 64, 4, 2, 128, 4)           \
+    X(OP, 64, 128, 2, 4, 128, 3)
+
+#define QLL_FOR_EACH_PIPE_W8_K256(X, OP)   \
+    X(OP, 128, 128, 4, 4, 256, 2)          \
+    X(OP, 128, 64, 4, 2, 256, 2)
+
 // Variants with 256-byte K stages (two fp8 / four bf16 MFMA steps per stage:
 // half the barriers per K); not for Block-FP8, whose stage is one K group.
 #define QLL_FOR_EACH_PIPE_K256(X, OP)      \
@@ -741,8 +822,7 @@ hipError_t launch_pipe_grouped(const GemmArgs& a, hipStream_t stream)
     template __global__ void qll::gemm_pipe_kernel<OP, BP, BQ, WP, WQ, KS, ST, false, true>(qll::GemmArgs);
 #define QLL_PIPE_GROUPED_ENTRY(OP, BP, BQ, WP, WQ, KS, ST)                           \
     {"p" #BP "x" #BQ "_w" #WP "x" #WQ "_k" #KS "_s" #ST, OP, 0, BP, BQ, WP, WQ, KS,    \
-     (ST) * ((BP) + (BQ)) * (KS), &qll::launch_pipe_grouped<OP, BP, BQ, WP, WQ, KS, ST>},
+     qll::pipe_lds_bytes<OP, BP, BQ, KS, ST>(), &qll::launch_pipe_grouped<OP, BP, BQ, WP, WQ, KS, ST>},
 #define QLL_PIPE_ENTRY(OP, BP, BQ, WP, WQ, KS, ST)                                   \
     {"p" #BP "x" #BQ "_w" #WP "x" #WQ "_k" #KS "_s" #ST, OP, 0, BP, BQ, WP, WQ, KS,    \
-     (ST) * (((BP) + (BQ)) * (KS) + qll::pipe_scale_bytes<OP, BP, BQ, KS>()),          \
-     &qll::launch_pipe<OP, BP, BQ, WP, WQ, KS, ST>},
+     qll::pipe_lds_bytes<OP, BP, BQ, KS, ST>(), &qll::launch_pipe<OP, BP, BQ, WP, WQ, KS, ST>},
