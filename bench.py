@@ -463,7 +463,8 @@ def kernel_symbol(qll, op, variant):
                 f"{v['wq']}, {v['kstage']}, {st}, false, {'true' if grouped else 'false'}>"
                 "(qll::GemmArgs)")
     if variant[0] in "kr":
-        return (f"void qll::gemm_skinny_kernel<{opn}, {v['bq'] // 16}, {v['wp']}, "
+        hr = v["bp"] if variant[0] == "k" else 16
+        return (f"void qll::gemm_skinny_kernel<{opn}, {v['bq'] // 16}, {v['wp']}, {hr}, "
                 f"{'true' if variant[0] == 'k' else 'false'}, ")
     return (f"void qll::gemm_tile_kernel<{opn}, {v['swap']}, {v['bp']}, {v['bq']}, "
             f"{v['wp']}, {v['wq']}, {v['kstage']}>(qll::GemmArgs)")

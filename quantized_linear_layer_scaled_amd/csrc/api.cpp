@@ -253,7 +253,7 @@ int load_table(const char* path, const char* arch, int cus_want, Table** out,
             int n = 0;
             const Variant* v = variants(op, &n);
             // a variant whose waves split K must split it into the kBiFold chunks
-            if (std::strncmp(v[vi].name, "k16x", 4) == 0 && v[vi].wp != kBiFold) {
+            if (v[vi].name[0] == 'k' && v[vi].wp != kBiFold) {
                 rc = QLL_ERR_TABLE;
                 *err = "batch-invariant entry splits K across a number of waves other than the fixed chunk count";
                 break;
@@ -310,8 +310,10 @@ qll_cfg heuristic(int op, int64_t M, int64_t N, int64_t K)
     } else if (M <= 64) {
         if (op == OP_BF16)  // eight waves = the kBiFold chunks
             name = M <= 16 ? "k16x16_w8" : (M <= 32 ? "k16x32_w8" : "k16x64_w8");
-        else if (M <= 16)
-            name = (N + 15) / 16 >= 2 * cus ? "k16x16_w8" : "k16x16_w16";
+        else if (M <= 16)  // 8-row workgroups when 16-row ones leave CUs idle
+            name = (N + 15) / 16 >= 2 * cus ? "k16x16_w8"
+                 : (N + 15) / 16 >= cus     ? "k16x16_w16"
+                                            : "k8x16_w16";
         else
             name = M <= 32 ? "k16x32_w8" : "k16x64_w8";
     } else if (op == OP_BLOCK) {

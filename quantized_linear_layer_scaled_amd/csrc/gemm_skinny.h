@@ -13,6 +13,9 @@
 //     range among themselves (KSPLIT), so that even N = 2048 yields W x 128
 //     independent streams; D MFMA steps of loads are issued before their
 //     MFMAs to keep many bytes in flight per wave;
+//   * HR = 8 gives a workgroup 8 weight rows only (the MFMA's other 8 rows
+//     are zero): twice the workgroups, so that a weight matrix of 2048 rows
+//     spreads over all 256 CUs instead of 128;
 //   * adds the W partial tiles through LDS in a fixed order (wave 0, 1, ...,
 //     W-1), so the result is deterministic and needs no second kernel.
 //   Without KSPLIT each wave owns 16 weight rows and the whole K range (used
@@ -26,9 +29,10 @@
 
 namespace qll {
 
-template <int OP, int RQ, int W, bool KSPLIT, int D>
+template <int OP, int RQ, int W, int HR, bool KSPLIT, int D>
 __global__ __launch_bounds__(W * 64) void gemm_skinny_kernel(GemmArgs a)
 {
+    static_assert(HR == 16 || (HR == 8 && KSPLIT), "8-row workgroups split K over waves");
     using Tr = OpTraits<OP>;
     using acc_t = typename Tr::acc_t;
     using elem_t = typename Tr::elem_t;
@@ -39,7 +43,8 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny_kernel(GemmArgs a)
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int N = a.N, M = a.M;
-    const int n0 = KSPLIT ? blockIdx.x * 16 : (blockIdx.x * W + wave) * 16;
+    const int n0 = KSPLIT ? blockIdx.x * HR : (blockIdx.x * W + wave) * 16;
+    const bool wrow = (lane & 15) < HR;  // this lane loads a weight row
     const int m0 = blockIdx.y * (16 * RQ);
     const int z = blockIdx.z;
     const int kbeg = z * a.kchunk;
@@ -102,7 +107,8 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny_kernel(GemmArgs a)
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
                 const bool ok = (s + d < s1) && (off + 16 * j < klim);
-                fb[d][j] = ok ? *(const uint4*)(bp + off + 16 * j) : make_uint4(0, 0, 0, 0);
+                fb[d][j] = ok && wrow ? *(const uint4*)(bp + off + 16 * j)
+                                      : make_uint4(0, 0, 0, 0);
 #pragma unroll
                 for (int r = 0; r < RQ; ++r)
                     fa[d][r][j] = ok ? *(const uint4*)(ap[r] + off + 16 * j)
@@ -111,7 +117,7 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny_kernel(GemmArgs a)
             if constexpr (MX) {
                 // a whole step is in range or not (K is a multiple of 128)
                 const bool ok = (s + d < s1) && (off < klim);
-                xb[d] = ok ? *(const uint32_t*)(sbp + 4 * (s + d)) : 0u;
+                xb[d] = ok && wrow ? *(const uint32_t*)(sbp + 4 * (s + d)) : 0u;
 #pragma unroll
                 for (int r = 0; r < RQ; ++r)
                     xa[d][r] = ok ? *(const uint32_t*)(sap[r] + 4 * (s + d)) : 0u;
@@ -157,7 +163,7 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny_kernel(GemmArgs a)
     auto emit = [&](int r, int ln, int v, elem_t e) __attribute__((always_inline)) {
         const int n = n0 + (ln >> 4) * 4 + v;
         const int m = m0 + r * 16 + (ln & 15);
-        if (m < M && n < N) {
+        if (m < M && n < N && (ln >> 4) * 4 + v < HR) {
             if (a.splits > 1)
                 ((elem_t*)a.ws)[((size_t)z * M + m) * N + n] = e;
             else
@@ -189,14 +195,14 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny_kernel(GemmArgs a)
     }
 }
 
-template <int OP, int RQ, int W, bool KSPLIT, int D>
+template <int OP, int RQ, int W, int HR, bool KSPLIT, int D>
 hipError_t launch_skinny(const GemmArgs& a, hipStream_t stream)
 {
-    const int rows = KSPLIT ? 16 : 16 * W;
+    const int rows = KSPLIT ? HR : 16 * W;
     dim3 grid((a.N + rows - 1) / rows, (a.M + 16 * RQ - 1) / (16 * RQ), a.splits);
     if (grid.y > 65535 || grid.z > 65535)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gemm_skinny_kernel<OP, RQ, W, KSPLIT, D>), grid, dim3(W * 64), 0,
+    hipLaunchKernelGGL((gemm_skinny_kernel<OP, RQ, W, HR, KSPLIT, D>), grid, dim3(W * 64), 0,
                        stream, a);
     return hipGetLastError();
 }
@@ -206,22 +212,25 @@ hipError_t launch_skinny(const GemmArgs& a, hipStream_t stream)
 // Registry entries of the skinny kernel.  Name: "k" (waves split K) or "r"
 // (waves split rows), weight rows x tokens per workgroup, waves (the wp
 // field holds the wave count).
-// X(OP, RQ, TOKENS, W, KSPLIT, D) is applied to every entry.
+// X(OP, RQ, TOKENS, W, KSPLIT, D, HR) is applied to every entry.
 // D is the number of K steps whose loads are in flight together: enough for
 // a wave's whole K chunk at K = 6144 (fp8) for the wave-split kernels, so the
 // weight stream costs one memory round trip.
 #define QLL_FOR_EACH_SKINNY(X, OP, DM)     \
-    X(OP, 1, 16, 8, true, 6 * (DM))        \
-    X(OP, 2, 32, 8, true, 4 * (DM))        \
-    X(OP, 4, 64, 8, true, 4 * (DM))        \
-    X(OP, 1, 16, 16, true, 4 * (DM))       \
-    X(OP, 1, 16, 4, false, 4 * (DM))       \
-    X(OP, 2, 32, 4, false, 4 * (DM))       \
-    X(OP, 4, 64, 4, false, 2 * (DM))
+    X(OP, 1, 16, 8, true, 6 * (DM), 16)    \
+    X(OP, 2, 32, 8, true, 4 * (DM), 16)    \
+    X(OP, 4, 64, 8, true, 4 * (DM), 16)    \
+    X(OP, 1, 16, 16, true, 4 * (DM), 16)   \
+    X(OP, 1, 16, 4, false, 4 * (DM), 16)   \
+    X(OP, 2, 32, 4, false, 4 * (DM), 16)   \
+    X(OP, 4, 64, 4, false, 2 * (DM), 16)   \
+    X(OP, 1, 16, 8, true, 6 * (DM), 8)     \
+    X(OP, 1, 16, 16, true, 4 * (DM), 8)    \
+    X(OP, 2, 32, 8, true, 4 * (DM), 8)
 
-#define QLL_SKINNY_INSTANTIATE(OP, RQ, TOK, W, KS, D) \
-    template __global__ void qll::gemm_skinny_kernel<OP, RQ, W, KS, D>(qll::GemmArgs);
-#define QLL_SKINNY_ENTRY(OP, RQ, TOK, W, KS, D)                                     \
-    {(KS) ? "k16x" #TOK "_w" #W : "r16x" #TOK "_w" #W, OP, 1, (KS) ? 16 : 16 * (W), \
-     TOK, W, 1, 0, (KS) ? (W) * (RQ) * 1024 : 0,                                      \
-     &qll::launch_skinny<OP, RQ, W, KS, D>},
+#define QLL_SKINNY_INSTANTIATE(OP, RQ, TOK, W, KS, D, HR) \
+    template __global__ void qll::gemm_skinny_kernel<OP, RQ, W, HR, KS, D>(qll::GemmArgs);
+#define QLL_SKINNY_ENTRY(OP, RQ, TOK, W, KS, D, HR)                                   \
+    {(KS) ? "k" #HR "x" #TOK "_w" #W : "r16x" #TOK "_w" #W, OP, 1, (KS) ? (HR) : 16 * (W), \
+     TOK, W, 1, 0, (KS) ? (W) * (RQ) * 1024 : 0,                                        \
+     &qll::launch_skinny<OP, RQ, W, HR, KS, D>},

@@ -362,23 +362,73 @@ __global__ __launch_bounds__(WP* WQ * 64) void gemm_w4_tile_kernel(GemmArgs a)
         }
     }
 
-    // lane element (i, j, v): m = p0 + wpi SP + 16 i + 4 (lane >> 4) + v,
-    //                         n = q0 + wqi SQ + 16 j + (lane & 15)
+    // Epilogue through LDS (the activation buffers, free once every wave is
+    // past its last group): each wave writes one 16-row block of its tile at
+    // a time into a private scratch, then every lane emits 8 consecutive
+    // columns of one row as one 16-byte store (two for fp32).  Lane element
+    // (i, j, v) is row 16 i + 4 (lane >> 4) + v, column 16 j + (lane & 15)
+    // of the wave's SP x SQ block.
+    __syncthreads();
+    static_assert(WP * WQ * 16 * SQ * 4 <= 2 * BP * 256, "epilogue scratch must fit");
+    float* scr = (float*)&As[0][0] + wave * 16 * SQ;
+    constexpr int CPR = SQ / 8;    // 8-column groups per row
+    constexpr int RPP = 64 / CPR;  // rows per pass
+    constexpr int PASSES = 16 / RPP;
+    static_assert(SQ % 8 == 0 && 64 % CPR == 0 && 16 % RPP == 0, "epilogue lane map");
+    const bool vec_ok = (N & 7) == 0;
+    const int c = (lane % CPR) * 8;
+    const int n = q0 + wqi * SQ + c;
 #pragma unroll
-    for (int i = 0; i < RP; ++i)
+    for (int i = 0; i < RP; ++i) {
 #pragma unroll
         for (int j = 0; j < RQ; ++j)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int m = p0 + wpi * SP + i * 16 + (lane >> 4) * 4 + v;
-                const int n = q0 + wqi * SQ + j * 16 + (lane & 15);
-                if (m < M && n < N) {
-                    if (a.splits > 1)
-                        ((float*)a.ws)[((size_t)z * M + m) * N + n] = acc[i][j][v];
-                    else
-                        store_one<OP_W4A16>(a, (size_t)m * N + n, acc[i][j][v], m, n);
+            for (int v = 0; v < 4; ++v)
+                scr[((lane >> 4) * 4 + v) * SQ + j * 16 + (lane & 15)] = acc[i][j][v];
+#pragma unroll
+        for (int pass = 0; pass < PASSES; ++pass) {
+            const int r = pass * RPP + lane / CPR;
+            const int m = p0 + wpi * SP + i * 16 + r;
+            float e[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+                e[t] = scr[r * SQ + c + t];
+            if (m >= M)
+                continue;
+            if (a.splits > 1 || a.out_dtype != OUT_BF16) {
+                float* dst = a.splits > 1 ? (float*)a.ws + ((size_t)z * M + m) * N + n
+                                          : (float*)a.out + (size_t)m * N + n;
+                if (vec_ok && n + 7 < N) {
+                    const v4f lo{e[0], e[1], e[2], e[3]}, hi{e[4], e[5], e[6], e[7]};
+                    if (a.splits > 1) {
+                        *(v4f*)dst = lo;
+                        *(v4f*)(dst + 4) = hi;
+                    } else {
+                        __builtin_nontemporal_store(lo, (v4f*)dst);
+                        __builtin_nontemporal_store(hi, (v4f*)(dst + 4));
+                    }
+                } else {
+                    for (int t = 0; t < 8; ++t)
+                        if (n + t < N)
+                            dst[t] = e[t];
+                }
+            } else {
+                uint16_t* dst = (uint16_t*)a.out + (size_t)m * N + n;
+                if (vec_ok && n + 7 < N) {
+                    v4i w;
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        w[t] = (int)((uint32_t)bf16_rne(e[2 * t]) |
+                                     ((uint32_t)bf16_rne(e[2 * t + 1]) << 16));
+                    __builtin_nontemporal_store(w, (v4i*)dst);
+                } else {
+                    for (int t = 0; t < 8; ++t)
+                        if (n + t < N)
+                            dst[t] = bf16_rne(e[t]);
                 }
             }
+        }
+    }
 }
 
 template <int BP, int BQ, int WP, int WQ>

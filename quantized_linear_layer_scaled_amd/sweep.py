@@ -118,9 +118,9 @@ def candidates(qll, op, M, N, K):
     out = []
     for v in qll.variants(op):
         name = v["name"]
-        if op == "bf16_bi" and name.startswith("k16x") and v["wp"] != 8:
+        if op == "bf16_bi" and name[0] == "k" and v["wp"] != 8:
             continue  # its waves split K into other chunks than the fixed eight
-        if name.startswith(("k16x", "r16x")) and M > 128:
+        if name[0] in "kr" and M > 128:
             continue  # skinny kernels hold all tokens of a tile in registers
         if name[0] in "np" and M <= 8 and v["bp"] >= 64 and not v["swap"]:
             continue  # 64+ token rows per tile for a handful of tokens

@@ -145,7 +145,7 @@ def test_mxfp4_registry_and_dispatch(qll):
     # tiled fallback
     assert "k16x16_w8" in names and "p128x128_w2x2_k128_s2" in names
     assert not any(n.startswith(("n", "s")) for n in names)
-    assert qll.select("mxfp4", 8, 4096, 4096)[0].startswith("k16x")
+    assert qll.select("mxfp4", 8, 4096, 4096)[0][0] == "k"
     assert qll.select("mxfp4", 2048, 4096, 4096)[0].startswith("p")
     # K bytes are K / 2: a 2-way split of K = 2048 (1024 bytes) is allowed,
     # a 4-way one rounds to 512-byte pieces, i.e. 2
@@ -287,7 +287,7 @@ def test_shipped_table_is_valid_for_mi355x(qll):
 def test_table_rules(qll, tmp_path):
     fp8 = qll.variants("fp8")[0]["name"]
     bi = [v["name"] for v in qll.variants("bf16_bi")]
-    single = [n for n in bi if not n.startswith("k16x")]
+    single = [n for n in bi if n[0] != "k"]
     head = "# test\ndevice gfx950 256\n"
     ok = write(tmp_path, head + f"fp8 4096 2048 1 {fp8} 2\nfp8 4096 2048 2 {fp8} 1\n")
     assert qll.table_validate(ok, "gfx950", 256) == (0, "")
@@ -308,8 +308,8 @@ def test_table_rules(qll, tmp_path):
     assert rc == 6 and "split" in why
     # ... and no variant whose waves split K into other than the eight chunks
     vs = qll.variants("bf16_bi")
-    k8 = [v["name"] for v in vs if v["name"].startswith("k16x") and v["wp"] == 8][0]
-    k16 = [v["name"] for v in vs if v["name"].startswith("k16x") and v["wp"] == 16][0]
+    k8 = [v["name"] for v in vs if v["name"][0] == "k" and v["wp"] == 8][0]
+    k16 = [v["name"] for v in vs if v["name"][0] == "k" and v["wp"] == 16][0]
     rc, why = qll.table_validate(write(tmp_path, head + f"bf16_bi 2048 2048 1 {k16} 1\n"),
                                  "gfx950", 256)
     assert rc == 6 and "waves" in why

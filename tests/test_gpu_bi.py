@@ -90,4 +90,4 @@ def test_selected_configs_keep_the_k_split(qll):
         eff = {qll.effective_splits("bf16_bi", K, s) for _, s in picks}
         assert len(eff) == 1, (N, K, eff)
         vs = {v["name"]: v for v in qll.variants("bf16_bi")}
-        assert not any(n.startswith("k16x") and vs[n]["wp"] != 8 for n, _ in picks), (N, K)
+        assert not any(n[0] == "k" and vs[n]["wp"] != 8 for n, _ in picks), (N, K)

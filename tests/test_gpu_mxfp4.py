@@ -150,7 +150,7 @@ def test_gemm_sequential_variants_agree_bitwise(qll, mx_cases):
                           cfg=("p128x128_w2x2_k128_s2", 1)).cpu().numpy()
     diff = []
     for name in names(qll):
-        if name.startswith("k16x"):
+        if name[0] == "k":
             continue
         y = qll.gemm_mxfp4(dA, dB, dsa, dsb, out_dtype="fp32", cfg=(name, 1)).cpu().numpy()
         if not np.array_equal(y.view(np.uint32), base.view(np.uint32)):
