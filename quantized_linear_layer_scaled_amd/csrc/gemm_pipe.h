@@ -241,6 +241,8 @@ void gemm_pipe_kernel(GemmArgs a)
     constexpr int LPS = MX ? (NSC + WAVES - 1) / WAVES : 0;
     constexpr int LPT = LPT0 + (BLK ? 2 : 0) + LPS;  // + the scale loads
     constexpr int STAGE_BYTES = ROWS * KSTAGE + SC_REGION;
+    // 256x256 tiles stream their fragments (see the K loop)
+    constexpr bool STREAM = BP * BQ >= 256 * 256;
     static_assert(ROWS * NC % THREADS == 0, "stage must split evenly over the waves");
     static_assert((NC & (NC - 1)) == 0 && KSTAGE % KSTEP == 0, "bad K stage");
     static_assert(STAGES >= 2 && (STAGES - 1) * LPT < 64, "bad pipeline depth");
@@ -567,76 +569,139 @@ void gemm_pipe_kernel(GemmArgs a)
         }
     }
 
-    // prologue: every ring slot receives a stage (0 .. STAGES-1); the
-    // fragments of step 0 go to register set 0
-    if (0 < nk)
-        issue(0, slot(I0{}));
-    if (1 < nk)
-        issue(1, slot(I1{}));
-    if constexpr (STAGES >= 3)
-        if (2 < nk)
-            issue(2, slot(I2{}));
-    if constexpr (STAGES >= 4)
-        if (3 < nk)
-            issue(3, slot(I3{}));
-    if (0 < nk) {
-        wait_stage(min(STAGES - 1, nk - 1));
-        load_step(slot(I0{}), 0, fr[0]);
-    }
+    if constexpr (!STREAM) {
+        // prologue: every ring slot receives a stage (0 .. STAGES-1); the
+        // fragments of step 0 go to register set 0
+        if (0 < nk)
+            issue(0, slot(I0{}));
+        if (1 < nk)
+            issue(1, slot(I1{}));
+        if constexpr (STAGES >= 3)
+            if (2 < nk)
+                issue(2, slot(I2{}));
+        if constexpr (STAGES >= 4)
+            if (3 < nk)
+                issue(3, slot(I3{}));
+        if (0 < nk) {
+            wait_stage(min(STAGES - 1, nk - 1));
+            load_step(slot(I0{}), 0, fr[0]);
+        }
 
-    // stage kt (J = kt mod U, U a multiple of STAGES with U * NSTEP even, so
-    // that ring slot and register set are compile-time constants): the steps
-    // of the stage run one after the other, each reading the next step's
-    // fragments first.  Before the last step, once stage kt+1 has landed for
-    // every wave and every wave holds its stage-kt fragments in registers,
-    // slot kt % STAGES takes stage kt + STAGES and the first step of stage
-    // kt+1 is read from the next slot.
-    constexpr int U = (NSTEP % 2 == 0 || STAGES % 2 == 0) ? STAGES : 2 * STAGES;
-    auto stage = [&](auto J, int kt) __attribute__((always_inline)) {
-        constexpr int j = decltype(J)::value;
-        constexpr int cs = j % STAGES, ns = (j + 1) % STAGES;
-        if constexpr (FOLD)
-            fold.before(kt * NSTEP, acc);  // chunk boundaries fall on stage starts
+        // stage kt (J = kt mod U, U a multiple of STAGES with U * NSTEP even, so
+        // that ring slot and register set are compile-time constants): the steps
+        // of the stage run one after the other, each reading the next step's
+        // fragments first.  Before the last step, once stage kt+1 has landed for
+        // every wave and every wave holds its stage-kt fragments in registers,
+        // slot kt % STAGES takes stage kt + STAGES and the first step of stage
+        // kt+1 is read from the next slot.
+        constexpr int U = (NSTEP % 2 == 0 || STAGES % 2 == 0) ? STAGES : 2 * STAGES;
+        auto stage = [&](auto J, int kt) __attribute__((always_inline)) {
+            constexpr int j = decltype(J)::value;
+            constexpr int cs = j % STAGES, ns = (j + 1) % STAGES;
+            if constexpr (FOLD)
+                fold.before(kt * NSTEP, acc);  // chunk boundaries fall on stage starts
+    #pragma unroll
+            for (int ks = 0; ks < NSTEP; ++ks) {
+                const int cp = (j * NSTEP + ks) & 1;
+                if (ks + 1 < NSTEP) {
+                    load_step(slot(std::integral_constant<int, cs>{}), ks + 1, fr[cp ^ 1]);
+                } else {
+                    // the fragments of this step are in registers on every path
+                    // from here on, so the compiler never holds the MFMAs for the
+                    // reads issued below
+                    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+                    if (kt + 1 < nk) {
+                        wait_stage(min(STAGES - 2, nk - 2 - kt));
+                        if (kt + STAGES < nk)
+                            issue(kt + STAGES, slot(std::integral_constant<int, cs>{}));
+                        load_step(slot(std::integral_constant<int, ns>{}), 0, fr[cp ^ 1]);
+                    }
+                }
+                compute_step(fr[cp], kt, ks);
+            }
+        };
+        for (int kt = 0; kt < nk; kt += U) {
+            stage(I0{}, kt);
+            if (kt + 1 < nk)
+                stage(I1{}, kt + 1);
+            if constexpr (U >= 3) {
+                if (kt + 2 < nk)
+                    stage(I2{}, kt + 2);
+            }
+            if constexpr (U >= 4) {
+                if (kt + 3 < nk)
+                    stage(I3{}, kt + 3);
+            }
+            if constexpr (U >= 6) {
+                if (kt + 4 < nk)
+                    stage(std::integral_constant<int, 4>{}, kt + 4);
+                if (kt + 5 < nk)
+                    stage(std::integral_constant<int, 5>{}, kt + 5);
+            }
+        }
+        static_assert(U <= 6 && U != 5, "unroll factor");
+    } else {
+        // Streamed fragments, for tiles whose two register sets of a whole K
+        // step would not fit next to the accumulators: one stage in flight
+        // ahead of the one being computed; per K step each wave reads its RQ
+        // B fragments, then its A fragments one row block at a time, each
+        // read issued before the MFMAs of the previous row block.  The other
+        // wave on the SIMD runs its MFMAs while one waits for its reads.
+        static_assert(STAGES == 2 && !BLK && !MX, "streamed tiles: two stages, no block scales");
+        if (0 < nk)
+            issue(0, slot(I0{}));
+        auto sstage = [&](auto J, int kt) __attribute__((always_inline)) {
+            constexpr int cs = decltype(J)::value, ns = cs ^ 1;
+            // stage kt has landed for every wave, and every wave is done
+            // with stage kt - 1: its slot takes stage kt + 1
+            wait_vm_barrier<0>();
+            if (kt + 1 < nk)
+                issue(kt + 1, slot(std::integral_constant<int, ns>{}));
+            if constexpr (FOLD)
+                fold.before(kt * NSTEP, acc);
+            const uint8_t* sp = slot(std::integral_constant<int, cs>{});
+            const uint8_t* sq = sp + BP * KSTAGE;
 #pragma unroll
-        for (int ks = 0; ks < NSTEP; ++ks) {
-            const int cp = (j * NSTEP + ks) & 1;
-            if (ks + 1 < NSTEP) {
-                load_step(slot(std::integral_constant<int, cs>{}), ks + 1, fr[cp ^ 1]);
-            } else {
-                // the fragments of this step are in registers on every path
-                // from here on, so the compiler never holds the MFMAs for the
-                // reads issued below
-                __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-                if (kt + 1 < nk) {
-                    wait_stage(min(STAGES - 2, nk - 2 - kt));
-                    if (kt + STAGES < nk)
-                        issue(kt + STAGES, slot(std::integral_constant<int, cs>{}));
-                    load_step(slot(std::integral_constant<int, ns>{}), 0, fr[cp ^ 1]);
+            for (int ks = 0; ks < NSTEP; ++ks) {
+                if (kbeg + kt * KSTAGE + ks * KSTEP >= kend)
+                    continue;  // steps past the K range (zero-filled)
+                const int off = ks * KSTEP + (lane >> 4) * KB;
+                uint4 bv[RQ][KB / 16];
+#pragma unroll
+                for (int i = 0; i < RQ; ++i) {
+                    const int row = wqi * SQ + i * 16 + (lane & 15);
+#pragma unroll
+                    for (int j = 0; j < KB / 16; ++j) {
+                        const int ch = (off >> 4) + j;
+                        bv[i][j] = *(const uint4*)(sq + row * KSTAGE + ((ch ^ swz<NC>(row)) << 4));
+                    }
+                }
+                uint4 av[2][KB / 16];
+                auto read_a = [&](int i, uint4* dst) __attribute__((always_inline)) {
+                    const int row = wpi * SP + i * 16 + (lane & 15);
+#pragma unroll
+                    for (int j = 0; j < KB / 16; ++j) {
+                        const int ch = (off >> 4) + j;
+                        dst[j] = *(const uint4*)(sp + row * KSTAGE + ((ch ^ swz<NC>(row)) << 4));
+                    }
+                };
+                read_a(0, av[0]);
+#pragma unroll
+                for (int i = 0; i < RP; ++i) {
+                    if (i + 1 < RP)
+                        read_a(i + 1, av[(i + 1) & 1]);
+#pragma unroll
+                    for (int j = 0; j < RQ; ++j)
+                        acc[i][j] = mfma_step<OP>(av[i & 1], bv[j], acc[i][j]);
                 }
             }
-            compute_step(fr[cp], kt, ks);
-        }
-    };
-    for (int kt = 0; kt < nk; kt += U) {
-        stage(I0{}, kt);
-        if (kt + 1 < nk)
-            stage(I1{}, kt + 1);
-        if constexpr (U >= 3) {
-            if (kt + 2 < nk)
-                stage(I2{}, kt + 2);
-        }
-        if constexpr (U >= 4) {
-            if (kt + 3 < nk)
-                stage(I3{}, kt + 3);
-        }
-        if constexpr (U >= 6) {
-            if (kt + 4 < nk)
-                stage(std::integral_constant<int, 4>{}, kt + 4);
-            if (kt + 5 < nk)
-                stage(std::integral_constant<int, 5>{}, kt + 5);
+        };
+        for (int kt = 0; kt < nk; kt += 2) {
+            sstage(I0{}, kt);
+            if (kt + 1 < nk)
+                sstage(I1{}, kt + 1);
         }
     }
-    static_assert(U <= 6 && U != 5, "unroll factor");
 
     if constexpr (FOLD)
         fold.finish(acc);
@@ -825,6 +890,11 @@ hipError_t launch_pipe_grouped(const GemmArgs& a, hipStream_t stream)
 #define QLL_FOR_EACH_PIPE_W8_K256(X, OP)   \
     X(OP, 128, 128, 4, 4, 256, 2)          \
     X(OP, 128, 64, 4, 2, 256, 2)
+
+// 256x256 tiles over 8 waves of 128x64, fragments streamed: half the
+// operand bytes per flop of a 128x256 tile, for grids of many tiles per CU.
+#define QLL_FOR_EACH_PIPE_BIG(X, OP)       \
+    X(OP, 256, 256, 2, 4, 128, 2)
 
 // Variants with 256-byte K stages (two fp8 / four bf16 MFMA steps per stage:
 // half the barriers per K); not for Block-FP8, whose stage is one K group.
