@@ -456,6 +456,10 @@ def kernel_symbol(qll, op, variant):
         if variant[0] == "t":
             return (f"void qll::gemm_w4_tile_kernel<{v['bp']}, {v['bq']}, {v['wp']}, "
                     f"{v['wq']}>(qll::GemmArgs)")
+        if variant[0] == "p":
+            st = variant.rsplit("_s", 1)[1]
+            return (f"void qll::gemm_w4_pipe_kernel<{v['bp']}, {v['bq']}, {v['wp']}, "
+                    f"{v['wq']}, {st}>(qll::GemmArgs)")
         return f"void qll::gemm_w4_skinny_kernel<{v['bq'] // 16}, {v['wp']}, "
     if variant[0] == "p":
         st = variant.rsplit("_s", 1)[1]

@@ -298,11 +298,12 @@ qll_cfg heuristic(int op, int64_t M, int64_t N, int64_t K)
     const char* name;
     bool exact = true;
     if (op == OP_W4A16) {
-        // few tokens: the wave-split decode kernel; more: LDS tiles (the
-        // fastest variants of the on-device sweep of the two sweep shapes)
+        // few tokens: the wave-split decode kernel; more: the pipelined
+        // tiles (the fastest variants of the on-device sweep of the two
+        // sweep shapes)
         name = M <= 16 ? "k16x16_w16"
              : M <= 64 ? "k16x32_w8"
-             : M <= 512 ? "t64x64_w2x2" : "t128x64_w2x2";
+             : M <= 512 ? "p64x64_w2x2_s3" : "p128x128_w2x4_s3";
     } else if (op == OP_MXFP4 && M > 32) {
         // 256-byte K stages (four MFMA steps of 128 elements per barrier):
         // fastest from 64 tokens up on the sweep shapes

@@ -24,7 +24,7 @@
 // feeds elements (l >> 4) * 32 + 8 t .. + 7 in step t = 0..3; the activation
 // fragments follow the same map, so every product still pairs a[m][k] with
 // q[n][k] and the group sum is unchanged.
-#include "gemm_tile.h"
+#include "gemm_pipe.h"
 
 namespace qll {
 
@@ -443,6 +443,287 @@ hipError_t launch_w4_tile(const GemmArgs& a, hipStream_t stream)
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- pipelined
+
+// The copy pipeline of the 8-bit GEMMs (gemm_pipe.h) applied to W4A16: one
+// 128-element group per stage.  The activations (BP rows x 256 bytes) and
+// the codes (BQ rows x 64 bytes) go from global memory straight into a ring
+// of S LDS slots with buffer_load_dwordx4 ... lds, the group's BQ weight
+// scales with buffer_load_dword ... lds beside them; S - 1 groups are in
+// flight ahead of the one computed, with one wait and one barrier per
+// group.  As in gemm_pipe.h, the 16-byte chunks of a staged row are
+// XOR-swizzled on the global side, and rows past M or N and offsets outside
+// the operand read as zeros.  Per group each wave reads its code runs and
+// scales once and the activation fragments of each step while the previous
+// step's MFMAs run; the products are summed per group exactly as in the
+// tiled kernel above (bitwise the same results).
+template <int BP, int BQ>
+constexpr int w4_pipe_stage_bytes()
+{
+    return BP * 256 + BQ * 64;
+}
+
+template <int BP, int BQ, int WP, int WQ, int S>
+constexpr int w4_pipe_waves_per_eu()
+{
+    constexpr int lds = S * (w4_pipe_stage_bytes<BP, BQ>() + BQ * 4);
+    constexpr int wgs = 163840 / lds < 4 ? 163840 / lds : 4;
+    constexpr int w = wgs * WP * WQ / 4;
+    return w < 1 ? 1 : (w > 8 ? 8 : w);
+}
+
+template <int BP, int BQ, int WP, int WQ, int S>
+__global__ __launch_bounds__(WP* WQ * 64)
+__attribute__((amdgpu_waves_per_eu(w4_pipe_waves_per_eu<BP, BQ, WP, WQ, S>())))
+void gemm_w4_pipe_kernel(GemmArgs a)
+{
+    constexpr int WAVES = WP * WQ;
+    constexpr int SP = BP / WP, SQ = BQ / WQ;
+    constexpr int RP = SP / 16, RQ = SQ / 16;
+    constexpr int AB = BP * 256, STAGE = w4_pipe_stage_bytes<BP, BQ>();
+    constexpr int IA = AB / 1024, IB = BQ * 64 / 1024;  // copy instructions per stage
+    constexpr int LPT0 = (IA + IB) / WAVES;
+    constexpr int NSC = BQ / 64;                        // scale copy units per stage
+    constexpr int LPS = (NSC + WAVES - 1) / WAVES;      // (units repeat: equal values)
+    constexpr int LPT = LPT0 + LPS;
+    static_assert(BP % 4 == 0 && BQ % 64 == 0 && (IA + IB) % WAVES == 0,
+                  "a stage must split into whole copy instructions per wave");
+    static_assert(S >= 2 && S <= 4 && (S - 1) * LPT < 64, "bad pipeline depth");
+
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[S * STAGE];
+    __shared__ __attribute__((aligned(16))) float lsc[S][BQ];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wpi = wave % WP, wqi = wave / WP;
+    const int M = a.M, N = a.N, K = a.K;
+    const int G = K / 128;
+    int tile_p, tile_q;
+    xcd_tile(blockIdx.x, (M + BP - 1) / BP, (N + BQ - 1) / BQ, 4, tile_p, tile_q);
+    const int p0 = tile_p * BP, q0 = tile_q * BQ;
+    const int z = blockIdx.y;
+    int g0, g1;
+    piece_groups(a, z, g0, g1);
+    const int nk = max(g1 - g0, 0);
+    const int kq = lane >> 4;
+
+    // the tile's activation rows, code rows and scale rows as buffers ending
+    // at the last row of each matrix
+    const uint32_t lda = (uint32_t)K * 2u, ldb = (uint32_t)K / 2u;
+    const v4i rsA = buffer_rsrc((const uint16_t*)a.A + (size_t)p0 * K,
+                                (uint32_t)min((uint64_t)(M - p0) * lda, (uint64_t)0x7FFFFFFF));
+    const v4i rsB = buffer_rsrc((const uint8_t*)a.B + (size_t)q0 * ldb,
+                                (uint32_t)min((uint64_t)(N - q0) * ldb, (uint64_t)0x7FFFFFFF));
+    const v4i rsS = buffer_rsrc(a.sb + (size_t)q0 * G,
+                                (uint32_t)min((uint64_t)(N - q0) * G * 4, (uint64_t)0x7FFFFFFF));
+
+    // copy instruction i of this wave: stage instruction ii = i * WAVES + wave
+    // (the first IA fill the activation part, the rest the code part); lane
+    // chunk L = 64 (instruction within its part) + lane holds the logical
+    // chunk (L mod NC) ^ swz(row) of row L / NC
+    uint32_t voff[LPT0];
+#pragma unroll
+    for (int i = 0; i < LPT0; ++i) {
+        const int ii = i * WAVES + wave;
+        if (ii < IA) {
+            const int L = ii * 64 + lane, row = L / 16, c = L % 16;
+            voff[i] = (uint32_t)row * lda + (uint32_t)((c ^ swz<16>(row)) << 4);
+        } else {
+            const int L = (ii - IA) * 64 + lane, row = L / 4, c = L % 4;
+            voff[i] = (uint32_t)row * ldb + (uint32_t)((c ^ swz<4>(row)) << 4);
+        }
+    }
+    auto issue = [&](int kt, int slot) __attribute__((always_inline)) {
+        const int g = g0 + kt;
+        uint8_t* buf = lds + slot * STAGE;
+#pragma unroll
+        for (int i = 0; i < LPT0; ++i) {
+            const int ii = i * WAVES + wave;
+            const bool pa = ii < IA;  // wave-uniform
+            dma16(voff[i] + (uint32_t)g * (pa ? 256u : 64u), pa ? rsA : rsB,
+                  __builtin_amdgcn_readfirstlane(
+                      (uint32_t)(uintptr_t)(buf + (pa ? ii * 1024 : AB + (ii - IA) * 1024))));
+        }
+#pragma unroll
+        for (int i = 0; i < LPS; ++i) {
+            const int u = (i * WAVES + wave) % NSC;
+            dma4((uint32_t)((u * 64 + lane) * G + g) * 4u, rsS,
+                 __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(&lsc[slot][u * 64])));
+        }
+    };
+
+    v4f acc[RP][RQ];
+#pragma unroll
+    for (int i = 0; i < RP; ++i)
+#pragma unroll
+        for (int j = 0; j < RQ; ++j)
+            acc[i][j] = v4f{0, 0, 0, 0};
+
+    // one group from ring slot J: a fresh partial over its four MFMA steps,
+    // promoted with the column's scale
+    auto compute = [&](auto J) __attribute__((always_inline)) {
+        constexpr int slot = decltype(J)::value;
+        const uint8_t* sa = lds + slot * STAGE;
+        const uint8_t* sb = sa + AB;
+        uint4 wq[RQ];
+        float sc[RQ];
+#pragma unroll
+        for (int j = 0; j < RQ; ++j) {
+            const int row = wqi * SQ + j * 16 + (lane & 15);
+            wq[j] = *(const uint4*)(sb + row * 64 + ((kq ^ swz<4>(row)) << 4));
+            sc[j] = lsc[slot][row];
+        }
+        uint4 af[2][RP];
+        auto read_a = [&](int t, uint4* dst) __attribute__((always_inline)) {
+#pragma unroll
+            for (int i = 0; i < RP; ++i) {
+                const int row = wpi * SP + i * 16 + (lane & 15);
+                const int ch = kq * 4 + t;
+                dst[i] = *(const uint4*)(sa + row * 256 + ((ch ^ swz<16>(row)) << 4));
+            }
+        };
+        v4f pp[RP][RQ];
+#pragma unroll
+        for (int i = 0; i < RP; ++i)
+#pragma unroll
+            for (int j = 0; j < RQ; ++j)
+                pp[i][j] = v4f{0, 0, 0, 0};
+        read_a(0, af[0]);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            if (t + 1 < 4)
+                read_a(t + 1, af[(t + 1) & 1]);
+            uint4 bf[RQ];
+#pragma unroll
+            for (int j = 0; j < RQ; ++j) {
+                const uint32_t wd = t == 0 ? wq[j].x : t == 1 ? wq[j].y : t == 2 ? wq[j].z : wq[j].w;
+                bf[j] = int4x8_to_bf16(wd);
+            }
+#pragma unroll
+            for (int i = 0; i < RP; ++i)
+#pragma unroll
+                for (int j = 0; j < RQ; ++j)
+                    pp[i][j] = mfma_bf16(af[t & 1][i], bf[j], pp[i][j]);
+        }
+#pragma unroll
+        for (int i = 0; i < RP; ++i)
+#pragma unroll
+            for (int j = 0; j < RQ; ++j)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    acc[i][j][v] = __builtin_fmaf(sc[j], pp[i][j][v], acc[i][j][v]);
+    };
+
+    // prologue: groups 0 .. S-2 in flight; at group kt, once it has landed
+    // for every wave and every wave is done with group kt - 1, that group's
+    // slot takes group kt + S - 1
+#pragma unroll
+    for (int kt = 0; kt < S - 1; ++kt)
+        if (kt < nk)
+            issue(kt, kt);
+    auto group = [&](auto J, int kt) __attribute__((always_inline)) {
+        constexpr int slot = decltype(J)::value;
+        const int younger = min(S - 2, nk - 1 - kt);  // later groups in flight
+        if (S >= 4 && younger >= 2)
+            wait_vm_barrier<(S >= 4 ? 2 : 0) * LPT>();
+        else if (S >= 3 && younger >= 1)
+            wait_vm_barrier<(S >= 3 ? 1 : 0) * LPT>();
+        else
+            wait_vm_barrier<0>();
+        if (kt + S - 1 < nk)
+            issue(kt + S - 1, (slot + S - 1) % S);
+        compute(J);
+    };
+    for (int kt = 0; kt < nk; kt += S) {
+        group(std::integral_constant<int, 0>{}, kt);
+        if (kt + 1 < nk)
+            group(std::integral_constant<int, 1>{}, kt + 1);
+        if constexpr (S >= 3)
+            if (kt + 2 < nk)
+                group(std::integral_constant<int, (S >= 3 ? 2 : 0)>{}, kt + 2);
+        if constexpr (S >= 4)
+            if (kt + 3 < nk)
+                group(std::integral_constant<int, (S >= 4 ? 3 : 0)>{}, kt + 3);
+    }
+
+    // Epilogue through LDS, as in the tiled kernel: each wave writes one
+    // 16-row block of its tile at a time into a private scratch, then every
+    // lane emits 8 consecutive columns of one row.
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");  // slots are free
+    static_assert(WAVES * 16 * SQ * 4 <= S * STAGE, "epilogue scratch must fit");
+    float* scr = (float*)lds + wave * 16 * SQ;
+    constexpr int CPR = SQ / 8;
+    constexpr int RPP = 64 / CPR;
+    constexpr int PASSES = 16 / RPP;
+    static_assert(SQ % 8 == 0 && 64 % CPR == 0 && 16 % RPP == 0, "epilogue lane map");
+    const bool vec_ok = (N & 7) == 0;
+    const int c = (lane % CPR) * 8;
+    const int n = q0 + wqi * SQ + c;
+#pragma unroll
+    for (int i = 0; i < RP; ++i) {
+#pragma unroll
+        for (int j = 0; j < RQ; ++j)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                scr[((lane >> 4) * 4 + v) * SQ + j * 16 + (lane & 15)] = acc[i][j][v];
+#pragma unroll
+        for (int pass = 0; pass < PASSES; ++pass) {
+            const int r = pass * RPP + lane / CPR;
+            const int m = p0 + wpi * SP + i * 16 + r;
+            float e[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+                e[t] = scr[r * SQ + c + t];
+            if (m >= M)
+                continue;
+            if (a.splits > 1 || a.out_dtype != OUT_BF16) {
+                float* dst = a.splits > 1 ? (float*)a.ws + ((size_t)z * M + m) * N + n
+                                          : (float*)a.out + (size_t)m * N + n;
+                if (vec_ok && n + 7 < N) {
+                    const v4f lo{e[0], e[1], e[2], e[3]}, hi{e[4], e[5], e[6], e[7]};
+                    if (a.splits > 1) {
+                        *(v4f*)dst = lo;
+                        *(v4f*)(dst + 4) = hi;
+                    } else {
+                        __builtin_nontemporal_store(lo, (v4f*)dst);
+                        __builtin_nontemporal_store(hi, (v4f*)(dst + 4));
+                    }
+                } else {
+                    for (int t = 0; t < 8; ++t)
+                        if (n + t < N)
+                            dst[t] = e[t];
+                }
+            } else {
+                uint16_t* dst = (uint16_t*)a.out + (size_t)m * N + n;
+                if (vec_ok && n + 7 < N) {
+                    v4i w;
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        w[t] = (int)((uint32_t)bf16_rne(e[2 * t]) |
+                                     ((uint32_t)bf16_rne(e[2 * t + 1]) << 16));
+                    __builtin_nontemporal_store(w, (v4i*)dst);
+                } else {
+                    for (int t = 0; t < 8; ++t)
+                        if (n + t < N)
+                            dst[t] = bf16_rne(e[t]);
+                }
+            }
+        }
+    }
+}
+
+template <int BP, int BQ, int WP, int WQ, int S>
+hipError_t launch_w4_pipe(const GemmArgs& a, hipStream_t stream)
+{
+    const long tiles = (long)((a.M + BP - 1) / BP) * ((a.N + BQ - 1) / BQ);
+    if (tiles > 0x7FFFFFFFL || (long)BP * a.K * 2 > 0x7FFFFFFFL)
+        return hipErrorInvalidValue;  // 32-bit buffer offsets within a tile
+    hipLaunchKernelGGL((gemm_w4_pipe_kernel<BP, BQ, WP, WQ, S>),
+                       dim3((unsigned)tiles, (unsigned)a.splits), dim3(WP * WQ * 64), 0, stream,
+                       a);
+    return hipGetLastError();
+}
+
 // the kernels the registry launches (needed by the device pass)
 template __global__ void gemm_w4_skinny_kernel<1, 8, 2>(GemmArgs);
 template __global__ void gemm_w4_skinny_kernel<1, 4, 4>(GemmArgs);
@@ -454,6 +735,25 @@ template __global__ void gemm_w4_tile_kernel<128, 64, 2, 2>(GemmArgs);
 template __global__ void gemm_w4_tile_kernel<64, 128, 2, 2>(GemmArgs);
 template __global__ void gemm_w4_tile_kernel<128, 128, 2, 2>(GemmArgs);
 template __global__ void gemm_w4_tile_kernel<256, 64, 4, 1>(GemmArgs);
+
+// X(BP, BQ, WP, WQ, S) for every pipelined W4A16 variant
+#define QLL_FOR_EACH_W4_PIPE(X) \
+    X(64, 64, 2, 2, 2)          \
+    X(64, 64, 2, 2, 3)          \
+    X(128, 64, 2, 2, 2)         \
+    X(128, 64, 2, 2, 3)         \
+    X(128, 64, 2, 2, 4)         \
+    X(64, 128, 2, 2, 3)         \
+    X(128, 128, 2, 2, 3)        \
+    X(128, 128, 2, 4, 3)        \
+    X(256, 64, 4, 1, 2)         \
+    X(256, 128, 4, 2, 2)        \
+    X(64, 128, 2, 4, 2)         \
+    X(64, 128, 2, 4, 3)         \
+    X(128, 128, 4, 2, 3)
+#define QLL_W4_PIPE_INSTANTIATE(BP, BQ, WP, WQ, S) \
+    template __global__ void gemm_w4_pipe_kernel<BP, BQ, WP, WQ, S>(GemmArgs);
+QLL_FOR_EACH_W4_PIPE(QLL_W4_PIPE_INSTANTIATE)
 
 
 hipError_t launch_quant_int4(const void* w, void* q, float* s, int64_t elems,
@@ -474,13 +774,19 @@ hipError_t launch_reduce_w4a16(const GemmArgs& a, hipStream_t stream)
 }
 
 // Registry.  Decode: "k16x<tokens>_w<waves>" (16 channels per workgroup, the
-// waves split K); tiles: "t<BP>x<BQ>_w<WP>x<WQ>" (one group per stage).
+// waves split K); tiles: "t<BP>x<BQ>_w<WP>x<WQ>" (one group per stage,
+// register prefetch) and "p<BP>x<BQ>_w<WP>x<WQ>_s<S>" (one group per stage,
+// S-slot LDS copy ring).
 #define QLL_W4_SKINNY(RQ, TOK, W, D)                                                 \
     {"k16x" #TOK "_w" #W, OP_W4A16, 1, 16, TOK, W, 1, 0, (W) * (RQ) * 1024,          \
      &launch_w4_skinny<RQ, W, D>},
 #define QLL_W4_TILE(BP, BQ, WP, WQ)                                                  \
     {"t" #BP "x" #BQ "_w" #WP "x" #WQ, OP_W4A16, 0, BP, BQ, WP, WQ, 64,               \
      2 * ((BP) * 256 + (BQ) * 64), &launch_w4_tile<BP, BQ, WP, WQ>},
+
+#define QLL_W4_PIPE_ENTRY(BP, BQ, WP, WQ, S)                                          \
+    {"p" #BP "x" #BQ "_w" #WP "x" #WQ "_s" #S, OP_W4A16, 0, BP, BQ, WP, WQ, 64,        \
+     (S) * ((BP) * 256 + (BQ) * 68), &launch_w4_pipe<BP, BQ, WP, WQ, S>},
 
 #if !defined(__HIP_DEVICE_COMPILE__)
 extern const Variant kVariantsW4a16[] = {
@@ -494,6 +800,7 @@ extern const Variant kVariantsW4a16[] = {
     QLL_W4_TILE(64, 128, 2, 2)
     QLL_W4_TILE(128, 128, 2, 2)
     QLL_W4_TILE(256, 64, 4, 1)
+    QLL_FOR_EACH_W4_PIPE(QLL_W4_PIPE_ENTRY)
 };
 extern const int kNumVariantsW4a16 = sizeof(kVariantsW4a16) / sizeof(Variant);
 #endif

@@ -133,7 +133,7 @@ def test_w4a16_registry_and_dispatch(qll):
     names = [v["name"] for v in qll.variants("w4a16")]
     assert "k16x16_w8" in names and "t128x128_w2x2" in names
     assert qll.select("w4a16", 1, 4096, 4096)[0] == "k16x16_w16"
-    assert qll.select("w4a16", 2048, 4096, 4096)[0].startswith("t")
+    assert qll.select("w4a16", 2048, 4096, 4096)[0].startswith(("t", "p"))
     # Split-K pieces on the packed weight bytes: 512 bytes = 8 groups
     assert qll.effective_splits("w4a16", 2048, 2) == 2
     assert qll.effective_splits("w4a16", 2048, 4) == 2
