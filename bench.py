@@ -460,7 +460,7 @@ def kernel_symbol(qll, op, variant):
             st = variant.rsplit("_s", 1)[1]
             return (f"void qll::gemm_w4_pipe_kernel<{v['bp']}, {v['bq']}, {v['wp']}, "
                     f"{v['wq']}, {st}>(qll::GemmArgs)")
-        return f"void qll::gemm_w4_skinny_kernel<{v['bq'] // 16}, {v['wp']}, "
+        return f"void qll::gemm_w4_skinny_kernel<{v['bq'] // 16}, {v['wp']}, {v['bp']}, "
     if variant[0] == "p":
         st = variant.rsplit("_s", 1)[1]
         return (f"void qll::gemm_pipe_kernel<{opn}, {v['bp']}, {v['bq']}, {v['wp']}, "

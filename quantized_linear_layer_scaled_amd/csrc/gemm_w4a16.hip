@@ -107,19 +107,23 @@ __device__ __forceinline__ void piece_groups(const GemmArgs& a, int z, int& g0, 
 
 // ---------------------------------------------------------------- decode
 
-// 16 output channels per workgroup, 16 * RQ tokens; the W waves split the
-// piece's groups into W contiguous runs, D groups of a run in flight at a
-// time; the wave partials are added in wave order through LDS.
-template <int RQ, int W, int D>
+// HR (16 or 8) output channels per workgroup, 16 * RQ tokens; the W waves
+// split the piece's groups into W contiguous runs, D groups of a run in
+// flight at a time; the wave partials are added in wave order through LDS.
+// With HR = 8 the MFMA's other 8 channel columns are zero: twice the
+// workgroups, so that 2048 channels spread over all 256 CUs.
+template <int RQ, int W, int HR, int D>
 __global__ __launch_bounds__(W * 64) void gemm_w4_skinny_kernel(GemmArgs a)
 {
+    static_assert(HR == 16 || HR == 8, "channels per workgroup");
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int N = a.N, M = a.M, K = a.K;
     const int G = K / 128;
-    const int n0 = blockIdx.x * 16;
+    const int n0 = blockIdx.x * HR;
     const int m0 = blockIdx.y * (16 * RQ);
     const int z = blockIdx.z;
+    const bool wcol = (lane & 15) < HR;  // this lane loads a channel's codes
     int pg0, pg1;
     piece_groups(a, z, pg0, pg1);
     const int TG = pg1 - pg0;
@@ -148,8 +152,9 @@ __global__ __launch_bounds__(W * 64) void gemm_w4_skinny_kernel(GemmArgs a)
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             const bool ok = g + d < g1;
-            wb[d] = ok ? *(const uint4*)(bp + (size_t)(g + d) * 64) : make_uint4(0, 0, 0, 0);
-            sc[d] = ok ? sp[g + d] : 0.0f;
+            wb[d] = ok && wcol ? *(const uint4*)(bp + (size_t)(g + d) * 64)
+                               : make_uint4(0, 0, 0, 0);
+            sc[d] = ok && wcol ? sp[g + d] : 0.0f;
 #pragma unroll
             for (int r = 0; r < RQ; ++r)
 #pragma unroll
@@ -197,7 +202,7 @@ __global__ __launch_bounds__(W * 64) void gemm_w4_skinny_kernel(GemmArgs a)
         const int r = e >> 8, ln = (e & 255) >> 2, v = e & 3;
         const int m = m0 + r * 16 + (ln >> 4) * 4 + v;
         const int n = n0 + (ln & 15);
-        if (m < M && n < N) {
+        if (m < M && n < N && (ln & 15) < HR) {
             if (a.splits > 1)
                 ((float*)a.ws)[((size_t)z * M + m) * N + n] = sum;
             else
@@ -206,13 +211,13 @@ __global__ __launch_bounds__(W * 64) void gemm_w4_skinny_kernel(GemmArgs a)
     }
 }
 
-template <int RQ, int W, int D>
+template <int RQ, int W, int HR, int D>
 hipError_t launch_w4_skinny(const GemmArgs& a, hipStream_t stream)
 {
-    dim3 grid((a.N + 15) / 16, (a.M + 16 * RQ - 1) / (16 * RQ), a.splits);
+    dim3 grid((a.N + HR - 1) / HR, (a.M + 16 * RQ - 1) / (16 * RQ), a.splits);
     if (grid.y > 65535 || grid.z > 65535)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gemm_w4_skinny_kernel<RQ, W, D>), grid, dim3(W * 64), 0, stream, a);
+    hipLaunchKernelGGL((gemm_w4_skinny_kernel<RQ, W, HR, D>), grid, dim3(W * 64), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -725,11 +730,19 @@ hipError_t launch_w4_pipe(const GemmArgs& a, hipStream_t stream)
 }
 
 // the kernels the registry launches (needed by the device pass)
-template __global__ void gemm_w4_skinny_kernel<1, 8, 2>(GemmArgs);
-template __global__ void gemm_w4_skinny_kernel<1, 4, 4>(GemmArgs);
-template __global__ void gemm_w4_skinny_kernel<2, 8, 2>(GemmArgs);
-template __global__ void gemm_w4_skinny_kernel<4, 8, 1>(GemmArgs);
-template __global__ void gemm_w4_skinny_kernel<1, 16, 1>(GemmArgs);
+// X(RQ, TOKENS, W, D, HR) for every decode variant
+#define QLL_FOR_EACH_W4_SKINNY(X) \
+    X(1, 16, 8, 2, 16)            \
+    X(1, 16, 4, 4, 16)            \
+    X(2, 32, 8, 2, 16)            \
+    X(4, 64, 8, 1, 16)            \
+    X(1, 16, 16, 1, 16)           \
+    X(1, 16, 8, 2, 8)             \
+    X(1, 16, 16, 1, 8)            \
+    X(2, 32, 8, 2, 8)
+#define QLL_W4_SKINNY_INSTANTIATE(RQ, TOK, W, D, HR) \
+    template __global__ void gemm_w4_skinny_kernel<RQ, W, HR, D>(GemmArgs);
+QLL_FOR_EACH_W4_SKINNY(QLL_W4_SKINNY_INSTANTIATE)
 template __global__ void gemm_w4_tile_kernel<64, 64, 2, 2>(GemmArgs);
 template __global__ void gemm_w4_tile_kernel<128, 64, 2, 2>(GemmArgs);
 template __global__ void gemm_w4_tile_kernel<64, 128, 2, 2>(GemmArgs);
@@ -773,13 +786,13 @@ hipError_t launch_reduce_w4a16(const GemmArgs& a, hipStream_t stream)
     return launch_reduce<OP_W4A16>(a, stream);
 }
 
-// Registry.  Decode: "k16x<tokens>_w<waves>" (16 channels per workgroup, the
-// waves split K); tiles: "t<BP>x<BQ>_w<WP>x<WQ>" (one group per stage,
+// Registry.  Decode: "k<channels>x<tokens>_w<waves>" (16 or 8 channels per
+// workgroup, the waves split K); tiles: "t<BP>x<BQ>_w<WP>x<WQ>" (one group per stage,
 // register prefetch) and "p<BP>x<BQ>_w<WP>x<WQ>_s<S>" (one group per stage,
 // S-slot LDS copy ring).
-#define QLL_W4_SKINNY(RQ, TOK, W, D)                                                 \
-    {"k16x" #TOK "_w" #W, OP_W4A16, 1, 16, TOK, W, 1, 0, (W) * (RQ) * 1024,          \
-     &launch_w4_skinny<RQ, W, D>},
+#define QLL_W4_SKINNY(RQ, TOK, W, D, HR)                                             \
+    {"k" #HR "x" #TOK "_w" #W, OP_W4A16, 1, HR, TOK, W, 1, 0, (W) * (RQ) * 1024,       \
+     &launch_w4_skinny<RQ, W, HR, D>},
 #define QLL_W4_TILE(BP, BQ, WP, WQ)                                                  \
     {"t" #BP "x" #BQ "_w" #WP "x" #WQ, OP_W4A16, 0, BP, BQ, WP, WQ, 64,               \
      2 * ((BP) * 256 + (BQ) * 64), &launch_w4_tile<BP, BQ, WP, WQ>},
@@ -790,11 +803,7 @@ hipError_t launch_reduce_w4a16(const GemmArgs& a, hipStream_t stream)
 
 #if !defined(__HIP_DEVICE_COMPILE__)
 extern const Variant kVariantsW4a16[] = {
-    QLL_W4_SKINNY(1, 16, 8, 2)
-    QLL_W4_SKINNY(1, 16, 4, 4)
-    QLL_W4_SKINNY(2, 32, 8, 2)
-    QLL_W4_SKINNY(4, 64, 8, 1)
-    QLL_W4_SKINNY(1, 16, 16, 1)
+    QLL_FOR_EACH_W4_SKINNY(QLL_W4_SKINNY)
     QLL_W4_TILE(64, 64, 2, 2)
     QLL_W4_TILE(128, 64, 2, 2)
     QLL_W4_TILE(64, 128, 2, 2)
