@@ -241,8 +241,9 @@ void gemm_pipe_kernel(GemmArgs a)
     constexpr int LPS = MX ? (NSC + WAVES - 1) / WAVES : 0;
     constexpr int LPT = LPT0 + (BLK ? 2 : 0) + LPS;  // + the scale loads
     constexpr int STAGE_BYTES = ROWS * KSTAGE + SC_REGION;
-    // 256x256 tiles stream their fragments (see the K loop)
-    constexpr bool STREAM = BP * BQ >= 256 * 256;
+    // 256x256 tiles and the Block-FP8 tiles stream their fragments (see the
+    // K loop)
+    constexpr bool STREAM = (BP * BQ >= 256 * 256 || BLK) && !MX;
     static_assert(ROWS * NC % THREADS == 0, "stage must split evenly over the waves");
     static_assert((NC & (NC - 1)) == 0 && KSTAGE % KSTEP == 0, "bad K stage");
     static_assert(STAGES >= 2 && (STAGES - 1) * LPT < 64, "bad pipeline depth");
@@ -642,21 +643,31 @@ void gemm_pipe_kernel(GemmArgs a)
         static_assert(U <= 6 && U != 5, "unroll factor");
     } else {
         // Streamed fragments, for tiles whose two register sets of a whole K
-        // step would not fit next to the accumulators: one stage in flight
-        // ahead of the one being computed; per K step each wave reads its RQ
-        // B fragments, then its A fragments one row block at a time, each
-        // read issued before the MFMAs of the previous row block.  The other
-        // wave on the SIMD runs its MFMAs while one waits for its reads.
-        static_assert(STAGES == 2 && !BLK && !MX, "streamed tiles: two stages, no block scales");
+        // step would not fit next to the accumulators (256x256 tiles; the
+        // Block-FP8 tiles, whose promotion needs registers of its own):
+        // STAGES - 1 stages in flight ahead of the one being computed; per K
+        // step each wave reads its RQ B fragments, then its A fragments one
+        // row block at a time, each read issued before the MFMAs of the
+        // previous row block.  The other waves on the SIMD run while one
+        // waits for its reads.
+        static_assert(!MX, "streamed tiles: no MXFP4");
         if (0 < nk)
             issue(0, slot(I0{}));
+        if constexpr (STAGES >= 3)
+            if (1 < nk)
+                issue(1, slot(I1{}));
+        if constexpr (STAGES >= 4)
+            if (2 < nk)
+                issue(2, slot(I2{}));
         auto sstage = [&](auto J, int kt) __attribute__((always_inline)) {
-            constexpr int cs = decltype(J)::value, ns = cs ^ 1;
-            // stage kt has landed for every wave, and every wave is done
-            // with stage kt - 1: its slot takes stage kt + 1
-            wait_vm_barrier<0>();
-            if (kt + 1 < nk)
-                issue(kt + 1, slot(std::integral_constant<int, ns>{}));
+            constexpr int cs = decltype(J)::value;
+            constexpr int fs = (cs + STAGES - 1) % STAGES;  // the slot of stage kt - 1
+            // stage kt has landed for every wave (younger ones may still be
+            // in flight), and every wave is done with stage kt - 1: its slot
+            // takes stage kt + STAGES - 1
+            wait_stage(min(STAGES - 2, nk - 1 - kt));
+            if (kt + STAGES - 1 < nk)
+                issue(kt + STAGES - 1, slot(std::integral_constant<int, fs>{}));
             if constexpr (FOLD)
                 fold.before(kt * NSTEP, acc);
             const uint8_t* sp = slot(std::integral_constant<int, cs>{});
@@ -686,20 +697,62 @@ void gemm_pipe_kernel(GemmArgs a)
                     }
                 };
                 read_a(0, av[0]);
-#pragma unroll
-                for (int i = 0; i < RP; ++i) {
-                    if (i + 1 < RP)
-                        read_a(i + 1, av[(i + 1) & 1]);
+                if constexpr (BLK) {
+                    // promotion as in compute_step, pipelined by row block:
+                    // the fresh partials of row block i + 1 are issued before
+                    // the fmas of row block i, so the matrix cores never wait
+                    // for the promotion of the previous block
+                    static_assert(SQ <= 128, "a wave's columns must share one weight block");
+                    const float* sc = lsc[kt % SC_SLOTS];
+                    const float qs = sc[256 + (((q0 & 127) + wqi * SQ) >> 7)];
+                    v4f pg[2][RQ];
 #pragma unroll
                     for (int j = 0; j < RQ; ++j)
-                        acc[i][j] = mfma_step<OP>(av[i & 1], bv[j], acc[i][j]);
+                        pg[0][j] = mfma_step<OP>(av[0], bv[j], v4f{0, 0, 0, 0});
+#pragma unroll
+                    for (int i = 0; i < RP; ++i) {
+                        if (i + 1 < RP) {
+                            read_a(i + 1, av[(i + 1) & 1]);
+#pragma unroll
+                            for (int j = 0; j < RQ; ++j)
+                                pg[(i + 1) & 1][j] =
+                                    mfma_step<OP>(av[(i + 1) & 1], bv[j], v4f{0, 0, 0, 0});
+                        }
+                        float4 ps = *(const float4*)(sc + wpi * SP + i * 16 + (lane >> 4) * 4);
+                        ps.x *= qs;
+                        ps.y *= qs;
+                        ps.z *= qs;
+                        ps.w *= qs;
+#pragma unroll
+                        for (int j = 0; j < RQ; ++j) {
+                            acc[i][j][0] = __builtin_fmaf(ps.x, pg[i & 1][j][0], acc[i][j][0]);
+                            acc[i][j][1] = __builtin_fmaf(ps.y, pg[i & 1][j][1], acc[i][j][1]);
+                            acc[i][j][2] = __builtin_fmaf(ps.z, pg[i & 1][j][2], acc[i][j][2]);
+                            acc[i][j][3] = __builtin_fmaf(ps.w, pg[i & 1][j][3], acc[i][j][3]);
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < RP; ++i) {
+                        if (i + 1 < RP)
+                            read_a(i + 1, av[(i + 1) & 1]);
+#pragma unroll
+                        for (int j = 0; j < RQ; ++j)
+                            acc[i][j] = mfma_step<OP>(av[i & 1], bv[j], acc[i][j]);
+                    }
                 }
             }
         };
-        for (int kt = 0; kt < nk; kt += 2) {
+        for (int kt = 0; kt < nk; kt += STAGES) {
             sstage(I0{}, kt);
             if (kt + 1 < nk)
                 sstage(I1{}, kt + 1);
+            if constexpr (STAGES >= 3)
+                if (kt + 2 < nk)
+                    sstage(I2{}, kt + 2);
+            if constexpr (STAGES >= 4)
+                if (kt + 3 < nk)
+                    sstage(I3{}, kt + 3);
         }
     }
 
