@@ -77,6 +77,9 @@ def parse():
                    help="rocprofv3 --pmc FETCH_SIZE counter_collection.csv of this command")
     p.add_argument("--write-csv", default=None,
                    help="rocprofv3 --pmc WRITE_SIZE counter_collection.csv of this command")
+    p.add_argument("--mfma-csv", default=None,
+                   help="rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE "
+                        "counter_collection.csv of this command")
     p.add_argument("--calib-copy", action="store_true",
                    help="also run a plain device copy of known size (counter calibration)")
     p.add_argument("--no-graph", action="store_true",
@@ -639,6 +642,26 @@ def hbm_traffic(fetch_csv, write_csv, kernel):
     return res
 
 
+XCDS = 8  # GRBM_GUI_ACTIVE adds up the busy cycles of the 8 XCDs
+
+
+def mfma_busy(csv_path, kernel, cus):
+    """Matrix-core busy fraction of `kernel` from its counters: the MFMA busy
+    cycles of all SIMDs (SQ_VALU_MFMA_BUSY_CYCLES) over the SIMD cycles of the
+    dispatch (GRBM_GUI_ACTIVE / XCDS cycles x 4 SIMDs x CUs)."""
+    busy = [v for k, v in counter_per_dispatch(csv_path, "SQ_VALU_MFMA_BUSY_CYCLES").items()
+            if k.startswith(kernel)]
+    gui = [v for k, v in counter_per_dispatch(csv_path, "GRBM_GUI_ACTIVE").items()
+           if k.startswith(kernel)]
+    if not busy or not gui:
+        return None
+    b = sum(busy[0]) / len(busy[0])
+    g = sum(gui[0]) / len(gui[0])
+    return {"mfma_busy_frac": round(b / (g / XCDS * 4 * cus), 4),
+            "SQ_VALU_MFMA_BUSY_CYCLES": round(b), "GRBM_GUI_ACTIVE": round(g),
+            "dispatches": len(busy[0])}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -804,6 +827,10 @@ def main():
         if tr:
             roof["traffic"] = round(tr["bytes_per_launch"])
             roof["traffic_detail"] = {k: round(v, 4) for k, v in tr.items()}
+    if args.mfma_csv and os.path.exists(args.mfma_csv):
+        mb = mfma_busy(args.mfma_csv, dom_sym, props.multi_processor_count)
+        if mb:
+            roof["mfma_counters"] = mb
     if dom_sym.startswith("void qll::gemm_pipe_kernel") and "true>" not in dom_sym:
         # the fetch the XCD structure implies (each XCD's L2 reads the rows
         # of its tiles once), per launch, plus the bf16 output
