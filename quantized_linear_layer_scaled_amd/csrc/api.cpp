@@ -498,7 +498,7 @@ const char* grouped_rule(int64_t M, int64_t E)
         return "p64x128_w2x2_k128_s3";
     if (per <= 256)
         return "p128x128_w2x2_k128_s2";
-    return "p128x256_w2x4_k128_s2";
+    return "p256x256_w2x4_k128_s2";
 }
 
 }  // namespace

@@ -13,6 +13,7 @@ QLL_FOR_EACH_PIPE_BIG(QLL_PIPE_INSTANTIATE, qll::OP_FP8)
 QLL_FOR_EACH_PIPE_W8_K256(QLL_PIPE_INSTANTIATE, qll::OP_FP8)
 QLL_FOR_EACH_PIPE(QLL_PIPE_GROUPED_INSTANTIATE, qll::OP_FP8)
 QLL_FOR_EACH_PIPE_W8(QLL_PIPE_GROUPED_INSTANTIATE, qll::OP_FP8)
+QLL_FOR_EACH_PIPE_BIG(QLL_PIPE_GROUPED_INSTANTIATE, qll::OP_FP8)
 template __global__ void qll::splitk_reduce_kernel<qll::OP_FP8>(qll::GemmArgs);
 
 namespace qll {
@@ -33,6 +34,7 @@ extern const int kNumVariantsFp8 = sizeof(kVariantsFp8) / sizeof(Variant);
 extern const Variant kVariantsFp8Grouped[] = {
     QLL_FOR_EACH_PIPE(QLL_PIPE_GROUPED_ENTRY, OP_FP8)
     QLL_FOR_EACH_PIPE_W8(QLL_PIPE_GROUPED_ENTRY, OP_FP8)
+    QLL_FOR_EACH_PIPE_BIG(QLL_PIPE_GROUPED_ENTRY, OP_FP8)
 };
 extern const int kNumVariantsFp8Grouped = sizeof(kVariantsFp8Grouped) / sizeof(Variant);
 #endif

@@ -28,10 +28,10 @@ def qll():
 
 
 def pipe_names(qll):
-    # the pipelined tiles with 128-byte K stages; the grouped GEMM has every
-    # one of them except the streamed 256x256 tile
+    # the pipelined tiles with 128-byte K stages: the grouped GEMM has every
+    # one of them
     return [v["name"] for v in qll.variants("fp8") if v["name"].endswith(
-        tuple(f"_k128_s{s}" for s in (2, 3, 4))) and v["bp"] * v["bq"] < 256 * 256]
+        tuple(f"_k128_s{s}" for s in (2, 3, 4)))]
 
 
 def grouped_case(counts, N, K, key):
