@@ -9,6 +9,7 @@ QLL_FOR_EACH_SKINNY(QLL_SKINNY_INSTANTIATE, qll::OP_BF16, 2)
 QLL_FOR_EACH_PIPE(QLL_PIPE_INSTANTIATE, qll::OP_BF16)
 QLL_FOR_EACH_PIPE_K256(QLL_PIPE_INSTANTIATE, qll::OP_BF16)
 QLL_FOR_EACH_PIPE_W8(QLL_PIPE_INSTANTIATE, qll::OP_BF16)
+QLL_FOR_EACH_PIPE_DEEP_K256(QLL_PIPE_INSTANTIATE, qll::OP_BF16)
 QLL_FOR_EACH_PIPE_W8_K256(QLL_PIPE_INSTANTIATE, qll::OP_BF16)
 template __global__ void qll::splitk_reduce_kernel<qll::OP_BF16>(qll::GemmArgs);
 
@@ -22,6 +23,7 @@ extern const Variant kVariantsBf16[] = {
     QLL_FOR_EACH_PIPE(QLL_PIPE_ENTRY, OP_BF16)
     QLL_FOR_EACH_PIPE_K256(QLL_PIPE_ENTRY, OP_BF16)
     QLL_FOR_EACH_PIPE_W8(QLL_PIPE_ENTRY, OP_BF16)
+    QLL_FOR_EACH_PIPE_DEEP_K256(QLL_PIPE_ENTRY, OP_BF16)
     QLL_FOR_EACH_PIPE_W8_K256(QLL_PIPE_ENTRY, OP_BF16)
 };
 extern const int kNumVariantsBf16 = sizeof(kVariantsBf16) / sizeof(Variant);

@@ -9,6 +9,7 @@ QLL_FOR_EACH_SKINNY(QLL_SKINNY_INSTANTIATE, qll::OP_FP8, 1)
 QLL_FOR_EACH_PIPE(QLL_PIPE_INSTANTIATE, qll::OP_FP8)
 QLL_FOR_EACH_PIPE_K256(QLL_PIPE_INSTANTIATE, qll::OP_FP8)
 QLL_FOR_EACH_PIPE_W8(QLL_PIPE_INSTANTIATE, qll::OP_FP8)
+QLL_FOR_EACH_PIPE_DEEP_K256(QLL_PIPE_INSTANTIATE, qll::OP_FP8)
 QLL_FOR_EACH_PIPE_BIG(QLL_PIPE_INSTANTIATE, qll::OP_FP8)
 QLL_FOR_EACH_PIPE_W8_K256(QLL_PIPE_INSTANTIATE, qll::OP_FP8)
 QLL_FOR_EACH_PIPE(QLL_PIPE_GROUPED_INSTANTIATE, qll::OP_FP8)
@@ -26,6 +27,7 @@ extern const Variant kVariantsFp8[] = {
     QLL_FOR_EACH_PIPE(QLL_PIPE_ENTRY, OP_FP8)
     QLL_FOR_EACH_PIPE_K256(QLL_PIPE_ENTRY, OP_FP8)
     QLL_FOR_EACH_PIPE_W8(QLL_PIPE_ENTRY, OP_FP8)
+    QLL_FOR_EACH_PIPE_DEEP_K256(QLL_PIPE_ENTRY, OP_FP8)
     QLL_FOR_EACH_PIPE_BIG(QLL_PIPE_ENTRY, OP_FP8)
     QLL_FOR_EACH_PIPE_W8_K256(QLL_PIPE_ENTRY, OP_FP8)
 };

@@ -9,6 +9,7 @@ QLL_FOR_EACH_SKINNY(QLL_SKINNY_INSTANTIATE, qll::OP_INT8, 2)
 QLL_FOR_EACH_PIPE(QLL_PIPE_INSTANTIATE, qll::OP_INT8)
 QLL_FOR_EACH_PIPE_K256(QLL_PIPE_INSTANTIATE, qll::OP_INT8)
 QLL_FOR_EACH_PIPE_W8(QLL_PIPE_INSTANTIATE, qll::OP_INT8)
+QLL_FOR_EACH_PIPE_DEEP_K256(QLL_PIPE_INSTANTIATE, qll::OP_INT8)
 QLL_FOR_EACH_PIPE_BIG(QLL_PIPE_INSTANTIATE, qll::OP_INT8)
 QLL_FOR_EACH_PIPE_W8_K256(QLL_PIPE_INSTANTIATE, qll::OP_INT8)
 template __global__ void qll::splitk_reduce_kernel<qll::OP_INT8>(qll::GemmArgs);
@@ -23,6 +24,7 @@ extern const Variant kVariantsInt8[] = {
     QLL_FOR_EACH_PIPE(QLL_PIPE_ENTRY, OP_INT8)
     QLL_FOR_EACH_PIPE_K256(QLL_PIPE_ENTRY, OP_INT8)
     QLL_FOR_EACH_PIPE_W8(QLL_PIPE_ENTRY, OP_INT8)
+    QLL_FOR_EACH_PIPE_DEEP_K256(QLL_PIPE_ENTRY, OP_INT8)
     QLL_FOR_EACH_PIPE_BIG(QLL_PIPE_ENTRY, OP_INT8)
     QLL_FOR_EACH_PIPE_W8_K256(QLL_PIPE_ENTRY, OP_INT8)
 };

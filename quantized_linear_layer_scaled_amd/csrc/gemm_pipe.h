@@ -100,6 +100,34 @@ __device__ __forceinline__ void wait_vm_barrier()
     asm volatile("s_barrier" ::: "memory");
 }
 
+// f(integral_constant<J>{}, kt + J) for J = J0 .. U-1 while kt + J < nk: the
+// stages of one unrolled round of the K loop, each with its ring slot and
+// register set known at compile time.
+template <int J, int U, typename F>
+__device__ __forceinline__ void for_stages(F&& f, int kt, int nk)
+{
+    if constexpr (J < U) {
+        if (kt + J < nk) {
+            f(std::integral_constant<int, J>{}, kt + J);
+            for_stages<J + 1, U>(f, kt, nk);
+        }
+    }
+}
+
+// wait_vm_barrier<Y * LPT>() for the largest Y <= min(younger, YMAX).
+template <int YMAX, int LPT>
+__device__ __forceinline__ void wait_younger(int younger)
+{
+    if constexpr (YMAX <= 0) {
+        wait_vm_barrier<0>();
+    } else {
+        if (younger >= YMAX)
+            wait_vm_barrier<YMAX * LPT>();
+        else
+            wait_younger<YMAX - 1, LPT>(younger);
+    }
+}
+
 // Waves per SIMD the register allocation has to allow: as many workgroups
 // as the LDS ring lets share a CU (160 KiB of LDS, at most four), each with
 // WP x WQ waves over the CU's four SIMDs.  Several resident workgroups are
@@ -114,10 +142,18 @@ constexpr int pipe_scale_bytes()
 }
 
 // LDS of the operand ring (and the Block-FP8 scale ring).
+// One ring slot: a stage's operand rows (and MXFP4 scale bytes), in whole
+// KiB so that every slot starts 1 KiB-aligned.
+template <int OP, int BP, int BQ, int KSTAGE>
+constexpr int pipe_slot_bytes()
+{
+    return ((BP + BQ) * KSTAGE + pipe_scale_bytes<OP, BP, BQ, KSTAGE>() + 1023) / 1024 * 1024;
+}
+
 template <int OP, int BP, int BQ, int KSTAGE, int STAGES>
 constexpr int pipe_ring_bytes()
 {
-    return STAGES * ((BP + BQ) * KSTAGE + pipe_scale_bytes<OP, BP, BQ, KSTAGE>()) +
+    return STAGES * pipe_slot_bytes<OP, BP, BQ, KSTAGE>() +
            (OP == OP_BLOCK ? (STAGES + 1) * 1280 : 0);
 }
 
@@ -256,10 +292,8 @@ void gemm_pipe_kernel(GemmArgs a)
 
     // One LDS object per ring slot, the slot known at compile time in the
     // unrolled K loop (constant LDS addresses for the fragment reads).
-    __shared__ __attribute__((aligned(1024))) uint8_t lds0[STAGE_BYTES];
-    __shared__ __attribute__((aligned(1024))) uint8_t lds1[STAGE_BYTES];
-    __shared__ __attribute__((aligned(1024))) uint8_t lds2[STAGES >= 3 ? STAGE_BYTES : 16];
-    __shared__ __attribute__((aligned(1024))) uint8_t lds3[STAGES >= 4 ? STAGE_BYTES : 16];
+    constexpr int SLOT = pipe_slot_bytes<OP, BP, BQ, KSTAGE>();
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[STAGES * SLOT];
     // Block-FP8: the K group's activation scales of the tile rows (256
     // floats) and its weight-block scales (64) per stage, in a ring of
     // STAGES + 1 entries, so that a stage's scales outlive the reuse of its
@@ -267,17 +301,9 @@ void gemm_pipe_kernel(GemmArgs a)
     constexpr int SC_SLOTS = BLK ? STAGES + 1 : 1;
     constexpr int SC_FLOATS = 320;
     __shared__ __attribute__((aligned(16))) float lsc[SC_SLOTS][BLK ? SC_FLOATS : 4];
-    static_assert(STAGES <= 4, "at most four ring slots");
+    static_assert(STAGES <= 8, "at most eight ring slots");
     auto slot = [&](auto J) __attribute__((always_inline)) -> uint8_t* {
-        constexpr int j = decltype(J)::value;
-        if constexpr (j == 0)
-            return lds0;
-        else if constexpr (j == 1)
-            return lds1;
-        else if constexpr (j == 2)
-            return lds2;
-        else
-            return lds3;
+        return ring + decltype(J)::value * SLOT;
     };
 
     const int tid = threadIdx.x;
@@ -533,19 +559,9 @@ void gemm_pipe_kernel(GemmArgs a)
     // wait for the oldest stage in flight with `younger` later stages still
     // allowed in flight
     auto wait_stage = [&](int younger) __attribute__((always_inline)) {
-        if (STAGES >= 4 && younger >= 3)
-            wait_vm_barrier<(STAGES >= 4 ? 3 : 0) * LPT>();
-        else if (STAGES >= 3 && younger >= 2)
-            wait_vm_barrier<(STAGES >= 3 ? 2 : 0) * LPT>();
-        else if (younger >= 1)
-            wait_vm_barrier<LPT>();
-        else
-            wait_vm_barrier<0>();
+        wait_younger<STAGES - 1, LPT>(younger);
     };
     using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, 1>;
-    using I2 = std::integral_constant<int, 2>;
-    using I3 = std::integral_constant<int, 3>;
 
     // The tile's scales, into LDS ahead of the operand stages (the stage
     // waits, which count only the younger copies, also cover these): unit u
@@ -573,16 +589,9 @@ void gemm_pipe_kernel(GemmArgs a)
     if constexpr (!STREAM) {
         // prologue: every ring slot receives a stage (0 .. STAGES-1); the
         // fragments of step 0 go to register set 0
-        if (0 < nk)
-            issue(0, slot(I0{}));
-        if (1 < nk)
-            issue(1, slot(I1{}));
-        if constexpr (STAGES >= 3)
-            if (2 < nk)
-                issue(2, slot(I2{}));
-        if constexpr (STAGES >= 4)
-            if (3 < nk)
-                issue(3, slot(I3{}));
+        for_stages<0, STAGES>([&](auto J, int kt) __attribute__((always_inline)) {
+            issue(kt, slot(J));
+        }, 0, nk);
         if (0 < nk) {
             wait_stage(min(STAGES - 1, nk - 1));
             load_step(slot(I0{}), 0, fr[0]);
@@ -621,26 +630,8 @@ void gemm_pipe_kernel(GemmArgs a)
                 compute_step(fr[cp], kt, ks);
             }
         };
-        for (int kt = 0; kt < nk; kt += U) {
-            stage(I0{}, kt);
-            if (kt + 1 < nk)
-                stage(I1{}, kt + 1);
-            if constexpr (U >= 3) {
-                if (kt + 2 < nk)
-                    stage(I2{}, kt + 2);
-            }
-            if constexpr (U >= 4) {
-                if (kt + 3 < nk)
-                    stage(I3{}, kt + 3);
-            }
-            if constexpr (U >= 6) {
-                if (kt + 4 < nk)
-                    stage(std::integral_constant<int, 4>{}, kt + 4);
-                if (kt + 5 < nk)
-                    stage(std::integral_constant<int, 5>{}, kt + 5);
-            }
-        }
-        static_assert(U <= 6 && U != 5, "unroll factor");
+        for (int kt = 0; kt < nk; kt += U)
+            for_stages<0, U>(stage, kt, nk);
     } else {
         // Streamed fragments, for tiles whose two register sets of a whole K
         // step would not fit next to the accumulators (256x256 tiles; the
@@ -651,14 +642,9 @@ void gemm_pipe_kernel(GemmArgs a)
         // previous row block.  The other waves on the SIMD run while one
         // waits for its reads.
         static_assert(!MX, "streamed tiles: no MXFP4");
-        if (0 < nk)
-            issue(0, slot(I0{}));
-        if constexpr (STAGES >= 3)
-            if (1 < nk)
-                issue(1, slot(I1{}));
-        if constexpr (STAGES >= 4)
-            if (2 < nk)
-                issue(2, slot(I2{}));
+        for_stages<0, STAGES - 1>([&](auto J, int kt) __attribute__((always_inline)) {
+            issue(kt, slot(J));
+        }, 0, nk);
         auto sstage = [&](auto J, int kt) __attribute__((always_inline)) {
             constexpr int cs = decltype(J)::value;
             constexpr int fs = (cs + STAGES - 1) % STAGES;  // the slot of stage kt - 1
@@ -743,17 +729,8 @@ void gemm_pipe_kernel(GemmArgs a)
                 }
             }
         };
-        for (int kt = 0; kt < nk; kt += STAGES) {
-            sstage(I0{}, kt);
-            if (kt + 1 < nk)
-                sstage(I1{}, kt + 1);
-            if constexpr (STAGES >= 3)
-                if (kt + 2 < nk)
-                    sstage(I2{}, kt + 2);
-            if constexpr (STAGES >= 4)
-                if (kt + 3 < nk)
-                    sstage(I3{}, kt + 3);
-        }
+        for (int kt = 0; kt < nk; kt += STAGES)
+            for_stages<0, STAGES>(sstage, kt, nk);
     }
 
     if constexpr (FOLD)
@@ -765,7 +742,7 @@ void gemm_pipe_kernel(GemmArgs a)
     // eight scattered 2-byte stores.
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");  // ring slots are free
     static_assert(WAVES * 16 * SQ * 4 <= STAGE_BYTES, "epilogue scratch must fit one slot");
-    elem_t* scr = (elem_t*)(lds0 + wave * 16 * SQ * 4);
+    elem_t* scr = (elem_t*)(ring + wave * 16 * SQ * 4);
     constexpr int CPR = SQ / 8;          // 8-column groups per row
     constexpr int RPP = 64 / CPR;        // rows per pass
     constexpr int PASSES = 16 / RPP;
@@ -943,6 +920,12 @@ hipError_t launch_pipe_grouped(const GemmArgs& a, hipStream_t stream)
 #define QLL_FOR_EACH_PIPE_W8_K256(X, OP)   \
     X(OP, 128, 128, 4, 4, 256, 2)          \
     X(OP, 128, 64, 4, 2, 256, 2)
+
+// A deeper ring of 256-byte stages for 64x64 tiles (the mid-size M of
+// weight-streaming shapes).  Rings of 6 and 8 128-byte stages of the small
+// tiles were measured too and never won.
+#define QLL_FOR_EACH_PIPE_DEEP_K256(X, OP) \
+    X(OP, 64, 64, 2, 2, 256, 4)
 
 // 256x256 tiles over 8 waves of 128x64, fragments streamed: half the
 // operand bytes per flop of a 128x256 tile, for grids of many tiles per CU.
