@@ -33,7 +33,7 @@ workload, and, when the rocprofv3 counter CSVs are given (--fetch-csv,
 --write-csv), the HBM traffic of the dominant kernel scaled by the same
 counters read on a copy kernel of known size (--calib-copy runs that copy).
 
-Other workloads (--workload int8|block|bi|vocab|moe|mxfp4|w4a16) print the
+Other workloads (--workload int8|block|bi|vocab|vocab_bi|moe|mxfp4|w4a16) print the
 same JSON shape; moe is the grouped (per-expert) FP8 GEMM of a 64-expert layer
 with synthetic top-8 routing (per-token quantization + gemm_fp8_grouped);
 mxfp4 is the FP8 sweep's shapes and data in MXFP4 (quantize_mxfp4 +
@@ -66,7 +66,8 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="fp8",
-                   choices=["fp8", "int8", "block", "bi", "vocab", "moe", "mxfp4", "w4a16"])
+                   choices=["fp8", "int8", "block", "bi", "vocab", "vocab_bi", "moe", "mxfp4",
+                            "w4a16"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=2048,
                    help="rows per problem the CPU oracle computes (the default covers "
@@ -270,6 +271,17 @@ def build_problems(torch, qll, workload):
             p.tensors["gemm"] = (t, grouped_args)
             p.variant, p.splits, p.eff_splits = qll.grouped_select(M, E), 1, 1
             probs.append(p)
+    elif workload == "vocab_bi":
+        # the batch-invariant bf16 path on the large-vocabulary data (the FP8
+        # path on the same data is --workload vocab)
+        N, K = W.VOCAB_SHAPE
+        w = dev_bf16(torch, W.vocab_weights(N, K))
+        x_all = dev_bf16(torch, W.vocab_activations(K))
+        for M in W.VOCAB_M:
+            p = Problem("bf16_bi", M, N, K)
+            add_gemm(p, "gemm_bf16_batch_invariant", x_all[:M].clone(), w.clone(), None, None)
+            probs.append(p)
+        del w
     elif workload == "bi":
         for N, K in W.BI_SHAPES:
             d = W.bi_inputs(N, K)
@@ -570,6 +582,18 @@ def cpu_baseline(workload, rows_cap):
             flops += 2.0 * rows.size * N * K
         desc = (f"min(M,{rows_cap}) evenly spaced rows of every grouped problem "
                 "(all experts), per-token quantization of all rows + grouped FP8 GEMM")
+    elif workload == "vocab_bi":
+        N, K = W.VOCAB_SHAPE
+        w = W.vocab_weights(N, K)
+        x = W.vocab_activations(K)
+        cap = min(rows_cap, 64)
+        for M in W.VOCAB_M:
+            r = min(M, cap)
+            t0 = time.perf_counter()
+            oracle.gemm_bf16(x[:r], w)
+            t_total += time.perf_counter() - t0
+            flops += 2.0 * r * N * K
+        desc = f"first min(M,{cap}) rows of every vocabulary-size bf16 problem"
     else:
         for N, K in W.BI_SHAPES:
             d = W.bi_inputs(N, K)
@@ -630,7 +654,9 @@ def hbm_traffic(fetch_csv, write_csv, kernel):
     for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         d = counter_per_dispatch(path, name)
         ks = [v for k, v in d.items() if k.startswith(kernel)]
-        cal = [v for k, v in d.items() if "copy" in k.lower() or "elementwise" in k.lower()]
+        # the calibration kernel (torch.mul into a new buffer), not the
+        # workload's own copies
+        cal = [v for k, v in d.items() if "MulFunctor" in k]
         if not ks or not cal:
             return None
         vals = ks[0]
@@ -873,6 +899,8 @@ def main():
                     "routing); per-token quantization + gemm_fp8_grouped, bf16 out",
              "vocab": "large-vocab FP8 dynamic projection N=151936 K=2048, "
                       "M in {1,8,64,512,2048}",
+             "vocab_bi": "large-vocab batch-invariant bf16 projection N=151936 K=2048, "
+                         "M in {1,8,64,512,2048}, bf16 out",
              "w4a16": "INT4 weight-only sweep: (N,K) in {(4096,2048),(2048,6144)}, "
                       "M in {1,4,8,16,32,64,256,512,1024,2048}; bf16 activations x int4 "
                       "weights (scale per 128-element group), bf16 out",
@@ -881,7 +909,7 @@ def main():
                       "activations + MXFP4 GEMM (E8M0 scale per 32), bf16 out"}
     dtype = {"fp8": "fp8e4m3", "vocab": "fp8e4m3", "block": "fp8e4m3", "int8": "int8",
              "moe": "fp8e4m3", "mxfp4": "fp4e2m1", "w4a16": "bf16 x int4",
-             "bi": "bf16"}[args.workload]
+             "bi": "bf16", "vocab_bi": "bf16"}[args.workload]
     line = {
         "metric": "TFLOPS/TOPS + % of HBM or MFMA roofline per (M,N,K), FP8/INT8 scaled_mm",
         "value": round(value, 3),
@@ -919,8 +947,8 @@ def main():
         both = [(r["gemm_us"], r["vendor_gemm_us"]) for r in per_shape
                 if r.get("vendor_gemm_us")]
         line["vendor_context"] = {
-            "library": "torch._scaled_mm (hipBLASLt), row-wise scales" if args.workload != "bi"
-                       else "torch.matmul (hipBLASLt)",
+            "library": "torch._scaled_mm (hipBLASLt), row-wise scales"
+                       if args.workload not in ("bi", "vocab_bi") else "torch.matmul (hipBLASLt)",
             "problems": len(both),
             "sum_gemm_us_ours": round(sum(a for a, _ in both), 2),
             "sum_gemm_us_vendor": round(sum(b for _, b in both), 2),
