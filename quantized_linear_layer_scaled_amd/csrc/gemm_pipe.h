@@ -741,7 +741,7 @@ void gemm_pipe_kernel(GemmArgs a)
     // columns of one row -- a 16-byte bf16 store (two for fp32) instead of
     // eight scattered 2-byte stores.
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");  // ring slots are free
-    static_assert(WAVES * 16 * SQ * 4 <= STAGE_BYTES, "epilogue scratch must fit one slot");
+    static_assert(WAVES * 16 * SQ * 4 <= STAGES * SLOT, "epilogue scratch must fit the ring");
     elem_t* scr = (elem_t*)(ring + wave * 16 * SQ * 4);
     constexpr int CPR = SQ / 8;          // 8-column groups per row
     constexpr int RPP = 64 / CPR;        // rows per pass
