@@ -763,7 +763,13 @@ template __global__ void gemm_w4_tile_kernel<256, 64, 4, 1>(GemmArgs);
     X(256, 128, 4, 2, 2)        \
     X(64, 128, 2, 4, 2)         \
     X(64, 128, 2, 4, 3)         \
-    X(128, 128, 4, 2, 3)
+    X(128, 128, 4, 2, 3)        \
+    X(128, 128, 1, 4, 3)        \
+    X(128, 256, 2, 4, 2)        \
+    X(128, 256, 2, 4, 3)        \
+    X(128, 256, 1, 8, 3)        \
+    X(64, 256, 1, 4, 3)         \
+    X(64, 256, 1, 4, 4)
 #define QLL_W4_PIPE_INSTANTIATE(BP, BQ, WP, WQ, S) \
     template __global__ void gemm_w4_pipe_kernel<BP, BQ, WP, WQ, S>(GemmArgs);
 QLL_FOR_EACH_W4_PIPE(QLL_W4_PIPE_INSTANTIATE)
