@@ -488,16 +488,15 @@ int run_gemm(int op, const void* A, const void* B, const float* sa,
 // Built-in tile rule of the grouped GEMM by the mean rows per expert (the
 // fastest variant measured on the 64-expert N = 1536, K = 2048 layer with
 // skewed top-8 routing at 16, 128, 1024 and 4096 tokens): thin row tiles when
-// experts get a few rows, taller ones as the weights get reused.
+// experts get a few rows, the 256x256 tile once the heavy experts get
+// hundreds (the skew puts most rows on a few experts).
 const char* grouped_rule(int64_t M, int64_t E)
 {
     const int64_t per = M / (E > 0 ? E : 1);
     if (per <= 4)
-        return "p32x128_w1x4_k128_s4";
+        return "p64x128_w2x2_k128_s2";
     if (per <= 32)
-        return "p64x128_w2x2_k128_s3";
-    if (per <= 256)
-        return "p128x128_w2x2_k128_s2";
+        return "p32x128_w1x4_k128_s4";
     return "p256x256_w2x4_k128_s2";
 }
 

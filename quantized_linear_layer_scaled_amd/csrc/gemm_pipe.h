@@ -196,6 +196,34 @@ constexpr int pipe_waves_per_eu()
     return w < 1 ? 1 : (w > 8 ? 8 : w);
 }
 
+// Grouped GEMM: the number of row tiles of BP rows over all experts, with
+// the offsets read as group_tile reads them (every lane gets the total).
+__device__ __forceinline__ int group_row_tiles(const int* __restrict__ off, int E, int M, int BP,
+                                               int lane)
+{
+    int total = 0, carry = 0;
+    for (int base = 0; base < E; base += 64) {
+        const int j = base + lane;
+        const bool live = j < E;
+        int lo = live ? min(max(off[j], 0), M) : 0;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int v = __shfl_up(lo, d, 64);
+            if (lane >= d)
+                lo = max(lo, v);
+        }
+        lo = max(lo, carry);
+        const int hi = live ? max(lo, min(max(off[j + 1], 0), M)) : lo;
+        int tiles = live ? (hi - lo + BP - 1) / BP : 0;
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1)
+            tiles += __shfl_xor(tiles, d, 64);
+        total += tiles;
+        carry = __shfl(hi, 63, 64);
+    }
+    return total;
+}
+
 // Grouped GEMM: the expert that owns virtual row tile t (tiles of BP rows,
 // numbered expert by expert) and its row range [m0, m1) for that tile.
 // Offsets are clamped to [0, M] and made non-decreasing, so no access leaves
@@ -317,9 +345,18 @@ void gemm_pipe_kernel(GemmArgs a)
     const uint8_t* Bp = (const uint8_t*)a.B;
     const float* sbp = a.sb;
     if constexpr (GROUPED) {
-        // virtual row tiles: at most one partial tile per expert
-        const int tpv = (a.M + BP - 1) / BP + a.E;
-        xcd_tile(blockIdx.x, tpv, tq, 4, tile_p, tile_q);
+        // The grid covers the most row tiles the experts can have (one
+        // partial tile each beyond ceil(M / BP)); the tiles they do have are
+        // counted here and spread evenly over the XCDs, and the workgroups
+        // beyond them on each XCD leave at once (else the XCDs that draw the
+        // end of the range would idle).
+        const int rows = __builtin_amdgcn_readfirstlane(
+            group_row_tiles(a.offsets, a.E, a.M, BP, lane));
+        const int T = rows * tq;
+        const int xcd = blockIdx.x & 7, loc = blockIdx.x >> 3;
+        if (loc >= (T >> 3) + (xcd < (T & 7) ? 1 : 0))
+            return;  // (the same for every wave)
+        xcd_tile(blockIdx.x, rows, tq, 4, tile_p, tile_q);
         int e, m0, m1;
         group_tile(a.offsets, a.E, a.M, tile_p, BP, lane, e, m0, m1);
         // equal in every lane: make them scalar (the buffer resources below

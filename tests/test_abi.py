@@ -210,9 +210,9 @@ def test_grouped_validation(qll):
     assert grp(variant="no_such_tile") == 1
     assert grp(variant="k16x16_w8") == 1      # only the pipelined tiles
     assert grp(M=0, A=None, sa=None, off=None) == 0
-    assert qll.grouped_select(128, 64) == "p32x128_w1x4_k128_s4"
-    assert qll.grouped_select(1024, 64) == "p64x128_w2x2_k128_s3"
-    assert qll.grouped_select(8192, 64) == "p128x128_w2x2_k128_s2"
+    assert qll.grouped_select(128, 64) == "p64x128_w2x2_k128_s2"
+    assert qll.grouped_select(1024, 64) == "p32x128_w1x4_k128_s4"
+    assert qll.grouped_select(8192, 64) == "p256x256_w2x4_k128_s2"
     assert qll.grouped_select(32768, 64) == "p256x256_w2x4_k128_s2"
     names = [v["name"] for v in qll.variants("fp8")]
     assert all(qll.grouped_select(M, 64) in names for M in (0, 1, 5000, 1 << 20))

@@ -47,7 +47,9 @@ def grouped_case(counts, N, K, key):
 # uneven experts: empty ones, partial tiles, a single row, more rows than a tile
 CASES = [((3, 0, 70, 1, 0, 129, 33, 8), 200, 528),
          ((64,), 96, 256),
-         ((0, 0, 5), 130, 1040)]
+         ((0, 0, 5), 130, 1040),
+         # more experts than one 64-lane scan of the offsets
+         (tuple((7 * i) % 5 for i in range(69)) + (140,), 96, 256)]
 
 
 @pytest.mark.parametrize("counts,N,K", CASES)
