@@ -277,9 +277,10 @@ int linear_fp8_dynamic_ex(const void* x, const void* B, const float* sb, void* q
  *   acc = sum_k e4m3(A[m][k]) * e4m3(B[e][n][k]) in fp32.
  *   A e4m3 [M][K]; B e4m3 [E][N][K]; sa fp32 [M]; sb fp32 [E][N];
  *   offsets: DEVICE int32 [E + 1], offsets[0] = 0, offsets[E] = M,
- *   non-decreasing (other values give unspecified output rows but never an
- *   access outside A, B, sa, sb or out: the kernel clamps them to [0, M] and
- *   takes their running maximum);
+ *   non-decreasing.  Other values are read as their running maximum clamped
+ *   to [0, M] (expert e then owns rows [c[e], c[e+1]) of those values, rows
+ *   that no expert owns are left unwritten), so no access leaves A, B, sa,
+ *   sb or out;
  *   out bf16 / fp32 [M][N].  K % 16 == 0, 1 <= E <= 65536.  No workspace.
  * variant (the _ex form): one of the pipelined variant names
  * ("p<BP>x<BQ>_w<WP>x<WQ>_k128_s<S>", as listed by qll_variant_info for the

@@ -84,6 +84,24 @@ def test_grouped_equals_per_expert_dense_bitwise(qll):
             assert torch.equal(y[lo:hi].view(torch.int32), ye.view(torch.int32)), (name, e)
 
 
+def test_grouped_offsets_read_as_clamped_running_maximum(qll):
+    # Offsets outside [0, M] or out of order are read as their running
+    # maximum clamped to [0, M]: here [-7, 60, 25, 200, 90] over M = 140 rows
+    # gives the experts the rows [0, 60), [60, 60), [60, 140), [140, 140).
+    counts = (40, 30, 50, 20)
+    N, K = 96, 256
+    _, A, B, sa, sb = grouped_case(counts, N, K, (workloads.W_TEST, 53))
+    bad = torch.tensor([-7, 60, 25, 200, 90], dtype=torch.int32).cuda()
+    owned = [(0, 0, 60), (2, 60, 140)]
+    dA, dB, dsa, dsb = dev_e4m3(A), dev_e4m3(B), dev(sa), dev(sb)
+    for name in ("p64x64_w2x2_k128_s3", "p128x128_w2x2_k128_s2", "p256x256_w2x4_k128_s2"):
+        y = qll.gemm_fp8_grouped(dA, dB, dsa, dsb, bad, out_dtype="fp32", variant=name)
+        torch.cuda.synchronize()
+        for e, lo, hi in owned:
+            ref, absref = oracle.gemm_fp8(A[lo:hi], B[e], sa[lo:hi], sb[e], with_abs=True)
+            check_fp(host_f64(y)[lo:hi], ref, absref, K, "fp32", f"grouped {name} expert {e}")
+
+
 @pytest.fixture(scope="module")
 def moe_weights(qll):
     N, K = workloads.MOE_SHAPE
