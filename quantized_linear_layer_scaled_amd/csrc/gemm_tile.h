@@ -476,12 +476,20 @@ hipError_t launch_tile(const GemmArgs& a, hipStream_t stream)
 
 // Second Split-K stage: each thread owns up to 4 consecutive columns of one
 // row and adds the partials of the pieces s = 0, 1, ..., S-1 in that order.
+// The partials were just stored by other CUs (an L2 or Infinity Cache round
+// trip each), so they are loaded kReduceBatch pieces at a time, all loads of
+// a batch in flight before the first add.
+constexpr int kReduceThreads = 128;
+constexpr int kReduceBatch = 8;
+
 template <int OP>
-__global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs a)
+__global__ __launch_bounds__(kReduceThreads) void splitk_reduce_kernel(GemmArgs a)
 {
     using elem_t = typename OpTraits<OP>::elem_t;
+    typedef elem_t v4e __attribute__((ext_vector_type(4)));
+    constexpr int ZB = kReduceBatch;
     const int NQ = (a.N + 3) / 4;
-    const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+    const long idx = (long)blockIdx.x * kReduceThreads + threadIdx.x;
     if (idx >= (long)a.M * NQ)
         return;
     const int m = (int)(idx / NQ);
@@ -489,22 +497,31 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs a)
     const elem_t* ws = (const elem_t*)a.ws;
     const size_t plane = (size_t)a.M * a.N;
     const size_t base = (size_t)m * a.N + n0;
+    const bool vec = (a.N & 3) == 0;
     elem_t s[4] = {0, 0, 0, 0};
-    if ((a.N & 3) == 0) {
-        for (int z = 0; z < a.splits; ++z) {
-            typedef elem_t v4e __attribute__((ext_vector_type(4)));
-            const v4e t = *(const v4e*)(ws + z * plane + base);
-            s[0] += t[0];
-            s[1] += t[1];
-            s[2] += t[2];
-            s[3] += t[3];
-        }
-    } else {
-        for (int z = 0; z < a.splits; ++z)
+    for (int z0 = 0; z0 < a.splits; z0 += ZB) {
+        v4e t[ZB];
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                if (n0 + j < a.N)
-                    s[j] += ws[z * plane + base + j];
+        for (int j = 0; j < ZB; ++j) {
+            t[j] = v4e{0, 0, 0, 0};
+            if (z0 + j < a.splits) {
+                const elem_t* src = ws + (size_t)(z0 + j) * plane + base;
+                if (vec) {
+                    t[j] = *(const v4e*)src;
+                } else {
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        if (n0 + c < a.N)
+                            t[j][c] = src[c];
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < ZB; ++j)
+            if (z0 + j < a.splits)
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    s[c] += t[j][c];
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j)
@@ -516,11 +533,11 @@ template <int OP>
 hipError_t launch_reduce(const GemmArgs& a, hipStream_t stream)
 {
     const long total = (long)a.M * ((a.N + 3) / 4);
-    const long blocks = (total + 255) / 256;
+    const long blocks = (total + kReduceThreads - 1) / kReduceThreads;
     if (blocks > 0x7FFFFFFFL)
         return hipErrorInvalidValue;
     hipLaunchKernelGGL(splitk_reduce_kernel<OP>, dim3((unsigned)blocks),
-                       dim3(256), 0, stream, a);
+                       dim3(kReduceThreads), 0, stream, a);
     return hipGetLastError();
 }
 
