@@ -769,7 +769,11 @@ template __global__ void gemm_w4_tile_kernel<256, 64, 4, 1>(GemmArgs);
     X(128, 256, 2, 4, 3)        \
     X(128, 256, 1, 8, 3)        \
     X(64, 256, 1, 4, 3)         \
-    X(64, 256, 1, 4, 4)
+    X(64, 256, 1, 4, 4)         \
+    X(32, 128, 1, 4, 3)         \
+    X(32, 128, 1, 4, 4)         \
+    X(32, 256, 1, 8, 3)         \
+    X(64, 128, 1, 4, 3)
 #define QLL_W4_PIPE_INSTANTIATE(BP, BQ, WP, WQ, S) \
     template __global__ void gemm_w4_pipe_kernel<BP, BQ, WP, WQ, S>(GemmArgs);
 QLL_FOR_EACH_W4_PIPE(QLL_W4_PIPE_INSTANTIATE)
