@@ -32,6 +32,10 @@ The line also carries the CPU oracle timed on a bounded sample of the same
 workload, and, when the rocprofv3 counter CSVs are given (--fetch-csv,
 --write-csv), the HBM traffic of the dominant kernel scaled by the same
 counters read on a copy kernel of known size (--calib-copy runs that copy).
+Without them the traffic comes from the workload's committed profile
+(profiles/<workload>_sweep_bench_line.json) when that profile measured the
+same kernel built from the same sources (a digest of the kernel and ABI
+sources is stored with the counters), and is null otherwise.
 
 Other workloads (--workload int8|block|bi|vocab|vocab_bi|moe|mxfp4|w4a16) print the
 same JSON shape; moe is the grouped (per-expert) FP8 GEMM of a 64-expert layer
@@ -646,6 +650,21 @@ def counter_per_dispatch(csv_path, counter):
     return out
 
 
+def source_digest() -> str:
+    """SHA-256 over the library's kernel and ABI sources (the build the
+    counters describe)."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "quantized_linear_layer_scaled_amd", "csrc")
+    files = sorted(os.path.join(csrc, f) for f in os.listdir(csrc)
+                   if f.endswith((".h", ".hip", ".cpp")))
+    for path in files + [os.path.join(ROOT, "include", "qll.h")]:
+        h.update(os.path.basename(path).encode())
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
 def hbm_traffic(fetch_csv, write_csv, kernel):
     """HBM bytes per launch of `kernel`: FETCH_SIZE and WRITE_SIZE (KiB per
     dispatch), each scaled by the ratio of known bytes to what the same
@@ -847,12 +866,31 @@ def main():
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_GBS, 4)}
     roof["traffic"] = None
+    digest = source_digest()
     if args.fetch_csv and args.write_csv and os.path.exists(args.fetch_csv) \
             and os.path.exists(args.write_csv):
         tr = hbm_traffic(args.fetch_csv, args.write_csv, dom_sym)
         if tr:
             roof["traffic"] = round(tr["bytes_per_launch"])
             roof["traffic_detail"] = {k: round(v, 4) for k, v in tr.items()}
+            roof["traffic_detail"]["source_digest"] = digest
+    else:
+        # counters taken earlier by the profiling runs of this workload, used
+        # only when they were taken on the same kernel built from the same
+        # sources
+        prof = os.path.join(ROOT, "profiles", f"{args.workload}_sweep_bench_line.json")
+        try:
+            with open(prof) as f:
+                old = json.load(f)["roofline"]
+        except (OSError, ValueError, KeyError):
+            old = None
+        if old and old.get("kernel") == dom_sym and old.get("traffic") and \
+                (old.get("traffic_detail") or {}).get("source_digest") == digest:
+            roof["traffic"] = old["traffic"]
+            roof["traffic_detail"] = dict(old["traffic_detail"])
+            roof["traffic_detail"]["from"] = (
+                f"profiles/{args.workload}_sweep_traffic.md: rocprofv3 --pmc FETCH_SIZE and "
+                "WRITE_SIZE runs of this workload on the same kernel and sources")
     if args.mfma_csv and os.path.exists(args.mfma_csv):
         mb = mfma_busy(args.mfma_csv, dom_sym, props.multi_processor_count)
         if mb:
