@@ -1,0 +1,91 @@
+"""Host logic of bench.py (no GPU): the rocprofv3 counter parsing and its
+calibration, the matrix-core busy fraction, the XCD fetch model and the
+source digest that ties stored counters to a build."""
+import csv
+import os
+import shutil
+import sys
+
+import pytest
+
+sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+import bench  # noqa: E402
+
+FIELDS = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+DOM = "void qll::gemm_pipe_kernel<1, 128, 128, 4, 4, 128, 4, false, false>(qll::GemmArgs)"
+CAL = "void at::native::vectorized_elementwise_kernel<4, at::native::MulFunctor<float>>(int)"
+
+
+def write_counters(path, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=FIELDS)
+        w.writeheader()
+        for i, (k, c, v) in enumerate(rows):
+            w.writerow({"Dispatch_Id": i + 1, "Kernel_Name": k, "Counter_Name": c,
+                        "Counter_Value": v})
+
+
+def test_counter_per_dispatch_groups_by_kernel(tmp_path):
+    p = tmp_path / "c.csv"
+    write_counters(p, [(DOM, "FETCH_SIZE", 10.0), (CAL, "FETCH_SIZE", 3.0),
+                       (DOM, "FETCH_SIZE", 30.0), (DOM, "WRITE_SIZE", 7.0)])
+    d = bench.counter_per_dispatch(str(p), "FETCH_SIZE")
+    assert d == {DOM: [10.0, 30.0], CAL: [3.0]}
+
+
+def test_hbm_traffic_scales_by_the_calibration_copy(tmp_path):
+    # the copy reads and writes CALIB_BYTES; its counters read half of that
+    # (factor 2), so the dominant kernel's mean KiB count doubles
+    cal_kib = bench.CALIB_BYTES / 1024.0 / 2
+    fetch, write = tmp_path / "f.csv", tmp_path / "w.csv"
+    write_counters(fetch, [(CAL, "FETCH_SIZE", 16.0), (CAL, "FETCH_SIZE", cal_kib),
+                           (DOM, "FETCH_SIZE", 1000.0), (DOM, "FETCH_SIZE", 3000.0)])
+    write_counters(write, [(CAL, "WRITE_SIZE", cal_kib), (DOM, "WRITE_SIZE", 500.0)])
+    tr = bench.hbm_traffic(str(fetch), str(write), "void qll::gemm_pipe_kernel<1, 128")
+    assert tr["FETCH_SIZE_factor"] == pytest.approx(2.0)
+    assert tr["FETCH_SIZE"] == pytest.approx(2000.0 * 1024 * 2)
+    assert tr["WRITE_SIZE"] == pytest.approx(500.0 * 1024 * 2)
+    assert tr["bytes_per_launch"] == pytest.approx((2000.0 + 500.0) * 1024 * 2)
+    # no calibration copy in the run: no figure rather than an unscaled one
+    write_counters(write, [(DOM, "WRITE_SIZE", 500.0)])
+    assert bench.hbm_traffic(str(fetch), str(write), "void qll::gemm_pipe_kernel") is None
+
+
+def test_mfma_busy_fraction(tmp_path):
+    p = tmp_path / "m.csv"
+    cus = 256
+    gui = 8 * 1000.0                      # summed over the 8 XCDs: 1000 cycles each
+    busy = 0.25 * 1000.0 * 4 * cus        # a quarter of the SIMD cycles
+    write_counters(p, [(DOM, "SQ_VALU_MFMA_BUSY_CYCLES", busy), (DOM, "GRBM_GUI_ACTIVE", gui)])
+    mb = bench.mfma_busy(str(p), "void qll::gemm_pipe_kernel", cus)
+    assert mb["mfma_busy_frac"] == pytest.approx(0.25)
+    assert mb["dispatches"] == 1
+
+
+def test_xcd_fill_bytes_bounds():
+    # one tile per XCD: every XCD fetches exactly its own rows (no sharing)
+    M, N, K, bp, bq = 256, 512, 1024, 128, 128
+    assert bench.xcd_fill_bytes(M, N, K, bp, bq) == 8 * (bp + bq) * K
+    # many tiles: between the algorithmic bytes (each row once on the whole
+    # chip) and every tile reading its own rows
+    M, N, K = 2048, 2048, 6144
+    got = bench.xcd_fill_bytes(M, N, K, 128, 128)
+    tiles = (M // 128) * (N // 128)
+    assert (M + N) * K <= got <= tiles * (128 + 128) * K
+    # ragged edges count only the rows that exist
+    assert bench.xcd_fill_bytes(100, 60, 256, 128, 128) == (100 + 60) * 256
+
+
+def test_source_digest_follows_the_sources(tmp_path, monkeypatch):
+    d0 = bench.source_digest()
+    assert len(d0) == 16 and int(d0, 16) >= 0
+    assert bench.source_digest() == d0
+    root = tmp_path / "repo"
+    shutil.copytree(os.path.join(bench.ROOT, "quantized_linear_layer_scaled_amd", "csrc"),
+                    root / "quantized_linear_layer_scaled_amd" / "csrc")
+    shutil.copytree(os.path.join(bench.ROOT, "include"), root / "include")
+    monkeypatch.setattr(bench, "ROOT", str(root))
+    assert bench.source_digest() == d0
+    with open(root / "quantized_linear_layer_scaled_amd" / "csrc" / "api.cpp", "a") as f:
+        f.write("\n")
+    assert bench.source_digest() != d0
