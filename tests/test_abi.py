@@ -315,3 +315,26 @@ def test_table_rules(qll, tmp_path):
     assert rc == 6 and "waves" in why
     assert qll.table_validate(write(tmp_path, head + f"bf16_bi 2048 2048 1 {k8} 1\n"),
                               "gfx950", 256) == (0, "")
+
+
+def test_heuristic_picks_are_registered_and_fit(qll):
+    # Without a device no table is installed, so select() reports the
+    # built-in heuristic: every pick must name a registered variant, with a
+    # split count the op accepts for that K and a workspace it can size.
+    shapes = {"int8": [(2048, 2048)], "fp8": [(4096, 2048), (2048, 6144), (151936, 2048)],
+              "block_fp8": [(12288, 2048), (2048, 6144)],
+              "bf16_bi": [(2048, 2048), (151936, 2048)],
+              "mxfp4": [(4096, 2048), (2048, 6144)], "w4a16": [(4096, 2048), (2048, 6144)]}
+    assert qll.table_entries() == 0
+    for op, nks in shapes.items():
+        names = {v["name"] for v in qll.variants(op)}
+        for N, K in nks:
+            for M in (1, 3, 16, 64, 100, 256, 1000, 2048, 8192):
+                name, splits = qll.select(op, M, N, K)
+                assert name in names, (op, M, N, K, name)
+                assert 1 <= splits <= 64
+                assert qll.effective_splits(op, K, splits) == splits, (op, M, N, K, splits)
+                if op == "bf16_bi":
+                    assert splits == 1  # batch invariance: K is never split across workgroups
+                ws = qll.workspace_bytes(op, M, N, K, (name, splits))
+                assert ws == (0 if splits == 1 else splits * M * N * 4), (op, M, N, K)
