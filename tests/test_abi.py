@@ -318,9 +318,11 @@ def test_table_rules(qll, tmp_path):
 
 
 def test_heuristic_picks_are_registered_and_fit(qll):
-    # Without a device no table is installed, so select() reports the
-    # built-in heuristic: every pick must name a registered variant, with a
-    # split count the op accepts for that K and a workspace it can size.
+    # With no table installed (qll_init(NULL): none on a GPU, and without a
+    # device none is ever installed) select() reports the built-in
+    # heuristic: every pick must name a registered variant, with a split
+    # count the op accepts for that K and a workspace it can size.
+    qll.load_library().qll_init(None)
     shapes = {"int8": [(2048, 2048)], "fp8": [(4096, 2048), (2048, 6144), (151936, 2048)],
               "block_fp8": [(12288, 2048), (2048, 6144)],
               "bf16_bi": [(2048, 2048), (151936, 2048)],
