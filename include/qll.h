@@ -305,18 +305,35 @@ int qll_grouped_select(int64_t M, int64_t E, char* buf, size_t cap);
 
 /* Load the dispatch table (per-shape tuning, "What the integration changes").
  * table_path NULL: $QLL_TABLE if set, else no table (built-in heuristic).
- * A table whose device line does not match the current device (gfx arch and
- * CU count) is not used: QLL_ERR_TABLE is returned and the heuristic stays in
- * force.  A batch-invariant section whose Split-K factor or orientation varies
- * with M for one (N, K) is rejected the same way.  Without a device the call
- * returns QLL_ERR_NO_DEVICE. */
+ * A table is keyed by device, as the review of vLLM PR #53446 keys its
+ * configs by device name after a table tuned on one H100 variant regressed
+ * another: its one device line ("device <arch> <CUs> <MHz> <name>") must
+ * match the current device's signature (see qll_device_signature) in gfx
+ * arch, CU count and peak engine clock -- MI350X and MI355X are both gfx950
+ * with 256 CUs and differ in clock -- and in device name when the table and
+ * the runtime both give one (the runtime reports an empty name in some
+ * environments, e.g. under the rocprofv3 tracer), else QLL_ERR_TABLE is
+ * returned and the heuristic stays in force.  A batch-invariant section whose
+ * effective Split-K factor varies with M for one (N, K) is rejected the same
+ * way (tile shape and orientation may vary: every batch-invariant variant sums
+ * K in the same fixed chunks, so they agree bit for bit).  Loading a table
+ * equal to one loaded before reuses it.  Without a device the call returns
+ * QLL_ERR_NO_DEVICE. */
 int qll_init(const char* table_path);
 
-/* Parse and check a dispatch table against a device signature (gfx arch name
- * and CU count) without installing it; no device needed.  Returns QLL_OK or
- * QLL_ERR_TABLE with a reason in err (NUL-terminated, truncated to cap). */
-int qll_table_validate(const char* path, const char* arch, int cus, char* err,
-                       size_t cap);
+/* Parse and check a dispatch table against a device signature (gfx arch name,
+ * CU count, peak engine clock in MHz, device name) without installing it; no
+ * device needed.  Returns QLL_OK or QLL_ERR_TABLE with a reason in err
+ * (NUL-terminated, truncated to cap); INVALID_ARG for null arguments. */
+int qll_table_validate(const char* path, const char* arch, int cus, int mhz,
+                       const char* name, char* err, size_t cap);
+
+/* The current device's signature as a table's device line holds it after the
+ * keyword: "<arch> <CUs> <MHz> <name>" (NUL-terminated into buf, cap bytes;
+ * the name may be empty).
+ * QLL_ERR_NO_DEVICE without a gfx950 device, INVALID_ARG for a null or too
+ * small buffer. */
+int qll_device_signature(char* buf, size_t cap);
 
 /* The configuration the entry point would use for this shape (table entry if
  * one exists, else the heuristic). */

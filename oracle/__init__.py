@@ -42,16 +42,36 @@ _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
 
 
+_DIGEST_PATH = _LIB_PATH + ".sha256"
+
+
+def _source_digest() -> str:
+    import hashlib
+    with open(_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def _built_digest() -> str | None:
+    try:
+        with open(_DIGEST_PATH) as f:
+            return f.read().strip()
+    except OSError:
+        return None
+
+
 def build(force: bool = True) -> str:
     """Compile ``oracle.c`` into ``liboracle.so`` with gcc (OpenMP, no FMA
-    contraction, SSE arithmetic)."""
-    if not force and os.path.exists(_LIB_PATH):
+    contraction, SSE arithmetic); the SHA-256 of the source it was built from
+    is written beside it."""
+    if not force and os.path.exists(_LIB_PATH) and _built_digest() == _source_digest():
         return _LIB_PATH
     tmp = _LIB_PATH + ".tmp"
     cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fPIC",
            "-shared", _SRC, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, _LIB_PATH)
+    with open(_DIGEST_PATH, "w") as f:
+        f.write(_source_digest() + "\n")
     return _LIB_PATH
 
 
@@ -59,9 +79,10 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB_PATH) or (
-            os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)):
-        build()
+    # rebuilt only when the source's content differs from what the library
+    # was built from (file times are not trusted: copies of the tree may
+    # reorder them)
+    build(force=False)
     lib = ctypes.CDLL(_LIB_PATH)
     lib.oracle_e4m3_decode.restype = ctypes.c_double
     lib.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]

@@ -88,7 +88,9 @@ def load_library():
     L.qll_grouped_select.argtypes = [_I64, _I64, ctypes.c_char_p, ctypes.c_size_t]
     L.qll_init.argtypes = [ctypes.c_char_p]
     L.qll_table_validate.argtypes = [ctypes.c_char_p, ctypes.c_char_p, ctypes.c_int,
-                                     ctypes.c_char_p, ctypes.c_size_t]
+                                     ctypes.c_int, ctypes.c_char_p, ctypes.c_char_p,
+                                     ctypes.c_size_t]
+    L.qll_device_signature.argtypes = [ctypes.c_char_p, ctypes.c_size_t]
     L.qll_select.argtypes = [ctypes.c_int, _I64, _I64, _I64, ctypes.POINTER(qll_cfg)]
     L.qll_workspace_bytes.argtypes = [ctypes.c_int, _I64, _I64, _I64,
                                       ctypes.POINTER(qll_cfg)]
@@ -158,6 +160,16 @@ def _stream(stream=None):
     torch = _torch()
     s = stream if stream is not None else torch.cuda.current_stream()
     return s.cuda_stream
+
+
+def _on(stream):
+    """Context in which the binding allocates what it hands to the library:
+    the stream the kernels are enqueued on, so that torch's caching allocator
+    never gives a temporary (the Split-K workspace) to other work before
+    those kernels have used it."""
+    import contextlib
+    torch = _torch()
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
 
 
 def _cfg(op: int, cfg):
@@ -230,11 +242,12 @@ def quantize_per_token_fp8(x, group: int | None = None, q=None, scales=None,
         raise ValueError("x must be a 2-D bfloat16 tensor")
     M, K = x.shape
     G = K if group in (None, 0, K) else int(group)
-    if q is None:
-        q = torch.empty((M, K), dtype=torch.float8_e4m3fn, device=x.device)
-    if scales is None:
-        scales = torch.empty((M, K // G if G else 0), dtype=torch.float32,
-                             device=x.device)
+    with _on(stream):
+        if q is None:
+            q = torch.empty((M, K), dtype=torch.float8_e4m3fn, device=x.device)
+        if scales is None:
+            scales = torch.empty((M, K // G if G else 0), dtype=torch.float32,
+                                 device=x.device)
     if tuple(q.shape) != (M, K) or tuple(scales.shape) != (M, K // G):
         raise ValueError("q / scales have the wrong shape")
     rc = load_library().quantize_per_token_fp8(
@@ -250,11 +263,12 @@ def quantize_weight_block_fp8(w, q=None, scales=None, stream=None):
     if w.dtype != torch.bfloat16 or w.dim() != 2:
         raise ValueError("w must be a 2-D bfloat16 tensor")
     N, K = w.shape
-    if q is None:
-        q = torch.empty((N, K), dtype=torch.float8_e4m3fn, device=w.device)
-    if scales is None:
-        scales = torch.empty(((N + 127) // 128, K // 128), dtype=torch.float32,
-                             device=w.device)
+    with _on(stream):
+        if q is None:
+            q = torch.empty((N, K), dtype=torch.float8_e4m3fn, device=w.device)
+        if scales is None:
+            scales = torch.empty(((N + 127) // 128, K // 128), dtype=torch.float32,
+                                 device=w.device)
     rc = load_library().quantize_weight_block_fp8(
         _dev_ptr(w, "w"), _bytes8(q, "q"), _dev_ptr(scales, "scales"), N, K,
         _stream(stream))
@@ -275,13 +289,14 @@ def _scaled_gemm(fn, op, A, B, sa, sb, sa_shape, sb_shape, out_dtype, out, cfg,
         raise ValueError(f"A is [M][{K}] but B is [N][{K2}]")
     pa, pb = _bytes8(A, "A"), _bytes8(B, "B")
     psa, psb = _f32(sa, "sa", sa_shape(M, N, K)), _f32(sb, "sb", sb_shape(M, N, K))
-    out = _out(out, M, N, out_dtype, A.device)
     c = _cfg(op, cfg)
-    ws, wsb = _workspace(op, M, N, K, c, workspace)
-    L = load_library()
-    args = [pa, pb, psa, psb, _dev_ptr(out, "out"), OUT[out_dtype], M, N, K,
-            ws.data_ptr() if ws is not None else None, wsb, _stream(stream)]
-    rc = getattr(L, fn + "_ex")(*args, ctypes.byref(c)) if c else getattr(L, fn)(*args)
+    with _on(stream):
+        out = _out(out, M, N, out_dtype, A.device)
+        ws, wsb = _workspace(op, M, N, K, c, workspace)
+        L = load_library()
+        args = [pa, pb, psa, psb, _dev_ptr(out, "out"), OUT[out_dtype], M, N, K,
+                ws.data_ptr() if ws is not None else None, wsb, _stream(stream)]
+        rc = getattr(L, fn + "_ex")(*args, ctypes.byref(c)) if c else getattr(L, fn)(*args)
     _check(fn, rc)
     return out
 
@@ -322,17 +337,18 @@ def gemm_bf16_batch_invariant(A, B, out_dtype="bf16", out=None, cfg=None,
     N, K2 = B.shape
     if K2 != K:
         raise ValueError(f"A is [M][{K}] but B is [N][{K2}]")
-    out = _out(out, M, N, out_dtype, A.device)
     c = _cfg(3, cfg)
-    ws, wsb = _workspace(3, M, N, K, c, workspace)
-    L = load_library()
-    args = [_dev_ptr(A, "A"), _dev_ptr(B, "B"), _dev_ptr(out, "out"),
-            OUT[out_dtype], M, N, K, ws.data_ptr() if ws is not None else None,
-            wsb, _stream(stream)]
-    if c:
-        rc = L.gemm_bf16_batch_invariant_ex(*args, ctypes.byref(c))
-    else:
-        rc = L.gemm_bf16_batch_invariant(*args)
+    with _on(stream):
+        out = _out(out, M, N, out_dtype, A.device)
+        ws, wsb = _workspace(3, M, N, K, c, workspace)
+        L = load_library()
+        args = [_dev_ptr(A, "A"), _dev_ptr(B, "B"), _dev_ptr(out, "out"),
+                OUT[out_dtype], M, N, K, ws.data_ptr() if ws is not None else None,
+                wsb, _stream(stream)]
+        if c:
+            rc = L.gemm_bf16_batch_invariant_ex(*args, ctypes.byref(c))
+        else:
+            rc = L.gemm_bf16_batch_invariant(*args)
     _check("gemm_bf16_batch_invariant", rc)
     return out
 
@@ -353,10 +369,11 @@ def quantize_mxfp4(x, q=None, scales=None, stream=None):
     M, K = x.shape
     if K % 32:
         raise ValueError("K must be a multiple of 32")
-    if q is None:
-        q = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
-    if scales is None:
-        scales = torch.empty((M, K // 32), dtype=torch.uint8, device=x.device)
+    with _on(stream):
+        if q is None:
+            q = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
+        if scales is None:
+            scales = torch.empty((M, K // 32), dtype=torch.uint8, device=x.device)
     rc = load_library().quantize_mxfp4(
         _dev_ptr(x, "x"), _u8(q, "q", (M, K // 2)), _u8(scales, "scales", (M, K // 32)),
         M, K, _stream(stream))
@@ -376,13 +393,14 @@ def gemm_mxfp4(A, B, sa, sb, out_dtype="bf16", out=None, cfg=None, workspace=Non
     K = 2 * K2
     pa, pb = _u8(A, "A", (M, K2)), _u8(B, "B", (N, K2))
     psa, psb = _u8(sa, "sa", (M, K // 32)), _u8(sb, "sb", (N, K // 32))
-    out = _out(out, M, N, out_dtype, A.device)
     c = _cfg(4, cfg)
-    ws, wsb = _workspace(4, M, N, K, c, workspace)
-    L = load_library()
-    args = [pa, pb, psa, psb, _dev_ptr(out, "out"), OUT[out_dtype], M, N, K,
-            ws.data_ptr() if ws is not None else None, wsb, _stream(stream)]
-    rc = L.gemm_mxfp4_ex(*args, ctypes.byref(c)) if c else L.gemm_mxfp4(*args)
+    with _on(stream):
+        out = _out(out, M, N, out_dtype, A.device)
+        ws, wsb = _workspace(4, M, N, K, c, workspace)
+        L = load_library()
+        args = [pa, pb, psa, psb, _dev_ptr(out, "out"), OUT[out_dtype], M, N, K,
+                ws.data_ptr() if ws is not None else None, wsb, _stream(stream)]
+        rc = L.gemm_mxfp4_ex(*args, ctypes.byref(c)) if c else L.gemm_mxfp4(*args)
     _check("gemm_mxfp4", rc)
     return out
 
@@ -396,10 +414,11 @@ def quantize_int4_weights(w, q=None, scales=None, stream=None):
     N, K = w.shape
     if K % 128:
         raise ValueError("K must be a multiple of 128")
-    if q is None:
-        q = torch.empty((N, K // 2), dtype=torch.uint8, device=w.device)
-    if scales is None:
-        scales = torch.empty((N, K // 128), dtype=torch.float32, device=w.device)
+    with _on(stream):
+        if q is None:
+            q = torch.empty((N, K // 2), dtype=torch.uint8, device=w.device)
+        if scales is None:
+            scales = torch.empty((N, K // 128), dtype=torch.float32, device=w.device)
     rc = load_library().quantize_int4_weights(
         _dev_ptr(w, "w"), _u8(q, "q", (N, K // 2)), _f32(scales, "scales", (N, K // 128)),
         N, K, _stream(stream))
@@ -419,13 +438,14 @@ def gemm_w4a16(A, B, scales, out_dtype="bf16", out=None, cfg=None, workspace=Non
     N = B.shape[0]
     pb = _u8(B, "B", (N, K // 2))
     ps = _f32(scales, "scales", (N, K // 128))
-    out = _out(out, M, N, out_dtype, A.device)
     c = _cfg(5, cfg)
-    ws, wsb = _workspace(5, M, N, K, c, workspace)
-    L = load_library()
-    args = [_dev_ptr(A, "A"), pb, ps, _dev_ptr(out, "out"), OUT[out_dtype], M, N, K,
-            ws.data_ptr() if ws is not None else None, wsb, _stream(stream)]
-    rc = L.gemm_w4a16_ex(*args, ctypes.byref(c)) if c else L.gemm_w4a16(*args)
+    with _on(stream):
+        out = _out(out, M, N, out_dtype, A.device)
+        ws, wsb = _workspace(5, M, N, K, c, workspace)
+        L = load_library()
+        args = [_dev_ptr(A, "A"), pb, ps, _dev_ptr(out, "out"), OUT[out_dtype], M, N, K,
+                ws.data_ptr() if ws is not None else None, wsb, _stream(stream)]
+        rc = L.gemm_w4a16_ex(*args, ctypes.byref(c)) if c else L.gemm_w4a16(*args)
     _check("gemm_w4a16", rc)
     return out
 
@@ -442,18 +462,24 @@ def linear_fp8_dynamic(x, B, sb, out_dtype="bf16", out=None, q=None, sa=None, cf
     N, K2 = B.shape
     if K2 != K:
         raise ValueError(f"x is [M][{K}] but B is [N][{K2}]")
-    if q is None:
-        q = torch.empty((M, K), dtype=torch.float8_e4m3fn, device=x.device)
-    if sa is None:
-        sa = torch.empty((M, 1), dtype=torch.float32, device=x.device)
-    out = _out(out, M, N, out_dtype, x.device)
+    # the quantizer writes M x K codes into q: its shape is checked before
+    # anything is enqueued
+    if q is not None and tuple(q.shape) != (M, K):
+        raise ValueError(f"q must have shape {(M, K)}")
     c = _cfg(1, cfg)
-    ws, wsb = _workspace(1, M, N, K, c, workspace)
-    L = load_library()
-    args = [_dev_ptr(x, "x"), _bytes8(B, "B"), _f32(sb, "sb", (N,)), _bytes8(q, "q"),
-            _f32(sa, "sa", (M,)), _dev_ptr(out, "out"), OUT[out_dtype], M, N, K,
-            ws.data_ptr() if ws is not None else None, wsb, _stream(stream)]
-    rc = L.linear_fp8_dynamic_ex(*args, ctypes.byref(c)) if c else L.linear_fp8_dynamic(*args)
+    with _on(stream):
+        if q is None:
+            q = torch.empty((M, K), dtype=torch.float8_e4m3fn, device=x.device)
+        if sa is None:
+            sa = torch.empty((M, 1), dtype=torch.float32, device=x.device)
+        out = _out(out, M, N, out_dtype, x.device)
+        ws, wsb = _workspace(1, M, N, K, c, workspace)
+        L = load_library()
+        args = [_dev_ptr(x, "x"), _bytes8(B, "B"), _f32(sb, "sb", (N,)), _bytes8(q, "q"),
+                _f32(sa, "sa", (M,)), _dev_ptr(out, "out"), OUT[out_dtype], M, N, K,
+                ws.data_ptr() if ws is not None else None, wsb, _stream(stream)]
+        rc = (L.linear_fp8_dynamic_ex(*args, ctypes.byref(c)) if c
+              else L.linear_fp8_dynamic(*args))
     _check("linear_fp8_dynamic", rc)
     return out, q, sa
 
@@ -471,7 +497,8 @@ def gemm_fp8_grouped(A, B, sa, sb, offsets, out_dtype="bf16", out=None, variant=
         raise ValueError(f"A is [M][{K}] but B is [E][N][{K2}]")
     if offsets.dtype != torch.int32 or tuple(offsets.shape) != (E + 1,):
         raise ValueError(f"offsets must be int32 of shape ({E + 1},)")
-    out = _out(out, M, N, out_dtype, A.device)
+    with _on(stream):
+        out = _out(out, M, N, out_dtype, A.device)
     args = [_bytes8(A, "A"), _bytes8(B, "B"), _f32(sa, "sa", (M,)),
             _f32(sb, "sb", (E, N)), _dev_ptr(offsets, "offsets"), _dev_ptr(out, "out"),
             OUT[out_dtype], M, N, K, E, _stream(stream)]
@@ -534,8 +561,37 @@ def table_entries() -> int:
     return load_library().qll_table_entries()
 
 
-def table_validate(path: str, arch: str = "gfx950", cus: int = 256):
-    """(status, reason) of checking a table file against a device signature."""
+def parse_signature(sig: str) -> tuple[str, int, int, str]:
+    """'<arch> <CUs> <MHz> <name>' -> (arch, cus, mhz, name); the name may be
+    empty."""
+    parts = sig.strip().split(None, 3)
+    if len(parts) < 3:
+        raise ValueError(f"bad device signature {sig!r}")
+    return parts[0], int(parts[1]), int(parts[2]), (parts[3].strip() if len(parts) > 3 else "")
+
+
+def table_signature(path: str) -> str | None:
+    """The device signature on a table file's device line (None if absent)."""
+    with open(path) as f:
+        for line in f:
+            t = line.strip()
+            if t.startswith("device ") or t.startswith("device\t"):
+                return t[len("device"):].strip()
+    return None
+
+
+def table_validate(path: str, signature: str):
+    """(status, reason) of checking a table file against a device signature
+    '<arch> <CUs> <MHz> <name>'."""
+    arch, cus, mhz, name = parse_signature(signature)
     buf = ctypes.create_string_buffer(512)
-    rc = load_library().qll_table_validate(path.encode(), arch.encode(), cus, buf, 512)
+    rc = load_library().qll_table_validate(path.encode(), arch.encode(), cus, mhz,
+                                           name.encode(), buf, 512)
     return rc, buf.value.decode()
+
+
+def device_signature() -> str:
+    """The current device's signature, as a table's device line holds it."""
+    buf = ctypes.create_string_buffer(512)
+    _check("qll_device_signature", load_library().qll_device_signature(buf, 512))
+    return buf.value.decode()

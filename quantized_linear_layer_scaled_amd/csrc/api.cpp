@@ -13,6 +13,7 @@
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -96,17 +97,40 @@ int64_t op_kbytes(int op, int64_t K)
 constexpr int64_t kMaxKMxfp4 = (int64_t)1 << 23;
 
 // The pipelined kernels address a tile's rows with 32-bit buffer offsets:
-// their tile rows times the row length in bytes must stay below 2^31.
-bool variant_fits(const Variant& v, int64_t kbytes)
+// for each operand, its tile rows times the bytes of one of its rows must stay
+// below 2^31 (A rows of W4A16 are bf16, 2K bytes; its B rows are K/2 bytes of
+// codes beside K/128 fp32 group scales).
+bool variant_fits(int op, const Variant& v, int64_t K)
 {
-    return v.name[0] != 'p' || (int64_t)v.bp * kbytes <= 0x7FFFFFFF;
+    if (v.name[0] != 'p')
+        return true;
+    const int64_t lim = 0x7FFFFFFF;
+    if (op == OP_W4A16)
+        return (int64_t)v.bp * 2 * K <= lim && (int64_t)v.bq * (K / 2) <= lim &&
+               (int64_t)v.bq * (K / 128) * 4 <= lim;
+    const int64_t kbytes = op_kbytes(op, K);
+    return (int64_t)v.bp * kbytes <= lim && (int64_t)v.bq * kbytes <= lim;
 }
 
 // ------------------------------------------------------------------ device
+// What a table is keyed by: gfx arch, compute units, peak engine clock and
+// the runtime's device name.  Two parts of one arch and CU count can still
+// differ in clock and power (MI350X and MI355X are both gfx950 with 256 CUs;
+// MI355X runs at up to 2400 MHz), and a table tuned on one can lose on the
+// other -- the cross-SKU regression that the review of vLLM PR #53446
+// reports for an H100 NVL table on H100 SXM, and why its configs are keyed
+// by device name.
+struct DeviceSig {
+    char arch[64] = {0};
+    int cus = 0;
+    int mhz = 0;
+    char name[256] = {0};
+};
+
 struct DeviceInfo {
     bool ok = false;
     int cus = 256;
-    char arch[64] = {0};
+    DeviceSig sig;
 };
 
 DeviceInfo& device_info()
@@ -127,13 +151,58 @@ DeviceInfo& device_info()
             return;
         }
         info.cus = p.multiProcessorCount;
-        std::snprintf(info.arch, sizeof info.arch, "%s", p.gcnArchName);
-        char* colon = std::strchr(info.arch, ':');
+        DeviceSig& g = info.sig;
+        std::snprintf(g.arch, sizeof g.arch, "%s", p.gcnArchName);
+        char* colon = std::strchr(g.arch, ':');
         if (colon)
             *colon = 0;
-        info.ok = std::strcmp(info.arch, "gfx950") == 0;
+        g.cus = p.multiProcessorCount;
+        g.mhz = p.clockRate / 1000;  // kHz
+        std::snprintf(g.name, sizeof g.name, "%s", p.name);
+        info.ok = std::strcmp(g.arch, "gfx950") == 0;
     });
     return info;
+}
+
+// "<arch> <cus> <mhz> <name>", the form of a table's device line after the
+// keyword.
+void format_sig(const DeviceSig& g, char* buf, size_t cap)
+{
+    std::snprintf(buf, cap, "%s %d %d %s", g.arch, g.cus, g.mhz, g.name);
+}
+
+// Parse a device line's fields (the keyword already skipped); the name is
+// the rest of the line with surrounding blanks removed.
+bool parse_sig(const char* p, DeviceSig* g)
+{
+    int used = 0;
+    char arch[64];
+    if (std::sscanf(p, "%63s %d %d %n", arch, &g->cus, &g->mhz, &used) != 3 || used <= 0)
+        return false;
+    std::snprintf(g->arch, sizeof g->arch, "%s", arch);
+    const char* q = p + used;
+    while (*q == ' ' || *q == '\t')
+        ++q;
+    size_t len = std::strlen(q);
+    while (len && (q[len - 1] == '\n' || q[len - 1] == '\r' || q[len - 1] == ' ' ||
+                   q[len - 1] == '\t'))
+        --len;
+    if (len >= sizeof g->name)
+        return false;
+    std::memcpy(g->name, q, len);
+    g->name[len] = 0;
+    return true;
+}
+
+// Arch, CU count and peak clock must match; the names too when both sides
+// have one (the runtime reports an empty name in some environments -- under
+// the rocprofv3 tracer, for one -- and the clock alone separates the gfx950
+// parts of 256 CUs).
+bool same_sig(const DeviceSig& table, const DeviceSig& dev)
+{
+    return std::strcmp(table.arch, dev.arch) == 0 && table.cus == dev.cus &&
+           table.mhz == dev.mhz &&
+           (!table.name[0] || !dev.name[0] || std::strcmp(table.name, dev.name) == 0);
 }
 
 // ------------------------------------------------------------------ table
@@ -145,21 +214,66 @@ int bucket_of(int64_t M)
     return b;
 }
 
-uint64_t table_key(int op, int64_t N, int64_t K, int bucket)
-{
-    return ((uint64_t)op << 60) ^ ((uint64_t)(N & 0xFFFFFF) << 36) ^
-           ((uint64_t)(K & 0xFFFFFF) << 12) ^ (uint64_t)bucket;
-}
-
-uint64_t shape_key(int op, int64_t N, int64_t K) { return table_key(op, N, K, 0); }
-
-struct Table {
-    std::unordered_map<uint64_t, qll_cfg> entries;
-    // batch-invariant: the Split-K factor and orientation fixed per (N, K)
-    std::unordered_map<uint64_t, std::pair<int, int>> bi_fixed;
+// (op, N, K, M bucket); bucket 0 names the whole (op, N, K) shape.
+struct Key {
+    int op;
+    int bucket;
+    int64_t N, K;
+    bool operator==(const Key& o) const
+    {
+        return op == o.op && bucket == o.bucket && N == o.N && K == o.K;
+    }
+};
+struct KeyHash {
+    size_t operator()(const Key& k) const
+    {
+        uint64_t h = (uint64_t)k.N * 0x9E3779B97F4A7C15ull;
+        h ^= ((uint64_t)k.K + 0x632BE59BD9B4E019ull) * 0xC2B2AE3D27D4EB4Full + (h << 6) + (h >> 2);
+        h ^= (uint64_t)(k.op * 8191 + k.bucket) * 0x165667B19E3779F9ull + (h << 6) + (h >> 2);
+        return (size_t)h;
+    }
 };
 
-Table* g_table = nullptr;  // replaced only by qll_init
+Key table_key(int op, int64_t N, int64_t K, int bucket) { return Key{op, bucket, N, K}; }
+
+Key shape_key(int op, int64_t N, int64_t K) { return Key{op, 0, N, K}; }
+
+struct Table {
+    std::unordered_map<Key, qll_cfg, KeyHash> entries;
+    // batch-invariant: the effective Split-K factor fixed per (N, K)
+    std::unordered_map<Key, std::pair<int, int>, KeyHash> bi_fixed;
+};
+
+std::atomic<Table*> g_table{nullptr};  // replaced only by qll_init
+
+// Every table qll_init has installed stays allocated until the process ends
+// (a call on another thread may still be reading the previous one), but a
+// table equal to one already loaded is not kept twice, so re-initializing
+// with the same file does not grow memory.
+Table* retain_table(Table* t)
+{
+    static std::mutex mu;
+    static std::vector<Table*> loaded;
+    std::lock_guard<std::mutex> lock(mu);
+    auto same = [](const Table& x, const Table& y) {
+        if (x.entries.size() != y.entries.size() || x.bi_fixed != y.bi_fixed)
+            return false;
+        for (const auto& kv : x.entries) {
+            auto it = y.entries.find(kv.first);
+            if (it == y.entries.end() || it->second.variant != kv.second.variant ||
+                it->second.splits != kv.second.splits)
+                return false;
+        }
+        return true;
+    };
+    for (Table* old : loaded)
+        if (same(*old, *t)) {
+            delete t;
+            return old;
+        }
+    loaded.push_back(t);
+    return t;
+}
 
 int find_variant(int op, const char* name)
 {
@@ -190,8 +304,7 @@ int64_t split_chunk(int op, int64_t K, int splits)
     return (chunk + kSplitGranule - 1) / kSplitGranule * kSplitGranule;
 }
 
-int load_table(const char* path, const char* arch, int cus_want, Table** out,
-               std::string* err)
+int load_table(const char* path, const DeviceSig& want, Table** out, std::string* err)
 {
     FILE* f = std::fopen(path, "r");
     if (!f) {
@@ -202,23 +315,23 @@ int load_table(const char* path, const char* arch, int cus_want, Table** out,
     char line[512];
     bool device_ok = false, device_seen = false;
     int rc = QLL_OK;
-    std::unordered_map<uint64_t, std::pair<int, int>> bi_seen;
+    std::unordered_map<Key, std::pair<int, int>, KeyHash> bi_seen;
     while (std::fgets(line, sizeof line, f)) {
         char* p = line;
         while (*p == ' ' || *p == '\t')
             ++p;
         if (*p == '#' || *p == '\n' || *p == 0)
             continue;
-        char a0[64], a1[128], a2[64];
-        if (std::strncmp(p, "device", 6) == 0) {
-            int cus = 0;
-            if (std::sscanf(p, "%63s %127s %d", a0, a1, &cus) != 3) {
+        char a0[64], a2[64];
+        if (std::strncmp(p, "device", 6) == 0 && (p[6] == ' ' || p[6] == '\t')) {
+            DeviceSig g;
+            if (device_seen || !parse_sig(p + 6, &g)) {
                 rc = QLL_ERR_TABLE;
-                *err = "bad device line";
+                *err = device_seen ? "more than one device line" : "bad device line";
                 break;
             }
             device_seen = true;
-            device_ok = std::strcmp(a1, arch) == 0 && cus == cus_want;
+            device_ok = same_sig(g, want);
             continue;
         }
         long long N = 0, K = 0;
@@ -242,7 +355,7 @@ int load_table(const char* path, const char* arch, int cus_want, Table** out,
         }
         {
             int n = 0;
-            if (!variant_fits(variants(op, &n)[vi], op_kbytes(op, K))) {
+            if (!variant_fits(op, variants(op, &n)[vi], K)) {
                 rc = QLL_ERR_TABLE;
                 *err = std::string("entry's variant does not support this K: ") + p;
                 break;
@@ -342,12 +455,14 @@ qll_cfg heuristic(int op, int64_t M, int64_t N, int64_t K)
             break;
         }
     const int64_t kbytes = op_kbytes(op, K);
-    if (!variant_fits(v[vi], kbytes))  // very long rows: the plain tiled kernel
+    if (!variant_fits(op, v[vi], K)) {  // very long rows: the plain tiled kernel
+        const char* fb = op == OP_W4A16 ? "t128x128_w2x2" : "n128x128_w2x2_k";
         for (int i = 0; i < n; ++i)
-            if (std::strncmp(v[i].name, "n128x128_w2x2_k", 15) == 0) {
+            if (std::strncmp(v[i].name, fb, std::strlen(fb)) == 0) {
                 vi = i;
                 break;
             }
+    }
     if (op == OP_BF16 || M <= 64)
         return qll_cfg{vi, 1};
     const int64_t tiles = ((v[vi].swap ? N : M) + v[vi].bp - 1) / v[vi].bp *
@@ -360,14 +475,12 @@ qll_cfg heuristic(int op, int64_t M, int64_t N, int64_t K)
 
 qll_cfg select_cfg(int op, int64_t M, int64_t N, int64_t K)
 {
-    Table* t = g_table;
+    const Table* t = g_table.load(std::memory_order_acquire);
     if (t) {
         auto it = t->entries.find(table_key(op, N, K, bucket_of(M)));
         if (it != t->entries.end())
             return it->second;
         if (op == OP_BF16) {
-            // a covered (N, K) keeps its table's split and orientation at
-            // every M
             auto fx = t->bi_fixed.find(shape_key(op, N, K));
             if (fx != t->bi_fixed.end()) {
                 // a covered (N, K) keeps its table's K split at every M
@@ -451,7 +564,7 @@ int run_gemm(int op, const void* A, const void* B, const float* sa,
     int nv = 0;
     const Variant* vs = variants(op, &nv);
     const Variant& v = vs[cfg.variant];
-    if (!variant_fits(v, op_kbytes(op, K)))
+    if (!variant_fits(op, v, K))
         return QLL_ERR_UNSUPPORTED;
     GemmArgs a;
     a.A = A;
@@ -501,6 +614,31 @@ const char* grouped_rule(int64_t M, int64_t E)
 }
 
 }  // namespace
+
+// For the entry point without a workspace argument (noalloc.hip): the
+// configuration a GEMM entry point picks for this shape, the Split-K
+// workspace it needs, and the common validated launch path.
+int gemm_plan(int op, int64_t M, int64_t N, int64_t K, qll_cfg* cfg, uint64_t* ws_need)
+{
+    *cfg = select_cfg(op, M, N, K);
+    const int s = effective_splits(op, K, cfg->splits);
+    *ws_need = s > 1 ? (uint64_t)s * (uint64_t)M * (uint64_t)N * 4u : 0u;
+    return QLL_OK;
+}
+
+int gemm_run(int op, const void* A, const void* B, const float* sa, const float* sb,
+             void* out, int out_dtype, int64_t M, int64_t N, int64_t K, void* ws,
+             size_t ws_bytes, void* stream, const qll_cfg* cfg)
+{
+    return run_gemm(op, A, B, sa, sb, out, out_dtype, M, N, K, ws, ws_bytes, stream, cfg);
+}
+
+int gemm_validate(int op, const void* A, const void* B, const float* sa, const float* sb,
+                  const void* out, int out_dtype, int64_t M, int64_t N, int64_t K)
+{
+    return validate_gemm(op, A, B, sa, sb, out, out_dtype, M, N, K);
+}
+
 }  // namespace qll
 
 using namespace qll;
@@ -701,7 +839,7 @@ int linear_fp8_dynamic_ex(const void* x, const void* B, const float* sb, void* q
     const qll_cfg c = cfg ? *cfg : select_cfg(OP_FP8, M, N, K);
     // the GEMM's own checks, before anything is enqueued
     int nv = 0;
-    if (!variant_fits(variants(OP_FP8, &nv)[c.variant], K))
+    if (!variant_fits(OP_FP8, variants(OP_FP8, &nv)[c.variant], K))
         return QLL_ERR_UNSUPPORTED;
     const int splits = effective_splits(OP_FP8, K, c.splits);
     if (splits > 1) {
@@ -762,7 +900,7 @@ int gemm_fp8_grouped_ex(const void* A, const void* B, const float* sa, const flo
     if (misaligned(A, 16) || misaligned(B, 16) || misaligned(out, 16) || misaligned(sa, 4) ||
         misaligned(sb, 4) || misaligned(offsets, 4))
         return QLL_ERR_MISALIGNED;
-    if (!variant_fits(vs[vi], K))
+    if (!variant_fits(OP_FP8, vs[vi], K))
         return QLL_ERR_UNSUPPORTED;
     GemmArgs a;
     a.A = A;
@@ -797,44 +935,57 @@ int qll_init(const char* table_path)
     const char* path = table_path;
     if (!path || !*path)
         path = std::getenv("QLL_TABLE");
-    if (!device_info().ok) {
-        int n = 0;
-        if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) {
-            (void)hipGetLastError();
-            return QLL_ERR_NO_DEVICE;
-        }
+    if (!device_info().ok)
         return QLL_ERR_NO_DEVICE;
-    }
     if (!path || !*path) {
-        g_table = nullptr;  // an old table stays allocated: calls may race
+        g_table.store(nullptr, std::memory_order_release);
         return QLL_OK;
     }
     Table* t = nullptr;
     std::string err;
-    const DeviceInfo& dev = device_info();
-    int rc = load_table(path, dev.arch, dev.cus, &t, &err);
+    int rc = load_table(path, device_info().sig, &t, &err);
     if (rc != QLL_OK) {
         if (std::getenv("QLL_LOG"))
             std::fprintf(stderr, "qll: table %s not used: %s\n", path, err.c_str());
-        g_table = nullptr;
+        g_table.store(nullptr, std::memory_order_release);
         return rc;
     }
-    g_table = t;
+    Table* kept = retain_table(t);  // (t itself may be gone now)
+    g_table.store(kept, std::memory_order_release);
     if (std::getenv("QLL_LOG"))
-        std::fprintf(stderr, "qll: table %s: %zu entries\n", path, t->entries.size());
+        std::fprintf(stderr, "qll: table %s: %zu entries\n", path, kept->entries.size());
     return QLL_OK;
 }
 
-int qll_table_validate(const char* path, const char* arch, int cus, char* err,
-                       size_t cap)
+int qll_table_validate(const char* path, const char* arch, int cus, int mhz,
+                       const char* name, char* err, size_t cap)
 {
-    if (!path || !arch)
+    if (!path || !arch || !name)
         return QLL_ERR_INVALID_ARG;
+    DeviceSig want;
+    std::snprintf(want.arch, sizeof want.arch, "%s", arch);
+    want.cus = cus;
+    want.mhz = mhz;
+    std::snprintf(want.name, sizeof want.name, "%s", name);
     std::string e;
-    const int rc = load_table(path, arch, cus, nullptr, &e);
+    const int rc = load_table(path, want, nullptr, &e);
     if (err && cap)
         std::snprintf(err, cap, "%s", e.c_str());
     return rc;
+}
+
+int qll_device_signature(char* buf, size_t cap)
+{
+    if (!buf || cap == 0)
+        return QLL_ERR_INVALID_ARG;
+    if (!device_info().ok)
+        return QLL_ERR_NO_DEVICE;
+    char tmp[400];
+    format_sig(device_info().sig, tmp, sizeof tmp);
+    if (std::strlen(tmp) + 1 > cap)
+        return QLL_ERR_INVALID_ARG;
+    std::memcpy(buf, tmp, std::strlen(tmp) + 1);
+    return QLL_OK;
 }
 
 int qll_select(int op, int64_t M, int64_t N, int64_t K, qll_cfg* cfg_out)
@@ -894,7 +1045,7 @@ int qll_variant_index(int op, const char* name)
 
 int qll_table_entries(void)
 {
-    Table* t = g_table;
+    const Table* t = g_table.load(std::memory_order_acquire);
     return t ? (int)t->entries.size() : 0;
 }
 

@@ -896,7 +896,7 @@ template <int OP, int BP, int BQ, int WP, int WQ, int KSTAGE, int STAGES>
 hipError_t launch_pipe(const GemmArgs& a, hipStream_t stream)
 {
     const long tiles = (long)((a.M + BP - 1) / BP) * ((a.N + BQ - 1) / BQ);
-    if (tiles > 0x7FFFFFFFL || (long)BP * a.kbytes > 0x7FFFFFFFL)
+    if (tiles > 0x7FFFFFFFL || (long)(BP > BQ ? BP : BQ) * a.kbytes > 0x7FFFFFFFL)
         return hipErrorInvalidValue;  // 32-bit buffer offsets within a tile
     if (a.splits > 1)
         hipLaunchKernelGGL((gemm_pipe_kernel<OP, BP, BQ, WP, WQ, KSTAGE, STAGES, true>),
@@ -912,7 +912,8 @@ template <int OP, int BP, int BQ, int WP, int WQ, int KSTAGE, int STAGES>
 hipError_t launch_pipe_grouped(const GemmArgs& a, hipStream_t stream)
 {
     const long tiles = (long)((a.M + BP - 1) / BP + a.E) * ((a.N + BQ - 1) / BQ);
-    if (a.splits != 1 || tiles > 0x7FFFFFFFL || (long)BP * a.kbytes > 0x7FFFFFFFL)
+    if (a.splits != 1 || tiles > 0x7FFFFFFFL ||
+        (long)(BP > BQ ? BP : BQ) * a.kbytes > 0x7FFFFFFFL)
         return hipErrorInvalidValue;
     hipLaunchKernelGGL((gemm_pipe_kernel<OP, BP, BQ, WP, WQ, KSTAGE, STAGES, false, true>),
                        dim3((unsigned)tiles, 1), dim3(WP * WQ * 64), 0, stream, a);

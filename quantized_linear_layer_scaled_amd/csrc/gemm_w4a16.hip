@@ -721,7 +721,8 @@ template <int BP, int BQ, int WP, int WQ, int S>
 hipError_t launch_w4_pipe(const GemmArgs& a, hipStream_t stream)
 {
     const long tiles = (long)((a.M + BP - 1) / BP) * ((a.N + BQ - 1) / BQ);
-    if (tiles > 0x7FFFFFFFL || (long)BP * a.K * 2 > 0x7FFFFFFFL)
+    if (tiles > 0x7FFFFFFFL || (long)BP * a.K * 2 > 0x7FFFFFFFL ||
+        (long)BQ * (a.K / 2) > 0x7FFFFFFFL || (long)BQ * (a.K / 128) * 4 > 0x7FFFFFFFL)
         return hipErrorInvalidValue;  // 32-bit buffer offsets within a tile
     hipLaunchKernelGGL((gemm_w4_pipe_kernel<BP, BQ, WP, WQ, S>),
                        dim3((unsigned)tiles, (unsigned)a.splits), dim3(WP * WQ * 64), 0, stream,

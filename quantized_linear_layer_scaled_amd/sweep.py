@@ -8,23 +8,30 @@ configuration), done on the device the table will serve, as in vLLM PR
 
 For every (op, N, K) and every M bucket (powers of two) it runs each
 registered kernel variant with each Split-K factor through the C entry
-point with a forced configuration, checks the result against a reference
-configuration of the same op (bit-exact for the INT8 int32 accumulators,
-normwise 1e-2 otherwise -- the oracle parity is the test suite's job), times
-the whole call (tile kernel plus Split-K reduction) by replaying a HIP graph
-of back-to-back calls that rotate through enough copies of the weights to
+point with a forced configuration, checks the result against an independent
+reference -- a float64 product of the decoded operands and scales computed
+with torch on the device (exact integer accumulators for INT8; normwise
+within 2e-3 for the fp32 output of the other ops) --, times the whole call
+(tile kernel plus Split-K reduction) by replaying a HIP graph of
+back-to-back calls that rotate through enough copies of the weights to
 exceed the 256 MB Infinity Cache (cold weights, as in serving, where every
 layer's weights come from HBM; the activations stay the same, as when the
 previous kernel has just written them), and keeps the fastest configuration
-per bucket.  The batch-invariant op only
-considers configurations without a cross-workgroup K split and whose waves,
-if they split K, split it into the op's fixed eight chunks, so the table it
-produces is accepted by the loader.
+per bucket.  The batch-invariant op only considers configurations without a
+cross-workgroup K split and whose waves, if they split K, split it into the
+op's fixed eight chunks, so the table it produces is accepted by the loader.
+
+Searches like this take long ("The costs behind the gains": ahead-of-time
+searches can take hours), so every finished (shape, M, configuration) is
+appended to a log as one JSON line the moment it is measured, and a run
+given the same log skips what the log already holds: a killed sweep resumes
+where it stopped.  The table is written from the log at the end.
 
     python -m quantized_linear_layer_scaled_amd.sweep --out tables/gfx950.tsv
     python -m quantized_linear_layer_scaled_amd.sweep --ops fp8 --shapes 4096x2048 --report
 
-The output is an append-free text table: one "device <arch> <CUs>" line and
+The table is plain text: one "device <arch> <CUs> <MHz> <name>" line (the
+device signature the library matches it against) and
 "op N K bucket variant splits  # us tflops" lines.
 """
 from __future__ import annotations
@@ -160,40 +167,131 @@ def time_config(torch, qll, op, A, Bs, sa, sb, cfg, ws, reps):
     return s.elapsed_time(e) * 1e3 / (2 * reps), outs[0]
 
 
-def sweep_shape(torch, qll, op, N, K, mlist, reps, log):
+_E2M1 = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def reference(torch, op, A, B, sa, sb):
+    """The op's product in float64 from the decoded operands and scales, on
+    the device: the acceptance check of every timed configuration (exact for
+    INT8, whose int32 accumulators it holds as integers)."""
+    f64 = torch.float64
+    if op == "int8":
+        return A.to(f64) @ B.to(f64).T
+    if op == "bf16_bi":
+        return A.to(f64) @ B.to(f64).T
+    if op == "fp8":
+        ref = A.float().to(f64) @ B.float().to(f64).T
+        return ref * sa.to(f64)[:, None] * sb.to(f64)[None, :]
+    if op == "block_fp8":
+        M, K = A.shape
+        N = B.shape[0]
+        a, b = A.float().to(f64), B.float().to(f64)
+        sbn = sb.to(f64).repeat_interleave(128, dim=0)[:N]  # [N][K/128]
+        ref = torch.zeros((M, N), dtype=f64, device=A.device)
+        for g in range(K // 128):
+            k = slice(128 * g, 128 * g + 128)
+            ref += (a[:, k] @ b[:, k].T) * (sa.to(f64)[:, g, None] * sbn[None, :, g])
+        return ref
+    if op == "mxfp4":
+        lut = torch.tensor(_E2M1 + [-v for v in _E2M1], dtype=f64, device=A.device)
+
+        def dec(codes, scales):
+            lo, hi = (codes & 15).long(), (codes >> 4).long()
+            v = torch.stack([lut[lo], lut[hi]], dim=-1).reshape(codes.shape[0], -1)
+            s = torch.exp2(scales.to(f64) - 127.0).repeat_interleave(32, dim=1)
+            return v * s
+        return dec(A, sa) @ dec(B, sb).T
+    if op == "w4a16":
+        lo, hi = (B & 15).to(torch.int16), (B >> 4).to(torch.int16)
+        v = torch.stack([lo, hi], dim=-1).reshape(B.shape[0], -1)
+        v = torch.where(v >= 8, v - 16, v).to(f64)
+        w = v * sb.to(f64).repeat_interleave(128, dim=1)
+        return A.to(f64) @ w.T
+    raise ValueError(op)
+
+
+def accept(torch, op, got, ref):
+    """INT8: the int32 accumulators equal the exact ones; otherwise the fp32
+    output is within 1e-3 of the float64 product, normwise (a broken
+    configuration -- a tile, split or K range handled wrongly -- is off by
+    O(1))."""
+    if op == "int8":
+        return bool(torch.equal(got.to(torch.float64), ref))
+    den = ref.abs().max().item() or 1.0
+    return bool(torch.isfinite(got).all()) and \
+        (got.double() - ref).abs().max().item() / den <= 1e-3
+
+
+def read_log(path):
+    """Entries of an append-only sweep log: key -> record.  A line cut short
+    by a kill is skipped (its configuration is measured again)."""
+    done = {}
+    if not path or not os.path.exists(path):
+        return done
+    with open(path) as f:
+        for line in f:
+            try:
+                r = json.loads(line)
+                done[r["key"]] = r
+            except (ValueError, KeyError):
+                continue
+    return done
+
+
+def entry_key(op, N, K, M, cfg):
+    return f"{op} {N} {K} {M} {cfg[0]} {cfg[1]}"
+
+
+def sweep_shape(torch, qll, op, N, K, mlist, reps, log, done=None, record=None):
+    """Best configuration per M for one (op, N, K).  `done` holds log records
+    of configurations measured before (skipped here); `record` receives each
+    new one as it is measured."""
+    done = {} if done is None else done
+    record = record or (lambda r: None)
     row_bytes = {"bf16_bi": 2 * K, "mxfp4": K // 2, "w4a16": K // 2}.get(op, K)
     # rotate through at least COLD_BYTES of weights per graph replay
     copies = max(2, min(64, -(-COLD_BYTES // max(1, N * row_bytes))))
     reps = max(reps, copies)
     Mmax = max(mlist)
-    A_all, Bs, sa_all, sb = _inputs(torch, op, Mmax, N, K, copies)
+    state = {}
+
+    def inputs():
+        if not state:
+            state["all"] = _inputs(torch, op, Mmax, N, K, copies)
+        return state["all"]
+
     results = {}
+    timed = 0
     for M in mlist:
-        A = A_all[:M].contiguous()
-        sa = sa_all[:M].contiguous() if sa_all is not None else None
         cands = candidates(qll, op, M, N, K)
-        need = max(qll.workspace_bytes(op, M, N, K, c) for c in cands)
-        ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
-        # reference: the plain heuristic choice without Split-K
-        ref_cfg = (qll.select(op, M, N, K)[0], 1)
-        if op == "int8":
-            ref = _call(qll, op, A, Bs[0], sa, sb, "int32", ref_cfg, ws)
-        else:
-            ref = _call(qll, op, A, Bs[0], sa, sb, "fp32", ref_cfg, ws).double()
-        rows = []
-        for cfg in cands:
-            if op == "int8":
-                got = _call(qll, op, A, Bs[0], sa, sb, "int32", cfg, ws)
-                ok = torch.equal(got, ref)
-            else:
-                got = _call(qll, op, A, Bs[0], sa, sb, "fp32", cfg, ws).double()
-                den = ref.abs().max().item() or 1.0
-                ok = (got - ref).abs().max().item() / den <= 1e-4
-            if not ok:
-                log(f"  PARITY FAIL {op} M={M} N={N} K={K} {cfg}")
-                continue
-            us, _ = time_config(torch, qll, op, A, Bs, sa, sb, cfg, ws, reps)
-            rows.append((us, cfg))
+        todo = [c for c in cands if entry_key(op, N, K, M, c) not in done]
+        rows = [(done[entry_key(op, N, K, M, c)]["us"], c) for c in cands
+                if entry_key(op, N, K, M, c) in done and done[entry_key(op, N, K, M, c)]["ok"]]
+        if todo:
+            A_all, Bs, sa_all, sb = inputs()
+            A = A_all[:M].contiguous()
+            sa = sa_all[:M].contiguous() if sa_all is not None else None
+            need = max(qll.workspace_bytes(op, M, N, K, c) for c in todo)
+            ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+            ref = reference(torch, op, A, Bs[0], sa, sb)
+            for cfg in todo:
+                got = _call(qll, op, A, Bs[0], sa, sb, "int32" if op == "int8" else "fp32",
+                            cfg, ws)
+                ok = accept(torch, op, got, ref)
+                us = None
+                if ok:
+                    us, _ = time_config(torch, qll, op, A, Bs, sa, sb, cfg, ws, reps)
+                    rows.append((us, cfg))
+                else:
+                    log(f"  PARITY FAIL {op} M={M} N={N} K={K} {cfg}")
+                rec = {"key": entry_key(op, N, K, M, cfg), "ok": ok, "us": us}
+                done[rec["key"]] = rec
+                record(rec)
+                timed += 1
+            del ws, ref
+        if not rows:
+            log(f"  {op} N={N} K={K} M={M}: no configuration passed")
+            continue
         rows.sort()
         best_us, best = rows[0]
         tflops = 2.0 * M * N * K / best_us / 1e6
@@ -201,8 +299,8 @@ def sweep_shape(torch, qll, op, N, K, mlist, reps, log):
         log(f"  {op} N={N} K={K} M={M}: best {best[0]} S={best[1]} {best_us:.2f} us "
             f"{tflops:.1f} TFLOPS; next: " +
             ", ".join(f"{c[0]}/S{c[1]} {u:.2f}" for u, c in rows[1:4]))
-        del ws
-    return results
+    state.clear()
+    return results, timed
 
 
 def main(argv=None):
@@ -212,6 +310,9 @@ def main(argv=None):
     ap.add_argument("--m", default=None, help="M values (default: 1..2048 powers of two)")
     ap.add_argument("--reps", type=int, default=20)
     ap.add_argument("--out", default=None, help="table path to write")
+    ap.add_argument("--log", default=None,
+                    help="append-only log of every measured configuration; a run "
+                         "given an existing log resumes from it (default: <out>.log.jsonl)")
     ap.add_argument("--json", default=None, help="also write all timings as JSON")
     args = ap.parse_args(argv)
 
@@ -220,37 +321,59 @@ def main(argv=None):
     import quantized_linear_layer_scaled_amd as qll
     qll.load_library()
     qll.init(None)  # sweep against the heuristic, never a stale table
-    props = torch.cuda.get_device_properties(0)
-    arch = getattr(props, "gcnArchName", "gfx950").split(":")[0]
-    cus = props.multi_processor_count
+    sig = qll.device_signature()
     mlist = [int(x) for x in args.m.split(",")] if args.m else DEFAULT_M
     log = lambda s: print(s, flush=True)
-    log(f"# sweep on {arch} with {cus} CUs")
+    log_path = args.log or (args.out + ".log.jsonl" if args.out else None)
+    done = read_log(log_path)
+    if done:
+        log(f"# resuming: {len(done)} configurations already measured in {log_path}")
+    logf = open(log_path, "a") if log_path else None
+    if logf and logf.tell() > 0:
+        with open(log_path, "rb") as f:
+            f.seek(-1, os.SEEK_END)
+            if f.read(1) != b"\n":
+                logf.write("\n")  # a record cut short by a kill stays on its own line
+
+    def record(rec):
+        if logf:
+            logf.write(json.dumps(rec) + "\n")
+            logf.flush()
+            os.fsync(logf.fileno())
+
+    log(f"# sweep on {sig}")
     lines = [f"# scaled_mm dispatch table, written by quantized_linear_layer_scaled_amd.sweep",
              f"# {time.strftime('%Y-%m-%d %H:%M:%S')}; reps {args.reps}",
-             f"device {arch} {cus}"]
+             f"device {sig}"]
     dump = {}
+    timed = 0
     for op in args.ops.split(","):
         shapes = DEFAULT_SHAPES[op]
         if args.shapes:
             shapes = [tuple(int(v) for v in s.split("x")) for s in args.shapes.split(",")]
         for N, K in shapes:
-            res = sweep_shape(torch, qll, op, N, K, mlist, args.reps, log)
+            res, n = sweep_shape(torch, qll, op, N, K, mlist, args.reps, log, done, record)
+            timed += n
             for M, (best, us, tf, top) in res.items():
                 lines.append(f"{op} {N} {K} {M} {best[0]} {best[1]}  # {us:.2f} us {tf:.1f} TFLOPS")
                 dump[f"{op} {N} {K} {M}"] = [[c[0], c[1], u] for u, c in top]
             torch.cuda.empty_cache()
+    if logf:
+        logf.close()
     text = "\n".join(lines) + "\n"
     if args.out:
         os.makedirs(os.path.dirname(os.path.abspath(args.out)), exist_ok=True)
-        with open(args.out, "w") as f:
+        tmp = args.out + ".tmp"
+        with open(tmp, "w") as f:
             f.write(text)
-        log(f"# wrote {args.out}")
+        os.replace(tmp, args.out)
+        log(f"# wrote {args.out} ({timed} configurations measured in this run)")
     else:
         sys.stdout.write(text)
     if args.json:
         with open(args.json, "w") as f:
             json.dump(dump, f, indent=1)
+    return {"timed": timed, "entries": len(lines) - 3}
 
 
 if __name__ == "__main__":

@@ -73,3 +73,42 @@ def sample_rows(M: int, n: int, seed: int = 0) -> np.ndarray:
     g = np.random.default_rng([seed, M])
     r = set([0, M - 1]) | set(g.choice(M, size=n - 2, replace=False).tolist())
     return np.array(sorted(r), dtype=np.int64)
+
+
+def check_all_rows(y: torch.Tensor, ref: torch.Tensor, out_dtype: str, what: str = ""):
+    """Every row of a full-size output against a float64 product computed on
+    the device (decoded operands times scales, a test-only reference): all
+    values finite and each row within the normwise bar of its own largest
+    reference value.  The oracle's sampled rows carry the elementwise bound;
+    this catches a tile that is misplaced or never written anywhere in the
+    output."""
+    yd = y.to(torch.float64)
+    assert bool(torch.isfinite(yd).all()), f"{what}: non-finite output"
+    tol = 1e-2 if out_dtype == "bf16" else 2e-3
+    err = (yd - ref).abs().amax(dim=1)
+    den = ref.abs().amax(dim=1).clamp_min(1e-300)
+    worst = (err / den).max().item() if err.numel() else 0.0
+    assert worst <= tol, f"{what}: a row's normwise error {worst:.3e} > {tol}"
+    return worst
+
+
+def fp8_product(q: torch.Tensor, qB: torch.Tensor, sa: torch.Tensor, sb: torch.Tensor):
+    """float64 (q * sa) (qB * sb)^T on the device, per-token x per-channel."""
+    f64 = torch.float64
+    ref = q.float().to(f64) @ qB.float().to(f64).T
+    return ref * sa.reshape(-1, 1).to(f64) * sb.reshape(1, -1).to(f64)
+
+
+def block_fp8_product(q: torch.Tensor, qB: torch.Tensor, sa: torch.Tensor, sb: torch.Tensor):
+    """float64 Block-FP8 product on the device: sum over 128-wide K groups of
+    the group's partial times sa[m][g] * sb[n / 128][g]."""
+    f64 = torch.float64
+    M, K = q.shape
+    N = qB.shape[0]
+    a, b = q.float().to(f64), qB.float().to(f64)
+    sbn = sb.to(f64).repeat_interleave(128, dim=0)[:N]
+    ref = torch.zeros((M, N), dtype=f64, device=q.device)
+    for g in range(K // 128):
+        k = slice(128 * g, 128 * g + 128)
+        ref += (a[:, k] @ b[:, k].T) * (sa.to(f64)[:, g, None] * sbn[None, :, g])
+    return ref

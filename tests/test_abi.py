@@ -276,45 +276,133 @@ def write(tmp_path, text):
     return str(p)
 
 
-def test_shipped_table_is_valid_for_mi355x(qll):
+SIG = "gfx950 256 2400 AMD Instinct MI355X"
+
+
+def test_shipped_table_is_keyed_by_device(qll):
     path = os.path.join(os.path.dirname(qll.LIB_PATH), "tables", "gfx950.tsv")
-    rc, why = qll.table_validate(path, "gfx950", 256)
+    sig = qll.table_signature(path)
+    arch, cus, mhz, name = qll.parse_signature(sig)
+    assert (arch, cus) == ("gfx950", 256) and mhz > 0 and name
+    rc, why = qll.table_validate(path, sig)
     assert rc == 0, why
-    rc, why = qll.table_validate(path, "gfx942", 304)
-    assert rc == 6 and "another device" in why
+    # a runtime that reports no name (as under the rocprofv3 tracer) is
+    # matched on arch, CUs and clock
+    assert qll.table_validate(path, f"{arch} {cus} {mhz}") == (0, "")
+    # the same arch and CU count at another clock (MI350X runs gfx950 with
+    # 256 CUs at a lower peak clock), another name, or another arch: rejected
+    for other in (f"{arch} {cus} {mhz - 200} {name}", f"{arch} {cus} {mhz} {name} X",
+                  f"gfx942 304 {mhz} {name}", f"{arch} 304 {mhz} {name}"):
+        rc, why = qll.table_validate(path, other)
+        assert rc == 6 and "another device" in why, other
 
 
 def test_table_rules(qll, tmp_path):
     fp8 = qll.variants("fp8")[0]["name"]
     bi = [v["name"] for v in qll.variants("bf16_bi")]
     single = [n for n in bi if n[0] != "k"]
-    head = "# test\ndevice gfx950 256\n"
+    head = f"# test\ndevice {SIG}\n"
     ok = write(tmp_path, head + f"fp8 4096 2048 1 {fp8} 2\nfp8 4096 2048 2 {fp8} 1\n")
-    assert qll.table_validate(ok, "gfx950", 256) == (0, "")
-    assert qll.table_validate(ok, "gfx950", 304)[0] == 6
-    assert qll.table_validate(write(tmp_path, f"fp8 4096 2048 1 {fp8} 2\n"), "gfx950", 256)[0] == 6
-    assert qll.table_validate(write(tmp_path, head + "fp8 4096 2048 3 x 1\n"), "gfx950", 256)[0] == 6
-    assert qll.table_validate(write(tmp_path, head + f"fp8 4096 2048 3 {fp8} 1\n"), "gfx950", 256)[0] == 6
-    assert qll.table_validate(write(tmp_path, head + f"int4 4096 2048 4 {fp8} 1\n"), "gfx950", 256)[0] == 6
-    assert qll.table_validate(str(tmp_path / "missing.tsv"), "gfx950", 256)[0] == 6
+    assert qll.table_validate(ok, SIG) == (0, "")
+    assert qll.table_validate(ok, "gfx950 304 2400 AMD Instinct MI355X")[0] == 6
+    assert qll.table_validate(ok, "gfx950 256 2200 AMD Instinct MI355X")[0] == 6
+    assert qll.table_validate(ok, "gfx950 256 2200")[0] == 6
+    assert qll.table_validate(ok, "gfx950 256 2400") == (0, "")
+    # a table written where the runtime reported no name matches on the rest
+    noname = write(tmp_path, f"device gfx950 256 2400\nfp8 4096 2048 1 {fp8} 2\n")
+    assert qll.table_validate(noname, SIG) == (0, "")
+    # no device line, a device line without clock and name, or two of them
+    assert qll.table_validate(write(tmp_path, f"fp8 4096 2048 1 {fp8} 2\n"), SIG)[0] == 6
+    rc, why = qll.table_validate(write(tmp_path, "device gfx950 256\n"), SIG)
+    assert rc == 6 and "device line" in why
+    rc, why = qll.table_validate(write(tmp_path, head + f"device {SIG}\n"), SIG)
+    assert rc == 6 and "device line" in why
+    assert qll.table_validate(write(tmp_path, head + "fp8 4096 2048 3 x 1\n"), SIG)[0] == 6
+    assert qll.table_validate(write(tmp_path, head + f"fp8 4096 2048 3 {fp8} 1\n"), SIG)[0] == 6
+    assert qll.table_validate(write(tmp_path, head + f"int4 4096 2048 4 {fp8} 1\n"), SIG)[0] == 6
+    assert qll.table_validate(str(tmp_path / "missing.tsv"), SIG)[0] == 6
     # batch-invariant: one effective K split per (N, K) ...
     good = write(tmp_path, head + f"bf16_bi 2048 2048 1 {single[0]} 1\n"
                                    f"bf16_bi 2048 2048 2 {single[1]} 1\n"
                                    f"bf16_bi 4096 2048 2 {single[1]} 2\n")
-    assert qll.table_validate(good, "gfx950", 256) == (0, "")
+    assert qll.table_validate(good, SIG) == (0, "")
     bad = write(tmp_path, head + f"bf16_bi 2048 2048 1 {single[0]} 1\n"
                                   f"bf16_bi 2048 2048 2048 {single[1]} 2\n")
-    rc, why = qll.table_validate(bad, "gfx950", 256)
+    rc, why = qll.table_validate(bad, SIG)
     assert rc == 6 and "split" in why
     # ... and no variant whose waves split K into other than the eight chunks
     vs = qll.variants("bf16_bi")
     k8 = [v["name"] for v in vs if v["name"][0] == "k" and v["wp"] == 8][0]
     k16 = [v["name"] for v in vs if v["name"][0] == "k" and v["wp"] == 16][0]
-    rc, why = qll.table_validate(write(tmp_path, head + f"bf16_bi 2048 2048 1 {k16} 1\n"),
-                                 "gfx950", 256)
+    rc, why = qll.table_validate(write(tmp_path, head + f"bf16_bi 2048 2048 1 {k16} 1\n"), SIG)
     assert rc == 6 and "waves" in why
     assert qll.table_validate(write(tmp_path, head + f"bf16_bi 2048 2048 1 {k8} 1\n"),
-                              "gfx950", 256) == (0, "")
+                              SIG) == (0, "")
+    # a pipelined entry whose tile rows times the row bytes of either operand
+    # reach 2^31 is refused (its 32-bit buffer offsets would wrap)
+    rc, why = qll.table_validate(
+        write(tmp_path, head + "fp8 4096 16777216 1 p64x128_w2x2_k128_s2 1\n"), SIG)
+    assert rc == 6 and "K" in why
+    assert qll.table_validate(
+        write(tmp_path, head + "fp8 4096 16777216 1 p128x64_w2x2_k128_s2 1\n"), SIG)[0] == 6
+    assert qll.table_validate(
+        write(tmp_path, head + "fp8 4096 8388608 1 p64x128_w2x2_k128_s2 1\n"), SIG) == (0, "")
+    rc, why = qll.table_validate(
+        write(tmp_path, head + "w4a16 4096 8388608 1 p128x64_w2x2_s2 1\n"), SIG)
+    assert rc == 6 and "K" in why
+
+
+def test_long_rows_select_a_fitting_variant(qll):
+    # The heuristic never picks a pipelined tile whose rows of either operand
+    # span 2^31 bytes or more; it falls back to the plain tiled kernel.
+    qll.load_library().qll_init(None)
+    lim = 0x7FFFFFFF
+    for op, K in (("fp8", 1 << 25), ("int8", 1 << 25), ("bf16_bi", 1 << 24),
+                  ("w4a16", 1 << 24), ("fp8", 1 << 22)):
+        for M in (128, 2048, 8192):
+            name, _ = qll.select(op, M, 4096, K)
+            v = [x for x in qll.variants(op) if x["name"] == name][0]
+            if name[0] == "p":
+                rowa = 2 * K if op in ("w4a16", "bf16_bi") else K
+                rowb = K // 2 if op == "w4a16" else rowa
+                assert v["bp"] * rowa <= lim and v["bq"] * rowb <= lim, (op, M, K, name)
+            if K >= (1 << 24):
+                assert name[0] != "p", (op, M, K, name)
+
+
+def test_forced_variant_too_long_for_its_tile_is_unsupported(qll):
+    # p64x128: A rows fit (64 x 2^24 bytes = 2^30) but B rows do not
+    # (128 x 2^24 = 2^31): refused before any launch (the pointers are fake)
+    L = qll.load_library()
+    vi = L.qll_variant_index(1, b"p64x128_w2x2_k128_s2")
+    c = qll.qll_cfg(vi, 1)
+    rc = L.gemm_fp8_scaled_ex(P, P, P, P, P, 0, 16, 16, 1 << 24, None, 0, None,
+                              ctypes.byref(c))
+    assert rc == 2  # QLL_ERR_UNSUPPORTED
+    vi = L.qll_variant_index(5, b"p128x64_w2x2_s2")
+    c = qll.qll_cfg(vi, 1)
+    # W4A16 A rows are bf16: 128 x 2 x 2^23 bytes = 2^31
+    rc = L.gemm_w4a16_ex(P, P, P, P, 0, 16, 16, 1 << 23, None, 0, None, ctypes.byref(c))
+    assert rc == 2
+
+
+def test_linear_fp8_dynamic_rejects_wrong_q_shape(qll):
+    # checked in the binding before anything is enqueued (CPU tensors: the
+    # shape check comes before any device-pointer check)
+    import torch
+    x = torch.zeros((4, 32), dtype=torch.bfloat16)
+    B = torch.zeros((8, 32), dtype=torch.float8_e4m3fn)
+    sb = torch.zeros((8,), dtype=torch.float32)
+    q = torch.zeros((2, 32), dtype=torch.float8_e4m3fn)
+    with pytest.raises(ValueError, match="q must have shape"):
+        qll.linear_fp8_dynamic(x, B, sb, q=q)
+
+
+def test_device_signature_without_device(qll):
+    import torch
+    if not torch.cuda.is_available():
+        buf = ctypes.create_string_buffer(256)
+        assert qll.load_library().qll_device_signature(buf, 256) == 5
 
 
 def test_heuristic_picks_are_registered_and_fit(qll):

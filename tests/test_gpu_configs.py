@@ -16,8 +16,8 @@ import workloads
 pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
-from gpu_util import (check_fp, dev, dev_bf16, dev_e4m3, host_codes,  # noqa: E402
-                      host_f64, sample_rows)
+from gpu_util import (block_fp8_product, check_all_rows, check_fp, dev,  # noqa: E402
+                      dev_bf16, dev_e4m3, fp8_product, host_codes, host_f64, sample_rows)
 
 
 @pytest.fixture(scope="module")
@@ -73,6 +73,7 @@ def test_fp8_dynamic_sweep(qll, fp8_weights, N, K):
         ref, absref = oracle.gemm_fp8(Aq_all[:M], B, sa_all[:M, 0].copy(), sb,
                                       rows=rows, with_abs=True)
         check_fp(host_f64(y)[rows], ref, absref, K, "bf16", f"fp8 N={N} K={K} M={M}")
+        check_all_rows(y, fp8_product(q, qB, sa, qsb), "bf16", f"fp8 N={N} K={K} M={M}")
 
 
 @pytest.mark.parametrize("N,K", workloads.BLOCK_SHAPES)
@@ -95,6 +96,7 @@ def test_block_fp8_sweep(qll, N, K):
         ref, absref = oracle.gemm_block_fp8(Aq_all[:M], B, sa_all[:M].copy(), sb,
                                             rows=rows, with_abs=True)
         check_fp(host_f64(y)[rows], ref, absref, K, "bf16", f"block N={N} K={K} M={M}")
+        check_all_rows(y, block_fp8_product(q, qB, sa, qsb), "bf16", f"block N={N} K={K} M={M}")
 
 
 def test_vocab_projection_both_paths(qll):
@@ -109,6 +111,8 @@ def test_vocab_projection_both_paths(qll):
     Aq_all, sa_all = oracle.quantize_fp8(a_full)
     dA = dev_bf16(a_full)
     bi_full = qll.gemm_bf16_batch_invariant(dA, dW)
+    check_all_rows(bi_full, dA.to(torch.float64) @ dW.to(torch.float64).T, "bf16",
+                   "vocab bf16 M=2048 every row")
     for M in workloads.VOCAB_M:
         rows = sample_rows(M, 3, seed=M)
         # bf16 batch-invariant path
@@ -125,3 +129,4 @@ def test_vocab_projection_both_paths(qll):
         ref, absref = oracle.gemm_fp8(Aq_all[:M], B, sa_all[:M, 0].copy(), sb[:, 0].copy(),
                                       rows=rows, with_abs=True)
         check_fp(host_f64(y8)[rows], ref, absref, K, "bf16", f"vocab fp8 M={M}")
+        check_all_rows(y8, fp8_product(q, qB, sa, qsb), "bf16", f"vocab fp8 M={M}")

@@ -66,3 +66,38 @@ def test_linear_large_m_sampled(qll):
     assert np.array_equal(host_codes(q), qr)
     check_fp(host_f64(y)[rows], ref, absref, K, "bf16", "linear M=512")
 
+
+
+@pytest.mark.parametrize("fn", ["gemm", "linear"])
+def test_side_stream_split_k_workspace(qll, fn):
+    # A forced Split-K call enqueued on a side stream while the default stream
+    # stays current: the binding's temporary workspace belongs to the side
+    # stream, so an allocation on the default stream right after the call
+    # (filled at once) cannot take its memory before the reduction has read
+    # it.  Bitwise equal to the same call on the default stream.
+    N, K, M = 2048, 6144, 256
+    w = workloads.weights_bf16(N, K, key=(workloads.W_TEST, 44))
+    B, sb = oracle.quantize_fp8(w)
+    dB, dsb = dev_e4m3(B), dev(sb[:, 0].copy())
+    x = dev_bf16(workloads.fp8_activations(M, K, key=(workloads.W_TEST, 45)))
+    q, sa = qll.quantize_per_token_fp8(x)
+    cfg = ("p64x64_w2x2_k128_s2", 4)
+    assert qll.workspace_bytes("fp8", M, N, K, cfg) > 0
+
+    def call(stream=None):
+        if fn == "gemm":
+            return qll.gemm_fp8_scaled(q, dB, sa, dsb, cfg=cfg, stream=stream)
+        return qll.linear_fp8_dynamic(x, dB, dsb, cfg=cfg, stream=stream)[0]
+
+    want = call()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    nbytes = qll.workspace_bytes("fp8", M, N, K, cfg)
+    for _ in range(3):
+        side.wait_stream(torch.cuda.current_stream())
+        got = call(stream=side)
+        junk = torch.full((nbytes,), 0x7F, dtype=torch.uint8, device="cuda")
+        junk.add_(1)
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.int16), want.view(torch.int16))
+        del junk
