@@ -300,6 +300,32 @@ int gemm_fp8_grouped_ex(const void* A, const void* B, const float* sa, const flo
 int qll_grouped_select(int64_t M, int64_t E, char* buf, size_t cap);
 
 /* ------------------------------------------------------------------ */
+/* Without device allocation                                           */
+/* ------------------------------------------------------------------ */
+
+/* Bytes of the static device array gemm_fp8_scaled_noalloc keeps its Split-K
+ * partial sums in (one array per GPU, held until the process ends). */
+#define QLL_NOALLOC_SCRATCH_BYTES (16u * 1024u * 1024u)
+
+/* gemm_fp8_scaled for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments without the workspace; the configuration, the kernels and
+ * the output are those of gemm_fp8_scaled for the same shape (bitwise).  When
+ * the configuration splits K, the partial sums go to a static device array of
+ * QLL_NOALLOC_SCRATCH_BYTES per GPU instead of a caller workspace; a shape
+ * whose partials (splits x M x N x 4 bytes) exceed it returns
+ * QLL_ERR_WORKSPACE before anything is enqueued.  Nothing is allocated or
+ * freed; the array's address on a device is looked up at qll_init (for the
+ * device current then) or at the first call on that device.  Every call on
+ * one GPU uses the same array: calls that overlap on one GPU (different
+ * streams or threads) race and must be serialized by the caller; the array
+ * needs no clearing between calls (every partial is written before it is
+ * read). */
+int gemm_fp8_scaled_noalloc(const void* A_e4m3, const void* B_e4m3, const float* sa,
+                            const float* sb, void* out, int out_dtype, int64_t M, int64_t N,
+                            int64_t K, void* stream);
+
+/* ------------------------------------------------------------------ */
 /* Dispatch, registry and support                                      */
 /* ------------------------------------------------------------------ */
 

@@ -91,6 +91,7 @@ def load_library():
                                      ctypes.c_int, ctypes.c_char_p, ctypes.c_char_p,
                                      ctypes.c_size_t]
     L.qll_device_signature.argtypes = [ctypes.c_char_p, ctypes.c_size_t]
+    L.gemm_fp8_scaled_noalloc.argtypes = _GEMM_ARGS[:9] + [_P]
     L.qll_select.argtypes = [ctypes.c_int, _I64, _I64, _I64, ctypes.POINTER(qll_cfg)]
     L.qll_workspace_bytes.argtypes = [ctypes.c_int, _I64, _I64, _I64,
                                       ctypes.POINTER(qll_cfg)]
@@ -315,6 +316,24 @@ def gemm_fp8_scaled(A, B, sa, sb, out_dtype="bf16", out=None, cfg=None,
     return _scaled_gemm("gemm_fp8_scaled", 1, A, B, sa, sb,
                         lambda M, N, K: (M,), lambda M, N, K: (N,), out_dtype,
                         out, cfg, workspace, stream)
+
+
+def gemm_fp8_scaled_noalloc(A, B, sa, sb, out, out_dtype="bf16", stream=None):
+    """gemm_fp8_scaled without a workspace (the library's static Split-K
+    scratch array; nothing allocated): the caller passes the output too."""
+    _ensure_init()
+    M, K = A.shape
+    N, K2 = B.shape
+    if K2 != K:
+        raise ValueError(f"A is [M][{K}] but B is [N][{K2}]")
+    if out is None:
+        raise ValueError("out must be given (this entry point allocates nothing)")
+    out = _out(out, M, N, out_dtype, A.device)
+    rc = load_library().gemm_fp8_scaled_noalloc(
+        _bytes8(A, "A"), _bytes8(B, "B"), _f32(sa, "sa", (M,)), _f32(sb, "sb", (N,)),
+        _dev_ptr(out, "out"), OUT[out_dtype], M, N, K, _stream(stream))
+    _check("gemm_fp8_scaled_noalloc", rc)
+    return out
 
 
 def gemm_block_fp8(A, B, sa, sb, out_dtype="bf16", out=None, cfg=None,

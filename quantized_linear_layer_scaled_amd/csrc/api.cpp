@@ -937,6 +937,10 @@ int qll_init(const char* table_path)
         path = std::getenv("QLL_TABLE");
     if (!device_info().ok)
         return QLL_ERR_NO_DEVICE;
+    if (noalloc_setup() != hipSuccess) {
+        (void)hipGetLastError();
+        return QLL_ERR_HIP;
+    }
     if (!path || !*path) {
         g_table.store(nullptr, std::memory_order_release);
         return QLL_OK;

@@ -80,6 +80,10 @@ const Variant* grouped_variants(int* count);
 // Second Split-K stage: out = epilogue(sum_{s ascending} ws[s]).
 hipError_t launch_splitk_reduce(int op, const GemmArgs& a, hipStream_t stream);
 
+// Looks up, for the current device, the address of the static scratch array
+// of gemm_fp8_scaled_noalloc (once per device).
+hipError_t noalloc_setup();
+
 // Quantizers.
 hipError_t launch_quant_rows(const void* x, void* q, float* s, int M, int K,
                              hipStream_t stream);
