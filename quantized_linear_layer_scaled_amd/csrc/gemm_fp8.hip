@@ -1,5 +1,6 @@
 // Kernel instantiations and variant registry of the fp8 GEMM.
 #include "gemm_pipe.h"
+#include "gemm_pipe32.h"
 #include "gemm_skinny.h"
 #include "gemm_tile.h"
 #include "variant_list.h"
@@ -12,6 +13,7 @@ QLL_FOR_EACH_PIPE_W8(QLL_PIPE_INSTANTIATE, qll::OP_FP8)
 QLL_FOR_EACH_PIPE_DEEP_K256(QLL_PIPE_INSTANTIATE, qll::OP_FP8)
 QLL_FOR_EACH_PIPE_BIG(QLL_PIPE_INSTANTIATE, qll::OP_FP8)
 QLL_FOR_EACH_PIPE_W8_K256(QLL_PIPE_INSTANTIATE, qll::OP_FP8)
+QLL_FOR_EACH_P32(QLL_P32_INSTANTIATE, qll::OP_FP8)
 QLL_FOR_EACH_PIPE(QLL_PIPE_GROUPED_INSTANTIATE, qll::OP_FP8)
 QLL_FOR_EACH_PIPE_W8(QLL_PIPE_GROUPED_INSTANTIATE, qll::OP_FP8)
 QLL_FOR_EACH_PIPE_BIG(QLL_PIPE_GROUPED_INSTANTIATE, qll::OP_FP8)
@@ -30,6 +32,7 @@ extern const Variant kVariantsFp8[] = {
     QLL_FOR_EACH_PIPE_DEEP_K256(QLL_PIPE_ENTRY, OP_FP8)
     QLL_FOR_EACH_PIPE_BIG(QLL_PIPE_ENTRY, OP_FP8)
     QLL_FOR_EACH_PIPE_W8_K256(QLL_PIPE_ENTRY, OP_FP8)
+    QLL_FOR_EACH_P32(QLL_P32_ENTRY, OP_FP8)
 };
 extern const int kNumVariantsFp8 = sizeof(kVariantsFp8) / sizeof(Variant);
 // the grouped (per-expert) GEMM runs the pipelined tiles over experts
