@@ -77,7 +77,8 @@ typedef enum {
     QLL_OP_BLOCK_FP8 = 2,
     QLL_OP_BF16_BI = 3,
     QLL_OP_MXFP4 = 4,
-    QLL_OP_W4A16 = 5
+    QLL_OP_W4A16 = 5,
+    QLL_OP_FP8_DYNAMIC = 6 /* linear_fp8_dynamic: quantizer + FP8 GEMM, or fused */
 } qll_op;
 
 /* A GEMM configuration: which registered kernel variant (tile shape, wave
@@ -249,14 +250,25 @@ int gemm_w4a16_ex(const void* A, const void* B, const float* scales, void* out,
                   size_t ws_bytes, void* stream, const qll_cfg* cfg);
 
 /* FP8 dynamic linear layer in one call ("FP8 dynamic quantization", same
- * section): quantize_per_token_fp8(x -> q, sa) followed by
- * gemm_fp8_scaled(q, B, sa, sb -> out) with the configuration the dispatch
- * (or cfg) picks, both enqueued on `stream`.  Results, codes and scales are
- * bitwise those of the two calls.
+ * section): per-token quantization of x (q, sa) and the scaled FP8 GEMM
+ * (q, B, sa, sb -> out), in one of two forms, chosen per shape by the
+ * dispatch under the op QLL_OP_FP8_DYNAMIC (or by cfg):
+ *   - two launches: quantize_per_token_fp8 then gemm_fp8_scaled with an FP8
+ *     GEMM variant (the first qll_num_variants(QLL_OP_FP8) indices, the same
+ *     as the FP8 op's; without a table entry of its own the op takes the
+ *     FP8 GEMM's choice);
+ *   - fused (the indices after them, names "f<rows>x16_w8_d<steps>"): one
+ *     launch whose workgroups quantize the tokens themselves inside the
+ *     wave-split decode GEMM; M <= 16 and K within the variant's register
+ *     chunk (d steps of 128 per wave: K <= 2048 for d2, <= 6144 for d6),
+ *     else QLL_ERR_UNSUPPORTED; no workspace.  Its output is bitwise that of
+ *     the two launches with the 8-wave decode GEMM of the same rows per
+ *     workgroup ("k16x16_w8" for f16, "k8x16_w8" for f8).
+ * Codes and scales are bitwise those of quantize_per_token_fp8 in both forms.
  *   x bf16 [M][K] (in); B e4m3 [N][K]; sb fp32 [N];
  *   q e4m3 [M][K] and sa fp32 [M] (out, required: the quantized activations);
  *   out bf16 / fp32 [M][N]; ws as for gemm_fp8_scaled (Split-K;
- *   qll_workspace_bytes(QLL_OP_FP8, ...)).
+ *   qll_workspace_bytes(QLL_OP_FP8_DYNAMIC, ...)).
  * Errors: those of the two calls; nothing is launched on an invalid argument. */
 int linear_fp8_dynamic(const void* x, const void* B, const float* sb, void* q,
                        float* sa, void* out, int out_dtype, int64_t M, int64_t N,

@@ -33,7 +33,8 @@ STATUS = {0: "QLL_OK", 1: "QLL_ERR_INVALID_ARG", 2: "QLL_ERR_UNSUPPORTED",
           3: "QLL_ERR_MISALIGNED", 4: "QLL_ERR_WORKSPACE", 5: "QLL_ERR_NO_DEVICE",
           6: "QLL_ERR_TABLE", 7: "QLL_ERR_HIP"}
 OUT = {"bf16": 0, "fp32": 1, "int32": 2}
-OPS = {"int8": 0, "fp8": 1, "block_fp8": 2, "bf16_bi": 3, "mxfp4": 4, "w4a16": 5}
+OPS = {"int8": 0, "fp8": 1, "block_fp8": 2, "bf16_bi": 3, "mxfp4": 4, "w4a16": 5,
+       "fp8_dynamic": 6}
 
 
 class QllError(RuntimeError):
@@ -485,14 +486,14 @@ def linear_fp8_dynamic(x, B, sb, out_dtype="bf16", out=None, q=None, sa=None, cf
     # anything is enqueued
     if q is not None and tuple(q.shape) != (M, K):
         raise ValueError(f"q must have shape {(M, K)}")
-    c = _cfg(1, cfg)
+    c = _cfg(6, cfg)  # the FP8 GEMM variants, then the fused ones
     with _on(stream):
         if q is None:
             q = torch.empty((M, K), dtype=torch.float8_e4m3fn, device=x.device)
         if sa is None:
             sa = torch.empty((M, 1), dtype=torch.float32, device=x.device)
         out = _out(out, M, N, out_dtype, x.device)
-        ws, wsb = _workspace(1, M, N, K, c, workspace)
+        ws, wsb = _workspace(6, M, N, K, c, workspace)
         L = load_library()
         args = [_dev_ptr(x, "x"), _bytes8(B, "B"), _f32(sb, "sb", (N,)), _bytes8(q, "q"),
                 _f32(sa, "sa", (M,)), _dev_ptr(out, "out"), OUT[out_dtype], M, N, K,

@@ -48,11 +48,14 @@ hipError_t launch_reduce_bf16(const GemmArgs&, hipStream_t);
 hipError_t launch_reduce_mxfp4(const GemmArgs&, hipStream_t);
 hipError_t launch_reduce_w4a16(const GemmArgs&, hipStream_t);
 
+// (for OP_FP8_DYN: its GEMM variants, i.e. the FP8 ones; the fused variants
+// follow them in that op's index space, see dyn_count)
 const Variant* variants(int op, int* count)
 {
     switch (op) {
     case OP_INT8: *count = kNumVariantsInt8; return kVariantsInt8;
-    case OP_FP8: *count = kNumVariantsFp8; return kVariantsFp8;
+    case OP_FP8:
+    case OP_FP8_DYN: *count = kNumVariantsFp8; return kVariantsFp8;
     case OP_BLOCK: *count = kNumVariantsBlock; return kVariantsBlock;
     case OP_BF16: *count = kNumVariantsBf16; return kVariantsBf16;
     case OP_MXFP4: *count = kNumVariantsMxfp4; return kVariantsMxfp4;
@@ -82,7 +85,22 @@ hipError_t launch_splitk_reduce(int op, const GemmArgs& a, hipStream_t stream)
 namespace {
 
 const char* const kOpNames[OP_COUNT] = {"int8", "fp8", "block_fp8", "bf16_bi", "mxfp4",
-                                         "w4a16"};
+                                         "w4a16", "fp8_dynamic"};
+
+// The FP8 dynamic linear layer's variant index space: the FP8 GEMM variants
+// (quantizer + GEMM, two launches) and then the fused variants.
+int dyn_count() { return kNumVariantsFp8 + kNumFusedVariants; }
+const FusedVariant* dyn_fused(int idx)
+{
+    return idx >= kNumVariantsFp8 && idx < dyn_count() ? &kFusedVariants[idx - kNumVariantsFp8]
+                                                       : nullptr;
+}
+// a fused variant runs M <= 16 tokens and K up to its register chunk
+bool fused_fits(const FusedVariant& f, int64_t M, int64_t K)
+{
+    return M <= 16 && K <= 0x3FFFFFFF && fused_steps_per_wave((int)K, f.w) <= f.d &&
+           2 * M * K <= 0x7FFFFFF0 && f.hr * K <= 0x7FFFFFF0;
+}
 
 // Bytes of one K-row of A or B: bf16 2 per element, packed MXFP4 one per two;
 // W4A16 counts the packed weight row (its Split-K pieces are cut on those
@@ -282,6 +300,10 @@ int find_variant(int op, const char* name)
     for (int i = 0; i < n; ++i)
         if (std::strcmp(v[i].name, name) == 0)
             return i;
+    if (op == OP_FP8_DYN)
+        for (int i = 0; i < kNumFusedVariants; ++i)
+            if (std::strcmp(kFusedVariants[i].name, name) == 0)
+                return kNumVariantsFp8 + i;
     return -1;
 }
 
@@ -353,7 +375,13 @@ int load_table(const char* path, const DeviceSig& want, Table** out, std::string
             *err = std::string("bad entry: ") + p;
             break;
         }
-        {
+        if (const FusedVariant* fv = op == OP_FP8_DYN ? dyn_fused(vi) : nullptr) {
+            if (!fused_fits(*fv, bucket, K) || splits != 1) {
+                rc = QLL_ERR_TABLE;
+                *err = std::string("fused entry beyond 16 tokens, its K chunk or one split: ") + p;
+                break;
+            }
+        } else {
             int n = 0;
             if (!variant_fits(op, variants(op, &n)[vi], K)) {
                 rc = QLL_ERR_TABLE;
@@ -407,6 +435,8 @@ int load_table(const char* path, const DeviceSig& want, Table** out, std::string
 // construction, the others fold their accumulator at the chunk boundaries).
 qll_cfg heuristic(int op, int64_t M, int64_t N, int64_t K)
 {
+    if (op == OP_FP8_DYN)  // two launches with the FP8 GEMM's rule
+        op = OP_FP8;
     const int cus = device_info().cus;
     const char* name;
     bool exact = true;
@@ -480,6 +510,8 @@ qll_cfg select_cfg(int op, int64_t M, int64_t N, int64_t K)
         auto it = t->entries.find(table_key(op, N, K, bucket_of(M)));
         if (it != t->entries.end())
             return it->second;
+        if (op == OP_FP8_DYN)  // no entry of its own: the FP8 GEMM's choice
+            return select_cfg(OP_FP8, M, N, K);
         if (op == OP_BF16) {
             auto fx = t->bi_fixed.find(shape_key(op, N, K));
             if (fx != t->bi_fixed.end()) {
@@ -543,8 +575,12 @@ int validate_cfg(int op, const qll_cfg* c)
 {
     int n = 0;
     variants(op, &n);
+    if (op == OP_FP8_DYN)
+        n = dyn_count();
     if (c->variant < 0 || c->variant >= n || c->splits < 1 || c->splits > kMaxSplits)
         return QLL_ERR_INVALID_ARG;
+    if (op == OP_FP8_DYN && dyn_fused(c->variant) && c->splits != 1)
+        return QLL_ERR_INVALID_ARG;  // a fused variant does not split K
     return QLL_OK;
 }
 
@@ -830,14 +866,32 @@ int linear_fp8_dynamic_ex(const void* x, const void* B, const float* sb, void* q
     int rc = validate_gemm(OP_FP8, x, B, sa, sb, out, out_dtype, M, N, K);
     if (rc != QLL_OK)
         return rc;
-    if (cfg && (rc = validate_cfg(OP_FP8, cfg)) != QLL_OK)
+    if (cfg && (rc = validate_cfg(OP_FP8_DYN, cfg)) != QLL_OK)
         return rc;
     if (misaligned(q, 16))
         return QLL_ERR_MISALIGNED;
     if (M == 0)
         return QLL_OK;
-    const qll_cfg c = cfg ? *cfg : select_cfg(OP_FP8, M, N, K);
-    // the GEMM's own checks, before anything is enqueued
+    const qll_cfg c = cfg ? *cfg : select_cfg(OP_FP8_DYN, M, N, K);
+    if (const FusedVariant* fv = dyn_fused(c.variant)) {
+        // one launch: quantizer inside the decode GEMM
+        if (!fused_fits(*fv, M, K))
+            return QLL_ERR_UNSUPPORTED;
+        FusedArgs f;
+        f.x = (const uint16_t*)x;
+        f.B = (const uint8_t*)B;
+        f.sb = sb;
+        f.q = (uint8_t*)q;
+        f.sa = sa;
+        f.out = out;
+        f.out_dtype = out_dtype;
+        f.M = (int)M;
+        f.N = (int)N;
+        f.K = (int)K;
+        return fv->launch(f, (hipStream_t)stream) == hipSuccess ? QLL_OK : QLL_ERR_HIP;
+    }
+    // two launches: the quantizer, then the FP8 GEMM with the GEMM's own
+    // checks done before anything is enqueued
     int nv = 0;
     if (!variant_fits(OP_FP8, variants(OP_FP8, &nv)[c.variant], K))
         return QLL_ERR_UNSUPPORTED;
@@ -1008,6 +1062,8 @@ int64_t qll_workspace_bytes(int op, int64_t M, int64_t N, int64_t K,
     qll_cfg c = cfg ? *cfg : select_cfg(op, M, N, K);
     if (validate_cfg(op, &c) != QLL_OK)
         return -QLL_ERR_INVALID_ARG;
+    if (op == OP_FP8_DYN && dyn_fused(c.variant))
+        return 0;
     const int s = effective_splits(op, K, c.splits);
     return s > 1 ? (int64_t)s * M * N * 4 : 0;
 }
@@ -1021,6 +1077,8 @@ int qll_effective_splits(int op, int64_t K, int32_t splits)
 
 int qll_num_variants(int op)
 {
+    if (op == OP_FP8_DYN)
+        return dyn_count();
     int n = 0;
     variants(op, &n);
     return n;
@@ -1028,13 +1086,24 @@ int qll_num_variants(int op)
 
 int qll_variant_info(int op, int idx, char* buf, size_t cap)
 {
+    if (op < 0 || op >= OP_COUNT || !buf || cap == 0)
+        return QLL_ERR_INVALID_ARG;
+    if (const FusedVariant* f = op == OP_FP8_DYN ? dyn_fused(idx) : nullptr) {
+        std::snprintf(buf, cap,
+                      "{\"name\": \"%s\", \"op\": \"%s\", \"swap\": 1, \"bp\": %d, "
+                      "\"bq\": 16, \"wp\": %d, \"wq\": 1, \"kstage\": 128, \"lds\": %d, "
+                      "\"fused\": 1, \"ksteps\": %d}",
+                      f->name, kOpNames[op], f->hr, f->w, f->w * 1024 + f->w * 64 + 64, f->d);
+        return QLL_OK;
+    }
     int n = 0;
     const Variant* v = variants(op, &n);
-    if (idx < 0 || idx >= n || !buf || cap == 0)
+    if (idx < 0 || idx >= n)
         return QLL_ERR_INVALID_ARG;
     std::snprintf(buf, cap,
                   "{\"name\": \"%s\", \"op\": \"%s\", \"swap\": %d, \"bp\": %d, "
-                  "\"bq\": %d, \"wp\": %d, \"wq\": %d, \"kstage\": %d, \"lds\": %d}",
+                  "\"bq\": %d, \"wp\": %d, \"wq\": %d, \"kstage\": %d, \"lds\": %d, "
+                  "\"fused\": 0}",
                   v[idx].name, kOpNames[op], v[idx].swap, v[idx].bp, v[idx].bq,
                   v[idx].wp, v[idx].wq, v[idx].kstage, v[idx].lds);
     return QLL_OK;

@@ -1,0 +1,238 @@
+// Fused FP8 dynamic linear layer for few tokens: per-token quantization of
+// the bf16 activations inside the Swap-AB decode GEMM, one launch instead of
+// the quantizer's launch plus the GEMM's ("FP8 dynamic quantization" of
+// "Helion in vLLM: A Unified Route to Tunable Linear Kernels", "What the
+// integration changes"; each kernel transition of a decode step costs a
+// launch and a round trip through memory).
+//
+// A workgroup owns HR weight rows (16, or 8 with the MFMA's other rows
+// zero) and all M <= 16 tokens, and its 8 waves split K on the grid of the
+// wave-split decode GEMM (gemm_skinny.h), so that the products are summed in
+// exactly that kernel's order:
+//   1. each wave issues the loads of its whole K chunk of weights (e4m3)
+//      and of the tokens (bf16, in the MFMA operand layout: lane l holds
+//      token l % 16 and 32 consecutive K elements of each step);
+//   2. the per-token maximum magnitude: within a lane, over the 4 lanes of
+//      a token by shuffles, over the 8 waves through LDS (one barrier);
+//   3. s = amax / 448 and the codes with the quantizer's own encode
+//      (quant_encode.h), so codes and scales are bitwise the quantizer's;
+//   4. the MFMAs of the chunk, the 8 partial tiles added in LDS in wave
+//      order, the epilogue (acc * s[m]) * sb[n].
+// The output is therefore bitwise that of quantize_per_token_fp8 followed by
+// the 8-wave decode GEMM with the same row count per workgroup.  Workgroup 0
+// also writes the codes and scales, which the call returns.
+//
+// Every workgroup reads all tokens' bf16 values (twice the bytes of their
+// codes) and encodes them, so this pays off for very few tokens only; the
+// dispatch table decides per shape.
+#include <algorithm>
+
+#include "gemm_tile.h"
+#include "quant_encode.h"
+
+namespace qll {
+
+
+// 32 bf16 values (64 bytes) -> 32 e4m3 codes (one MFMA operand)
+static __device__ __forceinline__ void encode32(const uint4* v, const Quot& d, uint4* c)
+{
+    uint2 e[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        e[i] = encode8(v[i], d);
+    c[0] = make_uint4(e[0].x, e[0].y, e[1].x, e[1].y);
+    c[1] = make_uint4(e[2].x, e[2].y, e[3].x, e[3].y);
+}
+
+template <int HR, int W, int D>
+__global__ __launch_bounds__(W * 64) void linear_fused_kernel(FusedArgs a)
+{
+    constexpr int KB = 32;          // bytes (codes) per lane per MFMA step
+    constexpr int KSTEP = 4 * KB;   // 128 K elements per step
+    constexpr int U = kFoldUnit / KSTEP;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int N = a.N, M = a.M, K = a.K;
+    const int n0 = blockIdx.x * HR;
+    const bool wrow = (lane & 15) < HR;
+    // the wave's steps, as the wave-split decode GEMM cuts them
+    const int T = (K + KSTEP - 1) / KSTEP;
+    const int TU = (T + U - 1) / U;
+    const int s0 = min(T, U * (wave * TU / W));
+    const int s1 = min(T, U * ((wave + 1) * TU / W));
+    const int ns = s1 - s0;  // <= D (checked on the host)
+
+    const int t = lane & 15;                 // this lane's token
+    const int koff = (lane >> 4) * KB;       // element offset within a step
+    // the tokens and the workgroup's weight rows as two buffers (one
+    // descriptor each, the same in every lane): a load at an offset outside
+    // (the K tail, the steps past this wave's range, weight rows past N or
+    // past the workgroup's HR) returns zeros, so every load is unconditional
+    // and the waits below count them exactly
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)a.x, (short)0, 2 * M * K, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.B + (size_t)n0 * K), (short)0, min(HR, N - n0) * K, 0x00020000);
+    constexpr int kOut = 0x7FFFFFF0;
+    // lanes of tokens past M read zeros (their output columns are
+    // discarded): no load path spent on copies of another row
+    const bool tok = t < M;
+    const int xrow = t * K;                   // element offset of the token's row
+    const int wrowoff = wrow ? t * K : kOut;  // byte offset of the weight row
+
+    // 1. loads: the tokens (32 bf16 per step) first, then the weights (32
+    // bytes per step): the wait for the tokens (in issue order) then leaves
+    // the weight stream in flight while the maximum and the codes are formed
+    uint4 wb[D][2], xb[D][4];
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+        const int e = (s0 + d) * KSTEP + koff;  // this lane's first element
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            xb[d][j] = __builtin_bit_cast(
+                uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                           rx, tok && d < ns && e + 8 * j < K ? 2 * (xrow + e + 8 * j) : kOut,
+                           0, 0));
+    }
+    // (empty asm with a memory clobber: the compiler keeps the three groups
+    // -- token loads, weight loads, the math -- in this order)
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+        const int e = (s0 + d) * KSTEP + koff;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            wb[d][j] = __builtin_bit_cast(
+                uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                           rw, wrow && d < ns && e + 16 * j < K ? wrowoff + e + 16 * j : kOut,
+                           0, 0));
+    }
+
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 2. the token's maximum magnitude over K (on the bf16 bits: for finite
+    // values the magnitude order is the integer order of the low 15 bits)
+    uint32_t mlo = 0, mhi = 0;
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            absmax_bits8(xb[d][j], mlo, mhi);
+    float amax = absmax_bits_value(mlo, mhi);
+    amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+    __shared__ float red_max[W][16];
+    if (lane < 16)
+        red_max[wave][lane] = amax;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < W; ++w)
+        amax = fmaxf(amax, red_max[w][t]);
+    // 3. the quantizer's scale and codes
+    const float sc = amax / 448.0f;
+    const Quot qd(sc);
+    v4f acc = v4f{0, 0, 0, 0};
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+        if (d >= ns)
+            break;
+        uint4 code[2];
+        encode32(xb[d], qd, code);
+        if (blockIdx.x == 0 && t < M) {
+            const int e = (s0 + d) * KSTEP + koff;
+            if (e < K) {
+                uint8_t* qp = a.q + (size_t)t * K + e;
+                // K is a multiple of 16: the run ends at a 16-byte boundary
+                *(uint4*)qp = code[0];
+                if (e + 16 < K)
+                    *(uint4*)(qp + 16) = code[1];
+            }
+        }
+        // 4. the step's MFMA: weights on the row side, tokens on the column
+        // side (the decode GEMM's Swap-AB orientation)
+        acc = mfma_step<OP_FP8>(wb[d], code, acc);
+    }
+    if (blockIdx.x == 0 && wave == 0 && lane < M)
+        a.sa[lane] = sc;  // lane < 16: token `lane`, its scale as computed above
+
+    // the 8 partial tiles, added in wave order (the decode GEMM's order)
+    __shared__ float red[W][256];
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+        red[wave][lane * 4 + v] = acc[v];
+    // the scale of each output column's token, from the lanes that hold it
+    __shared__ float tok_scale[16];
+    if (wave == 0 && lane < 16)
+        tok_scale[lane] = sc;
+    __syncthreads();
+    for (int e = threadIdx.x; e < 256; e += W * 64) {
+        float sum = red[0][e];
+#pragma unroll
+        for (int w = 1; w < W; ++w)
+            sum += red[w][e];
+        // element (lane ln, register v): n = n0 + (ln >> 4) * 4 + v,
+        // m = ln & 15
+        const int ln = e >> 2, v = e & 3;
+        const int n = n0 + (ln >> 4) * 4 + v;
+        const int m = ln & 15;
+        if (m < M && n < N && (ln >> 4) * 4 + v < HR) {
+            const float u = sum * tok_scale[m];
+            const float y = u * a.sb[n];
+            if (a.out_dtype == OUT_BF16)
+                ((uint16_t*)a.out)[(size_t)m * N + n] = bf16_rne(y);
+            else
+                ((float*)a.out)[(size_t)m * N + n] = y;
+        }
+    }
+}
+
+// K steps (of 128 elements) the busiest of W waves of a workgroup handles.
+int fused_steps_per_wave(int K, int W)
+{
+    const int T = (K + 127) / 128;
+    const int U = kFoldUnit / 128;
+    const int TU = (T + U - 1) / U;
+    int most = 0;
+    for (int w = 0; w < W; ++w) {
+        const int s0 = std::min(T, U * (w * TU / W));
+        const int s1 = std::min(T, U * ((w + 1) * TU / W));
+        most = std::max(most, s1 - s0);
+    }
+    return most;
+}
+
+template <int HR, int W, int D>
+hipError_t launch_fused(const FusedArgs& a, hipStream_t stream)
+{
+    if (a.M < 1 || a.M > 16 || fused_steps_per_wave(a.K, W) > D || a.N > 0x7FFFFFF0 ||
+        2 * (int64_t)a.M * a.K > 0x7FFFFFF0 || (int64_t)HR * a.K > 0x7FFFFFF0)
+        return hipErrorInvalidValue;  // (32-bit buffer offsets)
+    hipLaunchKernelGGL((linear_fused_kernel<HR, W, D>), dim3((a.N + HR - 1) / HR),
+                       dim3(W * 64), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace qll
+
+#define QLL_FOR_EACH_FUSED(X) \
+    X(16, 8, 2) X(8, 8, 2) X(16, 8, 6) X(8, 8, 6) X(16, 16, 2) X(8, 16, 2) X(16, 16, 4) X(8, 16, 4)
+#define QLL_FUSED_INSTANTIATE(HR, W, D) \
+    template __global__ void qll::linear_fused_kernel<HR, W, D>(qll::FusedArgs);
+QLL_FOR_EACH_FUSED(QLL_FUSED_INSTANTIATE)
+
+namespace qll {
+
+// host-side registry (the device pass only needs the kernels above): HR
+// weight rows per workgroup, W waves splitting K (the fold grid of the
+// W-wave decode GEMM), D K steps of 128 per wave in registers (W = 8: D = 2
+// for K <= 2048, 6 for K <= 6144; W = 16: D = 2 for K <= 4096, 4 for
+// K <= 8192)
+#if !defined(__HIP_DEVICE_COMPILE__)
+#define QLL_FUSED_ENTRY(HR, W, D) \
+    {"f" #HR "x16_w" #W "_d" #D, HR, W, D, &launch_fused<HR, W, D>},
+extern const FusedVariant kFusedVariants[] = {QLL_FOR_EACH_FUSED(QLL_FUSED_ENTRY)};
+extern const int kNumFusedVariants = sizeof(kFusedVariants) / sizeof(FusedVariant);
+#endif
+
+}  // namespace qll

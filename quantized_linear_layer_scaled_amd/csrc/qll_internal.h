@@ -15,7 +15,10 @@ enum Op : int {
     OP_BF16 = 3,
     OP_MXFP4 = 4,
     OP_W4A16 = 5,
-    OP_COUNT = 6
+    // the FP8 dynamic linear layer (quantizer + FP8 GEMM): its variants are
+    // the FP8 GEMM's (two launches) followed by the fused ones
+    OP_FP8_DYN = 6,
+    OP_COUNT = 7
 };
 enum Out : int { OUT_BF16 = 0, OUT_FP32 = 1, OUT_INT32 = 2 };
 
@@ -79,6 +82,30 @@ const Variant* grouped_variants(int* count);
 
 // Second Split-K stage: out = epilogue(sum_{s ascending} ws[s]).
 hipError_t launch_splitk_reduce(int op, const GemmArgs& a, hipStream_t stream);
+
+// The fused FP8 dynamic linear layer for few tokens (linear_fused.hip):
+// per-token quantization inside the wave-split decode GEMM.
+struct FusedArgs {
+    const uint16_t* x;  // bf16 [M][K]
+    const uint8_t* B;   // e4m3 [N][K]
+    const float* sb;    // [N]
+    uint8_t* q;         // e4m3 [M][K] (written by workgroup 0)
+    float* sa;          // [M] (written by workgroup 0)
+    void* out;          // [M][N]
+    int out_dtype;
+    int M, N, K;        // M <= 16
+};
+struct FusedVariant {
+    const char* name;
+    int hr;  // weight rows per workgroup
+    int w;   // waves splitting K
+    int d;   // K steps of 128 a wave holds in registers
+    hipError_t (*launch)(const FusedArgs&, hipStream_t);
+};
+extern const FusedVariant kFusedVariants[];
+extern const int kNumFusedVariants;
+// K steps the busiest of W waves of a fused workgroup handles (<= d to fit)
+int fused_steps_per_wave(int K, int W);
 
 // Looks up, for the current device, the address of the static scratch array
 // of gemm_fp8_scaled_noalloc (once per device).

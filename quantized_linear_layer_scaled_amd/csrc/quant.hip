@@ -21,6 +21,8 @@
 //   quant_groups128:   16 lanes per 1x128 group (8 bf16 per lane), shuffle
 //                      max inside the 16 lanes; no LDS;
 //   quant_weight_blocks: one workgroup per 128x128 weight block.
+#include <type_traits>
+
 #include "qll_internal.h"
 #include "quant_encode.h"
 
@@ -86,6 +88,69 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restr
         const int e = (c * TPR + t) * 8;
         if (e < K)
             *(uint2*)(qr + e) = encode8(v[c], d);
+    }
+}
+
+// Many rows of 2048..32768 elements: a grid of G workgroups (G < M) in which
+// workgroup b quantizes rows b, b + G, b + 2G, ...; the loads of its next row
+// are issued before the current row is reduced, encoded and stored, so that
+// reads and writes overlap (with one row per workgroup and all of them
+// resident at once, every row first loads and then every row stores).  The
+// arithmetic per row is quant_rows_kernel's with TPR = 256: bitwise the same
+// codes and scales.  Rows are read through a buffer resource (rows past M
+// read as zeros, so the next-row loads need no branch).
+template <int CH>
+__global__ __launch_bounds__(256) void quant_rows_loop_kernel(const uint16_t* __restrict__ x,
+                                                             uint8_t* __restrict__ q,
+                                                             float* __restrict__ s, int M,
+                                                             int K)
+{
+    const int tid = threadIdx.x;
+    const int G = gridDim.x;
+    const __amdgpu_buffer_rsrc_t rx =
+        __builtin_amdgcn_make_buffer_rsrc((void*)x, (short)0, 2 * M * K, 0x00020000);
+    auto load = [&](uint4* v, int m) __attribute__((always_inline)) {
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int e = (c * 256 + tid) * 8;
+            v[c] = __builtin_bit_cast(
+                uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                           rx, e < K ? 2 * (m * K + e) : 0x7FFFFFF0, 0, 0));
+        }
+    };
+    __shared__ float red[2][4];
+    uint4 v[2][CH];
+    auto row = [&](auto P, int m) __attribute__((always_inline)) {
+        constexpr int p = decltype(P)::value;
+        load(v[p ^ 1], m + G);  // the next row (zeros past M)
+        float amax = 0.0f;
+#pragma unroll
+        for (int c = 0; c < CH; ++c)
+            amax = fmaxf(amax, absmax8(v[p][c]));
+        amax = wave_max(amax);
+        if ((tid & 63) == 0)
+            red[p][tid >> 6] = amax;
+        __syncthreads();
+        amax = fmaxf(fmaxf(red[p][0], red[p][1]), fmaxf(red[p][2], red[p][3]));
+        const float sc = amax / 448.0f;
+        if (tid == 0)
+            s[m] = sc;
+        const Quot d(sc);
+        uint8_t* qr = q + (size_t)m * K;
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int e = (c * 256 + tid) * 8;
+            if (e < K)
+                *(uint2*)(qr + e) = encode8(v[p][c], d);
+        }
+    };
+    int m = blockIdx.x;
+    load(v[0], m);
+    for (; m < M; m += 2 * G) {
+        row(std::integral_constant<int, 0>{}, m);
+        if (m + G >= M)
+            break;
+        row(std::integral_constant<int, 1>{}, m + G);
     }
 }
 
@@ -199,6 +264,21 @@ hipError_t launch_quant_rows(const void* x, void* q, float* s, int M, int K,
     // a whole workgroup per row from 2048 elements on (short per-thread
     // chains, no idle lanes), narrower rows share a workgroup
     const int chunks = (K + 7) / 8;
+    // many rows of 2048..8192 elements: the row loop with G = 512 workgroups
+    // (two per CU, each with the next row's loads in flight)
+    constexpr int kLoopGrid = 512;
+    // (byte offsets of the rows up to M + G stay below 2^31)
+    if (M > kLoopGrid && chunks >= 256 && chunks <= 1024 &&
+        2 * ((int64_t)M + kLoopGrid) * K < ((int64_t)1 << 31)) {
+        const int G = kLoopGrid;
+        switch ((chunks + 255) / 256) {
+        case 1: hipLaunchKernelGGL(quant_rows_loop_kernel<1>, dim3(G), dim3(256), 0, stream, xp, qp, s, M, K); break;
+        case 2: hipLaunchKernelGGL(quant_rows_loop_kernel<2>, dim3(G), dim3(256), 0, stream, xp, qp, s, M, K); break;
+        case 3: hipLaunchKernelGGL(quant_rows_loop_kernel<3>, dim3(G), dim3(256), 0, stream, xp, qp, s, M, K); break;
+        default: hipLaunchKernelGGL(quant_rows_loop_kernel<4>, dim3(G), dim3(256), 0, stream, xp, qp, s, M, K); break;
+        }
+        return hipGetLastError();
+    }
     if (chunks <= 64)
         launch_rows<64, 1>(xp, qp, s, M, K, stream);
     else if (chunks <= 128)

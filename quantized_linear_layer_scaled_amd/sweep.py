@@ -52,7 +52,11 @@ DEFAULT_SHAPES = {
     "bf16_bi": [(2048, 2048), (4096, 2048), (151936, 2048)],
     "mxfp4": [(4096, 2048), (2048, 6144)],
     "w4a16": [(4096, 2048), (2048, 6144)],
+    # the FP8 dynamic linear layer (quantizer + GEMM in two launches, or the
+    # fused decode kernel), swept where the fused kernel can run
+    "fp8_dynamic": [(4096, 2048), (2048, 6144), (151936, 2048)],
 }
+DYN_M = [1, 2, 4, 8, 16]
 SPLITS = [1, 2, 4, 8]
 WS_LIMIT = 1 << 30
 COLD_BYTES = 384 << 20  # weights touched per timing replay: > the 256 MB Infinity Cache
@@ -86,6 +90,11 @@ def _inputs(torch, op, M, N, K, copies):
               for _ in range(copies)]
         sa = torch.randint(120, 134, (M, K // 32), device="cuda", dtype=torch.uint8, generator=g)
         sb = torch.randint(120, 134, (N, K // 32), device="cuda", dtype=torch.uint8, generator=g)
+    elif op == "fp8_dynamic":
+        A = torch.randn((M, K), device="cuda", generator=g).to(torch.bfloat16)
+        Bs = [e4m3((N, K)) for _ in range(copies)]
+        sa = None
+        sb = torch.rand(N, device="cuda", generator=g) * 1e-3 + 1e-4
     elif op == "w4a16":
         A = (torch.randn((M, K), device="cuda", generator=g)).to(torch.bfloat16)
         Bs = [torch.randint(0, 256, (N, K // 2), device="cuda", dtype=torch.uint8, generator=g)
@@ -105,8 +114,19 @@ def _inputs(torch, op, M, N, K, copies):
     return A, Bs, sa, sb
 
 
+_DYN_BUFS = {}
+
+
 def _call(qll, op, A, B, sa, sb, out_dtype, cfg, ws, out=None):
     kw = dict(out_dtype=out_dtype, cfg=cfg, workspace=ws, out=out)
+    if op == "fp8_dynamic":
+        import torch
+        key = (A.shape[0], A.shape[1])
+        if key not in _DYN_BUFS:  # codes and scales outside any graph capture
+            _DYN_BUFS[key] = (torch.empty(key, dtype=torch.float8_e4m3fn, device="cuda"),
+                              torch.empty((key[0], 1), dtype=torch.float32, device="cuda"))
+        q, s = _DYN_BUFS[key]
+        return qll.linear_fp8_dynamic(A, B, sb, q=q, sa=s, **kw)[0]
     if op == "int8":
         return qll.gemm_w8a8_int8(A, B, sa, sb, **kw)
     if op == "fp8":
@@ -120,11 +140,24 @@ def _call(qll, op, A, B, sa, sb, out_dtype, cfg, ws, out=None):
     return qll.gemm_bf16_batch_invariant(A, B, **kw)
 
 
+def fused_steps(K, W):
+    """K steps of 128 elements the busiest of W waves of a fused decode
+    workgroup handles (the cut of the W-wave decode GEMM)."""
+    T = -(-K // 128)
+    TU = -(-T // 2)
+    return max(min(T, 2 * ((w + 1) * TU // W)) - min(T, 2 * (w * TU // W)) for w in range(W))
+
+
 def candidates(qll, op, M, N, K):
     """(variant, splits) pairs worth timing for this shape."""
     out = []
     for v in qll.variants(op):
         name = v["name"]
+        if v.get("fused"):
+            # the fused linear layer: at most 16 tokens, K within its chunk
+            if M <= 16 and fused_steps(K, v["wp"]) <= v["ksteps"]:
+                out.append((name, 1))
+            continue
         if op == "bf16_bi" and name[0] == "k" and v["wp"] != 8:
             continue  # its waves split K into other chunks than the fixed eight
         if name[0] in "kr" and M > 128:
@@ -201,6 +234,10 @@ def reference(torch, op, A, B, sa, sb):
             s = torch.exp2(scales.to(f64) - 127.0).repeat_interleave(32, dim=1)
             return v * s
         return dec(A, sa) @ dec(B, sb).T
+    if op == "fp8_dynamic":
+        import quantized_linear_layer_scaled_amd as qll
+        q, s = qll.quantize_per_token_fp8(A)
+        return reference(torch, "fp8", q, B, s[:, 0], sb)
     if op == "w4a16":
         lo, hi = (B & 15).to(torch.int16), (B >> 4).to(torch.int16)
         v = torch.stack([lo, hi], dim=-1).reshape(B.shape[0], -1)
@@ -249,6 +286,8 @@ def sweep_shape(torch, qll, op, N, K, mlist, reps, log, done=None, record=None):
     done = {} if done is None else done
     record = record or (lambda r: None)
     row_bytes = {"bf16_bi": 2 * K, "mxfp4": K // 2, "w4a16": K // 2}.get(op, K)
+    if op == "fp8_dynamic":
+        mlist = [m for m in mlist if m <= max(DYN_M)]
     # rotate through at least COLD_BYTES of weights per graph replay
     copies = max(2, min(64, -(-COLD_BYTES // max(1, N * row_bytes))))
     reps = max(reps, copies)

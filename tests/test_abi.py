@@ -428,3 +428,42 @@ def test_heuristic_picks_are_registered_and_fit(qll):
                     assert splits == 1  # batch invariance: K is never split across workgroups
                 ws = qll.workspace_bytes(op, M, N, K, (name, splits))
                 assert ws == (0 if splits == 1 else splits * M * N * 4), (op, M, N, K)
+
+
+def test_fp8_dynamic_variant_space(qll):
+    # the FP8 dynamic linear layer: the FP8 GEMM variants at their own
+    # indices, then the fused ones; fused variants split nothing and need no
+    # workspace; without a table the op takes the FP8 GEMM's choice
+    L = qll.load_library()
+    fp8 = [v["name"] for v in qll.variants("fp8")]
+    dyn = qll.variants("fp8_dynamic")
+    assert [v["name"] for v in dyn[:len(fp8)]] == fp8
+    fused = dyn[len(fp8):]
+    assert fused and all(v["fused"] == 1 and v["name"].startswith("f") for v in fused)
+    for v in fused:
+        assert L.qll_variant_index(6, v["name"].encode()) == v["index"]
+        assert qll.workspace_bytes("fp8_dynamic", 1, 4096, 2048, (v["name"], 1)) == 0
+        assert L.qll_variant_index(1, v["name"].encode()) == -1  # not an FP8 GEMM
+    assert L.qll_workspace_bytes(6, 1, 4096, 2048,
+                                 ctypes.byref(qll.qll_cfg(fused[0]["index"], 2))) < 0
+    L.qll_init(None)
+    for M in (1, 16, 64, 2048):
+        assert qll.select("fp8_dynamic", M, 4096, 2048) == qll.select("fp8", M, 4096, 2048)
+
+
+def test_fp8_dynamic_table_rules(qll, tmp_path):
+    head = f"device {SIG}\n"
+    ok = write(tmp_path, head + "fp8_dynamic 4096 2048 1 f16x16_w8_d2 1\n"
+                                "fp8_dynamic 4096 2048 16 f8x16_w8_d2 1\n"
+                                "fp8_dynamic 2048 6144 2 f16x16_w8_d6 1\n"
+                                "fp8_dynamic 2048 6144 4 f8x16_w16_d4 1\n"
+                                "fp8_dynamic 4096 4096 8 f16x16_w16_d2 1\n"
+                                "fp8_dynamic 2048 6144 64 p64x64_w2x2_k128_s4 4\n")
+    assert qll.table_validate(ok, SIG) == (0, "")
+    for bad in ("fp8_dynamic 4096 2048 32 f16x16_w8_d2 1\n",   # beyond 16 tokens
+                "fp8_dynamic 4096 2048 1 f16x16_w8_d2 2\n",    # a fused variant splits nothing
+                "fp8_dynamic 2048 6144 1 f16x16_w8_d2 1\n",    # K beyond its register chunk
+                "fp8_dynamic 2048 6144 1 f16x16_w16_d2 1\n",   # (16 waves: 4 steps each)
+                "fp8 4096 2048 1 f16x16_w8_d2 1\n"):           # not an FP8 GEMM variant
+        rc, why = qll.table_validate(write(tmp_path, head + bad), SIG)
+        assert rc == 6, bad

@@ -101,3 +101,56 @@ def test_side_stream_split_k_workspace(qll, fn):
         torch.cuda.synchronize()
         assert torch.equal(got.view(torch.int16), want.view(torch.int16))
         del junk
+
+
+def fused_steps(K, W):
+    """K steps of 128 the busiest of W waves handles (the decode GEMM's cut)."""
+    T = -(-K // 128)
+    TU = -(-T // 2)
+    return max(min(T, 2 * ((w + 1) * TU // W)) - min(T, 2 * (w * TU // W)) for w in range(W))
+
+
+@pytest.mark.parametrize("N,K", [(4096, 2048), (2048, 6144), (520, 1040), (300, 2064)])
+def test_fused_equals_two_launches_and_oracle(qll, N, K):
+    # the fused variants: codes and scales bitwise the quantizer's (oracle),
+    # output bitwise the two launches with the 8-wave decode GEMM of the same
+    # rows per workgroup, and within the bound of the oracle
+    w = workloads.weights_bf16(N, K, key=(workloads.W_TEST, 50))
+    B, sb = oracle.quantize_fp8(w)
+    dB, dsb = dev_e4m3(B), dev(sb[:, 0].copy())
+    x_all = workloads.fp8_activations(16, K, key=(workloads.W_TEST, 51))
+    fused = [v for v in qll.variants("fp8_dynamic") if v.get("fused")]
+    assert len(fused) >= 4
+    ran = 0
+    for v in fused:
+        if fused_steps(K, v["wp"]) > v["ksteps"]:
+            with pytest.raises(qll.QllError):
+                qll.linear_fp8_dynamic(dev_bf16(x_all[:1]), dB, dsb, cfg=(v["name"], 1))
+            continue
+        for M in (1, 3, 16):
+            x = x_all[:M].copy()
+            qr, sr = oracle.quantize_fp8(x)
+            ref, absref = oracle.gemm_fp8(qr, B, sr[:, 0].copy(), sb[:, 0].copy(), with_abs=True)
+            dx = dev_bf16(x)
+            for od in ("bf16", "fp32"):
+                y, q, sa = qll.linear_fp8_dynamic(dx, dB, dsb, out_dtype=od, cfg=(v["name"], 1))
+                y2, _, _ = qll.linear_fp8_dynamic(
+                    dx, dB, dsb, out_dtype=od, cfg=(f"k{v['bp']}x16_w{v['wp']}", 1))
+                torch.cuda.synchronize()
+                assert np.array_equal(host_codes(q), qr), (v["name"], M)
+                assert np.array_equal(sa.cpu().numpy()[:, 0].view(np.uint32),
+                                      sr[:, 0].view(np.uint32)), (v["name"], M)
+                iv = torch.int16 if od == "bf16" else torch.int32
+                assert torch.equal(y.view(iv), y2.view(iv)), (v["name"], M, od)
+                check_fp(host_f64(y), ref, absref, K, od, f"fused {v['name']} M={M} {od}")
+                ran += 1
+    assert ran > 0
+
+
+def test_fused_refuses_more_than_16_tokens(qll):
+    N, K = 520, 1040
+    B = dev_e4m3(np.zeros((N, K), np.uint8))
+    sb = torch.ones(N, device="cuda")
+    x = dev_bf16(workloads.fp8_activations(17, K, key=(workloads.W_TEST, 52)))
+    with pytest.raises(qll.QllError, match="UNSUPPORTED"):
+        qll.linear_fp8_dynamic(x, B, sb, cfg=("f16x16_w8_d2", 1))
