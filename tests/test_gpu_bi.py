@@ -40,7 +40,7 @@ def test_rows_bitwise_equal_across_m(qll, N, K):
     # accuracy of the shared result against the oracle on sampled rows
     rows = sample_rows(2048, 12)
     ref, absref = oracle.gemm_bf16(d["A_full"], d["B"], rows=rows, with_abs=True)
-    check_fp(host_f64(full)[rows], ref, absref, K, "bf16", f"BI N={N} K={K}")
+    check_fp(host_f64(full)[rows], ref, absref, K, "bf16", f"BI N={N} K={K}", mfma="bf16")
 
 
 def test_other_rows_do_not_matter(qll):

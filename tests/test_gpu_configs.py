@@ -120,7 +120,7 @@ def test_vocab_projection_both_paths(qll):
         torch.cuda.synchronize()
         assert torch.equal(y.view(torch.int16), bi_full[:M].view(torch.int16)), M
         ref, absref = oracle.gemm_bf16(a_full[:M], w, rows=rows, with_abs=True)
-        check_fp(host_f64(y)[rows], ref, absref, K, "bf16", f"vocab bf16 M={M}")
+        check_fp(host_f64(y)[rows], ref, absref, K, "bf16", f"vocab bf16 M={M}", mfma="bf16")
         # FP8 dynamic path on the same data
         q, sa = qll.quantize_per_token_fp8(dA[:M].contiguous())
         y8 = qll.gemm_fp8_scaled(q, qB, sa, qsb)

@@ -200,7 +200,7 @@ def test_bf16_all_variants(qll, bf16_cases, shape, splits):
         for od in ("bf16", "fp32"):
             y = qll.gemm_bf16_batch_invariant(dA, dB, out_dtype=od, cfg=(name, splits))
             torch.cuda.synchronize()
-            check_fp(host_f64(y), ref, absref, K, od, f"bf16 {name} S={splits} {od}")
+            check_fp(host_f64(y), ref, absref, K, od, f"bf16 {name} S={splits} {od}", mfma="bf16")
 
 
 def test_bf16_integer_valued_exact(qll):

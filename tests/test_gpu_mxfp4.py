@@ -137,7 +137,7 @@ def test_gemm_all_variants(qll, mx_cases, shape, splits):
         for od in ("fp32", "bf16"):
             y = qll.gemm_mxfp4(dA, dB, dsa, dsb, out_dtype=od, cfg=(name, splits))
             torch.cuda.synchronize()
-            check_fp(host_f64(y), ref, absref, K, od, f"{name} S={splits} {od}")
+            check_fp(host_f64(y), ref, absref, K, od, f"{name} S={splits} {od}", mfma="fp4")
 
 
 def test_gemm_sequential_variants_agree_bitwise(qll, mx_cases):
@@ -213,7 +213,7 @@ def test_end_to_end_quantize_and_gemm(qll, M, N, K):
     assert np.array_equal(host_u8(qa), qa_ref) and np.array_equal(host_u8(sa), sa_ref)
     assert np.array_equal(host_u8(qb), qb_ref) and np.array_equal(host_u8(sb), sb_ref)
     ref, absref = oracle.gemm_mxfp4(qa_ref, qb_ref, sa_ref, sb_ref, with_abs=True)
-    check_fp(host_f64(y), ref, absref, K, "bf16", f"M={M} N={N} K={K}")
+    check_fp(host_f64(y), ref, absref, K, "bf16", f"M={M} N={N} K={K}", mfma="fp4")
 
 
 # ------------------------------------------------------------------ full size
@@ -246,4 +246,4 @@ def test_mx_sweep_full_size_sampled(qll, mx_weights, N, K):
         ref, absref = oracle.gemm_mxfp4(qa_all[:M], qb_ref, sa_all[:M], sb_ref, rows=rows,
                                         with_abs=True)
         check_fp(host_f64(y[torch.from_numpy(rows).cuda()]), ref, absref, K, "bf16",
-                 f"M={M} N={N} K={K}")
+                 f"M={M} N={N} K={K}", mfma="fp4")

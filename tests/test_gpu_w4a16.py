@@ -105,7 +105,7 @@ def test_gemm_all_variants(qll, w4_cases, shape, splits):
         for od in ("fp32", "bf16"):
             y = qll.gemm_w4a16(dA, dB, ds, out_dtype=od, cfg=(name, splits))
             torch.cuda.synchronize()
-            check_fp(host_f64(y), ref, absref, K, od, f"{name} S={splits} {od}")
+            check_fp(host_f64(y), ref, absref, K, od, f"{name} S={splits} {od}", mfma="w4a16")
 
 
 @pytest.mark.parametrize("M", [1, 40, 333])
@@ -147,7 +147,7 @@ def test_end_to_end(qll, M, N, K):
     assert np.array_equal(q.cpu().numpy(), q_ref)
     assert np.array_equal(s.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
     ref, absref = oracle.gemm_w4a16(x, q_ref, s_ref, with_abs=True)
-    check_fp(host_f64(y), ref, absref, K, "bf16", f"M={M} N={N} K={K}")
+    check_fp(host_f64(y), ref, absref, K, "bf16", f"M={M} N={N} K={K}", mfma="w4a16")
 
 
 @pytest.fixture(scope="module")
@@ -174,4 +174,4 @@ def test_w4_sweep_full_size_sampled(qll, w4_weights, N, K):
         rows = sample_rows(M, 6, seed=K)
         ref, absref = oracle.gemm_w4a16(x_all[:M], q_ref, s_ref, rows=rows, with_abs=True)
         check_fp(host_f64(y[torch.from_numpy(rows).cuda()]), ref, absref, K, "bf16",
-                 f"M={M} N={N} K={K}")
+                 f"M={M} N={N} K={K}", mfma="w4a16")
