@@ -5,7 +5,9 @@ Default workload (one "step"): the FP8 dynamic per-token sweep -- for
 (N, K) in {(4096, 2048), (2048, 6144)} and M in {1, 4, 8, 16, 32, 64, 256,
 512, 1024, 2048}: quantize the bf16 activations per token on the device
 (quantize_per_token_fp8), then run the scaled FP8 GEMM (gemm_fp8_scaled) with
-the configuration the dispatch picks, bf16 out.  Weights are quantized per
+the configuration the dispatch picks, bf16 out; where the fp8_dynamic
+dispatch names a fused variant for the shape, the problem is the one fused
+call of linear_fp8_dynamic instead (quantizer and GEMM in one kernel).  Weights are quantized per
 output channel on the device once, before timing.  Every (N, K, M) problem
 has its own buffers (about 350 MB touched per step, more than the 256 MB
 Infinity Cache), so a problem's weights come from HBM, not from a cache.
@@ -35,7 +37,15 @@ counters read on a copy kernel of known size (--calib-copy runs that copy).
 Without them the traffic comes from the workload's committed profile
 (profiles/<workload>_sweep_bench_line.json) when that profile measured the
 same kernel built from the same sources (a digest of the kernel and ABI
-sources is stored with the counters), and is null otherwise.
+sources is stored with the counters), and is null otherwise.  --mfma-csv
+(SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_MFMA, SQ_INSTS_VALU_MFMA_MOPS_*,
+GRBM_GUI_ACTIVE) adds the matrix-core counters with their calibration (busy
+cycles per instruction, MOPS against the algorithmic flops, the clock the
+dispatch ran at); --kernel-trace-csv (a rocprofv3 --kernel-trace run of the
+same command) adds the dominant kernel's traced duration over exactly the
+launches the per-call timing times, and the roofline fraction at that
+duration.  Both come from the committed profile under the same conditions
+as the traffic when not given.
 
 Other workloads (--workload int8|block|bi|vocab|vocab_bi|moe|mxfp4|w4a16) print the
 same JSON shape; moe is the grouped (per-expert) FP8 GEMM of a 64-expert layer
@@ -82,6 +92,10 @@ def parse():
                    help="rocprofv3 --pmc FETCH_SIZE counter_collection.csv of this command")
     p.add_argument("--write-csv", default=None,
                    help="rocprofv3 --pmc WRITE_SIZE counter_collection.csv of this command")
+    p.add_argument("--kernel-trace-csv", default=None,
+                   help="kernel trace CSV of a rocprofv3 --kernel-trace run of this same "
+                        "command: the dominant kernel's duration over the launches the "
+                        "per-call timing times, and its roofline fraction")
     p.add_argument("--mfma-csv", default=None,
                    help="rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE "
                         "counter_collection.csv of this command")
@@ -115,8 +129,11 @@ class Problem:
         return 2.0 * self.M * self.N * self.K
 
     def algo_bytes(self):
-        """Algorithmic HBM bytes of the GEMM: A + B + scales + bf16 out."""
+        """Algorithmic HBM bytes of the GEMM: A + B + scales + bf16 out (the
+        fused linear layer: bf16 tokens in, their codes and scales out too)."""
         M, N, K = self.M, self.N, self.K
+        if getattr(self, "fused", False):
+            return 2 * M * K + N * K + 4 * N + 2 * M * N + M * K + 4 * M
         if self.op == "bf16_bi":
             return 2 * M * K + 2 * N * K + 2 * M * N
         if self.op == "block_fp8":
@@ -188,6 +205,22 @@ def build_problems(torch, qll, workload):
         p.tensors["quant"] = (t, qargs)
         return q, s
 
+    def add_linear(p, x, B, sb, variant):
+        # linear_fp8_dynamic on a fused configuration: quantizer and GEMM in
+        # one kernel (timed and reported as the problem's "gemm" call)
+        q = torch.empty((p.M, p.K), dtype=torch.float8_e4m3fn, device="cuda")
+        sa = torch.empty((p.M, 1), dtype=torch.float32, device="cuda")
+        out = torch.empty((p.M, p.N), dtype=torch.bfloat16, device="cuda")
+        largs = lambda p, t: (t["x"].data_ptr(), t["B"].data_ptr(), t["sb"].data_ptr(),
+                              t["q"].data_ptr(), t["sa"].data_ptr(), t["out"].data_ptr(), 0,
+                              p.M, p.N, p.K, None, 0, stream)
+        t = dict(x=x, B=B, sb=sb, q=q, sa=sa, out=out)
+        p.keep += list(t.values())
+        p.calls.append(("gemm", L.linear_fp8_dynamic, largs(p, t)))
+        p.tensors["gemm"] = (t, largs)
+        p.variant, p.splits, p.eff_splits = variant, 1, 1
+        p.fused = True
+
     if workload in ("fp8", "vocab"):
         shapes = W.FP8_SHAPES if workload == "fp8" else [W.VOCAB_SHAPE]
         mlist = W.FP8_M if workload == "fp8" else W.VOCAB_M
@@ -203,8 +236,13 @@ def build_problems(torch, qll, workload):
             for M in mlist:
                 p = Problem("fp8", M, N, K)
                 # own copy of the weights per problem (cold for every problem)
-                q, s = add_quant(p, x_all[:M].clone(), 0)
-                add_gemm(p, "gemm_fp8_scaled", q, qw.clone(), s, sw.clone())
+                dyn = qll.select("fp8_dynamic", M, N, K)[0]
+                if dyn[0] == "f":
+                    # the dispatch runs this linear layer fused: one call
+                    add_linear(p, x_all[:M].clone(), qw.clone(), sw.clone(), dyn)
+                else:
+                    q, s = add_quant(p, x_all[:M].clone(), 0)
+                    add_gemm(p, "gemm_fp8_scaled", q, qw.clone(), s, sw.clone())
                 probs.append(p)
     elif workload == "mxfp4":
         for N, K in W.MX_SHAPES:
@@ -381,7 +419,8 @@ def vendor_us(torch, probs, replays, stream, max_copies=256):
             def call(A, B, sa, sb):
                 return torch._scaled_mm(A, B.t(), scale_a=sa.view(-1, 1), scale_b=sb.view(1, -1),
                                         out_dtype=torch.bfloat16)
-            base = (t["A"], t["B"], t["sa"], t["sb"])
+            # (a fused linear layer: the codes and scales its first run wrote)
+            base = (t.get("A", t.get("q")), t["B"], t["sa"], t["sb"])
         elif p.op == "bf16_bi":
             def call(A, Bt):
                 return torch.matmul(A, Bt)
@@ -470,7 +509,15 @@ def kernel_symbol(qll, op, variant):
     if grouped:
         op = "fp8"
     opn = {"int8": 0, "fp8": 1, "block_fp8": 2, "bf16_bi": 3, "mxfp4": 4, "w4a16": 5}[op]
+    if op == "fp8" and variant[0] == "f":  # the fused linear layer
+        v = next(x for x in qll.variants("fp8_dynamic") if x["name"] == variant)
+        return (f"void qll::linear_fused_kernel<{v['bp']}, {v['wp']}, {v['ksteps']}>"
+                "(qll::FusedArgs)")
     v = next(x for x in qll.variants(op) if x["name"] == variant)
+    if variant[0] == "p" and "_k64_" in variant:  # the 32x32x64 deep-ring tiles
+        st = variant.rsplit("_s", 1)[1]
+        return (f"void qll::gemm_p32_kernel<{opn}, {v['bp']}, {v['bq']}, {v['wp']}, "
+                f"{v['wq']}, {st}, false>(qll::GemmArgs)")
     if op == "w4a16":
         if variant[0] == "t":
             return (f"void qll::gemm_w4_tile_kernel<{v['bp']}, {v['bq']}, {v['wp']}, "
@@ -690,21 +737,93 @@ def hbm_traffic(fetch_csv, write_csv, kernel):
 XCDS = 8  # GRBM_GUI_ACTIVE adds up the busy cycles of the 8 XCDs
 
 
-def mfma_busy(csv_path, kernel, cus):
-    """Matrix-core busy fraction of `kernel` from its counters: the MFMA busy
-    cycles of all SIMDs (SQ_VALU_MFMA_BUSY_CYCLES) over the SIMD cycles of the
-    dispatch (GRBM_GUI_ACTIVE / XCDS cycles x 4 SIMDs x CUs)."""
-    busy = [v for k, v in counter_per_dispatch(csv_path, "SQ_VALU_MFMA_BUSY_CYCLES").items()
-            if k.startswith(kernel)]
-    gui = [v for k, v in counter_per_dispatch(csv_path, "GRBM_GUI_ACTIVE").items()
-           if k.startswith(kernel)]
-    if not busy or not gui:
+def dispatch_durations_ns(csv_path, kernel):
+    """[(duration ns) per dispatch of `kernel`] from a rocprofv3 counter CSV
+    (one row per counter: the first counter's rows), or [] without
+    timestamps."""
+    import csv
+    out, first = [], None
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            if not r.get("Kernel_Name", "").startswith(kernel):
+                continue
+            first = first or r.get("Counter_Name")
+            if r.get("Counter_Name") != first:
+                continue
+            try:
+                out.append(float(r["End_Timestamp"]) - float(r["Start_Timestamp"]))
+            except (KeyError, ValueError):
+                return []
+    return out
+
+
+def mfma_busy(csv_path, kernel, cus, flops_per_launch=None):
+    """Matrix-core counters of `kernel`, each per dispatch (mean):
+    SQ_VALU_MFMA_BUSY_CYCLES adds up, over every SIMD, the fixed number of
+    busy cycles of each MFMA instruction issued (SQ_INSTS_MFMA counts them;
+    the ratio is the cycles one instruction takes, e.g. 32 for the e4m3
+    16x16x128 step), so for power-of-two shapes it is a power of two times
+    that constant -- an exact count, not a sampled or saturated one.  The
+    busy fraction is those cycles over the SIMD cycles of the dispatch
+    (GRBM_GUI_ACTIVE / XCDS x 4 SIMDs x CUs); GRBM_GUI_ACTIVE / XCDS over the
+    dispatch's duration is the engine clock the kernel ran at, and the
+    SQ_INSTS_VALU_MFMA_MOPS_* counter x 512 its matrix-core operations (the
+    algorithmic 2MNK plus the padding of partial tiles)."""
+    def mean_of(counter):
+        d = [v for k, v in counter_per_dispatch(csv_path, counter).items() if k.startswith(kernel)]
+        return (sum(d[0]) / len(d[0]), len(d[0])) if d else (None, 0)
+    b, n = mean_of("SQ_VALU_MFMA_BUSY_CYCLES")
+    g, _ = mean_of("GRBM_GUI_ACTIVE")
+    if b is None or g is None:
         return None
-    b = sum(busy[0]) / len(busy[0])
-    g = sum(gui[0]) / len(gui[0])
-    return {"mfma_busy_frac": round(b / (g / XCDS * 4 * cus), 4),
-            "SQ_VALU_MFMA_BUSY_CYCLES": round(b), "GRBM_GUI_ACTIVE": round(g),
-            "dispatches": len(busy[0])}
+    res = {"mfma_busy_frac": round(b / (g / XCDS * 4 * cus), 4),
+           "SQ_VALU_MFMA_BUSY_CYCLES": round(b), "GRBM_GUI_ACTIVE": round(g),
+           "dispatches": n}
+    inst, _ = mean_of("SQ_INSTS_MFMA")
+    if inst:
+        res["SQ_INSTS_MFMA"] = round(inst)
+        res["busy_cycles_per_mfma"] = round(b / inst, 3)
+    for dt in ("F8", "I8", "BF16", "F6F4"):
+        mops, _ = mean_of(f"SQ_INSTS_VALU_MFMA_MOPS_{dt}")
+        if mops:
+            res[f"mops_{dt.lower()}_flops"] = round(mops * 512)
+            if flops_per_launch:
+                res["mops_over_algorithmic"] = round(mops * 512 / flops_per_launch, 4)
+    durs = dispatch_durations_ns(csv_path, kernel)
+    if durs:
+        dur = sum(durs) / len(durs)
+        res["dispatch_us"] = round(dur / 1e3, 3)
+        res["clock_ghz"] = round(g / XCDS / dur, 3)
+    return res
+
+
+def trace_timed_durations(csv_path, kernel, n_steps_dispatches, plan):
+    """Durations (us) of the launches of `kernel` that the per-call timing
+    times, from a rocprofv3 --kernel-trace CSV of a run of the same command.
+    The kernel's dispatches come in this order: n_steps_dispatches from the
+    first, warm-up, graph and eager steps; then per problem that uses it, in
+    problem order, its per-call graph of `copies` launches replayed once
+    untimed, `replays` times timed (these are the ones kept) and (1 +
+    replays) times warm.  plan: [(problem index, copies, replays)].
+    Returns {problem index: [durations]} or None when the counts disagree."""
+    import csv
+    durs = []
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            if r.get("Kernel_Name", "").startswith(kernel):
+                durs.append((int(r["Start_Timestamp"]),
+                             (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+    durs.sort()
+    d = [x for _, x in durs]
+    need = n_steps_dispatches + sum(2 * (1 + rep) * c for _, c, rep in plan)
+    if len(d) != need:
+        return None
+    out, at = {}, n_steps_dispatches
+    for i, c, rep in plan:
+        at += c  # the untimed replay
+        out[i] = d[at:at + rep * c]
+        at += rep * c + (1 + rep) * c  # the timed replays, then the warm graph
+    return out
 
 
 def main():
@@ -827,6 +946,8 @@ def main():
             rec[f"{kind}_copies"] = st["copies"]
             if eager_call[i][j]:
                 rec[f"{kind}_eager_us"] = round(sorted(eager_call[i][j])[len(eager_call[i][j]) // 2], 3)
+        if getattr(p, "fused", False):
+            rec["fused"] = True  # one kernel: quantizer and GEMM
         if vend is not None:
             rec["vendor_gemm_us"] = round(vend[i], 3) if vend[i] is not None else None
         t_gemm = rec["gemm_us"] * 1e-6
@@ -891,10 +1012,47 @@ def main():
             roof["traffic_detail"]["from"] = (
                 f"profiles/{args.workload}_sweep_traffic.md: rocprofv3 --pmc FETCH_SIZE and "
                 "WRITE_SIZE runs of this workload on the same kernel and sources")
+            # the matrix-core counters and the traced kernel duration of the
+            # same profiling runs (same kernel, same sources)
+            if old.get("mfma_counters") and not args.mfma_csv:
+                roof["mfma_counters"] = dict(old["mfma_counters"])
+                roof["mfma_counters"]["from"] = (
+                    f"profiles/{args.workload}_sweep_traffic.md (rocprofv3 --pmc run)")
+            kd = old.get("kernel_duration")
+            if kd and "avg_us" in kd and not args.kernel_trace_csv:
+                roof["kernel_duration"] = dict(kd)
+                roof["kernel_duration"]["from"] = (
+                    f"profiles/{args.workload}_sweep_kernel_stats.md: rocprofv3 --kernel-trace "
+                    "run of this workload on the same kernel and sources (kernel only, no "
+                    "in-graph gap)")
     if args.mfma_csv and os.path.exists(args.mfma_csv):
-        mb = mfma_busy(args.mfma_csv, dom_sym, props.multi_processor_count)
+        mb = mfma_busy(args.mfma_csv, dom_sym, props.multi_processor_count,
+                       flops_per_launch=dom[2] / dom[1])
         if mb:
             roof["mfma_counters"] = mb
+    if args.kernel_trace_csv and os.path.exists(args.kernel_trace_csv):
+        # the dominant kernel's own duration over the launches timed above
+        # (kernel time only, without the in-graph gap the events include)
+        users = [i for i, p in enumerate(probs) if p.eff_splits == 1 and
+                 kernel_symbol(qll, p.op, p.variant) == dom_sym]
+        steps_disp = len(users) * (1 + args.warmup + (1 + args.steps if not args.no_graph else 0)
+                                   + args.steps + (5 if not args.no_graph else 0))
+        gemm_j = {i: [k for k, _, _ in probs[i].calls].index("gemm") for i in users}
+        plan = [(i, call_plan[i][gemm_j[i]], args.replays) for i in users]
+        td = trace_timed_durations(args.kernel_trace_csv, dom_sym, steps_disp, plan)
+        if td:
+            t_k = sum(sum(v) / len(v) for v in td.values()) / len(td) * 1e-6
+            ka = (dom[2] / dom[1] if bound == "mfma" else dom[3] / dom[1]) / t_k
+            ka = ka / 1e12 if bound == "mfma" else ka / 1e9
+            roof["kernel_duration"] = {
+                "avg_us": round(t_k * 1e6, 3), "achieved": round(ka, 2),
+                "frac": round(ka / roof["peak"], 4),
+                "from": "rocprofv3 --kernel-trace of the same command: the durations of "
+                        "the launches the per-call timing times (kernel only, no in-graph "
+                        "gap)"}
+        else:
+            roof["kernel_duration"] = {"error": "the trace's dispatch count does not match "
+                                                "this command's launch plan"}
     if dom_sym.startswith("void qll::gemm_pipe_kernel") and "true>" not in dom_sym:
         # the fetch the XCD structure implies (each XCD's L2 reads the rows
         # of its tiles once), per launch, plus the bf16 output

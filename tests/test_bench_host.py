@@ -62,6 +62,51 @@ def test_mfma_busy_fraction(tmp_path):
     assert mb["dispatches"] == 1
 
 
+def test_mfma_counters_calibration(tmp_path):
+    # busy cycles = instructions x 32, MOPS x 512 = the algorithmic flops,
+    # clock = GRBM_GUI_ACTIVE / 8 XCDs / the dispatch's duration
+    p = tmp_path / "m.csv"
+    rows = [(DOM, "SQ_VALU_MFMA_BUSY_CYCLES", 32.0 * 4096), (DOM, "SQ_INSTS_MFMA", 4096.0),
+            (DOM, "SQ_INSTS_VALU_MFMA_MOPS_F8", 1e6 / 512), (DOM, "GRBM_GUI_ACTIVE", 8 * 20000.0)]
+    with open(p, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=FIELDS + ["Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        for k, c, v in rows:
+            w.writerow({"Dispatch_Id": 1, "Kernel_Name": k, "Counter_Name": c,
+                        "Counter_Value": v, "Start_Timestamp": 1000, "End_Timestamp": 11000})
+    mb = bench.mfma_busy(str(p), "void qll::gemm_pipe_kernel", 256, flops_per_launch=1e6)
+    assert mb["busy_cycles_per_mfma"] == 32.0
+    assert mb["mops_f8_flops"] == 1000000
+    assert mb["mops_over_algorithmic"] == pytest.approx(1.0)
+    assert mb["dispatch_us"] == pytest.approx(10.0)
+    assert mb["clock_ghz"] == pytest.approx(2.0)
+
+
+def write_trace(path, kernels):
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        t = 0
+        for k, dur in kernels:
+            w.writerow({"Kernel_Name": k, "Start_Timestamp": t, "End_Timestamp": t + dur})
+            t += dur + 100
+
+
+def test_trace_timed_durations_picks_the_timed_replays(tmp_path):
+    # 3 step dispatches, then problem 0 (copies 2, replays 3): 2 untimed, 6
+    # timed, 8 warm; then problem 4 (copies 1, replays 3): 1, 3, 4; another
+    # kernel interleaved is ignored
+    other = "void qll::splitk_reduce_kernel<1>(qll::GemmArgs)"
+    seq = [(DOM, 1)] * 3 + [(DOM, 2)] * 2 + [(DOM, 1000)] * 6 + [(other, 5)] + [(DOM, 3)] * 8
+    seq += [(DOM, 4)] + [(DOM, 2000)] * 3 + [(DOM, 7)] * 4
+    p = tmp_path / "t.csv"
+    write_trace(p, seq)
+    td = bench.trace_timed_durations(str(p), DOM, 3, [(0, 2, 3), (4, 1, 3)])
+    assert td == {0: [1.0] * 6, 4: [2.0] * 3}
+    # a count that does not match the plan: no figure
+    assert bench.trace_timed_durations(str(p), DOM, 4, [(0, 2, 3), (4, 1, 3)]) is None
+
+
 def test_xcd_fill_bytes_bounds():
     # one tile per XCD: every XCD fetches exactly its own rows (no sharing)
     M, N, K, bp, bq = 256, 512, 1024, 128, 128

@@ -27,6 +27,17 @@ def qll():
     return q
 
 
+def two_launch_cfg(qll, M, N, K):
+    """The FP8 GEMM configuration whose output the dispatched linear layer
+    reproduces bitwise: the fp8_dynamic entry itself, or for a fused variant
+    f{HR}x16_w{W}_d{D} the W-wave decode GEMM k{HR}x16_w{W}."""
+    name, splits = qll.select("fp8_dynamic", M, N, K)
+    if name[0] == "f":
+        v = next(x for x in qll.variants("fp8_dynamic") if x["name"] == name)
+        return (f"k{v['bp']}x16_w{v['wp']}", 1)
+    return (name, splits)
+
+
 @pytest.mark.parametrize("N,K", [(4096, 2048), (2048, 6144), (520, 1040)])
 def test_linear_equals_two_calls_and_oracle(qll, N, K):
     w = workloads.weights_bf16(N, K, key=(workloads.W_TEST, 40))
@@ -43,7 +54,8 @@ def test_linear_equals_two_calls_and_oracle(qll, N, K):
             for od in ("bf16", "fp32"):
                 y, q, sa = qll.linear_fp8_dynamic(dx, dB, dsb, out_dtype=od, cfg=cfg)
                 q2, sa2 = qll.quantize_per_token_fp8(dx)
-                y2 = qll.gemm_fp8_scaled(q2, dB, sa2, dsb, out_dtype=od, cfg=cfg)
+                y2 = qll.gemm_fp8_scaled(q2, dB, sa2, dsb, out_dtype=od,
+                                         cfg=cfg or two_launch_cfg(qll, M, N, K))
                 torch.cuda.synchronize()
                 assert np.array_equal(host_codes(q), qr), (M, cfg)
                 assert np.array_equal(sa.cpu().numpy().view(np.uint32), sr.view(np.uint32))
