@@ -17,7 +17,9 @@
 //   quant_rows:        TPR threads (64, 128 or 256) per row, the row held in
 //                      registers, max by cross-lane shuffles and, across the
 //                      waves of a row, through LDS (very long rows: one
-//                      workgroup per row, two passes);
+//                      workgroup per row, two passes); many rows: one wave
+//                      per row up to 4096 elements, a row loop with the next
+//                      row's loads in flight for longer ones;
 //   quant_groups128:   16 lanes per 1x128 group (8 bf16 per lane), shuffle
 //                      max inside the 16 lanes; no LDS;
 //   quant_weight_blocks: one workgroup per 128x128 weight block.
@@ -154,6 +156,52 @@ __global__ __launch_bounds__(256) void quant_rows_loop_kernel(const uint16_t* __
     }
 }
 
+// Many rows of up to 4096 elements: one wave per row, four rows per
+// 256-thread workgroup, lane l holding chunks l, l + 64, ... of its row (CH
+// of them).  The row is read through a buffer resource of its own (chunks
+// past K read as zeros), so no load is conditional and the wait before the
+// maximum covers them all at once; the maximum is a shuffle reduction inside
+// the wave, with no LDS and no barrier, so each wave streams on its own.
+// With every row in flight at once this keeps more bytes in the air than a
+// workgroup per row of 256 threads, each holding one or two chunks.  The
+// arithmetic is quant_rows_kernel's with TPR = 64: bitwise the same codes and
+// scales.
+template <int CH>
+__global__ __launch_bounds__(256) void quant_rows_wave_kernel(const uint16_t* __restrict__ x,
+                                                             uint8_t* __restrict__ q,
+                                                             float* __restrict__ s, int M,
+                                                             int K)
+{
+    const int lane = threadIdx.x & 63;
+    // (the wave's row, uniform across the wave: one descriptor per wave)
+    const int m = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (m >= M)
+        return;
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(x + (size_t)m * K), (short)0, 2 * K, 0x00020000);
+    uint4 v[CH];
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+        v[c] = __builtin_bit_cast(
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, (c * 64 + lane) * 16, 0, 0));
+    float amax = 0.0f;
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+        amax = fmaxf(amax, absmax8(v[c]));
+    amax = wave_max(amax);
+    const float sc = amax / 448.0f;
+    if (lane == 0)
+        s[m] = sc;
+    const Quot d(sc);
+    uint8_t* qr = q + (size_t)m * K;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+        const int e = (c * 64 + lane) * 8;
+        if (e < K)
+            *(uint2*)(qr + e) = encode8(v[c], d);
+    }
+}
+
 // Rows longer than 256 * 8 * 16 elements: one workgroup per row, two passes
 // over the row (the second one hits the caches).
 __global__ __launch_bounds__(256) void quant_rows_long_kernel(const uint16_t* __restrict__ x,
@@ -264,6 +312,23 @@ hipError_t launch_quant_rows(const void* x, void* q, float* s, int M, int K,
     // a whole workgroup per row from 2048 elements on (short per-thread
     // chains, no idle lanes), narrower rows share a workgroup
     const int chunks = (K + 7) / 8;
+    // many rows of up to 2048 elements (4096 from 2048 rows on): one wave per
+    // row (measured faster there, cold: M = 4096, K = 2048 8.0 against
+    // 12.0 us; M = 2048, K = 4096 8.8 against 9.7 us; from K = 6144 the row
+    // loop below is ahead)
+    if ((M >= 512 && chunks <= 256) || (M >= 2048 && chunks <= 512)) {
+        const dim3 grid((M + 3) / 4);
+        switch ((chunks + 63) / 64) {
+        case 1: hipLaunchKernelGGL(quant_rows_wave_kernel<1>, grid, dim3(256), 0, stream, xp, qp, s, M, K); break;
+        case 2: hipLaunchKernelGGL(quant_rows_wave_kernel<2>, grid, dim3(256), 0, stream, xp, qp, s, M, K); break;
+        case 3: hipLaunchKernelGGL(quant_rows_wave_kernel<3>, grid, dim3(256), 0, stream, xp, qp, s, M, K); break;
+        case 4: hipLaunchKernelGGL(quant_rows_wave_kernel<4>, grid, dim3(256), 0, stream, xp, qp, s, M, K); break;
+        case 5:
+        case 6: hipLaunchKernelGGL(quant_rows_wave_kernel<6>, grid, dim3(256), 0, stream, xp, qp, s, M, K); break;
+        default: hipLaunchKernelGGL(quant_rows_wave_kernel<8>, grid, dim3(256), 0, stream, xp, qp, s, M, K); break;
+        }
+        return hipGetLastError();
+    }
     // many rows of 2048..8192 elements: the row loop with G = 512 workgroups
     // (two per CU, each with the next row's loads in flight)
     constexpr int kLoopGrid = 512;

@@ -42,11 +42,15 @@ def assert_same(q, s, qr, sr, what):
 # K spans every row-kernel shape: 64, 128 and 256 threads per row, one to
 # sixteen 16-byte chunks per thread, and the two-pass kernel past 32768; more
 # than 512 rows of 2048..8192 take the row loop (one to four chunks, a ragged
-# K tail, workgroups with an odd number of rows)
+# K tail, workgroups with an odd number of rows); 512 rows and more of up to
+# 2048 elements (2048 rows and more of up to 4096) take one wave per row (one
+# to eight chunks per lane, ragged K tails, a partial last workgroup)
 @pytest.mark.parametrize("M,K", [(1, 16), (4, 608), (9, 1024), (301, 1040), (3, 2048),
                                  (5, 6144), (2048, 2048), (7, 4112), (2, 16400),
                                  (64, 20000), (3, 32768), (2, 40000),
-                                 (2048, 6144), (1500, 4112), (513, 8192), (1025, 2064)])
+                                 (2048, 6144), (1500, 4112), (513, 8192), (1025, 2064),
+                                 (512, 16), (600, 1040), (777, 2048), (2048, 4096),
+                                 (2101, 3088), (4096, 2048), (2050, 2576)])
 def test_per_token_bit_exact(qll, M, K):
     x = workloads.bf16_normal((M, K), (workloads.W_TEST, 20, M, K), outlier_frac=0.01)
     q, s = run_quant(qll, x)
