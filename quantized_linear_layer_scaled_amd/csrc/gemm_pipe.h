@@ -460,11 +460,14 @@ void gemm_pipe_kernel(GemmArgs a)
         }
     }
 
-    auto issue = [&](int kt, uint8_t* buf) __attribute__((always_inline)) {
+    // the operand copies i0 .. i1 - 1 of stage kt (of this wave's LPT0)
+    auto issue_ops = [&](int kt, uint8_t* buf, int i0, int i1) __attribute__((always_inline)) {
         const int kb0 = kt * KSTAGE;  // relative to kbeg
         const bool full = kbeg + kb0 + KSTAGE <= kend;
 #pragma unroll
         for (int i = 0; i < LPT0; ++i) {
+            if (i < i0 || i >= i1)
+                continue;
             uint32_t vo = voff[i] + (uint32_t)kb0;
             if (!full && kbeg + kb0 + chunk_of(i) * 16 >= kend)
                 vo = kOutOfRange;  // past the K range: zeros
@@ -472,6 +475,12 @@ void gemm_pipe_kernel(GemmArgs a)
                   __builtin_amdgcn_readfirstlane(
                       (uint32_t)(uintptr_t)(buf + (i * WAVES + wave) * 1024)));
         }
+    };
+    // the scale copies of stage kt (MXFP4 block scales, Block-FP8 scales)
+    auto issue_scales = [&](int kt, uint8_t* buf) __attribute__((always_inline)) {
+        const int kb0 = kt * KSTAGE;
+        const bool full = kbeg + kb0 + KSTAGE <= kend;
+        (void)full;
         if constexpr (MX) {
 #pragma unroll
             for (int i = 0; i < LPS; ++i) {
@@ -491,6 +500,10 @@ void gemm_pipe_kernel(GemmArgs a)
             dma4(sb_off == kOutOfRange ? kOutOfRange : sb_off + g4, rsSb,
                  __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(sc + 256)));
         }
+    };
+    auto issue = [&](int kt, uint8_t* buf) __attribute__((always_inline)) {
+        issue_ops(kt, buf, 0, LPT0);
+        issue_scales(kt, buf);
     };
 
     acc_t acc[RP][RQ];
@@ -689,8 +702,23 @@ void gemm_pipe_kernel(GemmArgs a)
             // in flight), and every wave is done with stage kt - 1: its slot
             // takes stage kt + STAGES - 1
             wait_stage(min(STAGES - 2, nk - 1 - kt));
-            if (kt + STAGES - 1 < nk)
-                issue(kt + STAGES - 1, slot(std::integral_constant<int, fs>{}));
+            // The copies of stage kt + STAGES - 1 are spread over the first
+            // half of the first K step's row blocks (two of RP row blocks
+            // carry 2 LPT0 / RP of them each) instead of all being issued
+            // here: the texture unit takes the CU's copies one after another,
+            // and a wave that had to issue all its copies first would wait
+            // for its place in that queue before its first MFMA.  (Step 0 of
+            // a stage kt < nk always lies in the K range, so it is never
+            // skipped.)
+            const bool fresh = kt + STAGES - 1 < nk;
+            uint8_t* const fslot = slot(std::integral_constant<int, fs>{});
+            if (fresh)
+                issue_scales(kt + STAGES - 1, fslot);
+            auto spread = [&](int ks, int i) __attribute__((always_inline)) {
+                if (ks == 0 && fresh && 2 * i < RP)
+                    issue_ops(kt + STAGES - 1, fslot, 2 * i * LPT0 / RP,
+                              2 * i + 2 >= RP ? LPT0 : (2 * i + 2) * LPT0 / RP);
+            };
             if constexpr (FOLD)
                 fold.before(kt * NSTEP, acc);
             const uint8_t* sp = slot(std::integral_constant<int, cs>{});
@@ -734,6 +762,7 @@ void gemm_pipe_kernel(GemmArgs a)
                         pg[0][j] = mfma_step<OP>(av[0], bv[j], v4f{0, 0, 0, 0});
 #pragma unroll
                     for (int i = 0; i < RP; ++i) {
+                        spread(ks, i);
                         if (i + 1 < RP) {
                             read_a(i + 1, av[(i + 1) & 1]);
 #pragma unroll
@@ -757,6 +786,7 @@ void gemm_pipe_kernel(GemmArgs a)
                 } else {
 #pragma unroll
                     for (int i = 0; i < RP; ++i) {
+                        spread(ks, i);
                         if (i + 1 < RP)
                             read_a(i + 1, av[(i + 1) & 1]);
 #pragma unroll
