@@ -808,8 +808,14 @@ void gemm_pipe_kernel(GemmArgs a)
     // columns of one row -- a 16-byte bf16 store (two for fp32) instead of
     // eight scattered 2-byte stores.
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");  // ring slots are free
-    static_assert(WAVES * 16 * SQ * 4 <= STAGES * SLOT, "epilogue scratch must fit the ring");
-    elem_t* scr = (elem_t*)(ring + wave * 16 * SQ * 4);
+    // Scratch rows of SQ + 4 words: a lane writes rows 4 (lane / 16) + v of
+    // its column, so that each half-wave's two lane groups (4 rows apart)
+    // fall on the two disjoint halves of the 32 LDS banks instead of on the
+    // same 16 (with rows of SQ words, a multiple of 32, every 16-lane group
+    // of a write hit the same banks).
+    constexpr int SQP = SQ + 4;
+    static_assert(WAVES * 16 * SQP * 4 <= STAGES * SLOT, "epilogue scratch must fit the ring");
+    elem_t* scr = (elem_t*)(ring + wave * 16 * SQP * 4);
     constexpr int CPR = SQ / 8;          // 8-column groups per row
     constexpr int RPP = 64 / CPR;        // rows per pass
     constexpr int PASSES = 16 / RPP;
@@ -855,7 +861,7 @@ void gemm_pipe_kernel(GemmArgs a)
         for (int j = 0; j < RQ; ++j)
 #pragma unroll
             for (int v = 0; v < 4; ++v)
-                scr[((lane >> 4) * 4 + v) * SQ + j * 16 + (lane & 15)] = acc[i][j][v];
+                scr[((lane >> 4) * 4 + v) * SQP + j * 16 + (lane & 15)] = acc[i][j][v];
 #pragma unroll
         for (int pass = 0; pass < PASSES; ++pass) {
             const int r = pass * RPP + lane / CPR;
@@ -863,7 +869,7 @@ void gemm_pipe_kernel(GemmArgs a)
             elem_t e[8];
 #pragma unroll
             for (int t = 0; t < 8; ++t)
-                e[t] = scr[r * SQ + c + t];
+                e[t] = scr[r * SQP + c + t];
             if (m >= M)
                 continue;
             if (a.splits > 1 || (OP == OP_INT8 && a.out_dtype == OUT_INT32)) {
