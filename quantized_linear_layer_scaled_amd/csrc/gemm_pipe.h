@@ -655,6 +655,15 @@ void gemm_pipe_kernel(GemmArgs a)
         // slot kt % STAGES takes stage kt + STAGES and the first step of stage
         // kt+1 is read from the next slot.
         constexpr int U = (NSTEP % 2 == 0 || STAGES % 2 == 0) ? STAGES : 2 * STAGES;
+        // Workgroups of up to 8 waves issue a stage's copies after the MFMAs
+        // of its last K step, not before them: the texture unit takes the
+        // CU's copies one after another, and a wave issuing its copies first
+        // would wait for its place in that queue before its MFMAs.  The slot
+        // is free from the barrier on either way.  With 16 waves (four MFMAs
+        // per wave per stage) the later issue cost more in copy latency than
+        // it saved (measured on 128x128 tiles: 3-5% slower; 4 and 8 waves:
+        // 2-10% faster).
+        constexpr bool DEFER = WAVES <= 8;
         auto stage = [&](auto J, int kt) __attribute__((always_inline)) {
             constexpr int j = decltype(J)::value;
             constexpr int cs = j % STAGES, ns = (j + 1) % STAGES;
@@ -672,12 +681,14 @@ void gemm_pipe_kernel(GemmArgs a)
                     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
                     if (kt + 1 < nk) {
                         wait_stage(min(STAGES - 2, nk - 2 - kt));
-                        if (kt + STAGES < nk)
+                        if (!DEFER && kt + STAGES < nk)
                             issue(kt + STAGES, slot(std::integral_constant<int, cs>{}));
                         load_step(slot(std::integral_constant<int, ns>{}), 0, fr[cp ^ 1]);
                     }
                 }
                 compute_step(fr[cp], kt, ks);
+                if (DEFER && ks + 1 == NSTEP && kt + STAGES < nk)
+                    issue(kt + STAGES, slot(std::integral_constant<int, cs>{}));
             }
         };
         for (int kt = 0; kt < nk; kt += U)
