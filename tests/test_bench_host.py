@@ -66,20 +66,26 @@ def test_mfma_counters_calibration(tmp_path):
     # busy cycles = instructions x 32, MOPS x 512 = the algorithmic flops,
     # clock = GRBM_GUI_ACTIVE / 8 XCDs / the dispatch's duration
     p = tmp_path / "m.csv"
-    rows = [(DOM, "SQ_VALU_MFMA_BUSY_CYCLES", 32.0 * 4096), (DOM, "SQ_INSTS_MFMA", 4096.0),
-            (DOM, "SQ_INSTS_VALU_MFMA_MOPS_F8", 1e6 / 512), (DOM, "GRBM_GUI_ACTIVE", 8 * 20000.0)]
-    with open(p, "w", newline="") as f:
-        w = csv.DictWriter(f, fieldnames=FIELDS + ["Start_Timestamp", "End_Timestamp"])
-        w.writeheader()
-        for k, c, v in rows:
-            w.writerow({"Dispatch_Id": 1, "Kernel_Name": k, "Counter_Name": c,
-                        "Counter_Value": v, "Start_Timestamp": 1000, "End_Timestamp": 11000})
+    def write(end_ns, gui):
+        rows = [(DOM, "SQ_VALU_MFMA_BUSY_CYCLES", 32.0 * 4096), (DOM, "SQ_INSTS_MFMA", 4096.0),
+                (DOM, "SQ_INSTS_VALU_MFMA_MOPS_F8", 1e6 / 512), (DOM, "GRBM_GUI_ACTIVE", gui)]
+        with open(p, "w", newline="") as f:
+            w = csv.DictWriter(f, fieldnames=FIELDS + ["Start_Timestamp", "End_Timestamp"])
+            w.writeheader()
+            for k, c, v in rows:
+                w.writerow({"Dispatch_Id": 1, "Kernel_Name": k, "Counter_Name": c,
+                            "Counter_Value": v, "Start_Timestamp": 1000, "End_Timestamp": end_ns})
+    write(201000, 8 * 400000.0)  # a 200 us dispatch at 2 GHz
     mb = bench.mfma_busy(str(p), "void qll::gemm_pipe_kernel", 256, flops_per_launch=1e6)
     assert mb["busy_cycles_per_mfma"] == 32.0
     assert mb["mops_f8_flops"] == 1000000
     assert mb["mops_over_algorithmic"] == pytest.approx(1.0)
-    assert mb["dispatch_us"] == pytest.approx(10.0)
+    assert mb["dispatch_us"] == pytest.approx(200.0)
     assert mb["clock_ghz"] == pytest.approx(2.0)
+    # a short dispatch: the counter's wider window would inflate the clock
+    write(11000, 8 * 20000.0)
+    mb = bench.mfma_busy(str(p), "void qll::gemm_pipe_kernel", 256, flops_per_launch=1e6)
+    assert mb["dispatch_us"] == pytest.approx(10.0) and "clock_ghz" not in mb
 
 
 def write_trace(path, kernels):
