@@ -23,6 +23,8 @@ matrix cores in an order of its own, so several results are correct):
 import numpy as np
 import torch
 
+from workloads import to_bf16_bits
+
 
 def dev_bf16(bits: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(
@@ -119,3 +121,26 @@ def block_fp8_product(q: torch.Tensor, qB: torch.Tensor, sa: torch.Tensor, sb: t
         k = slice(128 * g, 128 * g + 128)
         ref += (a[:, k] @ b[:, k].T) * (sa.to(f64)[:, g, None] * sbn[None, :, g])
     return ref
+
+
+def edge_rows(K, seed=22):
+    """zeros, signed zeros, tiny values that round to +-0, bf16 subnormals,
+    values at the clamp and scales on both sides of the reciprocal path's
+    range, as rows of K elements"""
+    g = np.random.default_rng(seed)
+    rows = []
+    r = np.zeros(K, np.uint16)
+    rows.append(r.copy())                            # all zero
+    r[:] = 0x8000
+    rows.append(r.copy())                            # all -0.0
+    big = to_bf16_bits(np.float32([448.0]))[0]
+    for scale in (1.0, 1e-3, 2.0**-55, 2.0**-58, 2.0**-61, 1e-30, 2.0**68, 2.0**71, 1e37):
+        v = (g.standard_normal(K) * scale).astype(np.float32)
+        v[::7] *= np.float32(1e-6)
+        b = to_bf16_bits(v)
+        b[0] = big if scale == 1.0 else b[0]
+        rows.append(b)
+    sub = np.arange(1, K + 1, dtype=np.uint16) & 0x7F    # bf16 subnormals
+    sub[1::2] |= 0x8000
+    rows.append(sub)
+    return np.stack(rows)

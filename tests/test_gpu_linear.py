@@ -159,6 +159,36 @@ def test_fused_equals_two_launches_and_oracle(qll, N, K):
     assert ran > 0
 
 
+def test_fused_edge_tokens(qll):
+    # tokens with zeros, signed zeros, bf16 subnormals, values at the clamp
+    # and scales on both sides of the quantizer's reciprocal range: codes and
+    # scales bitwise the oracle's, the output bitwise the two launches' and
+    # finite (an all-zero token gives scale 0, codes 0 and a zero row).  The
+    # token scaled by 1e37 is left out of the finiteness check: the epilogue
+    # multiplies left to right, (acc * s[m]) * sb[n], and acc * s[m]
+    # (~1e6 * 8e34) overflows fp32 before sb[n] would bring it back -- the
+    # same in both paths, which the bitwise check covers
+    from gpu_util import edge_rows
+    N, K = 520, 2048
+    w = workloads.weights_bf16(N, K, key=(workloads.W_TEST, 53))
+    B, sb = oracle.quantize_fp8(w)
+    dB, dsb = dev_e4m3(B), dev(sb[:, 0].copy())
+    x = edge_rows(K)[:16]
+    qr, sr = oracle.quantize_fp8(x)
+    for name in ("f16x16_w8_d2", "f8x16_w16_d2"):
+        v = next(t for t in qll.variants("fp8_dynamic") if t["name"] == name)
+        y, q, sa = qll.linear_fp8_dynamic(dev_bf16(x), dB, dsb, out_dtype="fp32", cfg=(name, 1))
+        y2, _, _ = qll.linear_fp8_dynamic(dev_bf16(x), dB, dsb, out_dtype="fp32",
+                                          cfg=(f"k{v['bp']}x16_w{v['wp']}", 1))
+        torch.cuda.synchronize()
+        assert np.array_equal(host_codes(q), qr), name
+        assert np.array_equal(sa.cpu().numpy()[:, 0].view(np.uint32), sr[:, 0].view(np.uint32)), name
+        assert torch.equal(y.view(torch.int32), y2.view(torch.int32)), name
+        huge = np.abs((x.astype(np.uint32) << 16).view(np.float32)).max(axis=1) > 1e30
+        assert bool(torch.isfinite(y[torch.from_numpy(~huge).cuda()]).all()), name
+        assert bool((y[0] == 0).all()) and bool((y[1] == 0).all()), name  # all-zero tokens
+
+
 def test_fused_refuses_more_than_16_tokens(qll):
     N, K = 520, 1040
     B = dev_e4m3(np.zeros((N, K), np.uint8))

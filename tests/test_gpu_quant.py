@@ -79,6 +79,20 @@ def test_golden_examples_on_gpu(qll, golden):
         assert np.all(q[0, n:] == 0)
 
 
+# the edge rows repeated over enough rows to take the many-row kernels: one
+# wave per row (512+ rows of <= 2048 elements, 2048+ rows of <= 4096) and
+# the row loop (513+ rows of 2048..8192 elements)
+@pytest.mark.parametrize("M,K", [(600, 256), (520, 1040), (2048, 4096), (530, 6144)])
+def test_edge_values_many_rows_bit_exact(qll, M, K):
+    from gpu_util import edge_rows
+    e = edge_rows(K)
+    x = workloads.bf16_normal((M, K), (workloads.W_TEST, 24, M, K))
+    x[::3] = e[np.arange(0, M, 3) % len(e)]
+    q, s = run_quant(qll, x)
+    qr, sr = oracle.quantize_fp8(x)
+    assert_same(q, s, qr, sr, f"edge rows M={M} K={K}")
+
+
 def test_edge_values_bit_exact(qll):
     # zeros, signed zeros, tiny values that round to +-0, subnormal ties,
     # bf16 subnormals, values at the clamp, an all-zero row
