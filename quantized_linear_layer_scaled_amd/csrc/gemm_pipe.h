@@ -819,6 +819,80 @@ void gemm_pipe_kernel(GemmArgs a)
     // columns of one row -- a 16-byte bf16 store (two for fp32) instead of
     // eight scattered 2-byte stores.
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");  // ring slots are free
+    // bf16 output of the per-token x per-channel ops (the common case): each
+    // accumulator is scaled, (acc * sa[m]) * sb[n], and rounded where the
+    // MFMA left it; the two lanes of a pair (neighbouring columns) trade
+    // values with one DPP swap, so that each lane holds two bf16x2 words of
+    // adjacent columns (rows 0-1 of its 4 in the even lane, 2-3 in the odd
+    // one).  The words of BB row blocks at a time go through LDS -- all of
+    // their writes, then all of their reads, then all of their 16-byte
+    // stores -- so the LDS round trips overlap instead of running one 16-row
+    // block after another, with half the bytes of staging the fp32 values.
+    // Same products and rounding (to nearest even) as the general path
+    // below, so the same bits.  Scratch rows of SQ / 2 + 4 words: the even
+    // and odd lanes' rows (2 apart) fall 8 banks apart and the lane groups
+    // (4 rows apart) 16 apart, so no write conflicts.
+    if constexpr (SCALED && PRE) {
+        if (scaled && a.out_dtype == OUT_BF16 && (N & 7) == 0) {
+            constexpr int SQB = SQ / 2 + 4;          // words per scratch row
+            constexpr int RBB = 16 * SQB * 4;        // bytes per 16-row block
+            constexpr int CAP = STAGES * SLOT / (WAVES * RBB);
+            constexpr int BB = CAP >= RP ? RP
+                               : (CAP >= 4 && RP % 4 == 0 ? 4 : (CAP >= 2 && RP % 2 == 0 ? 2 : 1));
+            static_assert(CAP >= 1, "epilogue scratch must fit the ring");
+            constexpr int CPR = SQ / 8, RPP = 64 / CPR, PASSES = 16 / RPP;
+            uint32_t* scr = (uint32_t*)(ring + wave * BB * RBB);
+            const bool odd = lane & 1;
+            float sbc[RQ];
+#pragma unroll
+            for (int j = 0; j < RQ; ++j)
+                sbc[j] = lpre[UA * 64 + wqi * SQ + j * 16 + (lane & 15)];
+            const int c = (lane % CPR) * 8;  // this lane's 8 output columns
+            const int n = q0 + wqi * SQ + c;
+#pragma unroll
+            for (int i0 = 0; i0 < RP; i0 += BB) {
+#pragma unroll
+                for (int b = 0; b < BB; ++b) {
+                    const int i = i0 + b;
+                    float sar[4];
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        sar[v] = lpre[wpi * SP + i * 16 + (lane >> 4) * 4 + v];
+                    const int r0 = b * 16 + (lane >> 4) * 4 + (odd ? 2 : 0);
+#pragma unroll
+                    for (int j = 0; j < RQ; ++j) {
+                        float y[4];
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            const float u = (float)acc[i][j][v] * sar[v];
+                            y[v] = u * sbc[j];
+                        }
+                        const float t0 = lane_pair_swap(odd ? y[0] : y[2]);
+                        const float t1 = lane_pair_swap(odd ? y[1] : y[3]);
+                        const int c2 = (j * 16 + (lane & 15)) >> 1;
+                        scr[r0 * SQB + c2] = odd ? bf16x2_rne(t0, y[2]) : bf16x2_rne(y[0], t0);
+                        scr[(r0 + 1) * SQB + c2] = odd ? bf16x2_rne(t1, y[3]) : bf16x2_rne(y[1], t1);
+                    }
+                }
+                uint4 w[BB][PASSES];
+#pragma unroll
+                for (int b = 0; b < BB; ++b)
+#pragma unroll
+                    for (int pass = 0; pass < PASSES; ++pass)
+                        w[b][pass] = *(const uint4*)&scr[(b * 16 + pass * RPP + lane / CPR) * SQB + c / 2];
+#pragma unroll
+                for (int b = 0; b < BB; ++b)
+#pragma unroll
+                    for (int pass = 0; pass < PASSES; ++pass) {
+                        const int m = p0 + wpi * SP + (i0 + b) * 16 + pass * RPP + lane / CPR;
+                        if (m < M && n < N)
+                            store16_stream((uint16_t*)a.out + (size_t)m * N + n, w[b][pass].x,
+                                           w[b][pass].y, w[b][pass].z, w[b][pass].w);
+                    }
+            }
+            return;
+        }
+    }
     // Scratch rows of SQ + 4 words: a lane writes rows 4 (lane / 16) + v of
     // its column, so that each half-wave's two lane groups (4 rows apart)
     // fall on the two disjoint halves of the 32 LDS banks instead of on the

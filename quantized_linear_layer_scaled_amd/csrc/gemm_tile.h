@@ -156,6 +156,22 @@ __device__ __forceinline__ uint16_t bf16_rne(float f)
     return (uint16_t)(u >> 16);
 }
 
+// Two values rounded to bf16 (nearest even) and packed, lo in bits 0..15:
+// gfx950's v_cvt_pk_bf16_f32, one instruction for the pair.  For finite
+// values and infinities it gives bf16_rne's bits.
+__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi)
+{
+    typedef __bf16 bf2_t __attribute__((ext_vector_type(2)));
+    typedef float f2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2_t){lo, hi}, bf2_t));
+}
+
+// The value of lane l ^ 1 (a DPP quad permute [1, 0, 3, 2]).
+__device__ __forceinline__ float lane_pair_swap(float x)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
+}
+
 // Epilogue value of one accumulator element (before the output cast).
 template <int OP>
 __device__ __forceinline__ float epilogue_value(typename OpTraits<OP>::elem_t v,

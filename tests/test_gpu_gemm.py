@@ -279,3 +279,35 @@ def test_swap_equals_ordinary_bitwise(qll, op, fp8_cases, bf16_cases, block_case
     ref = outs["n128x128_w2x2_k128"].view(torch.int32)
     diff = [n for n, y in outs.items() if not torch.equal(y.view(torch.int32), ref)]
     assert not diff, f"{op}: variants differing bitwise from n128x128: {diff}"
+
+
+@pytest.mark.parametrize("op", ["fp8", "int8"])
+def test_bf16_output_is_the_rounded_fp32_output(qll, op):
+    # The per-token x per-channel epilogue computes (acc * sa[m]) * sb[n] in
+    # fp32 and rounds it to bf16 (nearest even); the bf16 output must be the
+    # fp32 output rounded, bit for bit, whichever path the kernel takes
+    # (N a multiple of 8: scaled and rounded where the MFMA left it, paired
+    # across lanes and staged as bf16; otherwise staged in fp32)
+    g = np.random.default_rng(61)
+    for M, N, K in [(300, 648, 1024), (257, 520, 2048), (130, 264, 512), (37, 300, 1024)]:
+        if op == "fp8":
+            A = g.integers(0, 256, (M, K)).astype(np.uint8)
+            A[(A & 0x7F) == 0x7F] = 0
+            B = g.integers(0, 256, (N, K)).astype(np.uint8)
+            B[(B & 0x7F) == 0x7F] = 0
+            dA, dB = dev_e4m3(A), dev_e4m3(B)
+            fn = qll.gemm_fp8_scaled
+        else:
+            dA = dev(g.integers(-127, 128, (M, K)).astype(np.int8))
+            dB = dev(g.integers(-127, 128, (N, K)).astype(np.int8))
+            fn = qll.gemm_w8a8_int8
+        sa = dev(g.uniform(1e-3, 1e-2, M).astype(np.float32))
+        sb = dev(g.uniform(1e-3, 1e-2, N).astype(np.float32))
+        for name in names(qll, op):
+            if name[0] in "ks":
+                continue  # decode kernels: their own epilogue, covered elsewhere
+            y32 = fn(dA, dB, sa, sb, out_dtype="fp32", cfg=(name, 1))
+            y16 = fn(dA, dB, sa, sb, out_dtype="bf16", cfg=(name, 1))
+            torch.cuda.synchronize()
+            assert torch.equal(y16.view(torch.int16), y32.to(torch.bfloat16).view(torch.int16)), \
+                (op, name, M, N, K)
