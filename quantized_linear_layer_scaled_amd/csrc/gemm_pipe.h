@@ -819,9 +819,9 @@ void gemm_pipe_kernel(GemmArgs a)
     // columns of one row -- a 16-byte bf16 store (two for fp32) instead of
     // eight scattered 2-byte stores.
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");  // ring slots are free
-    // bf16 output of the per-token x per-channel ops (the common case): each
-    // accumulator is scaled, (acc * sa[m]) * sb[n], and rounded where the
-    // MFMA left it; the two lanes of a pair (neighbouring columns) trade
+    // bf16 output (the common case): each accumulator is scaled -- for the
+    // per-token x per-channel ops, (acc * sa[m]) * sb[n] -- and rounded where
+    // the MFMA left it; the two lanes of a pair (neighbouring columns) trade
     // values with one DPP swap, so that each lane holds two bf16x2 words of
     // adjacent columns (rows 0-1 of its 4 in the even lane, 2-3 in the odd
     // one).  The words of BB row blocks at a time go through LDS -- all of
@@ -832,8 +832,8 @@ void gemm_pipe_kernel(GemmArgs a)
     // below, so the same bits.  Scratch rows of SQ / 2 + 4 words: the even
     // and odd lanes' rows (2 apart) fall 8 banks apart and the lane groups
     // (4 rows apart) 16 apart, so no write conflicts.
-    if constexpr (SCALED && PRE) {
-        if (scaled && a.out_dtype == OUT_BF16 && (N & 7) == 0) {
+    if constexpr (!SCALED || PRE) {
+        if (a.out_dtype == OUT_BF16 && a.splits == 1 && (N & 7) == 0 && (!SCALED || scaled)) {
             constexpr int SQB = SQ / 2 + 4;          // words per scratch row
             constexpr int RBB = 16 * SQB * 4;        // bytes per 16-row block
             constexpr int CAP = STAGES * SLOT / (WAVES * RBB);
@@ -844,9 +844,11 @@ void gemm_pipe_kernel(GemmArgs a)
             uint32_t* scr = (uint32_t*)(ring + wave * BB * RBB);
             const bool odd = lane & 1;
             float sbc[RQ];
+            if constexpr (SCALED) {
 #pragma unroll
-            for (int j = 0; j < RQ; ++j)
-                sbc[j] = lpre[UA * 64 + wqi * SQ + j * 16 + (lane & 15)];
+                for (int j = 0; j < RQ; ++j)
+                    sbc[j] = lpre[UA * 64 + wqi * SQ + j * 16 + (lane & 15)];
+            }
             const int c = (lane % CPR) * 8;  // this lane's 8 output columns
             const int n = q0 + wqi * SQ + c;
 #pragma unroll
@@ -855,17 +857,23 @@ void gemm_pipe_kernel(GemmArgs a)
                 for (int b = 0; b < BB; ++b) {
                     const int i = i0 + b;
                     float sar[4];
+                    if constexpr (SCALED) {
 #pragma unroll
-                    for (int v = 0; v < 4; ++v)
-                        sar[v] = lpre[wpi * SP + i * 16 + (lane >> 4) * 4 + v];
+                        for (int v = 0; v < 4; ++v)
+                            sar[v] = lpre[wpi * SP + i * 16 + (lane >> 4) * 4 + v];
+                    }
                     const int r0 = b * 16 + (lane >> 4) * 4 + (odd ? 2 : 0);
 #pragma unroll
                     for (int j = 0; j < RQ; ++j) {
                         float y[4];
 #pragma unroll
                         for (int v = 0; v < 4; ++v) {
-                            const float u = (float)acc[i][j][v] * sar[v];
-                            y[v] = u * sbc[j];
+                            if constexpr (SCALED) {
+                                const float u = (float)acc[i][j][v] * sar[v];
+                                y[v] = u * sbc[j];
+                            } else {
+                                y[v] = (float)acc[i][j][v];
+                            }
                         }
                         const float t0 = lane_pair_swap(odd ? y[0] : y[2]);
                         const float t1 = lane_pair_swap(odd ? y[1] : y[3]);
