@@ -62,6 +62,103 @@ __device__ __forceinline__ void store16_stream(void* p, uint32_t x, uint32_t y, 
     __builtin_nontemporal_store(v4i{(int)x, (int)y, (int)z, (int)w}, (v4i*)p);
 }
 
+// bf16 output of one wave's RP x RQ accumulator blocks of 16 x 16 (lane
+// element (i, j, v): row 16 i + 4 (lane >> 4) + v, column 16 j + (lane & 15)
+// of the wave's block, whose first output row is m0 and first column n0).
+// With SCALED, an element is (acc * sa) * sb, sa = lsa[16 i + 4 (lane >> 4)
+// + v] and sb = lsb[16 j + (lane & 15)] (LDS copies of the block's row and
+// column scales), else the accumulator itself.  Each value is rounded where
+// the MFMA left it, to nearest even; the two lanes of a pair (neighbouring
+// columns) trade values with one DPP swap, so that each lane holds two
+// bf16x2 words of adjacent columns (rows 0-1 of its 4 in the even lane, 2-3
+// in the odd one).  The words of BB row blocks at a time go through the
+// wave's LDS scratch `scr` (16 BB rows of SQ / 2 + 4 words) -- all of their
+// writes, then all of their reads, then all of their 16-byte stores of 8
+// columns per lane -- so that the LDS round trips overlap instead of running
+// one row block after another, with half the bytes of staging fp32 values.
+// With rows of SQ / 2 + 4 words, the even and odd lanes' rows (2 apart) fall
+// 8 banks apart and the lane groups (4 rows apart) 16 apart: no write
+// conflicts.  N must be a multiple of 8; rows past M and columns past N are
+// not stored.
+template <int RP, int RQ, int BB, bool SCALED, typename Acc>
+__device__ __forceinline__ void store_bf16_batched(const Acc (&acc)[RP][RQ], uint32_t* scr,
+                                                   const float* lsa, const float* lsb,
+                                                   int lane, int m0, int n0, int M, int N,
+                                                   uint16_t* out)
+{
+    constexpr int SQ = RQ * 16;
+    constexpr int SQB = SQ / 2 + 4;
+    constexpr int CPR = SQ / 8, RPP = 64 / CPR, PASSES = 16 / RPP;
+    static_assert(RP % BB == 0 && SQ % 8 == 0 && 64 % CPR == 0 && 16 % RPP == 0,
+                  "epilogue lane map");
+    const bool odd = lane & 1;
+    float sbc[RQ];
+    if constexpr (SCALED) {
+#pragma unroll
+        for (int j = 0; j < RQ; ++j)
+            sbc[j] = lsb[j * 16 + (lane & 15)];
+    }
+    const int c = (lane % CPR) * 8;  // this lane's 8 output columns
+    const int n = n0 + c;
+#pragma unroll
+    for (int i0 = 0; i0 < RP; i0 += BB) {
+#pragma unroll
+        for (int b = 0; b < BB; ++b) {
+            const int i = i0 + b;
+            float sar[4];
+            if constexpr (SCALED) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    sar[v] = lsa[i * 16 + (lane >> 4) * 4 + v];
+            }
+            const int r0 = b * 16 + (lane >> 4) * 4 + (odd ? 2 : 0);
+#pragma unroll
+            for (int j = 0; j < RQ; ++j) {
+                float y[4];
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    if constexpr (SCALED) {
+                        const float u = (float)acc[i][j][v] * sar[v];
+                        y[v] = u * sbc[j];
+                    } else {
+                        y[v] = (float)acc[i][j][v];
+                    }
+                }
+                const float t0 = lane_pair_swap(odd ? y[0] : y[2]);
+                const float t1 = lane_pair_swap(odd ? y[1] : y[3]);
+                const int c2 = (j * 16 + (lane & 15)) >> 1;
+                scr[r0 * SQB + c2] = odd ? bf16x2_rne(t0, y[2]) : bf16x2_rne(y[0], t0);
+                scr[(r0 + 1) * SQB + c2] = odd ? bf16x2_rne(t1, y[3]) : bf16x2_rne(y[1], t1);
+            }
+        }
+        uint4 w[BB][PASSES];
+#pragma unroll
+        for (int b = 0; b < BB; ++b)
+#pragma unroll
+            for (int pass = 0; pass < PASSES; ++pass)
+                w[b][pass] = *(const uint4*)&scr[(b * 16 + pass * RPP + lane / CPR) * SQB + c / 2];
+#pragma unroll
+        for (int b = 0; b < BB; ++b)
+#pragma unroll
+            for (int pass = 0; pass < PASSES; ++pass) {
+                const int m = m0 + (i0 + b) * 16 + pass * RPP + lane / CPR;
+                if (m < M && n < N)
+                    store16_stream(out + (size_t)m * N + n, w[b][pass].x, w[b][pass].y,
+                                   w[b][pass].z, w[b][pass].w);
+            }
+    }
+}
+
+// The most row blocks of 16 that store_bf16_batched can batch in a wave's
+// share of `bytes` of scratch (RP itself, else 4 or 2 if they divide it).
+template <int RP, int SQ>
+constexpr int bf16_batch_blocks(int bytes)
+{
+    constexpr int rbb = 16 * (SQ / 2 + 4) * 4;
+    return bytes / rbb >= RP ? RP
+           : (bytes / rbb >= 4 && RP % 4 == 0 ? 4 : (bytes / rbb >= 2 && RP % 2 == 0 ? 2 : 1));
+}
+
 // Offset that lies outside every resource built here (num_records < 2^31).
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
@@ -819,85 +916,19 @@ void gemm_pipe_kernel(GemmArgs a)
     // columns of one row -- a 16-byte bf16 store (two for fp32) instead of
     // eight scattered 2-byte stores.
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");  // ring slots are free
-    // bf16 output (the common case): each accumulator is scaled -- for the
-    // per-token x per-channel ops, (acc * sa[m]) * sb[n] -- and rounded where
-    // the MFMA left it; the two lanes of a pair (neighbouring columns) trade
-    // values with one DPP swap, so that each lane holds two bf16x2 words of
-    // adjacent columns (rows 0-1 of its 4 in the even lane, 2-3 in the odd
-    // one).  The words of BB row blocks at a time go through LDS -- all of
-    // their writes, then all of their reads, then all of their 16-byte
-    // stores -- so the LDS round trips overlap instead of running one 16-row
-    // block after another, with half the bytes of staging the fp32 values.
-    // Same products and rounding (to nearest even) as the general path
-    // below, so the same bits.  Scratch rows of SQ / 2 + 4 words: the even
-    // and odd lanes' rows (2 apart) fall 8 banks apart and the lane groups
-    // (4 rows apart) 16 apart, so no write conflicts.
+    // bf16 output (the common case): store_bf16_batched, which scales each
+    // accumulator as the general path below does -- (acc * sa[m]) * sb[n]
+    // for the per-token x per-channel ops -- and rounds it the same way, so
+    // the same bits.
     if constexpr (!SCALED || PRE) {
         if (a.out_dtype == OUT_BF16 && a.splits == 1 && (N & 7) == 0 && (!SCALED || scaled)) {
-            constexpr int SQB = SQ / 2 + 4;          // words per scratch row
-            constexpr int RBB = 16 * SQB * 4;        // bytes per 16-row block
-            constexpr int CAP = STAGES * SLOT / (WAVES * RBB);
-            constexpr int BB = CAP >= RP ? RP
-                               : (CAP >= 4 && RP % 4 == 0 ? 4 : (CAP >= 2 && RP % 2 == 0 ? 2 : 1));
-            static_assert(CAP >= 1, "epilogue scratch must fit the ring");
-            constexpr int CPR = SQ / 8, RPP = 64 / CPR, PASSES = 16 / RPP;
-            uint32_t* scr = (uint32_t*)(ring + wave * BB * RBB);
-            const bool odd = lane & 1;
-            float sbc[RQ];
-            if constexpr (SCALED) {
-#pragma unroll
-                for (int j = 0; j < RQ; ++j)
-                    sbc[j] = lpre[UA * 64 + wqi * SQ + j * 16 + (lane & 15)];
-            }
-            const int c = (lane % CPR) * 8;  // this lane's 8 output columns
-            const int n = q0 + wqi * SQ + c;
-#pragma unroll
-            for (int i0 = 0; i0 < RP; i0 += BB) {
-#pragma unroll
-                for (int b = 0; b < BB; ++b) {
-                    const int i = i0 + b;
-                    float sar[4];
-                    if constexpr (SCALED) {
-#pragma unroll
-                        for (int v = 0; v < 4; ++v)
-                            sar[v] = lpre[wpi * SP + i * 16 + (lane >> 4) * 4 + v];
-                    }
-                    const int r0 = b * 16 + (lane >> 4) * 4 + (odd ? 2 : 0);
-#pragma unroll
-                    for (int j = 0; j < RQ; ++j) {
-                        float y[4];
-#pragma unroll
-                        for (int v = 0; v < 4; ++v) {
-                            if constexpr (SCALED) {
-                                const float u = (float)acc[i][j][v] * sar[v];
-                                y[v] = u * sbc[j];
-                            } else {
-                                y[v] = (float)acc[i][j][v];
-                            }
-                        }
-                        const float t0 = lane_pair_swap(odd ? y[0] : y[2]);
-                        const float t1 = lane_pair_swap(odd ? y[1] : y[3]);
-                        const int c2 = (j * 16 + (lane & 15)) >> 1;
-                        scr[r0 * SQB + c2] = odd ? bf16x2_rne(t0, y[2]) : bf16x2_rne(y[0], t0);
-                        scr[(r0 + 1) * SQB + c2] = odd ? bf16x2_rne(t1, y[3]) : bf16x2_rne(y[1], t1);
-                    }
-                }
-                uint4 w[BB][PASSES];
-#pragma unroll
-                for (int b = 0; b < BB; ++b)
-#pragma unroll
-                    for (int pass = 0; pass < PASSES; ++pass)
-                        w[b][pass] = *(const uint4*)&scr[(b * 16 + pass * RPP + lane / CPR) * SQB + c / 2];
-#pragma unroll
-                for (int b = 0; b < BB; ++b)
-#pragma unroll
-                    for (int pass = 0; pass < PASSES; ++pass) {
-                        const int m = p0 + wpi * SP + (i0 + b) * 16 + pass * RPP + lane / CPR;
-                        if (m < M && n < N)
-                            store16_stream((uint16_t*)a.out + (size_t)m * N + n, w[b][pass].x,
-                                           w[b][pass].y, w[b][pass].z, w[b][pass].w);
-                    }
-            }
+            constexpr int BB = bf16_batch_blocks<RP, SQ>(STAGES * SLOT / WAVES);
+            constexpr int RBB = 16 * (SQ / 2 + 4) * 4;
+            static_assert(STAGES * SLOT / WAVES >= RBB, "epilogue scratch must fit the ring");
+            store_bf16_batched<RP, RQ, BB, SCALED>(
+                acc, (uint32_t*)(ring + wave * BB * RBB), SCALED ? lpre + wpi * SP : nullptr,
+                SCALED ? lpre + UA * 64 + wqi * SQ : nullptr, lane, p0 + wpi * SP,
+                q0 + wqi * SQ, M, N, (uint16_t*)a.out);
             return;
         }
     }

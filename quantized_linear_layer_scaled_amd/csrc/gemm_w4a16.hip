@@ -651,10 +651,21 @@ void gemm_w4_pipe_kernel(GemmArgs a)
                 group(std::integral_constant<int, (S >= 4 ? 3 : 0)>{}, kt + 3);
     }
 
-    // Epilogue through LDS, as in the tiled kernel: each wave writes one
-    // 16-row block of its tile at a time into a private scratch, then every
-    // lane emits 8 consecutive columns of one row.
+    // Epilogue through LDS.  bf16 output: several 16-row blocks at a time,
+    // rounded where the MFMA left them (store_bf16_batched); otherwise, as in
+    // the tiled kernel, each wave writes one 16-row block of its tile at a
+    // time into a private scratch, then every lane emits 8 consecutive
+    // columns of one row.  Same values and rounding either way.
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");  // slots are free
+    if (a.splits == 1 && a.out_dtype == OUT_BF16 && (N & 7) == 0) {
+        constexpr int BB = bf16_batch_blocks<RP, SQ>(S * STAGE / WAVES);
+        constexpr int RBB = 16 * (SQ / 2 + 4) * 4;
+        static_assert(S * STAGE / WAVES >= RBB, "epilogue scratch must fit");
+        store_bf16_batched<RP, RQ, BB, false>(acc, (uint32_t*)(lds + wave * BB * RBB), nullptr,
+                                              nullptr, lane, p0 + wpi * SP, q0 + wqi * SQ, M, N,
+                                              (uint16_t*)a.out);
+        return;
+    }
     static_assert(WAVES * 16 * SQ * 4 <= S * STAGE, "epilogue scratch must fit");
     float* scr = (float*)lds + wave * 16 * SQ;
     constexpr int CPR = SQ / 8;
