@@ -675,7 +675,8 @@ def cpu_baseline(workload, rows_cap):
                 break
     except OSError:
         pass
-    return {"value": round(flops / t_total / 1e12, 6), "unit": "TFLOPS",
+    return {"value": round(flops / t_total / 1e12, 6),
+            "unit": "TOPS" if workload == "int8" else "TFLOPS",
             "cores": cores, "kind": "oracle", "sample": desc,
             "seconds": round(t_total, 2), "cpu_model": cpu_model,
             "cores_available": len(os.sched_getaffinity(0)),
