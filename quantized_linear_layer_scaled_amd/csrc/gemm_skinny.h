@@ -98,9 +98,14 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny_kernel(GemmArgs a)
     constexpr bool FOLD = OP == OP_BF16 && !KSPLIT;
     KFold<acc_t, 1, RQ> fold(FOLD ? a.kfold : 1, T, U);
 
+    // Block-FP8: the group scales of each step (weight block nb, and each
+    // token row's), loaded with the operands so that they are in flight
+    // together instead of one more round trip before the promotion
+    constexpr bool BLK = OP == OP_BLOCK;
     for (int s = s0; s < s1; s += D) {
         uint4 fb[D][NJ], fa[D][RQ][NJ];
         uint32_t xb[MX ? D : 1], xa[MX ? D : 1][RQ];
+        float gb[BLK ? D : 1], ga[BLK ? D : 1][RQ];
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             const int off = (s + d) * KSTEP;
@@ -113,6 +118,17 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny_kernel(GemmArgs a)
                 for (int r = 0; r < RQ; ++r)
                     fa[d][r][j] = ok ? *(const uint4*)(ap[r] + off + 16 * j)
                                      : make_uint4(0, 0, 0, 0);
+            }
+            if constexpr (BLK) {
+                // step s + d is K group (kbeg >> 7) + s + d (KSTEP = 128)
+                const bool ok = s + d < s1;
+                const int g = (kbeg >> 7) + s + d;
+                gb[d] = ok ? a.sb[nb * KG + g] : 0.0f;
+#pragma unroll
+                for (int r = 0; r < RQ; ++r) {
+                    const int m = min(m0 + r * 16 + (lane & 15), M - 1);
+                    ga[d][r] = ok ? a.sa[m * KG + g] : 0.0f;
+                }
             }
             if constexpr (MX) {
                 // a whole step is in range or not (K is a multiple of 128)
@@ -129,13 +145,10 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny_kernel(GemmArgs a)
                 continue;  // (every later step is past s1 too)
             if constexpr (FOLD)
                 fold.before(s + d, (acc_t(&)[1][RQ])acc);
-            if constexpr (OP == OP_BLOCK) {
-                const int g = (kbeg >> 7) + s + d;
-                const float sbv = a.sb[nb * KG + g];
+            if constexpr (BLK) {
 #pragma unroll
                 for (int r = 0; r < RQ; ++r) {
-                    const int m = min(m0 + r * 16 + (lane & 15), M - 1);
-                    const float sc = sbv * a.sa[m * KG + g];
+                    const float sc = gb[d] * ga[d][r];
                     v4f pg = mfma_step<OP>(fb[d], fa[d][r], v4f{0, 0, 0, 0});
 #pragma unroll
                     for (int v = 0; v < 4; ++v)
