@@ -12,6 +12,7 @@ QLL_FOR_EACH_PIPE_W8(QLL_PIPE_INSTANTIATE, qll::OP_INT8)
 QLL_FOR_EACH_PIPE_DEEP_K256(QLL_PIPE_INSTANTIATE, qll::OP_INT8)
 QLL_FOR_EACH_PIPE_BIG(QLL_PIPE_INSTANTIATE, qll::OP_INT8)
 QLL_FOR_EACH_PIPE_W8_K256(QLL_PIPE_INSTANTIATE, qll::OP_INT8)
+QLL_FOR_EACH_PIPE_KG2(QLL_PIPE_KG2_INSTANTIATE, qll::OP_INT8)
 template __global__ void qll::splitk_reduce_kernel<qll::OP_INT8>(qll::GemmArgs);
 
 namespace qll {
@@ -27,6 +28,7 @@ extern const Variant kVariantsInt8[] = {
     QLL_FOR_EACH_PIPE_DEEP_K256(QLL_PIPE_ENTRY, OP_INT8)
     QLL_FOR_EACH_PIPE_BIG(QLL_PIPE_ENTRY, OP_INT8)
     QLL_FOR_EACH_PIPE_W8_K256(QLL_PIPE_ENTRY, OP_INT8)
+    QLL_FOR_EACH_PIPE_KG2(QLL_PIPE_KG2_ENTRY, OP_INT8)
 };
 extern const int kNumVariantsInt8 = sizeof(kVariantsInt8) / sizeof(Variant);
 #endif

@@ -247,10 +247,11 @@ constexpr int pipe_slot_bytes()
     return ((BP + BQ) * KSTAGE + pipe_scale_bytes<OP, BP, BQ, KSTAGE>() + 1023) / 1024 * 1024;
 }
 
-template <int OP, int BP, int BQ, int KSTAGE, int STAGES>
+// KGRP K groups per workgroup (see gemm_pipe_kernel) have a ring each.
+template <int OP, int BP, int BQ, int KSTAGE, int STAGES, int KGRP = 1>
 constexpr int pipe_ring_bytes()
 {
-    return STAGES * pipe_slot_bytes<OP, BP, BQ, KSTAGE>() +
+    return KGRP * STAGES * pipe_slot_bytes<OP, BP, BQ, KSTAGE>() +
            (OP == OP_BLOCK ? (STAGES + 1) * 1280 : 0);
 }
 
@@ -269,27 +270,28 @@ constexpr int pipe_prescale_bytes()
     return ((BP + 63) / 64 + (BQ + 63) / 64) * 256;
 }
 
-template <int OP, int BP, int BQ, int KSTAGE, int STAGES>
+template <int OP, int BP, int BQ, int KSTAGE, int STAGES, int KGRP = 1>
 constexpr bool pipe_prescale()
 {
     return (OP == OP_INT8 || OP == OP_FP8) &&
-           pipe_wgs_per_cu(pipe_ring_bytes<OP, BP, BQ, KSTAGE, STAGES>() +
+           pipe_wgs_per_cu(pipe_ring_bytes<OP, BP, BQ, KSTAGE, STAGES, KGRP>() +
                            pipe_prescale_bytes<BP, BQ>()) ==
-               pipe_wgs_per_cu(pipe_ring_bytes<OP, BP, BQ, KSTAGE, STAGES>());
+               pipe_wgs_per_cu(pipe_ring_bytes<OP, BP, BQ, KSTAGE, STAGES, KGRP>());
 }
 
-template <int OP, int BP, int BQ, int KSTAGE, int STAGES>
+template <int OP, int BP, int BQ, int KSTAGE, int STAGES, int KGRP = 1>
 constexpr int pipe_lds_bytes()
 {
-    return pipe_ring_bytes<OP, BP, BQ, KSTAGE, STAGES>() +
-           (pipe_prescale<OP, BP, BQ, KSTAGE, STAGES>() ? pipe_prescale_bytes<BP, BQ>() : 0);
+    return pipe_ring_bytes<OP, BP, BQ, KSTAGE, STAGES, KGRP>() +
+           (pipe_prescale<OP, BP, BQ, KSTAGE, STAGES, KGRP>() ? pipe_prescale_bytes<BP, BQ>()
+                                                               : 0);
 }
 
-template <int OP, int BP, int BQ, int WP, int WQ, int KSTAGE, int STAGES>
+template <int OP, int BP, int BQ, int WP, int WQ, int KSTAGE, int STAGES, int KGRP = 1>
 constexpr int pipe_waves_per_eu()
 {
-    constexpr int wgs = pipe_wgs_per_cu(pipe_lds_bytes<OP, BP, BQ, KSTAGE, STAGES>());
-    constexpr int w = wgs * WP * WQ / 4;
+    constexpr int wgs = pipe_wgs_per_cu(pipe_lds_bytes<OP, BP, BQ, KSTAGE, STAGES, KGRP>());
+    constexpr int w = wgs * KGRP * WP * WQ / 4;
     return w < 1 ? 1 : (w > 8 ? 8 : w);
 }
 
@@ -372,11 +374,18 @@ __device__ __forceinline__ void group_tile(const int* __restrict__ off, int E, i
 // SPLITK only gives the first stage of a Split-K call its own kernel symbol
 // (the code is the same), so that traces separate the two kinds of launch.
 // GROUPED: the per-expert GEMM over rows sorted by expert (no Split-K).
+// KGRP = 2: two K groups of WP x WQ waves in one workgroup, each running the
+// whole pipeline on its half of the workgroup's K range (the first
+// ceil(stages / 2) stages, the rest) through a ring of its own; both run
+// the same number of stages, so they meet at every barrier, and at the end
+// the second group's partial tile is added to the first's through LDS, in
+// that order.  Twice the copy streams per tile and half its serial K depth,
+// with no second launch: the Split-K of the mid-size M within a workgroup.
 template <int OP, int BP, int BQ, int WP, int WQ, int KSTAGE, int STAGES, bool SPLITK,
-          bool GROUPED = false>
-__global__ __launch_bounds__(WP* WQ * 64)
-__attribute__((amdgpu_waves_per_eu(pipe_waves_per_eu<OP, BP, BQ, WP, WQ, KSTAGE, STAGES>())))
-void gemm_pipe_kernel(GemmArgs a)
+          bool GROUPED = false, int KGRP = 1>
+__global__ __launch_bounds__(KGRP* WP* WQ * 64)
+__attribute__((amdgpu_waves_per_eu(
+    pipe_waves_per_eu<OP, BP, BQ, WP, WQ, KSTAGE, STAGES, KGRP>()))) void gemm_pipe_kernel(GemmArgs a)
 {
     using Tr = OpTraits<OP>;
     using acc_t = typename Tr::acc_t;
@@ -418,7 +427,10 @@ void gemm_pipe_kernel(GemmArgs a)
     // One LDS object per ring slot, the slot known at compile time in the
     // unrolled K loop (constant LDS addresses for the fragment reads).
     constexpr int SLOT = pipe_slot_bytes<OP, BP, BQ, KSTAGE>();
-    __shared__ __attribute__((aligned(1024))) uint8_t ring[STAGES * SLOT];
+    static_assert(KGRP == 1 || (KGRP == 2 && !BLK && !MX && (OP == OP_FP8 || OP == OP_INT8) &&
+                                !(BP * BQ >= 256 * 256)),
+                  "K groups: the per-token x per-channel tiles with a register-set K loop");
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[KGRP * STAGES * SLOT];
     // Block-FP8: the K group's activation scales of the tile rows (256
     // floats) and its weight-block scales (64) per stage, in a ring of
     // STAGES + 1 entries, so that a stage's scales outlive the reuse of its
@@ -427,13 +439,16 @@ void gemm_pipe_kernel(GemmArgs a)
     constexpr int SC_FLOATS = 320;
     __shared__ __attribute__((aligned(16))) float lsc[SC_SLOTS][BLK ? SC_FLOATS : 4];
     static_assert(STAGES <= 8, "at most eight ring slots");
-    auto slot = [&](auto J) __attribute__((always_inline)) -> uint8_t* {
-        return ring + decltype(J)::value * SLOT;
-    };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+    // this wave's K group and its index within the group (wave-uniform)
+    const int kgi = KGRP > 1 ? __builtin_amdgcn_readfirstlane(tid >> 6) / (WP * WQ) : 0;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) % (WP * WQ);
+    uint8_t* const gring = KGRP > 1 ? ring + kgi * (STAGES * SLOT) : ring;
+    auto slot = [&](auto J) __attribute__((always_inline)) -> uint8_t* {
+        return gring + decltype(J)::value * SLOT;
+    };
     const int wpi = wave % WP, wqi = wave / WP;
     const int N = a.N;
     const int tq = (N + BQ - 1) / BQ;
@@ -474,9 +489,15 @@ void gemm_pipe_kernel(GemmArgs a)
     }
     const int q0 = tile_q * BQ;
     const int z = blockIdx.y;
-    const int kbeg = z * a.kchunk;
-    const int kend = min(a.kbytes, kbeg + a.kchunk);
-    const int nk = (kend - kbeg + KSTAGE - 1) / KSTAGE;
+    // the workgroup's K range [kbeg0, kend0), its group's part [kbeg, kend)
+    // of nk stages (the same nk for both groups; a short or empty second
+    // part reads zeros and skips its MFMAs past kend)
+    const int kbeg0 = z * a.kchunk;
+    const int kend0 = min(a.kbytes, kbeg0 + a.kchunk);
+    const int nk0 = (kend0 - kbeg0 + KSTAGE - 1) / KSTAGE;
+    const int nk = KGRP > 1 ? (nk0 + 1) / 2 : nk0;
+    const int kbeg = kbeg0 + kgi * nk * KSTAGE;
+    const int kend = KGRP > 1 ? min(kend0, kbeg + nk * KSTAGE) : kend0;
     const uint32_t ldk = (uint32_t)a.kbytes;
 
     // The tile's A rows and B rows as two buffers, each ending at the last
@@ -715,12 +736,12 @@ void gemm_pipe_kernel(GemmArgs a)
     // holds sa of tile rows 64u .. 64u + 63 (u < UA), then sb of the tile
     // columns; entries past M or N read as zero.
     constexpr bool SCALED = OP == OP_INT8 || OP == OP_FP8;
-    constexpr bool PRE = pipe_prescale<OP, BP, BQ, KSTAGE, STAGES>();
+    constexpr bool PRE = pipe_prescale<OP, BP, BQ, KSTAGE, STAGES, KGRP>();
     constexpr int UA = (BP + 63) / 64, UB = (BQ + 63) / 64;
     __shared__ __attribute__((aligned(16))) float lpre[PRE ? (UA + UB) * 64 : 1];
     const bool scaled = SCALED && a.splits == 1 && a.out_dtype != OUT_INT32;
     if constexpr (PRE) {
-        if (scaled) {
+        if (scaled && kgi == 0) {  // (the first K group writes the output)
             const v4i rsPa = buffer_rsrc(
                 a.sa + p0, (uint32_t)min((uint64_t)(M - p0) * 4, (uint64_t)0x7FFFFFFF));
             const v4i rsPb = buffer_rsrc(
@@ -916,6 +937,38 @@ void gemm_pipe_kernel(GemmArgs a)
     // columns of one row -- a 16-byte bf16 store (two for fp32) instead of
     // eight scattered 2-byte stores.
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");  // ring slots are free
+    if constexpr (KGRP > 1) {
+        // The second K group parks its accumulators at the end of the ring
+        // (its own ring, clear of the first group's epilogue scratch); the
+        // first adds them to its own, first group + second group, and goes
+        // on to the epilogue alone.
+        constexpr int PART = WP * WQ * RP * RQ * 4 * 64 * 4;
+        static_assert(PART <= STAGES * SLOT, "the partial tile must fit the second ring");
+        uint32_t* pt = (uint32_t*)(ring + KGRP * STAGES * SLOT - PART) + wave * (RP * RQ * 4 * 64);
+        if (kgi == 1) {
+#pragma unroll
+            for (int i = 0; i < RP; ++i)
+#pragma unroll
+                for (int j = 0; j < RQ; ++j)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        // (through a scalar: the bit cast of a vector element
+                        // in place reads the vector's first element)
+                        const elem_t e = acc[i][j][v];
+                        pt[((i * RQ + j) * 4 + v) * 64 + lane] = __builtin_bit_cast(uint32_t, e);
+                    }
+        }
+        __syncthreads();
+        if (kgi == 1)
+            return;
+#pragma unroll
+        for (int i = 0; i < RP; ++i)
+#pragma unroll
+            for (int j = 0; j < RQ; ++j)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    acc[i][j][v] += __builtin_bit_cast(elem_t, pt[((i * RQ + j) * 4 + v) * 64 + lane]);
+    }
     // bf16 output (the common case): store_bf16_batched, which scales each
     // accumulator as the general path below does -- (acc * sa[m]) * sb[n]
     // for the per-token x per-channel ops -- and rounds it the same way, so
@@ -1052,19 +1105,19 @@ void gemm_pipe_kernel(GemmArgs a)
     }
 }
 
-template <int OP, int BP, int BQ, int WP, int WQ, int KSTAGE, int STAGES>
+template <int OP, int BP, int BQ, int WP, int WQ, int KSTAGE, int STAGES, int KGRP = 1>
 hipError_t launch_pipe(const GemmArgs& a, hipStream_t stream)
 {
     const long tiles = (long)((a.M + BP - 1) / BP) * ((a.N + BQ - 1) / BQ);
     if (tiles > 0x7FFFFFFFL || (long)(BP > BQ ? BP : BQ) * a.kbytes > 0x7FFFFFFFL)
         return hipErrorInvalidValue;  // 32-bit buffer offsets within a tile
     if (a.splits > 1)
-        hipLaunchKernelGGL((gemm_pipe_kernel<OP, BP, BQ, WP, WQ, KSTAGE, STAGES, true>),
-                           dim3((unsigned)tiles, (unsigned)a.splits), dim3(WP * WQ * 64), 0,
+        hipLaunchKernelGGL((gemm_pipe_kernel<OP, BP, BQ, WP, WQ, KSTAGE, STAGES, true, false, KGRP>),
+                           dim3((unsigned)tiles, (unsigned)a.splits), dim3(KGRP * WP * WQ * 64), 0,
                            stream, a);
     else
-        hipLaunchKernelGGL((gemm_pipe_kernel<OP, BP, BQ, WP, WQ, KSTAGE, STAGES, false>),
-                           dim3((unsigned)tiles, 1), dim3(WP * WQ * 64), 0, stream, a);
+        hipLaunchKernelGGL((gemm_pipe_kernel<OP, BP, BQ, WP, WQ, KSTAGE, STAGES, false, false, KGRP>),
+                           dim3((unsigned)tiles, 1), dim3(KGRP * WP * WQ * 64), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -1149,3 +1202,23 @@ hipError_t launch_pipe_grouped(const GemmArgs& a, hipStream_t stream)
 #define QLL_PIPE_ENTRY(OP, BP, BQ, WP, WQ, KS, ST)                                   \
     {"p" #BP "x" #BQ "_w" #WP "x" #WQ "_k" #KS "_s" #ST, OP, 0, BP, BQ, WP, WQ, KS,    \
      qll::pipe_lds_bytes<OP, BP, BQ, KS, ST>(), &qll::launch_pipe<OP, BP, BQ, WP, WQ, KS, ST>},
+
+// Tiles of two K groups (the in-workgroup Split-K of gemm_pipe_kernel,
+// KGRP = 2) for the mid-size M: named p<BP>x<BQ>_w<WP>x<WQ>_k<KS>_s<ST>_g2,
+// the wave grid and ring of one group.
+#define QLL_FOR_EACH_PIPE_KG2(X, OP)       \
+    X(OP, 64, 64, 2, 2, 128, 2)            \
+    X(OP, 64, 64, 2, 2, 128, 4)            \
+    X(OP, 64, 64, 2, 2, 256, 2)            \
+    X(OP, 128, 32, 4, 1, 128, 3)           \
+    X(OP, 32, 128, 1, 4, 128, 3)           \
+    X(OP, 128, 64, 4, 2, 128, 3)           \
+    X(OP, 64, 128, 2, 4, 128, 3)
+#define QLL_PIPE_KG2_INSTANTIATE(OP, BP, BQ, WP, WQ, KS, ST)                                 \
+    template __global__ void qll::gemm_pipe_kernel<OP, BP, BQ, WP, WQ, KS, ST, false, false, 2>( \
+        qll::GemmArgs);                                                                          \
+    template __global__ void qll::gemm_pipe_kernel<OP, BP, BQ, WP, WQ, KS, ST, true, false, 2>(  \
+        qll::GemmArgs);
+#define QLL_PIPE_KG2_ENTRY(OP, BP, BQ, WP, WQ, KS, ST)                                 \
+    {"p" #BP "x" #BQ "_w" #WP "x" #WQ "_k" #KS "_s" #ST "_g2", OP, 0, BP, BQ, WP, WQ, KS, \
+     qll::pipe_lds_bytes<OP, BP, BQ, KS, ST, 2>(), &qll::launch_pipe<OP, BP, BQ, WP, WQ, KS, ST, 2>},

@@ -264,13 +264,14 @@ def test_swap_equals_ordinary_bitwise(qll, op, fp8_cases, bf16_cases, block_case
         A, B, _, _ = bf16_cases[(37, 300, 2056)]
         args = (dev_bf16(A), dev_bf16(B))
         fn = qll.gemm_bf16_batch_invariant
-    # fp8 and Block-FP8: the "k" skinny variants split K across waves
-    # (another summation order by design), every other variant accumulates K
-    # in one accumulator (Block-FP8: one promotion per K group, in order).
+    # fp8 and Block-FP8: the "k" skinny variants split K across waves and the
+    # two-K-group tiles ("_g2") split it between two wave groups (another
+    # summation order by design), every other variant accumulates K in one
+    # accumulator (Block-FP8: one promotion per K group, in order).
     # bf16: every variant sums K in the same eight chunks, so all agree except
     # a skinny variant whose waves split K into another number of chunks.
     if op != "bf16_bi":
-        single = [n for n in names(qll, op) if n[0] != "k"]
+        single = [n for n in names(qll, op) if n[0] != "k" and not n.endswith("_g2")]
     else:
         single = [v["name"] for v in qll.variants(op)
                   if not (v["name"][0] == "k" and v["wp"] != 8)]
@@ -311,3 +312,45 @@ def test_bf16_output_is_the_rounded_fp32_output(qll, op):
             torch.cuda.synchronize()
             assert torch.equal(y16.view(torch.int16), y32.to(torch.bfloat16).view(torch.int16)), \
                 (op, name, M, N, K)
+
+
+@pytest.mark.parametrize("op", ["fp8", "int8"])
+def test_k_groups_equal_split_k_two(qll, op):
+    # A two-K-group tile ("_g2") sums its K range in two halves inside the
+    # workgroup, the first group's partial plus the second's.  Where its
+    # split point is Split-K's (K = 2048 and 4096: both halfway), it must be
+    # bitwise the same tile run as two Split-K pieces added by the second
+    # stage -- same halves, same order -- for every output kind.
+    g = np.random.default_rng(67)
+    ran = 0
+    for M, N, K in [(130, 300, 2048), (37, 520, 4096)]:
+        if op == "fp8":
+            A = g.integers(0, 256, (M, K)).astype(np.uint8)
+            A[(A & 0x7F) == 0x7F] = 0
+            B = g.integers(0, 256, (N, K)).astype(np.uint8)
+            B[(B & 0x7F) == 0x7F] = 0
+            dA, dB = dev_e4m3(A), dev_e4m3(B)
+            fn = qll.gemm_fp8_scaled
+            kinds = ("fp32", "bf16")
+        else:
+            dA = dev(g.integers(-127, 128, (M, K)).astype(np.int8))
+            dB = dev(g.integers(-127, 128, (N, K)).astype(np.int8))
+            fn = qll.gemm_w8a8_int8
+            kinds = ("int32", "fp32", "bf16")
+        sa = dev(g.uniform(1e-3, 1e-2, M).astype(np.float32))
+        sb = dev(g.uniform(1e-3, 1e-2, N).astype(np.float32))
+        all_names = names(qll, op)
+        for name in all_names:
+            if not name.endswith("_g2"):
+                continue
+            # the same tile with one K group (any ring depth: same sums)
+            prefix = name[:-3].rsplit("_s", 1)[0] + "_s"
+            base = next(n for n in all_names if n.startswith(prefix) and not n.endswith("_g2"))
+            for od in kinds:
+                y1 = fn(dA, dB, sa, sb, out_dtype=od, cfg=(name, 1))
+                y2 = fn(dA, dB, sa, sb, out_dtype=od, cfg=(base, 2))
+                torch.cuda.synchronize()
+                iv = torch.int16 if od == "bf16" else torch.int32
+                assert torch.equal(y1.view(iv), y2.view(iv)), (op, name, base, od, M, N, K)
+                ran += 1
+    assert ran > 0
