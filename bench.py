@@ -528,10 +528,13 @@ def kernel_symbol(qll, op, variant):
                     f"{v['wq']}, {st}>(qll::GemmArgs)")
         return f"void qll::gemm_w4_skinny_kernel<{v['bq'] // 16}, {v['wp']}, {v['bp']}, "
     if variant[0] == "p":
-        st = variant.rsplit("_s", 1)[1]
+        # "_g2": two K groups per workgroup (the kernel's last argument)
+        kgrp = 2 if variant.endswith("_g2") else 1
+        st = variant[:-3] if kgrp == 2 else variant
+        st = st.rsplit("_s", 1)[1]
         return (f"void qll::gemm_pipe_kernel<{opn}, {v['bp']}, {v['bq']}, {v['wp']}, "
-                f"{v['wq']}, {v['kstage']}, {st}, false, {'true' if grouped else 'false'}>"
-                "(qll::GemmArgs)")
+                f"{v['wq']}, {v['kstage']}, {st}, false, {'true' if grouped else 'false'}, "
+                f"{kgrp}>(qll::GemmArgs)")
     if variant[0] in "kr":
         hr = v["bp"] if variant[0] == "k" else 16
         return (f"void qll::gemm_skinny_kernel<{opn}, {v['bq'] // 16}, {v['wp']}, {hr}, "
@@ -1059,7 +1062,7 @@ def main():
         else:
             roof["kernel_duration"] = {"error": "the trace's dispatch count does not match "
                                                 "this command's launch plan"}
-    if dom_sym.startswith("void qll::gemm_pipe_kernel") and "true>" not in dom_sym:
+    if dom_sym.startswith("void qll::gemm_pipe_kernel") and ", true, " not in dom_sym:
         # the fetch the XCD structure implies (each XCD's L2 reads the rows
         # of its tiles once), per launch, plus the bf16 output
         dp = [p for p in probs if p.eff_splits == 1 and

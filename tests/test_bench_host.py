@@ -12,7 +12,7 @@ sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
 import bench  # noqa: E402
 
 FIELDS = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
-DOM = "void qll::gemm_pipe_kernel<1, 128, 128, 4, 4, 128, 4, false, false>(qll::GemmArgs)"
+DOM = "void qll::gemm_pipe_kernel<1, 128, 128, 4, 4, 128, 4, false, false, 1>(qll::GemmArgs)"
 CAL = "void at::native::vectorized_elementwise_kernel<4, at::native::MulFunctor<float>>(int)"
 
 
@@ -140,3 +140,17 @@ def test_source_digest_follows_the_sources(tmp_path, monkeypatch):
     with open(root / "quantized_linear_layer_scaled_amd" / "csrc" / "api.cpp", "a") as f:
         f.write("\n")
     assert bench.source_digest() != d0
+
+
+def test_kernel_symbol_matches_the_demangled_pipe_kernels():
+    # the names rocprofv3 prints for the pipelined kernels carry every
+    # template argument, the K-group count included; bench.py must build
+    # the same string to find the dominant kernel in a trace
+    import quantized_linear_layer_scaled_amd as qll
+    qll.load_library()
+    assert bench.kernel_symbol(qll, "fp8", "p128x128_w4x4_k128_s3") == (
+        "void qll::gemm_pipe_kernel<1, 128, 128, 4, 4, 128, 3, false, false, 1>(qll::GemmArgs)")
+    assert bench.kernel_symbol(qll, "int8", "p64x64_w2x2_k128_s4_g2") == (
+        "void qll::gemm_pipe_kernel<0, 64, 64, 2, 2, 128, 4, false, false, 2>(qll::GemmArgs)")
+    assert bench.kernel_symbol(qll, "fp8_grouped", "p256x256_w2x4_k128_s2") == (
+        "void qll::gemm_pipe_kernel<1, 256, 256, 2, 4, 128, 2, false, true, 1>(qll::GemmArgs)")
