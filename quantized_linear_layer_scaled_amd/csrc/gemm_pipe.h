@@ -427,8 +427,8 @@ __attribute__((amdgpu_waves_per_eu(
     // One LDS object per ring slot, the slot known at compile time in the
     // unrolled K loop (constant LDS addresses for the fragment reads).
     constexpr int SLOT = pipe_slot_bytes<OP, BP, BQ, KSTAGE>();
-    static_assert(KGRP == 1 || (KGRP == 2 && !BLK && !MX && (OP == OP_FP8 || OP == OP_INT8) &&
-                                !(BP * BQ >= 256 * 256)),
+    static_assert(KGRP == 1 || (KGRP == 2 && !BLK && !MX && !GROUPED &&
+                                (OP == OP_FP8 || OP == OP_INT8) && !(BP * BQ >= 256 * 256)),
                   "K groups: the per-token x per-channel tiles with a register-set K loop");
     __shared__ __attribute__((aligned(1024))) uint8_t ring[KGRP * STAGES * SLOT];
     // Block-FP8: the K group's activation scales of the tile rows (256

@@ -41,6 +41,28 @@ def test_int8_full_bit_exact(qll):
                           oracle.bf16_encode(y))
 
 
+def test_int8_every_table_bucket_bit_exact(qll):
+    # every M bucket of the shipped INT8 table at N = K = 2048 -- the decode
+    # kernels, the pipelined tiles, the two-K-group tiles of the mid-size M
+    # -- through the dispatch: int32 accumulators and bf16 output bit-exact
+    # against the oracle on sampled rows
+    N, K = 2048, 2048
+    picks = set()
+    for M in (1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048):
+        d = workloads.int8_inputs(M, N, K, key=(workloads.W_TEST, 70, M))
+        rows = sample_rows(M, 12, seed=M)
+        acc, y = oracle.gemm_w8a8_int8(d["A"], d["B"], d["sa"], d["sb"], rows=rows)
+        A, B, sa, sb = dev(d["A"]), dev(d["B"]), dev(d["sa"]), dev(d["sb"])
+        o32 = qll.gemm_w8a8_int8(A, B, sa, sb, out_dtype="int32")
+        ob = qll.gemm_w8a8_int8(A, B, sa, sb, out_dtype="bf16")
+        torch.cuda.synchronize()
+        picks.add(qll.select("int8", M, N, K)[0])
+        assert np.array_equal(o32.cpu().numpy()[rows], acc), M
+        assert np.array_equal(ob.view(torch.int16).cpu().numpy().view(np.uint16)[rows],
+                              oracle.bf16_encode(y)), M
+    assert any(n.endswith("_g2") for n in picks), picks
+
+
 @pytest.fixture(scope="module")
 def fp8_weights():
     out = {}
