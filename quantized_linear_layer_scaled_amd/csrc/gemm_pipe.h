@@ -385,7 +385,8 @@ template <int OP, int BP, int BQ, int WP, int WQ, int KSTAGE, int STAGES, bool S
           bool GROUPED = false, int KGRP = 1>
 __global__ __launch_bounds__(KGRP* WP* WQ * 64)
 __attribute__((amdgpu_waves_per_eu(
-    pipe_waves_per_eu<OP, BP, BQ, WP, WQ, KSTAGE, STAGES, KGRP>()))) void gemm_pipe_kernel(GemmArgs a)
+    pipe_waves_per_eu<OP, BP, BQ, WP, WQ, KSTAGE, STAGES, KGRP>())))
+void gemm_pipe_kernel(GemmArgs a)
 {
     using Tr = OpTraits<OP>;
     using acc_t = typename Tr::acc_t;
@@ -967,7 +968,8 @@ __attribute__((amdgpu_waves_per_eu(
             for (int j = 0; j < RQ; ++j)
 #pragma unroll
                 for (int v = 0; v < 4; ++v)
-                    acc[i][j][v] += __builtin_bit_cast(elem_t, pt[((i * RQ + j) * 4 + v) * 64 + lane]);
+                    acc[i][j][v] +=
+                        __builtin_bit_cast(elem_t, pt[((i * RQ + j) * 4 + v) * 64 + lane]);
     }
     // bf16 output (the common case): store_bf16_batched, which scales each
     // accumulator as the general path below does -- (acc * sa[m]) * sb[n]
@@ -1111,13 +1113,15 @@ hipError_t launch_pipe(const GemmArgs& a, hipStream_t stream)
     const long tiles = (long)((a.M + BP - 1) / BP) * ((a.N + BQ - 1) / BQ);
     if (tiles > 0x7FFFFFFFL || (long)(BP > BQ ? BP : BQ) * a.kbytes > 0x7FFFFFFFL)
         return hipErrorInvalidValue;  // 32-bit buffer offsets within a tile
+    const dim3 block(KGRP * WP * WQ * 64);
     if (a.splits > 1)
-        hipLaunchKernelGGL((gemm_pipe_kernel<OP, BP, BQ, WP, WQ, KSTAGE, STAGES, true, false, KGRP>),
-                           dim3((unsigned)tiles, (unsigned)a.splits), dim3(KGRP * WP * WQ * 64), 0,
-                           stream, a);
+        hipLaunchKernelGGL(
+            (gemm_pipe_kernel<OP, BP, BQ, WP, WQ, KSTAGE, STAGES, true, false, KGRP>),
+            dim3((unsigned)tiles, (unsigned)a.splits), block, 0, stream, a);
     else
-        hipLaunchKernelGGL((gemm_pipe_kernel<OP, BP, BQ, WP, WQ, KSTAGE, STAGES, false, false, KGRP>),
-                           dim3((unsigned)tiles, 1), dim3(KGRP * WP * WQ * 64), 0, stream, a);
+        hipLaunchKernelGGL(
+            (gemm_pipe_kernel<OP, BP, BQ, WP, WQ, KSTAGE, STAGES, false, false, KGRP>),
+            dim3((unsigned)tiles, 1), block, 0, stream, a);
     return hipGetLastError();
 }
 
@@ -1221,4 +1225,5 @@ hipError_t launch_pipe_grouped(const GemmArgs& a, hipStream_t stream)
         qll::GemmArgs);
 #define QLL_PIPE_KG2_ENTRY(OP, BP, BQ, WP, WQ, KS, ST)                                 \
     {"p" #BP "x" #BQ "_w" #WP "x" #WQ "_k" #KS "_s" #ST "_g2", OP, 0, BP, BQ, WP, WQ, KS, \
-     qll::pipe_lds_bytes<OP, BP, BQ, KS, ST, 2>(), &qll::launch_pipe<OP, BP, BQ, WP, WQ, KS, ST, 2>},
+     qll::pipe_lds_bytes<OP, BP, BQ, KS, ST, 2>(),                                        \
+     &qll::launch_pipe<OP, BP, BQ, WP, WQ, KS, ST, 2>},
