@@ -388,7 +388,18 @@ int qll_effective_splits(int op, int64_t K, int32_t splits);
 
 /* Registered kernel variants of an op.  qll_variant_info writes a one-line
  * JSON description (name, orientation, tile, waves, K stage, LDS bytes) into
- * buf (NUL-terminated, truncated to cap) and returns QLL_OK. */
+ * buf (NUL-terminated, truncated to cap) and returns QLL_OK.
+ * Names, as the _ex forms take them:
+ *   k<rows>x<tokens>_w<W>        decode kernel, Swap-AB, its W waves split K
+ *   r<rows>x<tokens>_w<W>        decode kernel, its waves split the rows
+ *   n|s<BP>x<BQ>_w<WP>x<WQ>_k<KS>  register-prefetch tile, ordinary | Swap-AB
+ *   p<BP>x<BQ>_w<WP>x<WQ>_k<KS>_s<S>  tile fed by an S-slot LDS copy ring of
+ *                                KS-byte K stages; a "_g2" suffix: two such
+ *                                wave groups split K inside the workgroup
+ *   f<rows>x16_w<W>_d<D>         fused quantizer + decode GEMM (fp8_dynamic)
+ *   t<BP>x<BQ>_w<WP>x<WQ>        W4A16 register-staged tile
+ * The W4A16 tiles omit _k (one 128-element group per stage); FP8 tiles with
+ * _k64 run on the 32x32x64 matrix-core step. */
 int qll_num_variants(int op);
 int qll_variant_info(int op, int idx, char* buf, size_t cap);
 int qll_variant_index(int op, const char* name);
