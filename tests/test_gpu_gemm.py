@@ -354,3 +354,35 @@ def test_k_groups_equal_split_k_two(qll, op):
                 assert torch.equal(y1.view(iv), y2.view(iv)), (op, name, base, od, M, N, K)
                 ran += 1
     assert ran > 0
+
+
+@pytest.mark.parametrize("op", ["block_fp8", "bf16_bi", "mxfp4", "w4a16"])
+def test_unscaled_bf16_output_is_the_rounded_fp32_output(qll, op):
+    # The ops whose accumulator is the output value (Block-FP8 after its
+    # per-group promotion, bf16, MXFP4, W4A16): bf16 output must be the fp32
+    # output rounded to nearest even, bit for bit, for every variant -- with
+    # N a multiple of 8 the pipelined tiles round in the MFMA layout and
+    # stage bf16x2 words, otherwise they stage fp32
+    key = (workloads.W_TEST, 80)
+    for M, N, K in [(257, 520, 2048), (130, 264, 512), (37, 300, 1024)]:
+        x = dev_bf16(workloads.fp8_activations(M, K, key=(*key, M, K)))
+        w = dev_bf16(workloads.weights_bf16(N, K, key=(*key, N, K)))
+        if op == "block_fp8":
+            qa, sa = qll.quantize_per_token_fp8(x, group=128)
+            qb, sb = qll.quantize_weight_block_fp8(w)
+            fn = lambda od, cfg: qll.gemm_block_fp8(qa, qb, sa, sb, out_dtype=od, cfg=cfg)
+        elif op == "bf16_bi":
+            fn = lambda od, cfg: qll.gemm_bf16_batch_invariant(x, w, out_dtype=od, cfg=cfg)
+        elif op == "mxfp4":
+            qa, sa = qll.quantize_mxfp4(x)
+            qb, sb = qll.quantize_mxfp4(w)
+            fn = lambda od, cfg: qll.gemm_mxfp4(qa, qb, sa, sb, out_dtype=od, cfg=cfg)
+        else:
+            qb, sb = qll.quantize_int4_weights(w)
+            fn = lambda od, cfg: qll.gemm_w4a16(x, qb, sb, out_dtype=od, cfg=cfg)
+        for name in names(qll, op):
+            y32 = fn("fp32", (name, 1))
+            y16 = fn("bf16", (name, 1))
+            torch.cuda.synchronize()
+            assert torch.equal(y16.view(torch.int16), y32.to(torch.bfloat16).view(torch.int16)), \
+                (op, name, M, N, K)
