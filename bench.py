@@ -527,6 +527,11 @@ def kernel_symbol(qll, op, variant):
             return (f"void qll::gemm_w4_pipe_kernel<{v['bp']}, {v['bq']}, {v['wp']}, "
                     f"{v['wq']}, {st}>(qll::GemmArgs)")
         return f"void qll::gemm_w4_skinny_kernel<{v['bq'] // 16}, {v['wp']}, {v['bp']}, "
+    if variant[0] == "p" and variant.rsplit("_", 1)[1][0] == "r":
+        # "_r<RC>": operand copies through RC register stages
+        rc = variant.rsplit("_r", 1)[1]
+        return (f"void qll::gemm_pipe_rc_kernel<{opn}, {v['bp']}, {v['bq']}, {v['wp']}, "
+                f"{v['wq']}, {v['kstage']}, {rc}, false>(qll::GemmArgs)")
     if variant[0] == "p":
         # "_g2": two K groups per workgroup (the kernel's last argument)
         kgrp = 2 if variant.endswith("_g2") else 1

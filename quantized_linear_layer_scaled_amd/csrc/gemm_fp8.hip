@@ -14,6 +14,7 @@ QLL_FOR_EACH_PIPE_DEEP_K256(QLL_PIPE_INSTANTIATE, qll::OP_FP8)
 QLL_FOR_EACH_PIPE_BIG(QLL_PIPE_INSTANTIATE, qll::OP_FP8)
 QLL_FOR_EACH_PIPE_W8_K256(QLL_PIPE_INSTANTIATE, qll::OP_FP8)
 QLL_FOR_EACH_PIPE_KG2(QLL_PIPE_KG2_INSTANTIATE, qll::OP_FP8)
+QLL_FOR_EACH_PIPE_RC(QLL_PIPE_RC_INSTANTIATE, qll::OP_FP8)
 QLL_FOR_EACH_P32(QLL_P32_INSTANTIATE, qll::OP_FP8)
 QLL_FOR_EACH_PIPE(QLL_PIPE_GROUPED_INSTANTIATE, qll::OP_FP8)
 QLL_FOR_EACH_PIPE_W8(QLL_PIPE_GROUPED_INSTANTIATE, qll::OP_FP8)
@@ -34,6 +35,7 @@ extern const Variant kVariantsFp8[] = {
     QLL_FOR_EACH_PIPE_BIG(QLL_PIPE_ENTRY, OP_FP8)
     QLL_FOR_EACH_PIPE_W8_K256(QLL_PIPE_ENTRY, OP_FP8)
     QLL_FOR_EACH_PIPE_KG2(QLL_PIPE_KG2_ENTRY, OP_FP8)
+    QLL_FOR_EACH_PIPE_RC(QLL_PIPE_RC_ENTRY, OP_FP8)
     QLL_FOR_EACH_P32(QLL_P32_ENTRY, OP_FP8)
 };
 extern const int kNumVariantsFp8 = sizeof(kVariantsFp8) / sizeof(Variant);

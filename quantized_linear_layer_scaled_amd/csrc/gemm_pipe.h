@@ -211,6 +211,16 @@ __device__ __forceinline__ void for_stages(F&& f, int kt, int nk)
     }
 }
 
+// f(integral_constant<J>{}) for J = J0 .. U-1, unconditionally.
+template <int J, int U, typename F>
+__device__ __forceinline__ void unroll(F&& f)
+{
+    if constexpr (J < U) {
+        f(std::integral_constant<int, J>{});
+        unroll<J + 1, U>(f);
+    }
+}
+
 // wait_vm_barrier<Y * LPT>() for the largest Y <= min(younger, YMAX).
 template <int YMAX, int LPT>
 __device__ __forceinline__ void wait_younger(int younger)
@@ -381,12 +391,14 @@ __device__ __forceinline__ void group_tile(const int* __restrict__ off, int E, i
 // the second group's partial tile is added to the first's through LDS, in
 // that order.  Twice the copy streams per tile and half its serial K depth,
 // with no second launch: the Split-K of the mid-size M within a workgroup.
+// RC > 0 (gemm_pipe_rc_kernel): the operand copies go through registers
+// instead of the LDS copy path -- buffer_load_dwordx4 into one of RC register
+// sets, RC stages ahead, then ds_write_b128 into a two-slot LDS ring one
+// stage ahead of the MFMAs.  The LDS image is the same as the copy path's, so
+// the fragment reads and the products are too.
 template <int OP, int BP, int BQ, int WP, int WQ, int KSTAGE, int STAGES, bool SPLITK,
-          bool GROUPED = false, int KGRP = 1>
-__global__ __launch_bounds__(KGRP* WP* WQ * 64)
-__attribute__((amdgpu_waves_per_eu(
-    pipe_waves_per_eu<OP, BP, BQ, WP, WQ, KSTAGE, STAGES, KGRP>())))
-void gemm_pipe_kernel(GemmArgs a)
+          bool GROUPED, int KGRP, int RC>
+__device__ __forceinline__ void gemm_pipe_body(const GemmArgs& a)
 {
     using Tr = OpTraits<OP>;
     using acc_t = typename Tr::acc_t;
@@ -440,6 +452,9 @@ void gemm_pipe_kernel(GemmArgs a)
     constexpr int SC_FLOATS = 320;
     __shared__ __attribute__((aligned(16))) float lsc[SC_SLOTS][BLK ? SC_FLOATS : 4];
     static_assert(STAGES <= 8, "at most eight ring slots");
+    static_assert(RC == 0 || (STAGES == 2 && !STREAM && !MX && !BLK && !GROUPED && KGRP == 1 &&
+                              RC <= 4),
+                  "register-path copies: plain per-token x per-channel or bf16 tiles, two slots");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -755,7 +770,83 @@ void gemm_pipe_kernel(GemmArgs a)
         }
     }
 
-    if constexpr (!STREAM) {
+    if constexpr (RC > 0) {
+        // Register-path copies.  Stage s is loaded into register set s % RC
+        // (RC stages ahead), written to LDS slot s % 2 during stage s - 1, and
+        // published by stage s - 1's barrier, after which its first step's
+        // fragments are read.  Slot s % 2 last held stage s - 2, whose
+        // fragments every wave had read (and waited for) before the barrier
+        // of stage s - 2 + 1, so the writes of stage s need no other wait.
+        // The compiler tracks the loads (builtins) and waits for exactly the
+        // set a ds_write needs; the only asm copies (the tile's scales) are
+        // issued before them, so they only make such a wait stricter.
+        const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)((const uint8_t*)a.A + (size_t)p0 * ldk), (short)0,
+            (int)min((uint64_t)(M - p0) * ldk, (uint64_t)0x7FFFFFFF), 0x00020000);
+        const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(Bp + (size_t)q0 * ldk), (short)0,
+            (int)min((uint64_t)(N - q0) * ldk, (uint64_t)0x7FFFFFFF), 0x00020000);
+        uint4 rg[RC][LPT0];
+        auto gload = [&](int kt, uint4* dst) __attribute__((always_inline)) {
+            const int kb0 = kt * KSTAGE;
+            const bool full = kbeg + kb0 + KSTAGE <= kend;
+#pragma unroll
+            for (int i = 0; i < LPT0; ++i) {
+                uint32_t vo = voff[i] + (uint32_t)kb0;
+                if (!full && kbeg + kb0 + chunk_of(i) * 16 >= kend)
+                    vo = kOutOfRange;  // past the K range: zeros
+                dst[i] = __builtin_bit_cast(
+                    uint4, __builtin_amdgcn_raw_buffer_load_b128(in_a(i) ? rA : rB, (int)vo, 0, 0));
+            }
+        };
+        auto swrite = [&](const uint4* src, uint8_t* buf) __attribute__((always_inline)) {
+#pragma unroll
+            for (int i = 0; i < LPT0; ++i)
+                *(uint4*)(buf + ((i * WAVES + wave) * 64 + lane) * 16) = src[i];
+        };
+        // Every load, write and barrier below is issued unconditionally
+        // (stages past the K range load zeros and skip their MFMAs), so the
+        // loop body has no branch around a load and the compiler's waits
+        // stay exact: a ds_write waits only for its own stage's loads.
+        unroll<0, RC>([&](auto J) __attribute__((always_inline)) {
+            gload(decltype(J)::value, rg[decltype(J)::value]);
+        });
+        swrite(rg[0], slot(I0{}));
+        gload(RC, rg[0]);
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the writes have landed
+        __builtin_amdgcn_s_barrier();
+        load_step(slot(I0{}), 0, fr[0]);
+        // J = kt mod U: LDS slot, register set and fragment set are
+        // compile-time constants
+        constexpr int U = RC % 2 == 0 ? RC : 2 * RC;
+        auto stage = [&](auto J, int kt) __attribute__((always_inline)) {
+            constexpr int j = decltype(J)::value;
+            constexpr int cs = j % 2, ns = (j + 1) % 2, rs = (j + 1) % RC;
+            if constexpr (FOLD) {
+                if (kt < nk)
+                    fold.before(kt * NSTEP, acc);
+            }
+#pragma unroll
+            for (int ks = 0; ks < NSTEP; ++ks) {
+                const int cp = (j * NSTEP + ks) & 1;
+                if (ks + 1 < NSTEP) {
+                    load_step(slot(std::integral_constant<int, cs>{}), ks + 1, fr[cp ^ 1]);
+                } else {
+                    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+                    swrite(rg[rs], slot(std::integral_constant<int, ns>{}));
+                    gload(kt + 1 + RC, rg[rs]);
+                    __builtin_amdgcn_s_waitcnt(0xC07F);
+                    __builtin_amdgcn_s_barrier();
+                    load_step(slot(std::integral_constant<int, ns>{}), 0, fr[cp ^ 1]);
+                }
+                compute_step(fr[cp], kt, ks);  // (returns for stages past the K range)
+            }
+        };
+        for (int kt = 0; kt < nk; kt += U)
+            unroll<0, U>([&](auto J) __attribute__((always_inline)) {
+                stage(J, kt + decltype(J)::value);
+            });
+    } else if constexpr (!STREAM) {
         // prologue: every ring slot receives a stage (0 .. STAGES-1); the
         // fragments of step 0 go to register set 0
         for_stages<0, STAGES>([&](auto J, int kt) __attribute__((always_inline)) {
@@ -1107,6 +1198,42 @@ void gemm_pipe_kernel(GemmArgs a)
     }
 }
 
+template <int OP, int BP, int BQ, int WP, int WQ, int KSTAGE, int STAGES, bool SPLITK,
+          bool GROUPED = false, int KGRP = 1>
+__global__ __launch_bounds__(KGRP* WP* WQ * 64)
+__attribute__((amdgpu_waves_per_eu(
+    pipe_waves_per_eu<OP, BP, BQ, WP, WQ, KSTAGE, STAGES, KGRP>())))
+void gemm_pipe_kernel(GemmArgs a)
+{
+    gemm_pipe_body<OP, BP, BQ, WP, WQ, KSTAGE, STAGES, SPLITK, GROUPED, KGRP, 0>(a);
+}
+
+// One workgroup per CU: the register sets of the copies in flight take the
+// registers a second workgroup would need.
+template <int OP, int BP, int BQ, int WP, int WQ, int KSTAGE, int RC, bool SPLITK>
+__global__ __launch_bounds__(WP* WQ * 64)
+__attribute__((amdgpu_waves_per_eu(WP * WQ >= 8 ? WP * WQ / 4 : 1)))
+void gemm_pipe_rc_kernel(GemmArgs a)
+{
+    gemm_pipe_body<OP, BP, BQ, WP, WQ, KSTAGE, 2, SPLITK, false, 1, RC>(a);
+}
+
+template <int OP, int BP, int BQ, int WP, int WQ, int KSTAGE, int RC>
+hipError_t launch_pipe_rc(const GemmArgs& a, hipStream_t stream)
+{
+    const long tiles = (long)((a.M + BP - 1) / BP) * ((a.N + BQ - 1) / BQ);
+    if (tiles > 0x7FFFFFFFL || (long)(BP > BQ ? BP : BQ) * a.kbytes > 0x7FFFFFFFL)
+        return hipErrorInvalidValue;  // 32-bit buffer offsets within a tile
+    const dim3 block(WP * WQ * 64);
+    if (a.splits > 1)
+        hipLaunchKernelGGL((gemm_pipe_rc_kernel<OP, BP, BQ, WP, WQ, KSTAGE, RC, true>),
+                           dim3((unsigned)tiles, (unsigned)a.splits), block, 0, stream, a);
+    else
+        hipLaunchKernelGGL((gemm_pipe_rc_kernel<OP, BP, BQ, WP, WQ, KSTAGE, RC, false>),
+                           dim3((unsigned)tiles, 1), block, 0, stream, a);
+    return hipGetLastError();
+}
+
 template <int OP, int BP, int BQ, int WP, int WQ, int KSTAGE, int STAGES, int KGRP = 1>
 hipError_t launch_pipe(const GemmArgs& a, hipStream_t stream)
 {
@@ -1206,6 +1333,28 @@ hipError_t launch_pipe_grouped(const GemmArgs& a, hipStream_t stream)
 #define QLL_PIPE_ENTRY(OP, BP, BQ, WP, WQ, KS, ST)                                   \
     {"p" #BP "x" #BQ "_w" #WP "x" #WQ "_k" #KS "_s" #ST, OP, 0, BP, BQ, WP, WQ, KS,    \
      qll::pipe_lds_bytes<OP, BP, BQ, KS, ST>(), &qll::launch_pipe<OP, BP, BQ, WP, WQ, KS, ST>},
+
+// Tiles whose operand copies go through registers (gemm_pipe_rc_kernel):
+// named p<BP>x<BQ>_w<WP>x<WQ>_k<KS>_r<RC>, RC the register stages in flight.
+// A copy-path byte costs the LDS about twice what a ds_write byte does (a
+// probe copying L2-resident rows beside four bytes of ds_read per copied
+// byte: 18.9 TB/s through the copy path, 22.2 TB/s through registers), and
+// the fragment reads of these tiles load the LDS that much; the FP8 sweep
+// picks them by 1-4% at M = 512-2048.  INT8 and bf16 tiles gained nothing.
+#define QLL_FOR_EACH_PIPE_RC(X, OP)        \
+    X(OP, 128, 128, 4, 4, 128, 2)          \
+    X(OP, 128, 128, 4, 2, 128, 2)          \
+    X(OP, 128, 128, 2, 4, 128, 1)          \
+    X(OP, 128, 128, 2, 4, 128, 2)          \
+    X(OP, 128, 64, 4, 2, 128, 2)           \
+    X(OP, 64, 128, 2, 4, 128, 2)
+#define QLL_PIPE_RC_INSTANTIATE(OP, BP, BQ, WP, WQ, KS, RC)                                      \
+    template __global__ void qll::gemm_pipe_rc_kernel<OP, BP, BQ, WP, WQ, KS, RC, false>(       \
+        qll::GemmArgs);                                                                          \
+    template __global__ void qll::gemm_pipe_rc_kernel<OP, BP, BQ, WP, WQ, KS, RC, true>(qll::GemmArgs);
+#define QLL_PIPE_RC_ENTRY(OP, BP, BQ, WP, WQ, KS, RC)                                \
+    {"p" #BP "x" #BQ "_w" #WP "x" #WQ "_k" #KS "_r" #RC, OP, 0, BP, BQ, WP, WQ, KS,    \
+     qll::pipe_lds_bytes<OP, BP, BQ, KS, 2>(), &qll::launch_pipe_rc<OP, BP, BQ, WP, WQ, KS, RC>},
 
 // Tiles of two K groups (the in-workgroup Split-K of gemm_pipe_kernel,
 // KGRP = 2) for the mid-size M: named p<BP>x<BQ>_w<WP>x<WQ>_k<KS>_s<ST>_g2,

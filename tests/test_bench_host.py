@@ -154,3 +154,5 @@ def test_kernel_symbol_matches_the_demangled_pipe_kernels():
         "void qll::gemm_pipe_kernel<0, 64, 64, 2, 2, 128, 4, false, false, 2>(qll::GemmArgs)")
     assert bench.kernel_symbol(qll, "fp8_grouped", "p256x256_w2x4_k128_s2") == (
         "void qll::gemm_pipe_kernel<1, 256, 256, 2, 4, 128, 2, false, true, 1>(qll::GemmArgs)")
+    assert bench.kernel_symbol(qll, "fp8", "p128x128_w2x4_k128_r2") == (
+        "void qll::gemm_pipe_rc_kernel<1, 128, 128, 2, 4, 128, 2, false>(qll::GemmArgs)")
