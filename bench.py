@@ -1067,7 +1067,8 @@ def main():
         else:
             roof["kernel_duration"] = {"error": "the trace's dispatch count does not match "
                                                 "this command's launch plan"}
-    if dom_sym.startswith("void qll::gemm_pipe_kernel") and ", true, " not in dom_sym:
+    if dom_sym.startswith(("void qll::gemm_pipe_kernel", "void qll::gemm_pipe_rc_kernel")) \
+            and ", true, " not in dom_sym and ", true>" not in dom_sym:
         # the fetch the XCD structure implies (each XCD's L2 reads the rows
         # of its tiles once), per launch, plus the bf16 output
         dp = [p for p in probs if p.eff_splits == 1 and
