@@ -511,7 +511,7 @@ def kernel_symbol(qll, op, variant):
     opn = {"int8": 0, "fp8": 1, "block_fp8": 2, "bf16_bi": 3, "mxfp4": 4, "w4a16": 5}[op]
     if op == "fp8" and variant[0] == "f":  # the fused linear layer
         v = next(x for x in qll.variants("fp8_dynamic") if x["name"] == variant)
-        return (f"void qll::linear_fused_kernel<{v['bp']}, {v['wp']}, {v['ksteps']}>"
+        return (f"void qll::linear_fused_kernel<{v['bp']}, {v['wp']}, {v['ksteps']}, {v['bq']}>"
                 "(qll::FusedArgs)")
     v = next(x for x in qll.variants(op) if x["name"] == variant)
     if variant[0] == "p" and "_k64_" in variant:  # the 32x32x64 deep-ring tiles

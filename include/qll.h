@@ -257,9 +257,11 @@ int gemm_w4a16_ex(const void* A, const void* B, const float* scales, void* out,
  *     GEMM variant (the first qll_num_variants(QLL_OP_FP8) indices, the same
  *     as the FP8 op's; without a table entry of its own the op takes the
  *     FP8 GEMM's choice);
- *   - fused (the indices after them, names "f<rows>x16_w8_d<steps>"): one
- *     launch whose workgroups quantize the tokens themselves inside the
- *     wave-split decode GEMM; M <= 16 and K within the variant's register
+ *   - fused (the indices after them, names "f<rows>x<tokens>_w<W>_d<steps>"):
+ *     one launch whose workgroups quantize the tokens themselves inside the
+ *     wave-split decode GEMM; M <= tokens (4, 8 or 16; the 4- and 8-token
+ *     forms encode only that many tokens' values per wave) and K within the
+ *     variant's register
  *     chunk (d steps of 128 per wave: K <= 2048 for d2, <= 6144 for d6),
  *     else QLL_ERR_UNSUPPORTED; no workspace.  Its output is bitwise that of
  *     the two launches with the 8-wave decode GEMM of the same rows per
@@ -396,7 +398,10 @@ int qll_effective_splits(int op, int64_t K, int32_t splits);
  *   p<BP>x<BQ>_w<WP>x<WQ>_k<KS>_s<S>  tile fed by an S-slot LDS copy ring of
  *                                KS-byte K stages; a "_g2" suffix: two such
  *                                wave groups split K inside the workgroup
- *   f<rows>x16_w<W>_d<D>         fused quantizer + decode GEMM (fp8_dynamic)
+ *   f<rows>x<T>_w<W>_d<D>        fused quantizer + decode GEMM for M <= T
+ *                                (fp8_dynamic)
+ *   p<BP>x<BQ>_w<WP>x<WQ>_k<KS>_r<R>  tile whose operand copies go through
+ *                                R register stages into a two-slot LDS ring
  *   t<BP>x<BQ>_w<WP>x<WQ>        W4A16 register-staged tile
  * The W4A16 tiles omit _k (one 128-element group per stage); FP8 tiles with
  * _k64 run on the 32x32x64 matrix-core step. */

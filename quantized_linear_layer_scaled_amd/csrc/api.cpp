@@ -98,7 +98,7 @@ const FusedVariant* dyn_fused(int idx)
 // a fused variant runs M <= 16 tokens and K up to its register chunk
 bool fused_fits(const FusedVariant& f, int64_t M, int64_t K)
 {
-    return M <= 16 && K <= 0x3FFFFFFF && fused_steps_per_wave((int)K, f.w) <= f.d &&
+    return M <= f.tok && K <= 0x3FFFFFFF && fused_steps_per_wave((int)K, f.w) <= f.d &&
            2 * M * K <= 0x7FFFFFF0 && f.hr * K <= 0x7FFFFFF0;
 }
 
@@ -378,7 +378,7 @@ int load_table(const char* path, const DeviceSig& want, Table** out, std::string
         if (const FusedVariant* fv = op == OP_FP8_DYN ? dyn_fused(vi) : nullptr) {
             if (!fused_fits(*fv, bucket, K) || splits != 1) {
                 rc = QLL_ERR_TABLE;
-                *err = std::string("fused entry beyond 16 tokens, its K chunk or one split: ") + p;
+                *err = std::string("fused entry beyond its tokens, its K chunk or one split: ") + p;
                 break;
             }
         } else {
@@ -1091,9 +1091,11 @@ int qll_variant_info(int op, int idx, char* buf, size_t cap)
     if (const FusedVariant* f = op == OP_FP8_DYN ? dyn_fused(idx) : nullptr) {
         std::snprintf(buf, cap,
                       "{\"name\": \"%s\", \"op\": \"%s\", \"swap\": 1, \"bp\": %d, "
-                      "\"bq\": 16, \"wp\": %d, \"wq\": 1, \"kstage\": 128, \"lds\": %d, "
+                      "\"bq\": %d, \"wp\": %d, \"wq\": 1, \"kstage\": 128, \"lds\": %d, "
                       "\"fused\": 1, \"ksteps\": %d}",
-                      f->name, kOpNames[op], f->hr, f->w, f->w * 1024 + f->w * 64 + 64, f->d);
+                      f->name, kOpNames[op], f->hr, f->tok, f->w,
+                      f->w * 1024 + f->w * 64 + 64 + (f->tok < 16 ? f->w * f->d * f->tok * 128 : 0),
+                      f->d);
         return QLL_OK;
     }
     int n = 0;

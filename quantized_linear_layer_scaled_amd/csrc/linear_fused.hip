@@ -44,9 +44,22 @@ static __device__ __forceinline__ void encode32(const uint4* v, const Quot& d, u
     c[1] = make_uint4(e[2].x, e[2].y, e[3].x, e[3].y);
 }
 
-template <int HR, int W, int D>
+// TOK = 16: every lane holds its token's values in the MFMA operand layout
+// and encodes them there (16 tokens x 32 values of a step per wave, whatever
+// M is).  TOK = 4 or 8 (M <= TOK): the wave's lanes hold only the tokens
+// there are -- lane L takes the 16-byte chunk L % 16 of each step of tokens
+// L / 16 + 4 h, h < TOK / 4 -- so a wave encodes TOK instead of 16 tokens'
+// values (a wave64 VALU instruction takes four cycles: at K = 6144 the
+// 16-token encode of every workgroup cost ~5 us), and the codes reach the
+// MFMA layout through the wave's own LDS buffer.  The maximum, the scale and
+// the encode of each value are the same, so the codes, scales and output are
+// bitwise those of TOK = 16.
+template <int HR, int W, int D, int TOK>
 __global__ __launch_bounds__(W * 64) void linear_fused_kernel(FusedArgs a)
 {
+    static_assert(TOK == 4 || TOK == 8 || TOK == 16, "4, 8 or 16 tokens");
+    constexpr bool DENSE = TOK < 16;
+    constexpr int NCH = DENSE ? TOK / 4 : 1;  // token chunks per lane per step (dense)
     constexpr int KB = 32;          // bytes (codes) per lane per MFMA step
     constexpr int KSTEP = 4 * KB;   // 128 K elements per step
     constexpr int U = kFoldUnit / KSTEP;
@@ -80,19 +93,35 @@ __global__ __launch_bounds__(W * 64) void linear_fused_kernel(FusedArgs a)
     const int xrow = t * K;                   // element offset of the token's row
     const int wrowoff = wrow ? t * K : kOut;  // byte offset of the weight row
 
-    // 1. loads: the tokens (32 bf16 per step) first, then the weights (32
-    // bytes per step): the wait for the tokens (in issue order) then leaves
-    // the weight stream in flight while the maximum and the codes are formed
-    uint4 wb[D][2], xb[D][4];
+    // 1. loads: the tokens (32 bf16 per step; dense: NCH chunks of 8) first,
+    // then the weights (32 bytes per step): the wait for the tokens (in issue
+    // order) then leaves the weight stream in flight while the maximum and
+    // the codes are formed
+    const int dj = lane & 15;  // dense: this lane's chunk of each step
+    uint4 wb[D][2], xb[DENSE ? 1 : D][4], xd[DENSE ? D : 1][NCH];
+    if constexpr (DENSE) {
 #pragma unroll
-    for (int d = 0; d < D; ++d) {
-        const int e = (s0 + d) * KSTEP + koff;  // this lane's first element
+        for (int d = 0; d < D; ++d) {
+            const int e = (s0 + d) * KSTEP + dj * 8;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            xb[d][j] = __builtin_bit_cast(
-                uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                           rx, tok && d < ns && e + 8 * j < K ? 2 * (xrow + e + 8 * j) : kOut,
-                           0, 0));
+            for (int h = 0; h < NCH; ++h) {
+                const int tk = (lane >> 4) + 4 * h;
+                xd[d][h] = __builtin_bit_cast(
+                    uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                               rx, tk < M && d < ns && e < K ? 2 * (tk * K + e) : kOut, 0, 0));
+            }
+        }
+    } else {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            const int e = (s0 + d) * KSTEP + koff;  // this lane's first element
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                xb[d][j] = __builtin_bit_cast(
+                    uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                               rx, tok && d < ns && e + 8 * j < K ? 2 * (xrow + e + 8 * j) : kOut,
+                               0, 0));
+        }
     }
     // (empty asm with a memory clobber: the compiler keeps the three groups
     // -- token loads, weight loads, the math -- in this order)
@@ -113,33 +142,101 @@ __global__ __launch_bounds__(W * 64) void linear_fused_kernel(FusedArgs a)
 
     // 2. the token's maximum magnitude over K (on the bf16 bits: for finite
     // values the magnitude order is the integer order of the low 15 bits)
-    uint32_t mlo = 0, mhi = 0;
-#pragma unroll
-    for (int d = 0; d < D; ++d)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            absmax_bits8(xb[d][j], mlo, mhi);
-    float amax = absmax_bits_value(mlo, mhi);
-    amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
-    amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
     __shared__ float red_max[W][16];
-    if (lane < 16)
-        red_max[wave][lane] = amax;
-    __syncthreads();
+    float amax = 0.0f, sc = 0.0f;
+    float dsc[NCH];  // dense: the scales of this lane's tokens
+    if constexpr (DENSE) {
+        float dmax[NCH];
 #pragma unroll
-    for (int w = 0; w < W; ++w)
-        amax = fmaxf(amax, red_max[w][t]);
-    // 3. the quantizer's scale and codes
-    const float sc = amax / 448.0f;
+        for (int h = 0; h < NCH; ++h) {
+            uint32_t mlo = 0, mhi = 0;
+#pragma unroll
+            for (int d = 0; d < D; ++d)
+                absmax_bits8(xd[d][h], mlo, mhi);
+            float m = absmax_bits_value(mlo, mhi);
+            // over the 16 lanes of the token
+            m = fmaxf(m, __shfl_xor(m, 1, 64));
+            m = fmaxf(m, __shfl_xor(m, 2, 64));
+            m = fmaxf(m, __shfl_xor(m, 4, 64));
+            m = fmaxf(m, __shfl_xor(m, 8, 64));
+            dmax[h] = m;
+            if (dj == 0)
+                red_max[wave][(lane >> 4) + 4 * h] = m;
+        }
+        if (lane < 16 && lane >= TOK)
+            red_max[wave][lane] = 0.0f;
+        __syncthreads();
+#pragma unroll
+        for (int h = 0; h < NCH; ++h) {
+#pragma unroll
+            for (int w = 0; w < W; ++w)
+                dmax[h] = fmaxf(dmax[h], red_max[w][(lane >> 4) + 4 * h]);
+            dsc[h] = dmax[h] / 448.0f;
+        }
+        // the MFMA-layout lane's token scale (the epilogue's and workgroup
+        // 0's copy): the same maximum and quotient
+#pragma unroll
+        for (int w = 0; w < W; ++w)
+            amax = fmaxf(amax, red_max[w][t]);
+        sc = amax / 448.0f;
+    } else {
+        uint32_t mlo = 0, mhi = 0;
+#pragma unroll
+        for (int d = 0; d < D; ++d)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                absmax_bits8(xb[d][j], mlo, mhi);
+        amax = absmax_bits_value(mlo, mhi);
+        amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+        amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+        if (lane < 16)
+            red_max[wave][lane] = amax;
+        __syncthreads();
+#pragma unroll
+        for (int w = 0; w < W; ++w)
+            amax = fmaxf(amax, red_max[w][t]);
+        // 3. the quantizer's scale and codes
+        sc = amax / 448.0f;
+    }
     const Quot qd(sc);
+    // dense: the codes of this wave's steps, [step][token][128], written in
+    // the dense layout and read back in the MFMA operand layout
+    __shared__ __attribute__((aligned(16))) uint8_t cbuf[DENSE ? W : 1][DENSE ? D * TOK * 128 : 16];
+    if constexpr (DENSE) {
+#pragma unroll
+        for (int h = 0; h < NCH; ++h) {
+            const Quot dq(dsc[h]);
+            const int tk = (lane >> 4) + 4 * h;
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                if (d >= ns)
+                    break;
+                const uint2 c8 = encode8(xd[d][h], dq);
+                *(uint2*)&cbuf[wave][(d * TOK + tk) * 128 + dj * 8] = c8;
+                if (blockIdx.x == 0 && tk < M) {
+                    const int e = (s0 + d) * KSTEP + dj * 8;
+                    if (e < K)
+                        *(uint2*)(a.q + (size_t)tk * K + e) = c8;
+                }
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
     v4f acc = v4f{0, 0, 0, 0};
 #pragma unroll
     for (int d = 0; d < D; ++d) {
         if (d >= ns)
             break;
         uint4 code[2];
-        encode32(xb[d], qd, code);
-        if (blockIdx.x == 0 && t < M) {
+        if constexpr (DENSE) {
+            // this lane's 32 codes in the MFMA layout (tokens past TOK: zero)
+            const uint8_t* cp = &cbuf[wave][(d * TOK + (t < TOK ? t : 0)) * 128 + koff];
+            code[0] = t < TOK ? *(const uint4*)cp : make_uint4(0, 0, 0, 0);
+            code[1] = t < TOK ? *(const uint4*)(cp + 16) : make_uint4(0, 0, 0, 0);
+        } else {
+            encode32(xb[d], qd, code);
+        }
+        if (!DENSE && blockIdx.x == 0 && t < M) {
             const int e = (s0 + d) * KSTEP + koff;
             if (e < K) {
                 uint8_t* qp = a.q + (size_t)t * K + e;
@@ -202,23 +299,26 @@ int fused_steps_per_wave(int K, int W)
     return most;
 }
 
-template <int HR, int W, int D>
+template <int HR, int W, int D, int TOK>
 hipError_t launch_fused(const FusedArgs& a, hipStream_t stream)
 {
-    if (a.M < 1 || a.M > 16 || fused_steps_per_wave(a.K, W) > D || a.N > 0x7FFFFFF0 ||
+    if (a.M < 1 || a.M > TOK || fused_steps_per_wave(a.K, W) > D || a.N > 0x7FFFFFF0 ||
         2 * (int64_t)a.M * a.K > 0x7FFFFFF0 || (int64_t)HR * a.K > 0x7FFFFFF0)
         return hipErrorInvalidValue;  // (32-bit buffer offsets)
-    hipLaunchKernelGGL((linear_fused_kernel<HR, W, D>), dim3((a.N + HR - 1) / HR),
+    hipLaunchKernelGGL((linear_fused_kernel<HR, W, D, TOK>), dim3((a.N + HR - 1) / HR),
                        dim3(W * 64), 0, stream, a);
     return hipGetLastError();
 }
 
 }  // namespace qll
 
-#define QLL_FOR_EACH_FUSED(X) \
-    X(16, 8, 2) X(8, 8, 2) X(16, 8, 6) X(8, 8, 6) X(16, 16, 2) X(8, 16, 2) X(16, 16, 4) X(8, 16, 4)
-#define QLL_FUSED_INSTANTIATE(HR, W, D) \
-    template __global__ void qll::linear_fused_kernel<HR, W, D>(qll::FusedArgs);
+#define QLL_FOR_EACH_FUSED(X)                                                              \
+    X(16, 8, 2, 16) X(8, 8, 2, 16) X(16, 8, 6, 16) X(8, 8, 6, 16) X(16, 16, 2, 16)          \
+    X(8, 16, 2, 16) X(16, 16, 4, 16) X(8, 16, 4, 16)                                        \
+    X(16, 8, 2, 4) X(16, 8, 2, 8) X(8, 8, 6, 4) X(8, 8, 6, 8) X(8, 16, 4, 4) X(8, 16, 4, 8) \
+    X(16, 16, 2, 4) X(16, 16, 2, 8)
+#define QLL_FUSED_INSTANTIATE(HR, W, D, TOK) \
+    template __global__ void qll::linear_fused_kernel<HR, W, D, TOK>(qll::FusedArgs);
 QLL_FOR_EACH_FUSED(QLL_FUSED_INSTANTIATE)
 
 namespace qll {
@@ -229,8 +329,8 @@ namespace qll {
 // for K <= 2048, 6 for K <= 6144; W = 16: D = 2 for K <= 4096, 4 for
 // K <= 8192)
 #if !defined(__HIP_DEVICE_COMPILE__)
-#define QLL_FUSED_ENTRY(HR, W, D) \
-    {"f" #HR "x16_w" #W "_d" #D, HR, W, D, &launch_fused<HR, W, D>},
+#define QLL_FUSED_ENTRY(HR, W, D, TOK) \
+    {"f" #HR "x" #TOK "_w" #W "_d" #D, HR, W, D, TOK, &launch_fused<HR, W, D, TOK>},
 extern const FusedVariant kFusedVariants[] = {QLL_FOR_EACH_FUSED(QLL_FUSED_ENTRY)};
 extern const int kNumFusedVariants = sizeof(kFusedVariants) / sizeof(FusedVariant);
 #endif

@@ -100,6 +100,7 @@ struct FusedVariant {
     int hr;  // weight rows per workgroup
     int w;   // waves splitting K
     int d;   // K steps of 128 a wave holds in registers
+    int tok; // most tokens (M) it takes: 4, 8 or 16
     hipError_t (*launch)(const FusedArgs&, hipStream_t);
 };
 extern const FusedVariant kFusedVariants[];

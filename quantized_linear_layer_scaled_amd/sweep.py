@@ -154,8 +154,8 @@ def candidates(qll, op, M, N, K):
     for v in qll.variants(op):
         name = v["name"]
         if v.get("fused"):
-            # the fused linear layer: at most 16 tokens, K within its chunk
-            if M <= 16 and fused_steps(K, v["wp"]) <= v["ksteps"]:
+            # the fused linear layer: at most its tokens, K within its chunk
+            if M <= v["bq"] and fused_steps(K, v["wp"]) <= v["ksteps"]:
                 out.append((name, 1))
             continue
         if op == "bf16_bi" and name[0] == "k" and v["wp"] != 8:

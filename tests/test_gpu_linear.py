@@ -139,7 +139,7 @@ def test_fused_equals_two_launches_and_oracle(qll, N, K):
             with pytest.raises(qll.QllError):
                 qll.linear_fp8_dynamic(dev_bf16(x_all[:1]), dB, dsb, cfg=(v["name"], 1))
             continue
-        for M in (1, 3, 16):
+        for M in (1, 3, v["bq"]):
             x = x_all[:M].copy()
             qr, sr = oracle.quantize_fp8(x)
             ref, absref = oracle.gemm_fp8(qr, B, sr[:, 0].copy(), sb[:, 0].copy(), with_abs=True)
@@ -175,24 +175,32 @@ def test_fused_edge_tokens(qll):
     dB, dsb = dev_e4m3(B), dev(sb[:, 0].copy())
     x = edge_rows(K)[:16]
     qr, sr = oracle.quantize_fp8(x)
-    for name in ("f16x16_w8_d2", "f8x16_w16_d2"):
+    for name in ("f16x16_w8_d2", "f8x16_w16_d2", "f16x8_w8_d2", "f16x4_w16_d2"):
         v = next(t for t in qll.variants("fp8_dynamic") if t["name"] == name)
-        y, q, sa = qll.linear_fp8_dynamic(dev_bf16(x), dB, dsb, out_dtype="fp32", cfg=(name, 1))
-        y2, _, _ = qll.linear_fp8_dynamic(dev_bf16(x), dB, dsb, out_dtype="fp32",
-                                          cfg=(f"k{v['bp']}x16_w{v['wp']}", 1))
-        torch.cuda.synchronize()
-        assert np.array_equal(host_codes(q), qr), name
-        assert np.array_equal(sa.cpu().numpy()[:, 0].view(np.uint32), sr[:, 0].view(np.uint32)), name
-        assert torch.equal(y.view(torch.int32), y2.view(torch.int32)), name
-        huge = np.abs((x.astype(np.uint32) << 16).view(np.float32)).max(axis=1) > 1e30
-        assert bool(torch.isfinite(y[torch.from_numpy(~huge).cuda()]).all()), name
-        assert bool((y[0] == 0).all()) and bool((y[1] == 0).all()), name  # all-zero tokens
+        for r0 in range(0, len(x), v["bq"]):
+            # the edge rows in groups of the variant's tokens (the first group
+            # holds the all-zero tokens)
+            xs = x[r0:r0 + v["bq"]].copy()
+            y, q, sa = qll.linear_fp8_dynamic(dev_bf16(xs), dB, dsb, out_dtype="fp32",
+                                              cfg=(name, 1))
+            y2, _, _ = qll.linear_fp8_dynamic(dev_bf16(xs), dB, dsb, out_dtype="fp32",
+                                              cfg=(f"k{v['bp']}x16_w{v['wp']}", 1))
+            torch.cuda.synchronize()
+            assert np.array_equal(host_codes(q), qr[r0:r0 + v["bq"]]), (name, r0)
+            assert np.array_equal(sa.cpu().numpy()[:, 0].view(np.uint32),
+                                  sr[r0:r0 + v["bq"], 0].view(np.uint32)), (name, r0)
+            assert torch.equal(y.view(torch.int32), y2.view(torch.int32)), (name, r0)
+            huge = np.abs((xs.astype(np.uint32) << 16).view(np.float32)).max(axis=1) > 1e30
+            assert bool(torch.isfinite(y[torch.from_numpy(~huge).cuda()]).all()), (name, r0)
+            if r0 == 0:
+                assert bool((y[0] == 0).all()) and bool((y[1] == 0).all()), name  # zero tokens
 
 
-def test_fused_refuses_more_than_16_tokens(qll):
+def test_fused_refuses_more_than_its_tokens(qll):
     N, K = 520, 1040
     B = dev_e4m3(np.zeros((N, K), np.uint8))
     sb = torch.ones(N, device="cuda")
     x = dev_bf16(workloads.fp8_activations(17, K, key=(workloads.W_TEST, 52)))
-    with pytest.raises(qll.QllError, match="UNSUPPORTED"):
-        qll.linear_fp8_dynamic(x, B, sb, cfg=("f16x16_w8_d2", 1))
+    for name, tok in (("f16x16_w8_d2", 16), ("f16x8_w8_d2", 8), ("f16x4_w8_d2", 4)):
+        with pytest.raises(qll.QllError, match="UNSUPPORTED"):
+            qll.linear_fp8_dynamic(x[:tok + 1], B, sb, cfg=(name, 1))
