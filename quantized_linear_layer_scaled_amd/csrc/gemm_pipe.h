@@ -1208,8 +1208,10 @@ void gemm_pipe_kernel(GemmArgs a)
     gemm_pipe_body<OP, BP, BQ, WP, WQ, KSTAGE, STAGES, SPLITK, GROUPED, KGRP, 0>(a);
 }
 
-// One workgroup per CU: the register sets of the copies in flight take the
-// registers a second workgroup would need.
+// Register cap for WP x WQ / 4 waves per SIMD (one workgroup's share): the
+// register sets of the copies in flight take registers a second workgroup
+// would need (the 16-wave tiles run one workgroup per CU; 8-wave tiles that
+// stay under 128 registers can still pair).
 template <int OP, int BP, int BQ, int WP, int WQ, int KSTAGE, int RC, bool SPLITK>
 __global__ __launch_bounds__(WP* WQ * 64)
 __attribute__((amdgpu_waves_per_eu(WP * WQ >= 8 ? WP * WQ / 4 : 1)))
