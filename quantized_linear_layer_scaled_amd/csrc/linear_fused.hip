@@ -44,22 +44,56 @@ static __device__ __forceinline__ void encode32(const uint4* v, const Quot& d, u
     c[1] = make_uint4(e[2].x, e[2].y, e[3].x, e[3].y);
 }
 
+// V bf16 values (V / 2 words, V = 2 or 4) -> V e4m3 codes in one dword: the
+// per-value arithmetic of encode8 (quant_encode.h), so the same codes.
+template <int V>
+static __device__ __forceinline__ uint32_t encode_small(const uint32_t* w, const Quot& d)
+{
+    float f[V];
+#pragma unroll
+    for (int i = 0; i < V / 2; ++i) {
+        f[2 * i] = bf16_lo(w[i]);
+        f[2 * i + 1] = bf16_hi(w[i]);
+    }
+    if (d.s == 0.0f)
+        return 0u;
+    if (d.fast) {
+#pragma unroll
+        for (int i = 0; i < V; ++i)
+            f[i] = clamp448(d.by_reciprocal(f[i]));
+    } else {
+#pragma unroll
+        for (int i = 0; i < V; ++i)
+            f[i] = clamp448(f[i] / d.s);
+    }
+    int r = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+    if constexpr (V == 4)
+        r = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], r, true);
+    return (uint32_t)r;
+}
+
 // TOK = 16: every lane holds its token's values in the MFMA operand layout
 // and encodes them there (16 tokens x 32 values of a step per wave, whatever
-// M is).  TOK = 4 or 8 (M <= TOK): the wave's lanes hold only the tokens
-// there are -- lane L takes the 16-byte chunk L % 16 of each step of tokens
-// L / 16 + 4 h, h < TOK / 4 -- so a wave encodes TOK instead of 16 tokens'
-// values (a wave64 VALU instruction takes four cycles: at K = 6144 the
-// 16-token encode of every workgroup cost ~5 us), and the codes reach the
-// MFMA layout through the wave's own LDS buffer.  The maximum, the scale and
-// the encode of each value are the same, so the codes, scales and output are
-// bitwise those of TOK = 16.
+// M is).  TOK = 1, 2, 4 or 8 (M <= TOK): the wave's lanes hold only the
+// tokens there are -- VPL = 2 TOK values of a step per lane (8 from TOK = 4
+// on: 16-byte chunks), lane L taking run L % (128 / VPL) of token
+// L / (128 / VPL) + (64 VPL / 128) h -- so a wave encodes TOK instead of 16
+// tokens' values (a wave64 VALU instruction takes four cycles: at K = 6144
+// the 16-token encode of every workgroup cost ~5 us), and the codes reach
+// the MFMA layout through the wave's own LDS buffer.  The maximum, the scale
+// and the encode of each value are the same, so the codes, scales and output
+// are bitwise those of TOK = 16.
 template <int HR, int W, int D, int TOK>
 __global__ __launch_bounds__(W * 64) void linear_fused_kernel(FusedArgs a)
 {
-    static_assert(TOK == 4 || TOK == 8 || TOK == 16, "4, 8 or 16 tokens");
+    static_assert(TOK == 1 || TOK == 2 || TOK == 4 || TOK == 8 || TOK == 16,
+                  "1, 2, 4, 8 or 16 tokens");
     constexpr bool DENSE = TOK < 16;
-    constexpr int NCH = DENSE ? TOK / 4 : 1;  // token chunks per lane per step (dense)
+    constexpr int VPL = TOK >= 4 ? 8 : 2 * TOK;   // dense: values of a step per lane and run
+    constexpr int VW = VPL / 2;                   // ... in 32-bit words
+    constexpr int LPTOK = 128 / VPL;              // lanes per token
+    constexpr int TPP = 64 / LPTOK;               // tokens per pass over the lanes
+    constexpr int NCH = DENSE ? TOK / TPP : 1;    // passes (runs per lane per step)
     constexpr int KB = 32;          // bytes (codes) per lane per MFMA step
     constexpr int KSTEP = 4 * KB;   // 128 K elements per step
     constexpr int U = kFoldUnit / KSTEP;
@@ -97,18 +131,33 @@ __global__ __launch_bounds__(W * 64) void linear_fused_kernel(FusedArgs a)
     // then the weights (32 bytes per step): the wait for the tokens (in issue
     // order) then leaves the weight stream in flight while the maximum and
     // the codes are formed
-    const int dj = lane & 15;  // dense: this lane's chunk of each step
-    uint4 wb[D][2], xb[DENSE ? 1 : D][4], xd[DENSE ? D : 1][NCH];
+    const int dj = lane % LPTOK;  // dense: this lane's run of each step
+    const int dt = lane / LPTOK;  // dense: its token in the first pass
+    uint4 wb[D][2], xb[DENSE ? 1 : D][4];
+    uint32_t xd[DENSE ? D : 1][NCH][VW];
     if constexpr (DENSE) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
-            const int e = (s0 + d) * KSTEP + dj * 8;
+            const int e = (s0 + d) * KSTEP + dj * VPL;
 #pragma unroll
             for (int h = 0; h < NCH; ++h) {
-                const int tk = (lane >> 4) + 4 * h;
-                xd[d][h] = __builtin_bit_cast(
-                    uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                               rx, tk < M && d < ns && e < K ? 2 * (tk * K + e) : kOut, 0, 0));
+                const int tk = dt + TPP * h;
+                const int off = tk < M && d < ns && e < K ? 2 * (tk * K + e) : kOut;
+                if constexpr (VW == 4) {
+                    const uint4 v = __builtin_bit_cast(
+                        uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
+                    xd[d][h][0] = v.x;
+                    xd[d][h][1] = v.y;
+                    xd[d][h][2] = v.z;
+                    xd[d][h][3] = v.w;
+                } else if constexpr (VW == 2) {
+                    const uint2 v = __builtin_bit_cast(
+                        uint2, __builtin_amdgcn_raw_buffer_load_b64(rx, off, 0, 0));
+                    xd[d][h][0] = v.x;
+                    xd[d][h][1] = v.y;
+                } else {
+                    xd[d][h][0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rx, off, 0, 0);
+                }
             }
         }
     } else {
@@ -152,16 +201,19 @@ __global__ __launch_bounds__(W * 64) void linear_fused_kernel(FusedArgs a)
             uint32_t mlo = 0, mhi = 0;
 #pragma unroll
             for (int d = 0; d < D; ++d)
-                absmax_bits8(xd[d][h], mlo, mhi);
+#pragma unroll
+                for (int i = 0; i < VW; ++i) {
+                    mlo = max(mlo, xd[d][h][i] & 0x7FFFu);
+                    mhi = max(mhi, xd[d][h][i] & 0x7FFF0000u);
+                }
             float m = absmax_bits_value(mlo, mhi);
-            // over the 16 lanes of the token
-            m = fmaxf(m, __shfl_xor(m, 1, 64));
-            m = fmaxf(m, __shfl_xor(m, 2, 64));
-            m = fmaxf(m, __shfl_xor(m, 4, 64));
-            m = fmaxf(m, __shfl_xor(m, 8, 64));
+            // over the LPTOK lanes of the token
+#pragma unroll
+            for (int o = 1; o < LPTOK; o <<= 1)
+                m = fmaxf(m, __shfl_xor(m, o, 64));
             dmax[h] = m;
             if (dj == 0)
-                red_max[wave][(lane >> 4) + 4 * h] = m;
+                red_max[wave][dt + TPP * h] = m;
         }
         if (lane < 16 && lane >= TOK)
             red_max[wave][lane] = 0.0f;
@@ -170,7 +222,7 @@ __global__ __launch_bounds__(W * 64) void linear_fused_kernel(FusedArgs a)
         for (int h = 0; h < NCH; ++h) {
 #pragma unroll
             for (int w = 0; w < W; ++w)
-                dmax[h] = fmaxf(dmax[h], red_max[w][(lane >> 4) + 4 * h]);
+                dmax[h] = fmaxf(dmax[h], red_max[w][dt + TPP * h]);
             dsc[h] = dmax[h] / 448.0f;
         }
         // the MFMA-layout lane's token scale (the epilogue's and workgroup
@@ -206,17 +258,30 @@ __global__ __launch_bounds__(W * 64) void linear_fused_kernel(FusedArgs a)
 #pragma unroll
         for (int h = 0; h < NCH; ++h) {
             const Quot dq(dsc[h]);
-            const int tk = (lane >> 4) + 4 * h;
+            const int tk = dt + TPP * h;
 #pragma unroll
             for (int d = 0; d < D; ++d) {
                 if (d >= ns)
                     break;
-                const uint2 c8 = encode8(xd[d][h], dq);
-                *(uint2*)&cbuf[wave][(d * TOK + tk) * 128 + dj * 8] = c8;
-                if (blockIdx.x == 0 && tk < M) {
-                    const int e = (s0 + d) * KSTEP + dj * 8;
-                    if (e < K)
+                uint8_t* const cdst = &cbuf[wave][(d * TOK + tk) * 128 + dj * VPL];
+                const int e = (s0 + d) * KSTEP + dj * VPL;
+                const bool wq = blockIdx.x == 0 && tk < M && e < K;  // workgroup 0: the codes out
+                if constexpr (VPL == 8) {
+                    const uint2 c8 = encode8(make_uint4(xd[d][h][0], xd[d][h][1], xd[d][h][2],
+                                                        xd[d][h][3]), dq);
+                    *(uint2*)cdst = c8;
+                    if (wq)
                         *(uint2*)(a.q + (size_t)tk * K + e) = c8;
+                } else if constexpr (VPL == 4) {
+                    const uint32_t c4 = encode_small<4>(xd[d][h], dq);
+                    *(uint32_t*)cdst = c4;
+                    if (wq)
+                        *(uint32_t*)(a.q + (size_t)tk * K + e) = c4;
+                } else {
+                    const uint16_t c2 = (uint16_t)encode_small<2>(xd[d][h], dq);
+                    *(uint16_t*)cdst = c2;
+                    if (wq)
+                        *(uint16_t*)(a.q + (size_t)tk * K + e) = c2;
                 }
             }
         }
@@ -316,7 +381,7 @@ hipError_t launch_fused(const FusedArgs& a, hipStream_t stream)
     X(16, 8, 2, 16) X(8, 8, 2, 16) X(16, 8, 6, 16) X(8, 8, 6, 16) X(16, 16, 2, 16)          \
     X(8, 16, 2, 16) X(16, 16, 4, 16) X(8, 16, 4, 16)                                        \
     X(16, 8, 2, 4) X(16, 8, 2, 8) X(8, 8, 6, 4) X(8, 8, 6, 8) X(8, 16, 4, 4) X(8, 16, 4, 8) \
-    X(16, 16, 2, 4) X(16, 16, 2, 8)
+    X(16, 16, 2, 4) X(16, 16, 2, 8) X(16, 8, 2, 1) X(16, 8, 2, 2) X(8, 8, 6, 1) X(8, 8, 6, 2)
 #define QLL_FUSED_INSTANTIATE(HR, W, D, TOK) \
     template __global__ void qll::linear_fused_kernel<HR, W, D, TOK>(qll::FusedArgs);
 QLL_FOR_EACH_FUSED(QLL_FUSED_INSTANTIATE)
