@@ -259,10 +259,10 @@ int gemm_w4a16_ex(const void* A, const void* B, const float* scales, void* out,
  *     FP8 GEMM's choice);
  *   - fused (the indices after them, names "f<rows>x<tokens>_w<W>_d<steps>"):
  *     one launch whose workgroups quantize the tokens themselves inside the
- *     wave-split decode GEMM; M <= tokens (4, 8 or 16; the 4- and 8-token
- *     forms encode only that many tokens' values per wave) and K within the
- *     variant's register
- *     chunk (d steps of 128 per wave: K <= 2048 for d2, <= 6144 for d6),
+ *     wave-split decode GEMM; M <= tokens (1, 2, 4, 8 or 16; the forms
+ *     below 16 encode only that many tokens' values per wave) and K within
+ *     the variant's register chunk (d steps of 128 per wave: K <= 2048 for
+ *     d2, <= 6144 for d6),
  *     else QLL_ERR_UNSUPPORTED; no workspace.  Its output is bitwise that of
  *     the two launches with the 8-wave decode GEMM of the same rows per
  *     workgroup ("k16x16_w8" for f16, "k8x16_w8" for f8).

@@ -95,7 +95,8 @@ const FusedVariant* dyn_fused(int idx)
     return idx >= kNumVariantsFp8 && idx < dyn_count() ? &kFusedVariants[idx - kNumVariantsFp8]
                                                        : nullptr;
 }
-// a fused variant runs M <= 16 tokens and K up to its register chunk
+// a fused variant runs M up to its tokens (at most 16) and K up to its
+// register chunk
 bool fused_fits(const FusedVariant& f, int64_t M, int64_t K)
 {
     return M <= f.tok && K <= 0x3FFFFFFF && fused_steps_per_wave((int)K, f.w) <= f.d &&

@@ -6,7 +6,7 @@
 // launch and a round trip through memory).
 //
 // A workgroup owns HR weight rows (16, or 8 with the MFMA's other rows
-// zero) and all M <= 16 tokens, and its 8 waves split K on the grid of the
+// zero) and all M <= TOK <= 16 tokens, and its W waves split K on the grid of the
 // wave-split decode GEMM (gemm_skinny.h), so that the products are summed in
 // exactly that kernel's order:
 //   1. each wave issues the loads of its whole K chunk of weights (e4m3)

@@ -93,14 +93,14 @@ struct FusedArgs {
     float* sa;          // [M] (written by workgroup 0)
     void* out;          // [M][N]
     int out_dtype;
-    int M, N, K;        // M <= 16
+    int M, N, K;        // M <= the variant's tokens (<= 16)
 };
 struct FusedVariant {
     const char* name;
     int hr;  // weight rows per workgroup
     int w;   // waves splitting K
     int d;   // K steps of 128 a wave holds in registers
-    int tok; // most tokens (M) it takes: 4, 8 or 16
+    int tok; // most tokens (M) it takes: 1, 2, 4, 8 or 16
     hipError_t (*launch)(const FusedArgs&, hipStream_t);
 };
 extern const FusedVariant kFusedVariants[];
