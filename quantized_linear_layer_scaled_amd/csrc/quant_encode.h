@@ -10,9 +10,12 @@
 // instructions (one of them quarter rate), which dominates the arithmetic of
 // the quantizers.  Every value of a group shares s, so the kernels take the
 // reciprocal y = 1 / s once (correctly rounded) and per value form
-//     q0 = x * y,  r = fma(-q0, s, x),  q = fma(r, y, q0)
+//     q0 = x * y,  r = fma(q0, s, -x),  q = fma(-r, y, q0)
 // (one correction step from the exactly computed residual, Markstein's
-// division scheme).  For bf16 x and s = amax / 448 with amax a bf16 value,
+// division scheme, with the residual's sign flipped: r = -(x - q0 s) exactly,
+// since rounding is symmetric, and a zero x keeps its sign through both fmas,
+// so the quotient needs no copysign -- the negations are free operand
+// modifiers, the copysign was an instruction per value).  For bf16 x and s = amax / 448 with amax a bf16 value,
 // s in [2^-64, 2^64], this q equals the correctly rounded x / s whenever
 // either of them is at least 2^-10, and both are below 2^-10 otherwise, so
 // the e4m3 code (+-0 below 2^-10, sign from x) is the same; this was checked
@@ -65,8 +68,8 @@ struct Quot {
     __device__ __forceinline__ float by_reciprocal(float x) const
     {
         const float q0 = x * y;
-        const float r = __builtin_fmaf(-q0, s, x);
-        return __builtin_copysignf(__builtin_fmaf(r, y, q0), x);
+        const float r = __builtin_fmaf(q0, s, -x);
+        return __builtin_fmaf(-r, y, q0);
     }
 };
 

@@ -1,10 +1,14 @@
 /* Checks the reciprocal-based quotient of the FP8 quantizer kernels against
  * the correctly rounded fp32 division, over bf16 inputs:
  *   s = amax / 448 (amax a positive finite bf16 value, s in [2^-64, 2^64]),
- *   y = 1 / s, q0 = x * y, r = fma(-q0, s, x), q = copysign(fma(r, y, q0), x)
+ *   y = 1 / s, q0 = x * y, r = fma(q0, s, -x), q = fma(-r, y, q0)
  * for every bf16 x with |x| <= amax.  A pair passes if q equals x / s bit for
  * bit, or if both are below 2^-10 in magnitude with the sign of x (then both
- * encode to the same signed e4m3 zero).
+ * encode to the same signed e4m3 zero).  The residual is formed as q0 s - x
+ * and subtracted (r' = -r exactly, rounding being symmetric), so that a
+ * zero x keeps its sign through both fmas (-0 * y + -0 = -0) and no
+ * copysign is needed; the program also checks that q equals the
+ * copysign(fma(fma(-q0, s, x), y, q0), x) form bit for bit.
  * usage: quot_check <amax stride> ; prints "pairs <n> exact <e> bad <b>". */
 #include <math.h>
 #include <stdint.h>
@@ -42,9 +46,15 @@ int main(int argc, char** argv)
                 const float x = bf16(hx | (neg ? 0x8000u : 0u));
                 const float want = x / s;
                 const float q0 = x * y;
-                const float r = fmaf(-q0, s, x);
-                const float got = copysignf(fmaf(r, y, q0), x);
+                const float r = fmaf(q0, s, -x);
+                const float got = fmaf(-r, y, q0);
+                const float old = copysignf(fmaf(fmaf(-q0, s, x), y, q0), x);
                 ++pairs;
+                if (bits(got) != bits(old)) {
+                    if (++bad <= 5)
+                        printf("forms differ amax=%a x=%a %a %a\n", amax, x, got, old);
+                    continue;
+                }
                 if (bits(got) == bits(want)) {
                     ++exact;
                     continue;
