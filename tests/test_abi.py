@@ -460,6 +460,8 @@ def test_fp8_dynamic_table_rules(qll, tmp_path):
                                 "fp8_dynamic 4096 4096 8 f16x16_w16_d2 1\n"
                                 "fp8_dynamic 4096 2048 4 f16x4_w8_d2 1\n"
                                 "fp8_dynamic 2048 6144 8 f8x8_w8_d6 1\n"
+                                "fp8_dynamic 2048 6144 1 f8x1_w8_d6 1\n"
+                                "fp8_dynamic 4096 2048 2 f16x2_w8_d2 1\n"
                                 "fp8_dynamic 2048 6144 64 p64x64_w2x2_k128_s4 4\n")
     assert qll.table_validate(ok, SIG) == (0, "")
     for bad in ("fp8_dynamic 4096 2048 32 f16x16_w8_d2 1\n",   # beyond 16 tokens
@@ -468,6 +470,8 @@ def test_fp8_dynamic_table_rules(qll, tmp_path):
                 "fp8_dynamic 2048 6144 1 f16x16_w16_d2 1\n",   # (16 waves: 4 steps each)
                 "fp8_dynamic 4096 2048 8 f16x4_w8_d2 1\n",    # beyond its 4 tokens
                 "fp8_dynamic 2048 6144 16 f8x8_w8_d6 1\n",    # beyond its 8 tokens
+                "fp8_dynamic 4096 2048 2 f16x1_w8_d2 1\n",    # beyond its one token
+                "fp8_dynamic 4096 2048 4 f16x2_w8_d2 1\n",    # beyond its 2 tokens
                 "fp8 4096 2048 1 f16x16_w8_d2 1\n"):           # not an FP8 GEMM variant
         rc, why = qll.table_validate(write(tmp_path, head + bad), SIG)
         assert rc == 6, bad
