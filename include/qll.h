@@ -264,8 +264,8 @@ int gemm_w4a16_ex(const void* A, const void* B, const float* scales, void* out,
  *     the variant's register chunk (d steps of 128 per wave: K <= 2048 for
  *     d2, <= 6144 for d6),
  *     else QLL_ERR_UNSUPPORTED; no workspace.  Its output is bitwise that of
- *     the two launches with the 8-wave decode GEMM of the same rows per
- *     workgroup ("k16x16_w8" for f16, "k8x16_w8" for f8).
+ *     the two launches with the W-wave decode GEMM of the same rows per
+ *     workgroup ("k16x16_w8" for f16..._w8, "k8x16_w16" for f8..._w16).
  * Codes and scales are bitwise those of quantize_per_token_fp8 in both forms.
  *   x bf16 [M][K] (in); B e4m3 [N][K]; sb fp32 [N];
  *   q e4m3 [M][K] and sa fp32 [M] (out, required: the quantized activations);
