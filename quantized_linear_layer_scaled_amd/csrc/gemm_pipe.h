@@ -773,10 +773,11 @@ __device__ __forceinline__ void gemm_pipe_body(const GemmArgs& a)
     if constexpr (RC > 0) {
         // Register-path copies.  Stage s is loaded into register set s % RC
         // (RC stages ahead), written to LDS slot s % 2 during stage s - 1, and
-        // published by stage s - 1's barrier, after which its first step's
-        // fragments are read.  Slot s % 2 last held stage s - 2, whose
-        // fragments every wave had read (and waited for) before the barrier
-        // of stage s - 2 + 1, so the writes of stage s need no other wait.
+        // published by the barrier that ends stage s - 1, after which its
+        // first step's fragments are read.  Slot s % 2 last held stage s - 2,
+        // whose fragments every wave had read (and waited for) before the
+        // barrier that ended stage s - 2, and every wave writing stage s has
+        // passed that barrier, so the writes need no other wait.
         // The compiler tracks the loads (builtins) and waits for exactly the
         // set a ds_write needs; the only asm copies (the tile's scales) are
         // issued before them, so they only make such a wait stricter.
